@@ -1,0 +1,153 @@
+"""Seeded synthetic inputs for the GEMM workloads.
+
+This module only draws random numbers and encodes them (bf16 rounding, the
+MX e4m3 / e8m0 quantiser that prepares block-scaled operands).  It performs
+no part of the matrix product; the HIP library and the CPU oracle both take
+its bytes as given.
+
+All generation happens on the CPU with a ``torch.Generator`` seeded per
+workload: A is drawn first, then B, so one seed fixes both operands.
+
+MX encoding (input preparation, not the product).  The pages name
+block-scaled MMA ("Modern GPU Programming For MLSys - 书籍总结", sections
+2.4 and 2.6) but do not define the encodings; they are read from the public
+OCP Microscaling (MX) v1.0 specification: blocks of 32 consecutive
+reduction-axis elements share one E8M0 scale 2^(e-127); elements are OCP
+E4M3 ("fn": max finite 448, no infinity).  The shared exponent is
+floor(log2(amax)) - 8, where 8 is the largest exponent of E4M3, and each
+element is v / 2^X rounded to nearest-even E4M3 with saturation to +-448.
+An all-zero block gets scale code 127 and zero codes.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import torch
+
+MX_BLOCK = 32
+E4M3_MAX = 448.0
+E4M3_EMAX = 8
+
+
+def generator(seed: int) -> torch.Generator:
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    return g
+
+
+def uniform_bf16(shape, gen: torch.Generator) -> torch.Tensor:
+    """i.i.d. uniform[-1, 1) rounded (nearest-even) to bf16."""
+    return (torch.rand(shape, generator=gen, dtype=torch.float32) * 2.0 - 1.0).to(torch.bfloat16)
+
+
+def normal_bf16(shape, gen: torch.Generator) -> torch.Tensor:
+    """i.i.d. N(0, 1) rounded (nearest-even) to bf16."""
+    return torch.randn(shape, generator=gen, dtype=torch.float32).to(torch.bfloat16)
+
+
+def integer_bf16(shape, gen: torch.Generator, lo: int = -4, hi: int = 4) -> torch.Tensor:
+    """i.i.d. integers in [lo, hi] (exact in bf16)."""
+    return torch.randint(lo, hi + 1, shape, generator=gen, dtype=torch.int32).to(torch.bfloat16)
+
+
+def mx_quantize(x: torch.Tensor):
+    """Quantise a float32 [R, K] tensor (K a multiple of 32) into OCP MX form.
+
+    Returns (codes uint8 [R, K], scales uint8 [R, K/32]): e4m3 codes of
+    v / 2^X and the e8m0 code X + 127 of each 32-element block along K."""
+    if x.dim() != 2 or x.shape[1] % MX_BLOCK:
+        raise ValueError("x must be [R, K] with K a multiple of 32")
+    R, K = x.shape
+    blocks = x.float().reshape(R, K // MX_BLOCK, MX_BLOCK)
+    amax = blocks.abs().amax(dim=2)
+    # floor(log2(amax)) exactly: amax = m * 2^e with m in [0.5, 1)
+    _, e = torch.frexp(amax)
+    shared = e.to(torch.int32) - 1 - E4M3_EMAX
+    code = torch.clamp(shared + 127, 0, 254)
+    code = torch.where(amax == 0, torch.full_like(code, 127), code)
+    x_eff = (code - 127).to(torch.int32)
+    scaled = torch.ldexp(blocks, (-x_eff).unsqueeze(2).to(torch.float32))
+    scaled = torch.clamp(scaled, -E4M3_MAX, E4M3_MAX)
+    q = scaled.to(torch.float8_e4m3fn).view(torch.uint8).reshape(R, K)
+    return q.contiguous(), code.to(torch.uint8).contiguous()
+
+
+def integer_e4m3(shape, gen: torch.Generator, lo: int = -8, hi: int = 8) -> torch.Tensor:
+    """e4m3 codes of i.i.d. integers in [lo, hi] (all exact in e4m3)."""
+    v = torch.randint(lo, hi + 1, shape, generator=gen, dtype=torch.int32).to(torch.float32)
+    return v.to(torch.float8_e4m3fn).view(torch.uint8).contiguous()
+
+
+@dataclass
+class Bf16Problem:
+    """A (M,K) row-major bf16; B stored row-major as (K,N) when not
+    b_colmajor, else stored as (N,K) (column-major K x N)."""
+    name: str
+    M: int
+    N: int
+    K: int
+    A: torch.Tensor
+    B: torch.Tensor
+    b_colmajor: bool
+
+
+@dataclass
+class MxProblem:
+    """A (M,K) e4m3 codes row-major; B stored as (N,K) e4m3 codes (column-major
+    K x N); SA (M, K/32) and SB (N, K/32) e8m0 codes."""
+    name: str
+    M: int
+    N: int
+    K: int
+    A: torch.Tensor
+    B: torch.Tensor
+    SA: torch.Tensor
+    SB: torch.Tensor
+
+
+def bf16_problem(M: int, N: int, K: int, dist: str = "normal", b_colmajor: bool = False,
+                 seed: int = 0, name: str | None = None) -> Bf16Problem:
+    g = generator(seed)
+    draw = {"normal": normal_bf16, "uniform": uniform_bf16, "integer": integer_bf16}[dist]
+    A = draw((M, K), g)
+    B = draw((N, K) if b_colmajor else (K, N), g)
+    return Bf16Problem(name or f"bf16_{M}x{N}x{K}_{dist}", M, N, K, A.contiguous(), B.contiguous(),
+                       b_colmajor)
+
+
+def mx_problem(M: int, N: int, K: int, dist: str = "normal", seed: int = 0,
+               name: str | None = None) -> MxProblem:
+    g = generator(seed)
+    if dist == "normal":
+        A, SA = mx_quantize(torch.randn((M, K), generator=g, dtype=torch.float32))
+        B, SB = mx_quantize(torch.randn((N, K), generator=g, dtype=torch.float32))
+    elif dist == "integer":
+        A = integer_e4m3((M, K), g)
+        B = integer_e4m3((N, K), g)
+        SA = torch.full((M, K // MX_BLOCK), 127, dtype=torch.uint8)
+        SB = torch.full((N, K // MX_BLOCK), 127, dtype=torch.uint8)
+    else:
+        raise ValueError(dist)
+    return MxProblem(name or f"mx_{M}x{N}x{K}_{dist}", M, N, K, A, B, SA, SB)
+
+
+# The workloads: the single-tile case, the square cases, the ragged and skinny
+# cases, and the MX case.
+WORKLOADS = {
+    "tile128_nn": dict(kind="bf16", M=128, N=128, K=128, dist="uniform", b_colmajor=False),
+    "square4096_nn": dict(kind="bf16", M=4096, N=4096, K=4096, dist="normal", b_colmajor=False),
+    "square8192_nt": dict(kind="bf16", M=8192, N=8192, K=8192, dist="uniform", b_colmajor=True),
+    "ragged4001x3003x2050_nn": dict(kind="bf16", M=4001, N=3003, K=2050, dist="normal",
+                                    b_colmajor=False),
+    "skinny16x8192x8192_nn": dict(kind="bf16", M=16, N=8192, K=8192, dist="normal",
+                                  b_colmajor=False),
+    "mx8192": dict(kind="mx", M=8192, N=8192, K=8192, dist="normal"),
+}
+
+
+def workload(name: str, seed: int = 0):
+    w = dict(WORKLOADS[name])
+    kind = w.pop("kind")
+    if kind == "bf16":
+        return bf16_problem(seed=seed, name=name, **w)
+    return mx_problem(seed=seed, name=name, **w)

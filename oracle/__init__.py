@@ -1,0 +1,253 @@
+"""ctypes front end of the CPU oracle (``oracle/oracle.c``).
+
+TEST INFRASTRUCTURE ONLY: the test-suite, the smoke check and the benchmark's
+CPU-baseline leg may use this module; the GEMM library never does.  It shares
+no code with the HIP library and does not import it.
+
+Operands are passed as numpy arrays of raw codes (``uint16`` bf16 bits,
+``uint8`` e4m3 / e8m0 codes).  Any 2-D view works: the element strides of the
+view are handed to the C loops, so a transposed view of a column-major B is
+read in place.
+
+``Oracle(path)`` binds one compiled copy of oracle.c; the module-level
+functions use the default copy ``oracle/liboracle.so``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(_HERE, "oracle.c")
+LIBRARY = os.path.join(_HERE, "liboracle.so")
+
+_i64 = ctypes.c_int64
+_vp = ctypes.c_void_p
+
+
+def build(src: str = SOURCE, out: str = LIBRARY) -> str:
+    """Compile an oracle source with the host C compiler into a shared object."""
+    tmp = out + ".tmp"
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread",
+           "-ffp-contract=off", src, "-o", tmp, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
+def default_threads() -> int:
+    """Host threads the oracle uses: the cores this process may run on."""
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:  # pragma: no cover
+        return max(1, os.cpu_count() or 1)
+
+
+def _strides(x: np.ndarray):
+    return tuple(s // x.itemsize for s in x.strides)
+
+
+def _check2d(x: np.ndarray, dtype, name: str):
+    if not isinstance(x, np.ndarray) or x.ndim != 2 or x.dtype != dtype:
+        raise TypeError(f"{name} must be a 2-D numpy array of {np.dtype(dtype).name}")
+    for s in x.strides:
+        if s % x.itemsize:
+            raise ValueError(f"{name} strides must be whole elements")
+
+
+class Oracle:
+    """One loaded copy of the oracle library."""
+
+    def __init__(self, path: str = LIBRARY):
+        lib = ctypes.CDLL(path)
+        lib.oracle_bf16_value.restype = ctypes.c_double
+        lib.oracle_bf16_value.argtypes = [ctypes.c_uint16]
+        lib.oracle_e4m3_value.restype = ctypes.c_double
+        lib.oracle_e4m3_value.argtypes = [ctypes.c_uint8]
+        lib.oracle_e8m0_value.restype = ctypes.c_double
+        lib.oracle_e8m0_value.argtypes = [ctypes.c_uint8]
+        lib.oracle_tile_ledger.restype = ctypes.c_int
+        lib.oracle_tile_ledger.argtypes = [_i64] * 6 + [_vp, _vp]
+        lib.oracle_gemm_bf16.restype = ctypes.c_int
+        lib.oracle_gemm_bf16.argtypes = ([_i64] * 3 + [_vp, _i64, _i64] * 2
+                                         + [_vp, _vp, _i64, ctypes.c_int])
+        lib.oracle_gemm_bf16_at.restype = ctypes.c_int
+        lib.oracle_gemm_bf16_at.argtypes = ([_i64] * 3 + [_vp, _i64, _i64] * 2
+                                            + [_vp, _vp, _i64, _vp, _vp, ctypes.c_int])
+        lib.oracle_gemm_mxfp8.restype = ctypes.c_int
+        lib.oracle_gemm_mxfp8.argtypes = ([_i64] * 3 + [_vp, _i64, _i64] * 2 + [_vp, _i64] * 2
+                                          + [_vp, _vp, _i64, ctypes.c_int])
+        lib.oracle_gemm_mxfp8_at.restype = ctypes.c_int
+        lib.oracle_gemm_mxfp8_at.argtypes = ([_i64] * 3 + [_vp, _i64, _i64] * 2
+                                             + [_vp, _i64] * 2
+                                             + [_vp, _vp, _i64, _vp, _vp, ctypes.c_int])
+        self.lib = lib
+        self.path = path
+
+    # ---------------------------------------------------------------- decoders
+    def bf16_value(self, code: int) -> float:
+        return self.lib.oracle_bf16_value(int(code))
+
+    def e4m3_value(self, code: int) -> float:
+        return self.lib.oracle_e4m3_value(int(code))
+
+    def e8m0_value(self, code: int) -> float:
+        return self.lib.oracle_e8m0_value(int(code))
+
+    # ------------------------------------------------------------------ ledger
+    def tile_ledger(self, m_tile, n_tile, k_tile, element_bytes, stages, smem_limit) -> dict:
+        """Per-K-step tile ledger ("GPU 执行模型", section "Tile 小账本")."""
+        out = (ctypes.c_int64 * 4)()
+        ai = ctypes.c_double()
+        rc = self.lib.oracle_tile_ledger(m_tile, n_tile, k_tile, element_bytes, stages,
+                                         smem_limit, ctypes.cast(out, _vp),
+                                         ctypes.cast(ctypes.pointer(ai), _vp))
+        if rc != 0:
+            raise ValueError("tile sizes, element bytes and stages must all be positive")
+        return {"smem_bytes": out[0], "flops": out[1], "hbm_bytes": out[2],
+                "arithmetic_intensity": ai.value, "fits_smem": bool(out[3])}
+
+    # -------------------------------------------------------------------- GEMM
+    def gemm_bf16(self, A: np.ndarray, B: np.ndarray, nthreads: int | None = None):
+        """C = A @ B for bf16 bit arrays A (M,K) and B (K,N), any strides.
+
+        Returns (C, absC): binary64 arrays of shape (M,N); absC[i,j] is
+        sum_k |a(i,k)| |b(k,j)|.  Round C to float32 for the fp32 result."""
+        _check2d(A, np.uint16, "A")
+        _check2d(B, np.uint16, "B")
+        M, K = A.shape
+        K2, N = B.shape
+        if K2 != K:
+            raise ValueError("inner dimensions differ")
+        C = np.zeros((M, N), np.float64)
+        absC = np.zeros((M, N), np.float64)
+        ars, acs = _strides(A)
+        brs, bcs = _strides(B)
+        rc = self.lib.oracle_gemm_bf16(M, N, K, A.ctypes.data, ars, acs, B.ctypes.data, brs, bcs,
+                                       C.ctypes.data, absC.ctypes.data, N,
+                                       nthreads or default_threads())
+        if rc != 0:
+            raise ValueError(f"oracle_gemm_bf16 rejected its arguments ({rc})")
+        return C, absC
+
+    def gemm_bf16_at(self, A: np.ndarray, B: np.ndarray, rows, cols,
+                     nthreads: int | None = None):
+        """(A @ B)[rows[t], cols[t]] and the matching magnitude products."""
+        _check2d(A, np.uint16, "A")
+        _check2d(B, np.uint16, "B")
+        M, K = A.shape
+        K2, N = B.shape
+        if K2 != K:
+            raise ValueError("inner dimensions differ")
+        rows = np.ascontiguousarray(rows, np.int64)
+        cols = np.ascontiguousarray(cols, np.int64)
+        n = rows.size
+        out = np.zeros(n, np.float64)
+        absout = np.zeros(n, np.float64)
+        ars, acs = _strides(A)
+        brs, bcs = _strides(B)
+        rc = self.lib.oracle_gemm_bf16_at(M, N, K, A.ctypes.data, ars, acs, B.ctypes.data,
+                                          brs, bcs, rows.ctypes.data, cols.ctypes.data, n,
+                                          out.ctypes.data, absout.ctypes.data,
+                                          nthreads or default_threads())
+        if rc != 0:
+            raise ValueError(f"oracle_gemm_bf16_at rejected its arguments ({rc})")
+        return out, absout
+
+    @staticmethod
+    def _mx_args(A, B, SA, SB):
+        _check2d(A, np.uint8, "A")
+        _check2d(B, np.uint8, "B")
+        M, K = A.shape
+        K2, N = B.shape
+        if K2 != K:
+            raise ValueError("inner dimensions differ")
+        if K % 32:
+            raise ValueError("K must be a multiple of 32")
+        for S, rows_, name in ((SA, M, "SA"), (SB, N, "SB")):
+            _check2d(S, np.uint8, name)
+            if S.shape != (rows_, K // 32) or (K > 0 and S.strides[1] != 1):
+                raise ValueError(f"{name} must be ({rows_}, K/32) with unit column stride")
+        return M, N, K
+
+    def gemm_mxfp8(self, A, B, SA, SB, nthreads: int | None = None):
+        """MX block-scaled GEMM.  A (M,K) and B (K,N) e4m3 codes, SA (M,K/32)
+        and SB (N,K/32) e8m0 codes.  Returns (C, absC) in binary64."""
+        M, N, K = self._mx_args(A, B, SA, SB)
+        C = np.zeros((M, N), np.float64)
+        absC = np.zeros((M, N), np.float64)
+        ars, acs = _strides(A)
+        brs, bcs = _strides(B)
+        rc = self.lib.oracle_gemm_mxfp8(M, N, K, A.ctypes.data, ars, acs, B.ctypes.data, brs, bcs,
+                                        SA.ctypes.data, SA.strides[0], SB.ctypes.data,
+                                        SB.strides[0], C.ctypes.data, absC.ctypes.data, N,
+                                        nthreads or default_threads())
+        if rc != 0:
+            raise ValueError(f"oracle_gemm_mxfp8 rejected its arguments ({rc})")
+        return C, absC
+
+    def gemm_mxfp8_at(self, A, B, SA, SB, rows, cols, nthreads: int | None = None):
+        M, N, K = self._mx_args(A, B, SA, SB)
+        rows = np.ascontiguousarray(rows, np.int64)
+        cols = np.ascontiguousarray(cols, np.int64)
+        n = rows.size
+        out = np.zeros(n, np.float64)
+        absout = np.zeros(n, np.float64)
+        ars, acs = _strides(A)
+        brs, bcs = _strides(B)
+        rc = self.lib.oracle_gemm_mxfp8_at(M, N, K, A.ctypes.data, ars, acs, B.ctypes.data,
+                                           brs, bcs, SA.ctypes.data, SA.strides[0],
+                                           SB.ctypes.data, SB.strides[0], rows.ctypes.data,
+                                           cols.ctypes.data, n, out.ctypes.data,
+                                           absout.ctypes.data, nthreads or default_threads())
+        if rc != 0:
+            raise ValueError(f"oracle_gemm_mxfp8_at rejected its arguments ({rc})")
+        return out, absout
+
+
+_default: Oracle | None = None
+
+
+def default() -> Oracle:
+    """The oracle built from oracle.c in this directory (rebuilt if stale)."""
+    global _default
+    if _default is None:
+        if not os.path.exists(LIBRARY) or os.path.getmtime(LIBRARY) < os.path.getmtime(SOURCE):
+            build()
+        _default = Oracle(LIBRARY)
+    return _default
+
+
+def bf16_value(code):
+    return default().bf16_value(code)
+
+
+def e4m3_value(code):
+    return default().e4m3_value(code)
+
+
+def e8m0_value(code):
+    return default().e8m0_value(code)
+
+
+def tile_ledger(*args, **kw):
+    return default().tile_ledger(*args, **kw)
+
+
+def gemm_bf16(*args, **kw):
+    return default().gemm_bf16(*args, **kw)
+
+
+def gemm_bf16_at(*args, **kw):
+    return default().gemm_bf16_at(*args, **kw)
+
+
+def gemm_mxfp8(*args, **kw):
+    return default().gemm_mxfp8(*args, **kw)
+
+
+def gemm_mxfp8_at(*args, **kw):
+    return default().gemm_mxfp8_at(*args, **kw)
