@@ -1,0 +1,210 @@
+#!/usr/bin/env python3
+"""Throughput of the gfx950 GEMM library on one MI355X.
+
+One step = one call of the library on one batch of seeded synthetic
+operands already resident in HBM (the whole hot path: tile scheduler,
+global->LDS loads, MFMA loop, tails, fp32 epilogue, all inside one kernel
+launch).  The default workload is the square bf16 GEMM M=N=K=8192 with
+row-major A and column-major B (NT), entries uniform[-1, 1] rounded to bf16,
+seed 0, fp32 output.
+
+Prints ONE JSON line: TFLOP/s (2 M N K per step / time), the roofline block
+of the GEMM kernel (per-launch duration from HIP events on the launch
+stream, against the MI355X dense MFMA peak) and the CPU oracle timed on a
+bounded row sample of the same workload on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "GEMM TFLOP/s at 8192³ bf16 + % of MI355X dense MFMA peak (1 GPU)"
+PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}   # MI355X dense MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="square8192_nt")
+    ap.add_argument("--all", action="store_true", help="also print one line per other workload")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=256,
+                    help="rows of A in the oracle's timed sample")
+    return ap.parse_args()
+
+
+def operand_bytes(w) -> int:
+    if w["kind"] == "mx":
+        M, N, K = w["M"], w["N"], w["K"]
+        return M * K + N * K + (M + N) * (K // 32) + 4 * M * N
+    M, N, K = w["M"], w["N"], w["K"]
+    return 2 * (M * K + K * N) + 4 * M * N
+
+
+def bench_workload(name: str, steps: int, warmup: int):
+    import torch
+    import dense_gemm_mxfp8_amd as dg
+    from dense_gemm_mxfp8_amd import inputs
+
+    dev = torch.device("cuda:0")
+    w = inputs.WORKLOADS[name]
+    prob = inputs.workload(name, seed=0)
+    M, N, K = prob.M, prob.N, prob.K
+    stream = torch.cuda.current_stream(dev)
+    s = stream.cuda_stream
+    C = torch.empty((M, N), dtype=torch.float32, device=dev)
+    # A memory-bound problem whose B fits in the 256 MiB Infinity Cache is
+    # timed over rotating copies of its operands so that every step streams
+    # from HBM.
+    bytes_per_step = operand_bytes(w)
+    copies = 4 if bytes_per_step < 512 * 2**20 and 2 * M * N * K / bytes_per_step < 300 else 1
+    if w["kind"] == "mx":
+        ops = [(prob.A.to(dev), prob.B.to(dev), prob.SA.to(dev), prob.SB.to(dev))
+               for _ in range(copies)]
+
+        def step(i):
+            A, B, SA, SB = ops[i % copies]
+            rc = dg.gemm_mxfp8(M, N, K, A.data_ptr(), K, B.data_ptr(), K, SA.data_ptr(),
+                               SB.data_ptr(), C.data_ptr(), N, s)
+            if rc:
+                raise RuntimeError(dg.gemm_strerror(rc))
+        dtype, peak_key = "fp8(e4m3)+e8m0", "fp8"
+    else:
+        ops = [(prob.A.to(dev), prob.B.to(dev)) for _ in range(copies)]
+        fn = dg.gemm_bf16_nt if prob.b_colmajor else dg.gemm_bf16
+        ldb = K if prob.b_colmajor else N
+
+        def step(i):
+            A, B = ops[i % copies]
+            rc = fn(M, N, K, A.data_ptr(), K, B.data_ptr(), ldb, C.data_ptr(), N, s)
+            if rc:
+                raise RuntimeError(dg.gemm_strerror(rc))
+        dtype, peak_key = "bf16", "bf16"
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record(stream)
+        step(i)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = np.array([a.elapsed_time(b) for a, b in zip(starts, ends)])  # ms per launch
+    flops = 2.0 * M * N * K
+    ms_step = wall * 1e3 / steps
+    res = {
+        "workload": name, "M": M, "N": N, "K": K, "dtype": dtype, "peak_key": peak_key,
+        "flops": flops, "bytes": bytes_per_step, "ms_per_step": ms_step,
+        "kernel_ms_mean": float(per.mean()), "kernel_ms_median": float(np.median(per)),
+        "kernel_ms_p10": float(np.percentile(per, 10)),
+        "kernel_ms_p90": float(np.percentile(per, 90)),
+        "tflops": flops / (ms_step * 1e-3) / 1e12,
+        "layout": ("NT" if getattr(prob, "b_colmajor", True) else "NN"),
+        "dist": w.get("dist"), "operand_copies": copies,
+    }
+    return res, prob
+
+
+def cpu_baseline(prob, rows: int):
+    """The oracle, untouched, on rows [0, rows) of the same product."""
+    import torch
+    import oracle
+    from dense_gemm_mxfp8_amd.inputs import MxProblem
+
+    rows = min(rows, prob.M)
+    if isinstance(prob, MxProblem):
+        A = prob.A[:rows].numpy()
+        t0 = time.perf_counter()
+        oracle.gemm_mxfp8(A, prob.B.numpy().T, prob.SA[:rows].numpy(), prob.SB.numpy())
+    else:
+        A = prob.A[:rows].contiguous().view(torch.int16).numpy().view(np.uint16)
+        B = prob.B.view(torch.int16).numpy().view(np.uint16)
+        Bv = B.T if prob.b_colmajor else B
+        t0 = time.perf_counter()
+        oracle.gemm_bf16(A, Bv)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * rows * prob.N * prob.K
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.default_threads(),
+            "kind": "oracle",
+            "sample": f"rows 0..{rows - 1} of A against all of B ({rows}x{prob.N}x{prob.K}), "
+                      f"{dt:.2f} s wall"}
+
+
+def line(res, steps, warmup, cpu=None, headline=True):
+    peak = PEAK_TFLOPS[res["peak_key"]]
+    achieved = res["flops"] / (res["kernel_ms_mean"] * 1e-3) / 1e12
+    ai = res["flops"] / res["bytes"]
+    ridge = peak * 1e12 / (PEAK_HBM_GBS * 1e9)
+    if ai < ridge:
+        gbs = res["bytes"] / (res["kernel_ms_mean"] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}
+    else:
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None}
+    out = {
+        "metric": METRIC if headline else f"GEMM TFLOP/s ({res['workload']})",
+        "value": round(res["tflops"], 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": steps,
+        "warmup": warmup, "ms_per_step": round(res["ms_per_step"], 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": res["dtype"], "data": "synthetic",
+        "config": {"workload": res["workload"], "M": res["M"], "N": res["N"], "K": res["K"],
+                   "layout": res["layout"], "dist": res["dist"], "seed": 0,
+                   "output": "fp32", "parallelism": "single-gpu"},
+        "kernel_ms": {"mean": round(res["kernel_ms_mean"], 5),
+                      "median": round(res["kernel_ms_median"], 5),
+                      "p10": round(res["kernel_ms_p10"], 5), "p90": round(res["kernel_ms_p90"], 5)},
+        "pct_of_peak": round(100 * achieved / peak, 2),
+        "roofline": roof,
+    }
+    if cpu is not None:
+        out["cpu_baseline"] = cpu
+    return out
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the GEMM needs no collectives; multi-GPU sharding is a design note only).",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    names = [args.workload]
+    if args.all:
+        from dense_gemm_mxfp8_amd.inputs import WORKLOADS
+        names += [n for n in WORKLOADS if n != args.workload]
+    for i, name in enumerate(names):
+        print(f"[bench] {name}: warmup {args.warmup}, steps {args.steps}", file=sys.stderr,
+              flush=True)
+        res, prob = bench_workload(name, args.steps, args.warmup)
+        cpu = None
+        if i == 0 and not args.no_cpu_baseline:
+            print(f"[bench] oracle on {args.cpu_rows} rows", file=sys.stderr, flush=True)
+            cpu = cpu_baseline(prob, args.cpu_rows)
+        print(json.dumps(line(res, args.steps, args.warmup, cpu, headline=(i == 0))), flush=True)
+        del prob
+        torch.cuda.empty_cache()
+
+
+if __name__ == "__main__":
+    main()

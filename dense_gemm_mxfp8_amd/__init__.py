@@ -1,0 +1,159 @@
+"""Python binding of libgemm, the gfx950 dense GEMM library.
+
+The binding only marshals arguments: every step of the product runs in the
+HIP kernels of ``libgemm.so``.  PyTorch provides device memory and the current
+stream.  If the library is missing the calls raise; there is no fallback.
+
+Raw entry points mirror the C ABI of include/libgemm.h one to one
+(``gemm_bf16``, ``gemm_bf16_nt``, ``gemm_mxfp8``, ``gemm_strerror``,
+``gemm_version``) and take integers for pointers and the stream.  The tensor
+helpers ``bf16`` and ``mxfp8`` build those arguments from torch tensors.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(_PKG, "libgemm.so")
+
+GEMM_OK = 0
+GEMM_ERR_INVALID_ARG = -1
+GEMM_ERR_UNSUPPORTED = -2
+GEMM_ERR_LAUNCH = -3
+
+_lib = None
+_i64 = ctypes.c_int64
+_vp = ctypes.c_void_p
+
+
+def library() -> ctypes.CDLL:
+    """The loaded libgemm.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIBRARY):
+            raise RuntimeError(f"{LIBRARY} is missing: build it with "
+                               "`python -m dense_gemm_mxfp8_amd.build`")
+        lib = ctypes.CDLL(LIBRARY)
+        sig = [_i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp]
+        for name in ("gemm_bf16", "gemm_bf16_nt"):
+            fn = getattr(lib, name)
+            fn.restype = ctypes.c_int
+            fn.argtypes = sig
+        lib.gemm_mxfp8.restype = ctypes.c_int
+        lib.gemm_mxfp8.argtypes = [_i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _i64, _vp]
+        lib.gemm_strerror.restype = ctypes.c_char_p
+        lib.gemm_strerror.argtypes = [ctypes.c_int]
+        lib.gemm_version.restype = ctypes.c_int
+        lib.gemm_version.argtypes = []
+        _lib = lib
+    return _lib
+
+
+# ---------------------------------------------------------------- raw C ABI
+
+def gemm_bf16(M, N, K, A, lda, B, ldb, C, ldc, stream) -> int:
+    return library().gemm_bf16(M, N, K, A, lda, B, ldb, C, ldc, stream)
+
+
+def gemm_bf16_nt(M, N, K, A, lda, B, ldb, C, ldc, stream) -> int:
+    return library().gemm_bf16_nt(M, N, K, A, lda, B, ldb, C, ldc, stream)
+
+
+def gemm_mxfp8(M, N, K, A, lda, B, ldb, scaleA, scaleB, C, ldc, stream) -> int:
+    return library().gemm_mxfp8(M, N, K, A, lda, B, ldb, scaleA, scaleB, C, ldc, stream)
+
+
+def gemm_strerror(code: int) -> str:
+    return library().gemm_strerror(code).decode()
+
+
+def gemm_version() -> int:
+    return library().gemm_version()
+
+
+class GemmError(RuntimeError):
+    def __init__(self, code: int):
+        super().__init__(f"libgemm error {code}: {gemm_strerror(code)}")
+        self.code = code
+
+
+def _check(rc: int):
+    if rc != GEMM_OK:
+        raise GemmError(rc)
+
+
+# ---------------------------------------------------------------- tensor API
+
+def _stream(device):
+    import torch
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _out(out, M, N, device):
+    import torch
+    if out is None:
+        return torch.empty((M, N), dtype=torch.float32, device=device)
+    if out.shape != (M, N) or out.dtype != torch.float32 or (N > 1 and out.stride(1) != 1):
+        raise ValueError("out must be a float32 (M, N) tensor with unit column stride")
+    return out
+
+
+def bf16(A, B, out=None):
+    """C = A @ B in fp32 from bf16 CUDA tensors.
+
+    A: (M, K), row-major rows (unit column stride).  B: a (K, N) tensor that is
+    either row-major (unit column stride: ``gemm_bf16``) or column-major
+    (unit row stride, e.g. ``Bt.t()`` of an (N, K) tensor: ``gemm_bf16_nt``)."""
+    import torch
+    if A.dtype != torch.bfloat16 or B.dtype != torch.bfloat16:
+        raise TypeError("A and B must be bfloat16")
+    if A.dim() != 2 or B.dim() != 2 or A.shape[1] != B.shape[0]:
+        raise ValueError("A must be (M, K) and B (K, N)")
+    M, K = A.shape
+    N = B.shape[1]
+    if M > 0 and K > 1 and A.stride(1) != 1:
+        raise ValueError("A needs unit column stride")
+    lda = A.stride(0) if M > 1 else max(K, 1)
+    C = _out(out, M, N, A.device)
+    ldc = C.stride(0) if M > 1 else max(N, 1)
+    if N <= 1 or B.stride(1) == 1:
+        ldb = B.stride(0) if K > 1 else max(N, 1)
+        fn = gemm_bf16
+    elif B.stride(0) == 1:
+        ldb = B.stride(1)
+        fn = gemm_bf16_nt
+    else:
+        raise ValueError("B must have a unit stride along N (row-major) or K (column-major)")
+    _check(fn(M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, C.data_ptr(), ldc,
+              _stream(A.device)))
+    return C
+
+
+def mxfp8(A, SA, B, SB, out=None):
+    """MX block-scaled fp8 GEMM from uint8 CUDA tensors.
+
+    A: (M, K) E4M3 codes, row-major.  B: (N, K) E4M3 codes, i.e. the K x N
+    operand stored column-major.  SA: (M, K/32) and SB: (N, K/32) E8M0 codes,
+    dense row-major."""
+    import torch
+    for t, name in ((A, "A"), (B, "B"), (SA, "SA"), (SB, "SB")):
+        if t.dtype != torch.uint8 or t.dim() != 2:
+            raise TypeError(f"{name} must be a 2-D uint8 tensor")
+    M, K = A.shape
+    N = B.shape[0]
+    if B.shape[1] != K or K % 32:
+        raise ValueError("B must be (N, K) with K a multiple of 32")
+    if SA.shape != (M, K // 32) or SB.shape != (N, K // 32):
+        raise ValueError("scales must be (M, K/32) and (N, K/32)")
+    if not (SA.is_contiguous() and SB.is_contiguous()):
+        raise ValueError("scales must be dense row-major")
+    if (M > 0 and K > 1 and A.stride(1) != 1) or (N > 0 and K > 1 and B.stride(1) != 1):
+        raise ValueError("A and B need unit stride along K")
+    lda = A.stride(0) if M > 1 else max(K, 1)
+    ldb = B.stride(0) if N > 1 else max(K, 1)
+    C = _out(out, M, N, A.device)
+    ldc = C.stride(0) if M > 1 else max(N, 1)
+    _check(gemm_mxfp8(M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, SA.data_ptr(),
+                      SB.data_ptr(), C.data_ptr(), ldc, _stream(A.device)))
+    return C

@@ -1,0 +1,621 @@
+// libgemm.hip -- hand-written gfx950 (MI355X, CDNA4) GEMM kernels and the C ABI
+// declared in include/libgemm.h.
+//
+// C[M x N] = A[M x K] * B[K x N], fp32 accumulate and output, for bf16
+// operands (B row-major "NN" or column-major "NT") and for MX block-scaled fp8
+// operands (E4M3 codes, one E8M0 scale per 32 K-elements).  The problem
+// statement and the tile bookkeeping follow "GPU 执行模型" (sections
+// "Tile 的容量约束", "Tile 小账本", "流水与异步搬运", "正确性契约"); the
+// block-scaled MMA follows "Modern GPU Programming For MLSys - 书籍总结"
+// (sections 2.4 and 2.6).  The pages' kernel design targets NVIDIA Blackwell
+// (TMA, TMEM, mbarriers, clusters); none of that exists on CDNA4, so the
+// kernels here are built from gfx950 primitives instead:
+//
+//   * global->LDS tile loads: `global_load_lds_dwordx4` (16 bytes per lane,
+//     written straight into LDS, no VGPR round trip) when rows are 16-byte
+//     aligned, else predicated element loads through VGPRs;
+//   * LDS layout: every operand row holds 128 bytes of K (64 bf16 or 128
+//     fp8); its eight 16-byte chunks are XOR-swizzled with the row index so
+//     that the fragment reads of 8 consecutive rows hit 8 different bank
+//     groups;
+//   * two LDS stages: the loads of k-tile t+1 are in flight while the matrix
+//     cores work on k-tile t; one `s_waitcnt vmcnt(0)` + barrier per k-tile
+//     hands a stage from the loaders to the readers (the role the pages give
+//     to mbarrier phases);
+//   * matrix cores: v_mfma_f32_32x32x16_bf16 and
+//     v_mfma_scale_f32_32x32x64_f8f6f4 accumulating in registers;
+//   * row-major B (NN): `ds_read_b64_tr_b16` transposes 4x16 blocks on the way
+//     out of LDS so the B fragment arrives K-contiguous per lane;
+//   * a persistent grid with a static strided tile walk, grouped raster order
+//     and an XCD-aware remap of workgroup ids;
+//   * tails: rows past M / columns past N re-read the last valid row or
+//     column (finite data, never stored); the partial last k-tile is loaded
+//     with element predicates and zero fill;
+//   * epilogue: predicated fp32 stores straight from the accumulators.
+//
+// Lane layouts used below (checked on gfx950 with one-hot / random-integer
+// single-instruction tests):
+//   v_mfma_f32_32x32x16_bf16: lane l supplies A[l%32][8*(l/32) + j] and
+//     B[8*(l/32) + j][l%32], j = 0..7; accumulator register i of lane l is
+//     D[8*(i/4) + 4*(l/32) + i%4][l%32].
+//   v_mfma_scale_f32_32x32x64_f8f6f4 (fp8): lane l supplies row l%32; bytes
+//     0..15 hold k = 16*(l/32) + j, bytes 16..31 hold k = 32 + 16*(l/32) + j;
+//     the scale operand of lane q applies to row q%32, 32-block q/32.
+//   ds_read_b64_tr_b16: within each 16-lane group, output element e of lane i
+//     is element i%4 of the 8-byte word addressed by lane 4*e + i/4.
+
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+#include <stdint.h>
+#include <string.h>
+
+#include "libgemm.h"
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+#define LDS_AS __attribute__((address_space(3)))
+
+constexpr int kRowBytes = 128;   // bytes of K held per LDS operand row
+constexpr int kThreads = 256;    // 4 waves: a 2 x 2 arrangement of wave tiles
+constexpr int kWaves = 4;
+
+enum Kind { kBf16NT = 0, kBf16NN = 1, kMx = 2 };
+
+struct Args {
+    const uint8_t* A;
+    const uint8_t* B;
+    float* C;
+    const uint8_t* SA;
+    const uint8_t* SB;
+    int64_t lda, ldb, ldc;  // elements
+    int M, N, K;
+    int tiles_m, tiles_n, num_tiles, group_m;
+    int kt_full;   // k-tiles lying entirely inside K
+    int kt_total;  // kt_full, plus one if K leaves a partial tile
+    int sld;       // scale codes per row: K / 32
+    int xcd_remap; // 1: grid is a multiple of 8, spread tiles per XCD
+};
+
+// ---------------------------------------------------------------------------
+// Tile scheduler: static strided walk over tiles in grouped order.
+// ---------------------------------------------------------------------------
+
+__device__ inline int logical_block(const Args& a) {
+    int bid = blockIdx.x;
+    if (!a.xcd_remap) return bid;
+    // Workgroups are dispatched round-robin over the 8 XCDs; renumber them so
+    // that consecutive logical ids (and hence neighbouring tiles) share an XCD
+    // and its L2.
+    int per_xcd = gridDim.x >> 3;
+    return (bid & 7) * per_xcd + (bid >> 3);
+}
+
+__device__ inline void tile_coords(const Args& a, int t, int& tm, int& tn) {
+    int per_group = a.group_m * a.tiles_n;
+    int g = t / per_group;
+    int first = g * a.group_m;
+    int gsz = min(a.tiles_m - first, a.group_m);
+    int r = t - g * per_group;
+    tm = first + r % gsz;
+    tn = r / gsz;
+}
+
+__device__ inline void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Swizzled byte offset of 16-byte chunk `chunk` of K-contiguous LDS row `row`.
+__device__ inline int kc_offset(int row, int chunk) {
+    return row * kRowBytes + ((chunk ^ (row & 7)) << 4);
+}
+
+// Swizzled byte offset of element column n of k-row `k` in the N-contiguous
+// LDS tile of row-major B (NN); rows hold BN bf16.
+template <int BN>
+__device__ inline int nn_offset(int k, int n) {
+    int chunk = (n >> 3) ^ ((k & 3) << 1);
+    return k * (BN * 2) + (chunk << 4) + ((n & 7) << 1);
+}
+
+// ---------------------------------------------------------------------------
+// Global -> LDS loads.
+// ---------------------------------------------------------------------------
+
+// Direct (DMA-style) load of R K-contiguous rows x 128 bytes into LDS.  Each
+// wave instruction fills 1 KiB = 8 rows; lane i lands at byte 16*i of it, so
+// the lane fetches the logical chunk that the swizzle places there.
+template <int R>
+__device__ inline void load_kc_direct(uint8_t LDS_AS* dst, const uint8_t* g, int64_t ld_bytes,
+                                      int row0, int nrows, int64_t kbyte, int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < R / 32; ++i) {
+        int q = i * kWaves + wave;
+        int r = q * 8 + (lane >> 3);
+        int c = (lane & 7) ^ (lane >> 3);
+        int gr = min(row0 + r, nrows - 1);
+        const uint8_t* src = g + (int64_t)gr * ld_bytes + kbyte + c * 16;
+        __builtin_amdgcn_global_load_lds((const void*)src, (void LDS_AS*)(dst + q * 1024), 16, 0, 0);
+    }
+}
+
+// Predicated load of R K-contiguous rows through VGPRs: element k of row r is
+// read only if k < K (zero otherwise); rows past nrows re-read row nrows-1.
+template <int R, int ESZ>
+__device__ inline void load_kc_reg(uint8_t LDS_AS* dst, const uint8_t* g, int64_t ld, int row0,
+                                   int nrows, int k0, int K, int tid) {
+    constexpr int EPC = 16 / ESZ;  // elements per 16-byte chunk
+#pragma unroll
+    for (int i = 0; i < R * 8 / kThreads; ++i) {
+        int idx = i * kThreads + tid;
+        int r = idx >> 3, c = idx & 7;
+        int gr = min(row0 + r, nrows - 1);
+        int kb = k0 + c * EPC;
+        const uint8_t* src = g + ((int64_t)gr * ld + kb) * ESZ;
+        i32x4 v = {0, 0, 0, 0};
+        if (kb + EPC <= K && (((uintptr_t)src) & 3) == 0) {
+            const int* s = (const int*)src;
+            v[0] = s[0]; v[1] = s[1]; v[2] = s[2]; v[3] = s[3];
+        } else {
+            uint8_t b[16];
+#pragma unroll
+            for (int e = 0; e < 16; ++e) b[e] = 0;
+            if (ESZ == 2) {
+                const uint16_t* s = (const uint16_t*)src;
+#pragma unroll
+                for (int e = 0; e < EPC; ++e) {
+                    uint16_t x = (kb + e < K) ? s[e] : (uint16_t)0;
+                    b[2 * e] = (uint8_t)x;
+                    b[2 * e + 1] = (uint8_t)(x >> 8);
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < EPC; ++e) b[e] = (kb + e < K) ? src[e] : (uint8_t)0;
+            }
+            memcpy(&v, b, 16);
+        }
+        *(i32x4 LDS_AS*)(dst + kc_offset(r, c)) = v;
+    }
+}
+
+// Direct load of the 64 x BN bf16 tile of row-major B (rows are k).  Requires
+// N % 8 == 0; chunks past N re-read the last full chunk (never stored).
+template <int BN>
+__device__ inline void load_nn_direct(uint8_t LDS_AS* dst, const uint8_t* g, int64_t ldb, int k0,
+                                      int n0, int N, int wave, int lane) {
+    constexpr int kRowB = BN * 2;
+    constexpr int kLoads = 64 * kRowB / 1024;
+#pragma unroll
+    for (int i = 0; i < kLoads / kWaves; ++i) {
+        int q = i * kWaves + wave;
+        int off = q * 1024 + lane * 16;
+        int kk = off / kRowB;
+        int p = (off % kRowB) >> 4;
+        int c = p ^ ((kk & 3) << 1);
+        int n = min(n0 + c * 8, N - 8);
+        const uint8_t* src = g + ((int64_t)(k0 + kk) * ldb + n) * 2;
+        __builtin_amdgcn_global_load_lds((const void*)src, (void LDS_AS*)(dst + q * 1024), 16, 0, 0);
+    }
+}
+
+// Predicated load of the 64 x BN bf16 tile of row-major B through VGPRs.
+template <int BN>
+__device__ inline void load_nn_reg(uint8_t LDS_AS* dst, const uint8_t* g, int64_t ldb, int k0,
+                                   int K, int n0, int N, int tid) {
+    constexpr int kChunks = 64 * BN / 8;
+#pragma unroll
+    for (int i = 0; i < kChunks / kThreads; ++i) {
+        int idx = i * kThreads + tid;
+        int kk = idx / (BN / 8);
+        int c = idx % (BN / 8);
+        int k = k0 + kk;
+        int nb = n0 + c * 8;
+        i32x4 v = {0, 0, 0, 0};
+        if (k < K) {
+            const uint16_t* s = (const uint16_t*)(g + ((int64_t)k * ldb + nb) * 2);
+            if (nb + 8 <= N && (((uintptr_t)s) & 3) == 0) {
+                const int* s4 = (const int*)s;
+                v[0] = s4[0]; v[1] = s4[1]; v[2] = s4[2]; v[3] = s4[3];
+            } else {
+                uint16_t h[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) h[e] = (nb + e < N) ? s[e] : (uint16_t)0;
+                memcpy(&v, h, 16);
+            }
+        }
+        *(i32x4 LDS_AS*)(dst + nn_offset<BN>(kk, c * 8)) = v;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// The GEMM kernel.
+// ---------------------------------------------------------------------------
+
+template <int BM, int BN, int KIND, bool DIRECT>
+__global__ __launch_bounds__(kThreads, (BM * BN >= 256 * 256) ? 1 : 2) void gemm_kernel(Args a) {
+    constexpr int ESZ = (KIND == kMx) ? 1 : 2;        // operand element bytes
+    constexpr int BK = kRowBytes / ESZ;                // K elements per k-tile
+    constexpr int WTM = BM / 2, WTN = BN / 2;          // wave tile
+    constexpr int MB = WTM / 32, NB = WTN / 32;        // 32x32 MFMA blocks per wave
+    constexpr int A_BYTES = BM * kRowBytes;
+    constexpr int B_BYTES = BN * kRowBytes;
+    constexpr int STAGE = A_BYTES + B_BYTES;
+
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int64_t lda_b = a.lda * ESZ;
+    const int64_t ldb_b = a.ldb * ESZ;
+
+    const int G = gridDim.x;
+    for (int t = logical_block(a); t < a.num_tiles; t += G) {
+        int tm, tn;
+        tile_coords(a, t, tm, tn);
+        const int m0 = tm * BM, n0 = tn * BN;
+
+        f32x16 acc[MB][NB];
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
+#pragma unroll
+            for (int j = 0; j < NB; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+        // MX scales of the current and the next k-tile, one dword (four
+        // 32-blocks) per MFMA row block, pre-shifted per lane half.
+        int sa_cur[MB], sb_cur[NB], sa_nxt[MB], sb_nxt[NB];
+
+        auto load_scales = [&](int kt, int* sa, int* sb) {
+            if constexpr (KIND == kMx) {
+                const int h = lane >> 5;
+#pragma unroll
+                for (int i = 0; i < MB; ++i) {
+                    int row = min(m0 + wm * WTM + i * 32 + (lane & 31), a.M - 1);
+                    const uint8_t* p = a.SA + (int64_t)row * a.sld + kt * 4;
+                    uint32_t w = 0;
+#pragma unroll
+                    for (int b = 0; b < 4; ++b)
+                        w |= (uint32_t)((kt * 4 + b < a.sld) ? p[b] : 127) << (8 * b);
+                    sa[i] = (int)(h ? (w >> 8) : w);
+                }
+#pragma unroll
+                for (int j = 0; j < NB; ++j) {
+                    int col = min(n0 + wn * WTN + j * 32 + (lane & 31), a.N - 1);
+                    const uint8_t* p = a.SB + (int64_t)col * a.sld + kt * 4;
+                    uint32_t w = 0;
+#pragma unroll
+                    for (int b = 0; b < 4; ++b)
+                        w |= (uint32_t)((kt * 4 + b < a.sld) ? p[b] : 127) << (8 * b);
+                    sb[j] = (int)(h ? (w >> 8) : w);
+                }
+            }
+        };
+
+        auto load_stage = [&](int kt, int buf) {
+            uint8_t LDS_AS* As = (uint8_t LDS_AS*)smem + buf * STAGE;
+            uint8_t LDS_AS* Bs = As + A_BYTES;
+            const int k0 = kt * BK;
+            if (DIRECT && kt < a.kt_full) {
+                load_kc_direct<BM>(As, a.A, lda_b, m0, a.M, (int64_t)k0 * ESZ, wave, lane);
+                if constexpr (KIND == kBf16NN)
+                    load_nn_direct<BN>(Bs, a.B, a.ldb, k0, n0, a.N, wave, lane);
+                else
+                    load_kc_direct<BN>(Bs, a.B, ldb_b, n0, a.N, (int64_t)k0 * ESZ, wave, lane);
+            } else {
+                load_kc_reg<BM, ESZ>(As, a.A, a.lda, m0, a.M, k0, a.K, tid);
+                if constexpr (KIND == kBf16NN)
+                    load_nn_reg<BN>(Bs, a.B, a.ldb, k0, a.K, n0, a.N, tid);
+                else
+                    load_kc_reg<BN, ESZ>(Bs, a.B, a.ldb, n0, a.N, k0, a.K, tid);
+            }
+        };
+
+        auto compute = [&](int buf) {
+            const uint8_t LDS_AS* As = (const uint8_t LDS_AS*)smem + buf * STAGE;
+            const uint8_t LDS_AS* Bs = As + A_BYTES;
+            if constexpr (KIND == kMx) {
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    i32x8 af[MB], bfr[NB];
+                    const int h = lane >> 5;
+#pragma unroll
+                    for (int i = 0; i < MB; ++i) {
+                        int row = wm * WTM + i * 32 + (lane & 31);
+                        i32x4 lo = *(const i32x4 LDS_AS*)(As + kc_offset(row, 4 * s + h));
+                        i32x4 hi = *(const i32x4 LDS_AS*)(As + kc_offset(row, 4 * s + 2 + h));
+                        af[i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                    }
+#pragma unroll
+                    for (int j = 0; j < NB; ++j) {
+                        int row = wn * WTN + j * 32 + (lane & 31);
+                        i32x4 lo = *(const i32x4 LDS_AS*)(Bs + kc_offset(row, 4 * s + h));
+                        i32x4 hi = *(const i32x4 LDS_AS*)(Bs + kc_offset(row, 4 * s + 2 + h));
+                        bfr[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                    }
+#pragma unroll
+                    for (int i = 0; i < MB; ++i)
+#pragma unroll
+                        for (int j = 0; j < NB; ++j) {
+                            if (s == 0)
+                                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                                    af[i], bfr[j], acc[i][j], 0, 0, 0, sa_cur[i], 0, sb_cur[j]);
+                            else
+                                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                                    af[i], bfr[j], acc[i][j], 0, 0, 2, sa_cur[i], 2, sb_cur[j]);
+                        }
+                }
+            } else {
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) {
+                    bf16x8 af[MB], bfr[NB];
+                    const int chunk = 2 * ks + (lane >> 5);
+#pragma unroll
+                    for (int i = 0; i < MB; ++i) {
+                        int row = wm * WTM + i * 32 + (lane & 31);
+                        af[i] = *(const bf16x8 LDS_AS*)(As + kc_offset(row, chunk));
+                    }
+                    if constexpr (KIND == kBf16NN) {
+                        const int g = lane >> 4, li = lane & 15;
+#pragma unroll
+                        for (int j = 0; j < NB; ++j) {
+                            int n = wn * WTN + j * 32 + 16 * (g & 1) + 4 * (li & 3);
+                            int k = ks * 16 + 8 * (g >> 1) + (li >> 2);
+                            bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                                (bf16x4 LDS_AS*)(Bs + nn_offset<BN>(k, n)));
+                            bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                                (bf16x4 LDS_AS*)(Bs + nn_offset<BN>(k + 4, n)));
+                            bfr[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                        }
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < NB; ++j) {
+                            int row = wn * WTN + j * 32 + (lane & 31);
+                            bfr[j] = *(const bf16x8 LDS_AS*)(Bs + kc_offset(row, chunk));
+                        }
+                    }
+#pragma unroll
+                    for (int i = 0; i < MB; ++i)
+#pragma unroll
+                        for (int j = 0; j < NB; ++j)
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j],
+                                                                                acc[i][j], 0, 0, 0);
+                }
+            }
+        };
+
+        // Prologue: stage 0.
+        load_scales(0, sa_cur, sb_cur);
+        load_stage(0, 0);
+        wait_vmem();
+        __syncthreads();
+
+        for (int kt = 0; kt < a.kt_total; ++kt) {
+            const bool more = kt + 1 < a.kt_total;
+            if (more) {
+                load_stage(kt + 1, (kt + 1) & 1);
+                load_scales(kt + 1, sa_nxt, sb_nxt);
+            }
+            compute(kt & 1);
+            wait_vmem();
+            __syncthreads();
+            if constexpr (KIND == kMx) {
+                if (more) {
+#pragma unroll
+                    for (int i = 0; i < MB; ++i) sa_cur[i] = sa_nxt[i];
+#pragma unroll
+                    for (int j = 0; j < NB; ++j) sb_cur[j] = sb_nxt[j];
+                }
+            }
+        }
+
+        // Epilogue: predicated fp32 stores of the accumulators.
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
+#pragma unroll
+            for (int j = 0; j < NB; ++j) {
+                const int col = n0 + wn * WTN + j * 32 + (lane & 31);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int row = m0 + wm * WTM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                    if (row < a.M && col < a.N) a.C[(int64_t)row * a.ldc + col] = acc[i][j][r];
+                }
+            }
+    }
+}
+
+// C[0:M, 0:N] := 0 (the K == 0 product).
+__global__ void zero_fill_kernel(float* C, int64_t ldc, int M, int N) {
+    int64_t total = (int64_t)M * N;
+    for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+         idx += (int64_t)gridDim.x * blockDim.x) {
+        int64_t r = idx / N, c = idx - r * N;
+        C[r * ldc + c] = 0.0f;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Host side.
+// ---------------------------------------------------------------------------
+
+struct DeviceInfo {
+    int checked;
+    int supported;
+    int cus;
+};
+
+constexpr int kMaxDevices = 64;
+DeviceInfo g_devices[kMaxDevices];
+std::mutex g_devices_mutex;
+
+int device_info(DeviceInfo* out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return GEMM_ERR_UNSUPPORTED;
+    }
+    std::lock_guard<std::mutex> lock(g_devices_mutex);
+    DeviceInfo& d = g_devices[dev];
+    if (!d.checked) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+            (void)hipGetLastError();
+            return GEMM_ERR_UNSUPPORTED;
+        }
+        d.supported = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+        d.cus = prop.multiProcessorCount;
+        d.checked = 1;
+    }
+    *out = d;
+    return d.supported ? GEMM_OK : GEMM_ERR_UNSUPPORTED;
+}
+
+bool aligned16(const void* p) { return (((uintptr_t)p) & 15) == 0; }
+
+template <int BM, int BN, int KIND, bool DIRECT>
+int launch(Args a, int cus, hipStream_t stream) {
+    a.tiles_m = (a.M + BM - 1) / BM;
+    a.tiles_n = (a.N + BN - 1) / BN;
+    a.num_tiles = a.tiles_m * a.tiles_n;
+    a.group_m = a.tiles_m < 8 ? a.tiles_m : 8;
+    const int occupancy = (BM * BN >= 256 * 256) ? 1 : 2;
+    int grid = cus * occupancy;
+    if (grid > a.num_tiles) grid = a.num_tiles;
+    if (grid >= 8) grid -= grid % 8;
+    a.xcd_remap = (grid % 8 == 0) ? 1 : 0;
+    hipLaunchKernelGGL((gemm_kernel<BM, BN, KIND, DIRECT>), dim3(grid), dim3(kThreads), 0, stream, a);
+    return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
+}
+
+int zero_fill(float* C, int64_t ldc, int64_t M, int64_t N, hipStream_t stream) {
+    int64_t total = M * N;
+    int64_t blocks = (total + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    hipLaunchKernelGGL(zero_fill_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, C, ldc, (int)M,
+                       (int)N);
+    return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
+}
+
+// Common argument checks; returns GEMM_OK to proceed, 1 for "nothing to do".
+int check_common(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+                 int64_t ldb, int64_t ldb_min, const float* C, int64_t ldc) {
+    if (M < 0 || N < 0 || K < 0) return GEMM_ERR_INVALID_ARG;
+    if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return GEMM_ERR_INVALID_ARG;
+    if (M == 0 || N == 0) return 1;
+    if (C == nullptr || ldc < N) return GEMM_ERR_INVALID_ARG;
+    if (K > 0) {
+        if (A == nullptr || B == nullptr) return GEMM_ERR_INVALID_ARG;
+        if (lda < K || ldb < ldb_min) return GEMM_ERR_INVALID_ARG;
+    }
+    return GEMM_OK;
+}
+
+Args make_args(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+               int64_t ldb, float* C, int64_t ldc, int bk) {
+    Args a;
+    memset(&a, 0, sizeof a);
+    a.A = (const uint8_t*)A;
+    a.B = (const uint8_t*)B;
+    a.C = C;
+    a.lda = lda;
+    a.ldb = ldb;
+    a.ldc = ldc;
+    a.M = (int)M;
+    a.N = (int)N;
+    a.K = (int)K;
+    a.kt_full = (int)(K / bk);
+    a.kt_total = (int)((K + bk - 1) / bk);
+    return a;
+}
+
+// Tile choice: 256 x 256 when that still gives every CU at least ~3/4 of a
+// tile's worth of work, else 128 x 128 (two workgroups per CU).
+bool use_big_tiles(int64_t M, int64_t N, int cus) {
+    int64_t big = ((M + 255) / 256) * ((N + 255) / 256);
+    return big * 4 >= (int64_t)cus * 3;
+}
+
+int bf16_dispatch(bool nt, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                  const void* B, int64_t ldb, float* C, int64_t ldc, void* stream) {
+    int rc = check_common(M, N, K, A, lda, B, ldb, nt ? K : N, C, ldc);
+    if (rc == 1) return GEMM_OK;
+    if (rc != GEMM_OK) return rc;
+    DeviceInfo dev;
+    rc = device_info(&dev);
+    if (rc != GEMM_OK) return rc;
+    hipStream_t s = (hipStream_t)stream;
+    if (K == 0) return zero_fill(C, ldc, M, N, s);
+    Args a = make_args(M, N, K, A, lda, B, ldb, C, ldc, 64);
+    const bool direct = aligned16(A) && aligned16(B) && (lda % 8 == 0) && (ldb % 8 == 0) &&
+                        (nt || (N % 8 == 0));
+    const bool big = use_big_tiles(M, N, dev.cus);
+    if (nt) {
+        if (big) return direct ? launch<256, 256, kBf16NT, true>(a, dev.cus, s)
+                               : launch<256, 256, kBf16NT, false>(a, dev.cus, s);
+        return direct ? launch<128, 128, kBf16NT, true>(a, dev.cus, s)
+                      : launch<128, 128, kBf16NT, false>(a, dev.cus, s);
+    }
+    if (big) return direct ? launch<256, 256, kBf16NN, true>(a, dev.cus, s)
+                           : launch<256, 256, kBf16NN, false>(a, dev.cus, s);
+    return direct ? launch<128, 128, kBf16NN, true>(a, dev.cus, s)
+                  : launch<128, 128, kBf16NN, false>(a, dev.cus, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+int gemm_bf16(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+              int64_t ldb, float* C, int64_t ldc, void* stream) {
+    return bf16_dispatch(false, M, N, K, A, lda, B, ldb, C, ldc, stream);
+}
+
+int gemm_bf16_nt(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+                 int64_t ldb, float* C, int64_t ldc, void* stream) {
+    return bf16_dispatch(true, M, N, K, A, lda, B, ldb, C, ldc, stream);
+}
+
+int gemm_mxfp8(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+               int64_t ldb, const uint8_t* scaleA, const uint8_t* scaleB, float* C, int64_t ldc,
+               void* stream) {
+    int rc = check_common(M, N, K, A, lda, B, ldb, K, C, ldc);
+    if (rc == 1) return GEMM_OK;
+    if (rc != GEMM_OK) return rc;
+    if (K % 32 != 0) return GEMM_ERR_INVALID_ARG;
+    if (K > 0 && (scaleA == nullptr || scaleB == nullptr)) return GEMM_ERR_INVALID_ARG;
+    DeviceInfo dev;
+    rc = device_info(&dev);
+    if (rc != GEMM_OK) return rc;
+    hipStream_t s = (hipStream_t)stream;
+    if (K == 0) return zero_fill(C, ldc, M, N, s);
+    Args a = make_args(M, N, K, A, lda, B, ldb, C, ldc, 128);
+    a.SA = scaleA;
+    a.SB = scaleB;
+    a.sld = (int)(K / 32);
+    const bool direct = aligned16(A) && aligned16(B) && (lda % 16 == 0) && (ldb % 16 == 0);
+    if (use_big_tiles(M, N, dev.cus))
+        return direct ? launch<256, 256, kMx, true>(a, dev.cus, s)
+                      : launch<256, 256, kMx, false>(a, dev.cus, s);
+    return direct ? launch<128, 128, kMx, true>(a, dev.cus, s)
+                  : launch<128, 128, kMx, false>(a, dev.cus, s);
+}
+
+const char* gemm_strerror(int code) {
+    switch (code) {
+        case GEMM_OK: return "success";
+        case GEMM_ERR_INVALID_ARG: return "invalid argument (size, leading dimension, pointer or K alignment)";
+        case GEMM_ERR_UNSUPPORTED: return "unsupported device (a gfx950 GPU is required)";
+        case GEMM_ERR_LAUNCH: return "kernel launch failed";
+        default: return "unknown error code";
+    }
+}
+
+int gemm_version(void) { return 100; }
+
+}  // extern "C"

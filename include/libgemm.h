@@ -1,0 +1,106 @@
+/*
+ * libgemm.h -- C ABI of the MI355X (gfx950) dense GEMM library.
+ *
+ * Operation (the matrix product of "GPU 执行模型", section "Tile 的容量约束"):
+ *
+ *     C[M x N] = A[M x K] * B[K x N]
+ *
+ * with fp32 accumulation and fp32 output, for
+ *   - bf16 operands (gemm_bf16: B row-major; gemm_bf16_nt: B column-major), and
+ *   - MX block-scaled fp8 operands (gemm_mxfp8): OCP E4M3 ("fn") element
+ *     codes with one OCP E8M0 scale code per 32 consecutive K-elements of each
+ *     row of A and each column of B.  This is the block-scaled MMA of
+ *     "Modern GPU Programming For MLSys - 书籍总结", sections 2.4 and 2.6; the
+ *     encodings follow the OCP Microscaling (MX) v1.0 specification.  Each
+ *     output is sum over blocks b of 2^(sa-127) * 2^(sb-127) * (sum of the
+ *     32 element products of block b).
+ *
+ * Conventions shared by every entry point (the correctness contract of
+ * "GPU 执行模型", section "正确性契约"):
+ *   - Sizes and leading dimensions are in ELEMENTS, as int64_t.
+ *   - A is row-major: element (i, k) at A[i*lda + k], lda >= K.
+ *   - C is row-major fp32: element (i, j) at C[i*ldc + j], ldc >= N.  C is
+ *     overwritten (no alpha/beta); elements outside the M x N block and the
+ *     padding of every operand (ld > extent) are never read into a result
+ *     and C outside M x N is never written.
+ *   - Pointers are DEVICE pointers on the current HIP device.  The caller owns
+ *     every buffer; the library never allocates, frees, copies or
+ *     synchronises during a call.  Any element alignment is accepted (2 bytes
+ *     for bf16, 1 byte for fp8, 4 bytes for C); 16-byte aligned operands with
+ *     leading dimensions that keep rows 16-byte aligned take the fastest path.
+ *   - C must not alias A, B or the scales (undefined if it does).
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the legacy default
+ *     stream) and the call returns without waiting; completion is observed
+ *     through the stream.  Calls contain no host synchronisation and no
+ *     allocation, so they may be captured into a HIP graph.
+ *   - Results are deterministic: the same inputs give bitwise-identical C
+ *     (no atomics, fixed reduction order for a given shape and layout).
+ *   - M == 0 or N == 0: nothing is done and GEMM_OK is returned.
+ *     K == 0: C[0:M, 0:N] is set to zero.
+ *   - NaN and Inf propagate as in IEEE arithmetic (a NaN operand makes the
+ *     outputs it feeds NaN; Inf * 0 is NaN).  fp32 subnormal results may be
+ *     flushed by the matrix cores; that lies inside the accuracy contract.
+ *   - Accuracy: |C - exact| <= 1e-3 * sum_k |a(i,k)| |b(k,j)| elementwise for
+ *     K <= 16384; integer-valued operands whose partial sums stay below 2^24
+ *     give exact results.
+ *   - The library never aborts the process.  Errors are returned as the
+ *     codes below and leave C untouched.
+ */
+#ifndef LIBGEMM_H
+#define LIBGEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GEMM_OK 0
+/* a size is negative, a leading dimension too small, a pointer NULL with a
+ * non-empty extent, or (MX) K not a multiple of 32 */
+#define GEMM_ERR_INVALID_ARG (-1)
+/* the current device is not a gfx950 (MI355X-class) GPU, or no device */
+#define GEMM_ERR_UNSUPPORTED (-2)
+/* the HIP runtime reported an error when the kernel was enqueued */
+#define GEMM_ERR_LAUNCH (-3)
+
+/* bf16 GEMM, B row-major: A bf16 M x K (lda >= K), B bf16 K x N with
+ * element (k, j) at B[k*ldb + j] (ldb >= N), C fp32 M x N (ldc >= N). */
+int gemm_bf16(int64_t M, int64_t N, int64_t K,
+              const void* A, int64_t lda,
+              const void* B, int64_t ldb,
+              float* C, int64_t ldc,
+              void* stream);
+
+/* bf16 GEMM, B column-major ("NT"): element (k, j) of B at B[j*ldb + k],
+ * ldb >= K (B is stored as N rows of K).  Otherwise as gemm_bf16. */
+int gemm_bf16_nt(int64_t M, int64_t N, int64_t K,
+                 const void* A, int64_t lda,
+                 const void* B, int64_t ldb,
+                 float* C, int64_t ldc,
+                 void* stream);
+
+/* MX block-scaled fp8 GEMM.  A: E4M3 codes, M x K row-major (lda >= K).
+ * B: E4M3 codes, column-major, element (k, j) at B[j*ldb + k] (ldb >= K).
+ * scaleA: E8M0 codes, dense row-major M x (K/32): the scale of A's row i for
+ * k in [32b, 32b+32) is scaleA[i*(K/32) + b].  scaleB: E8M0 codes, dense
+ * N x (K/32): the scale of B's column j for block b is scaleB[j*(K/32) + b].
+ * K must be a multiple of 32.  C fp32 M x N (ldc >= N). */
+int gemm_mxfp8(int64_t M, int64_t N, int64_t K,
+               const void* A, int64_t lda,
+               const void* B, int64_t ldb,
+               const uint8_t* scaleA, const uint8_t* scaleB,
+               float* C, int64_t ldc,
+               void* stream);
+
+/* Static text for a return code (never NULL). */
+const char* gemm_strerror(int code);
+
+/* Library version: major*10000 + minor*100 + patch. */
+int gemm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBGEMM_H */

@@ -185,6 +185,30 @@ static void mx_element(const job_t* J, int64_t i, int64_t j, double* c, double* 
 
 static void* run_full_bf16(void* p) {
     job_t* J = (job_t*)p;
+    if (J->b_cs == 1 && J->N > 1) {
+        /* Row-major B: the same ascending-k binary64 sums, formed a whole
+         * output row at a time (i-k-j order) so that B is read along its
+         * rows.  Every element sees exactly the additions of bf16_element in
+         * the same order, so the results are bit-identical to it. */
+        for (int64_t i = J->lo; i < J->hi; ++i) {
+            double* crow = J->C + i * J->ldc;
+            double* arow = J->absC ? J->absC + i * J->ldc : NULL;
+            for (int64_t j = 0; j < J->N; ++j) {
+                crow[j] = 0.0;
+                if (arow) arow[j] = 0.0;
+            }
+            for (int64_t k = 0; k < J->K; ++k) {
+                double x = oracle_bf16_value(J->A16[i * J->a_rs + k * J->a_cs]);
+                const uint16_t* brow = J->B16 + k * J->b_rs;
+                for (int64_t j = 0; j < J->N; ++j) {
+                    double y = oracle_bf16_value(brow[j]);
+                    crow[j] += x * y;
+                    if (arow) arow[j] += fabs(x) * fabs(y);
+                }
+            }
+        }
+        return NULL;
+    }
     for (int64_t i = J->lo; i < J->hi; ++i)
         for (int64_t j = 0; j < J->N; ++j) {
             double c, a;

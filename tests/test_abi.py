@@ -1,0 +1,76 @@
+"""Host-side checks of the C ABI: the library loads, exports every entry point
+that include/libgemm.h declares, and rejects bad arguments before touching a
+device.  No GPU needed (no call here reaches the HIP runtime)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import dense_gemm_mxfp8_amd as dg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "libgemm.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?\w+\s*\**\s*(gemm_\w+)\s*\(", text, flags=re.M)
+
+
+def test_header_declares_the_entry_points():
+    names = set(declared_functions())
+    assert {"gemm_bf16", "gemm_bf16_nt", "gemm_mxfp8", "gemm_strerror", "gemm_version"} <= names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(dg.LIBRARY)
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} declared in libgemm.h but not exported"
+
+
+def test_version_and_messages():
+    assert dg.gemm_version() >= 100
+    for code in (0, -1, -2, -3, 99):
+        assert isinstance(dg.gemm_strerror(code), str) and dg.gemm_strerror(code)
+
+
+FAKE = 0x1000  # never dereferenced: validation fails first
+
+
+@pytest.mark.parametrize("fn", ["gemm_bf16", "gemm_bf16_nt"])
+def test_bf16_rejects_bad_arguments(fn):
+    f = getattr(dg, fn)
+    nt = fn.endswith("_nt")
+    ok_ldb = 16 if nt else 8   # K=16, N=8
+    bad = [
+        (-1, 8, 16, FAKE, 16, FAKE, ok_ldb, FAKE, 8),
+        (4, -1, 16, FAKE, 16, FAKE, ok_ldb, FAKE, 8),
+        (4, 8, -1, FAKE, 16, FAKE, ok_ldb, FAKE, 8),
+        (4, 8, 16, FAKE, 15, FAKE, ok_ldb, FAKE, 8),       # lda < K
+        (4, 8, 16, FAKE, 16, FAKE, ok_ldb - 1, FAKE, 8),   # ldb too small
+        (4, 8, 16, FAKE, 16, FAKE, ok_ldb, FAKE, 7),       # ldc < N
+        (4, 8, 16, 0, 16, FAKE, ok_ldb, FAKE, 8),          # null A
+        (4, 8, 16, FAKE, 16, 0, ok_ldb, FAKE, 8),          # null B
+        (4, 8, 16, FAKE, 16, FAKE, ok_ldb, 0, 8),          # null C
+    ]
+    for args in bad:
+        assert f(*args, 0) == dg.GEMM_ERR_INVALID_ARG, args
+
+
+def test_mx_rejects_bad_arguments():
+    f = dg.gemm_mxfp8
+    assert f(4, 8, 48, FAKE, 48, FAKE, 48, FAKE, FAKE, FAKE, 8, 0) == dg.GEMM_ERR_INVALID_ARG
+    assert f(4, 8, 64, FAKE, 64, FAKE, 64, 0, FAKE, FAKE, 8, 0) == dg.GEMM_ERR_INVALID_ARG
+    assert f(4, 8, 64, FAKE, 64, FAKE, 64, FAKE, 0, FAKE, 8, 0) == dg.GEMM_ERR_INVALID_ARG
+    assert f(4, 8, 64, FAKE, 63, FAKE, 64, FAKE, FAKE, FAKE, 8, 0) == dg.GEMM_ERR_INVALID_ARG
+    assert f(4, 8, 64, FAKE, 64, FAKE, 60, FAKE, FAKE, FAKE, 8, 0) == dg.GEMM_ERR_INVALID_ARG
+    assert f(-4, 8, 64, FAKE, 64, FAKE, 64, FAKE, FAKE, FAKE, 8, 0) == dg.GEMM_ERR_INVALID_ARG
+
+
+def test_empty_extents_are_a_no_op():
+    # M == 0 or N == 0: success without touching any pointer or the device
+    assert dg.gemm_bf16(0, 8, 16, 0, 16, 0, 8, 0, 8, 0) == dg.GEMM_OK
+    assert dg.gemm_bf16_nt(4, 0, 16, 0, 16, 0, 16, 0, 1, 0) == dg.GEMM_OK
+    assert dg.gemm_mxfp8(0, 0, 64, 0, 64, 0, 64, 0, 0, 0, 1, 0) == dg.GEMM_OK
