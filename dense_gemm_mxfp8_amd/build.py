@@ -11,7 +11,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(PKG, "libgemm.so")
 
 HIPCC_FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950", "-O3", "-std=c++20", "-fPIC", "-shared",
     # keep the compiler from forming packed fp32 instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]

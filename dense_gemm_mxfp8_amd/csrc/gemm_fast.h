@@ -1,0 +1,567 @@
+// gemm_fast.h -- the aligned fast path of the gfx950 GEMM kernels.
+//
+// One workgroup of 4 waves owns a 256 x 256 output tile at a time (a 2 x 2
+// arrangement of 128 x 128 wave tiles, 256 fp32 accumulators per lane in the
+// AGPR file) and walks a persistent, XCD-aware sequence of tiles.  The K loop
+// streams k-tiles of RB bytes per operand row (RB = 128: 64 bf16 or 128 fp8;
+// RB = 64: 32 bf16) through S LDS stages:
+//
+//   * global -> LDS: `buffer_load_dwordx4 ... lds` against a per-tile buffer
+//     descriptor.  Every wave instruction fills 1 KiB of LDS; lane i lands at
+//     byte 16 i and fetches the global 16-byte chunk that the swizzle places
+//     there.  Rows past M (or N) lie beyond the descriptor's size and read as
+//     zero, so the tails need no predicates on the load side.
+//   * LDS layout: each operand row holds RB bytes of K; its 16-byte chunks
+//     are XOR-swizzled with bits of the row index chosen for gfx950's
+//     64-bank LDS (16 lanes of a 128-bit read are served per clock, so any
+//     16 consecutive rows must spread one logical chunk over all 16
+//     bank groups of 256 bytes).
+//   * Row-major B ("NN") is staged N-contiguous (k rows of 512 bytes) and
+//     read with `ds_read_b64_tr_b16`, which transposes 4 x 16 bf16 blocks on
+//     the way into registers.
+//   * k-tile t + S - 1 is issued while k-tile t is multiplied; one barrier
+//     per k-tile hands a stage from the loaders to the readers, the role the
+//     pages give to mbarrier phases.  Every stage is its own __shared__
+//     object and the K loop is unrolled by S, so the compiler can tell the
+//     in-flight DMA writes of later stages apart from the reads of the
+//     current one and does not serialise them.
+//   * MFMA fragments are double-buffered across k-steps: the LDS reads of
+//     step s + 1 are in flight while step s's MFMAs run.
+//   * the last, partial k-tile (K mod BK != 0) is loaded through registers
+//     with element predicates (zero fill past K).
+//   * epilogue: fp32 stores straight from the accumulators, predicated only
+//     on edge tiles.
+//
+// Fast-path preconditions (checked on the host): 16-byte aligned A and B,
+// leading dimensions that keep every row 16-byte aligned, 256 rows of either
+// operand spanning less than 2 GiB, and for row-major B, N % 8 == 0.  The MX
+// variant also needs K % 128 == 0.
+
+#pragma once
+
+#include <type_traits>
+#include <utility>
+
+namespace fast {
+
+constexpr int kTile = 256;      // BM = BN
+constexpr int kThreads = 256;   // 4 waves in a 2 x 2 arrangement
+constexpr int kWaves = 4;
+constexpr int kWaveTile = 128;  // each wave: 128 x 128 outputs
+constexpr int kBlocks = 4;      // 32 x 32 MFMA blocks per wave tile side
+constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
+
+enum Kind { kNT = 0, kNN = 1, kMX = 2 };
+
+struct Args {
+    const uint8_t* A;
+    const uint8_t* B;
+    float* C;
+    const uint8_t* SA;
+    const uint8_t* SB;
+    int64_t lda_b, ldb_b;  // leading dimensions in bytes
+    int64_t ldc;           // elements
+    int M, N, K;
+    int tiles_m, tiles_n, num_tiles, group_m;
+    int kt_total;  // number of k-tiles, the last one possibly partial
+    int kt_full;   // number of k-tiles lying entirely inside K
+    int sld;       // MX scale bytes per row (K / 32)
+    int xcd_remap;
+};
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+#define FAST_LDS __attribute__((address_space(3)))
+
+// s_waitcnt encodings (gfx9): vmcnt in [3:0] and [15:14], expcnt [6:4],
+// lgkmcnt [11:8].
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4)); }
+
+// Barrier that keeps the compiler from moving memory operations across it,
+// without the workgroup fence of __syncthreads (whose release would wait for
+// every outstanding global load, including the stages still in flight).
+__device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// Swizzle of 16-byte chunk columns for K-contiguous rows of RB bytes.
+template <int RB>
+__device__ __forceinline__ int swz(int row) {
+    if constexpr (RB == 128) return (row >> 1) & 7;
+    else return (row >> 2) & 3;
+}
+
+// Byte offset of chunk `chunk` of K-contiguous row `row`.
+template <int RB>
+__device__ __forceinline__ int kc_off(int row, int chunk) {
+    return row * RB + ((chunk ^ swz<RB>(row)) << 4);
+}
+
+// Byte offset of element column n of k-row k in the N-contiguous stage of
+// row-major B (512-byte rows of 256 bf16).
+__device__ __forceinline__ int nn_off(int k, int n) {
+    return k * 512 + ((((n >> 3) ^ ((k & 3) << 2))) << 4) + ((n & 7) << 1);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+    int n = bytes > 0x7fffffff ? 0x7fffffff : (int)bytes;
+    if (n < 0) n = 0;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, kRsrcWord3);
+}
+
+__device__ __forceinline__ int logical_block(const Args& a) {
+    int bid = blockIdx.x;
+    if (!a.xcd_remap) return bid;
+    // Workgroups are dispatched round-robin over the 8 XCDs; renumber them
+    // so that consecutive logical ids (neighbouring tiles) share an XCD and
+    // its L2.
+    int per_xcd = gridDim.x >> 3;
+    return (bid & 7) * per_xcd + (bid >> 3);
+}
+
+// Grouped raster: tiles are walked in column-major order inside bands of
+// group_m tile rows, so concurrently running tiles share A rows and B columns.
+__device__ __forceinline__ void tile_coords(const Args& a, int t, int& tm, int& tn) {
+    int per_group = a.group_m * a.tiles_n;
+    int g = t / per_group;
+    int first = g * a.group_m;
+    int gsz = min(a.tiles_m - first, a.group_m);
+    int r = t - g * per_group;
+    tm = first + r % gsz;
+    tn = r / gsz;
+}
+
+// Predicated register load of the partial last k-tile of a K-contiguous
+// operand (256 rows x RB bytes): element k is read only when k < K, rows past
+// `rows` are zero.
+template <int RB, int ESZ>
+__device__ __forceinline__ void load_kc_tail(uint8_t FAST_LDS* dst, const uint8_t* g, int64_t ld_b,
+                                             int rows, int kvalid_b, int tid) {
+    constexpr int CPR = RB / 16;
+#pragma unroll
+    for (int i = 0; i < kTile * CPR / kThreads; ++i) {
+        int idx = i * kThreads + tid;
+        int r = idx / CPR, c = idx % CPR;
+        i32x4 v = {0, 0, 0, 0};
+        if (r < rows) {
+            const uint8_t* src = g + (int64_t)r * ld_b + c * 16;
+            if (c * 16 + 16 <= kvalid_b) {
+                v = *(const i32x4*)src;
+            } else if (c * 16 < kvalid_b) {
+                // the chunk straddles K: assemble its valid bytes (K * ESZ is
+                // a multiple of ESZ, so whole elements are taken)
+                const int nb = kvalid_b - c * 16;
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    uint32_t word = 0;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (4 * w + e < nb) word |= (uint32_t)src[4 * w + e] << (8 * e);
+                    v[w] = (int)word;
+                }
+            }
+        }
+        *(i32x4 FAST_LDS*)(dst + kc_off<RB>(r, c)) = v;
+    }
+}
+
+// Predicated register load of a partial k-tile of row-major B (k rows of 256
+// bf16): rows k >= kvalid are zero.  Columns are in range by the N % 8 == 0
+// precondition except past N, which only feed discarded outputs and are
+// zero-filled here.
+template <int BK>
+__device__ __forceinline__ void load_nn_tail(uint8_t FAST_LDS* dst, const uint8_t* g, int64_t ldb_b,
+                                             int kvalid, int ncols, int tid) {
+#pragma unroll
+    for (int i = 0; i < BK * 32 / kThreads; ++i) {
+        int idx = i * kThreads + tid;
+        int kk = idx >> 5, c = idx & 31;
+        i32x4 v = {0, 0, 0, 0};
+        if (kk < kvalid && c * 8 < ncols) v = *(const i32x4*)(g + (int64_t)kk * ldb_b + c * 16);
+        *(i32x4 FAST_LDS*)(dst + nn_off(kk, c * 8)) = v;
+    }
+}
+
+// Compile-time loop: f(integral_constant<int, B>), ..., f(integral_constant<int, E-1>).
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
+// Instruction-group masks of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSgMfma = 0x008;
+constexpr int kSgVmem = 0x010;
+constexpr int kSgDsRead = 0x100;
+
+// Interleave the 16 MFMAs of one k-step with NR LDS fragment reads and ND
+// DMA instructions so that memory instructions issue while the matrix core
+// is busy instead of in bursts.
+template <int NR, int ND>
+__device__ __forceinline__ void interleave_step() {
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+        __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+        if (m < NR) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
+        if (m < ND) __builtin_amdgcn_sched_group_barrier(kSgVmem, 1, 0);
+    }
+}
+
+template <int KIND, int RB, int S, bool TAIL>
+__global__ __launch_bounds__(kThreads, 1) void gemm_fast_kernel(Args a) {
+    constexpr int ESZ = (KIND == kMX) ? 1 : 2;  // operand element bytes
+    constexpr int BK = RB / ESZ;                // K elements per k-tile
+    constexpr int OPB = kTile * RB;             // bytes of one operand in one stage
+    constexpr int SCB = (KIND == kMX) ? 2 * kTile * 4 : 0;  // MX scale bytes per stage
+    constexpr int STAGE = 2 * OPB + SCB;
+    constexpr int NI = RB / 16;                 // DMA instructions per wave per operand
+    constexpr int RPK = 1024 / RB;              // K-contiguous rows per KiB
+    // MFMA k-steps per k-tile: 16 bf16 or 64 fp8 elements per step
+    constexpr int KS = (KIND == kMX) ? BK / 64 : BK / 16;
+    static_assert(KS % 2 == 0, "fragment double-buffering needs an even step count");
+    static_assert(S >= 2 && S * STAGE <= 160 * 1024, "LDS budget");
+    // DMA instructions per wave per k-tile: both operands, plus (MX) one
+    // scale instruction per operand.
+    constexpr int L = 2 * NI + (KIND == kMX ? 2 : 0);
+    // The DMA of a k-tile is spread over k-steps 0 .. KS-2 of the previous
+    // k-tile's multiplication (all of it is issued before that k-tile's
+    // closing wait, so the vmcnt bookkeeping stays exact).
+    constexpr int DPS = (L + KS - 2) / (KS - 1);  // DMA instructions per k-step
+    static_assert(KS >= 2, "need a step before the closing wait");
+    typedef typename std::conditional<KIND == kMX, i32x8, bf16x8>::type Frag;
+
+    __shared__ __attribute__((aligned(1024))) uint8_t st0[STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t st1[STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t st2[S > 2 ? STAGE : 16];
+    __shared__ __attribute__((aligned(1024))) uint8_t st3[S > 3 ? STAGE : 16];
+    __shared__ __attribute__((aligned(1024))) uint8_t st4[S > 4 ? STAGE : 16];
+    auto stage_ptr = [&](auto sidx) -> uint8_t FAST_LDS* {
+        constexpr int s = decltype(sidx)::value;
+        if constexpr (s == 0) return (uint8_t FAST_LDS*)st0;
+        else if constexpr (s == 1) return (uint8_t FAST_LDS*)st1;
+        else if constexpr (s == 2) return (uint8_t FAST_LDS*)st2;
+        else if constexpr (s == 3) return (uint8_t FAST_LDS*)st3;
+        else return (uint8_t FAST_LDS*)st4;
+    };
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int h = lane >> 5;
+    const int l32 = lane & 31;
+
+    // ---- per-lane constants of the DMA loads ------------------------------
+    // K-contiguous operand: instruction i of this wave fills KiB (4 i + wave)
+    // of the operand's stage area; the swizzle of its rows does not depend
+    // on i, so one lane offset plus a scalar row step covers all of them.
+    const int kc_row0 = wave * RPK + lane / (RB / 16);
+    const int kc_chunk = (lane % (RB / 16)) ^ swz<RB>(kc_row0);
+    const int a_voff = (int)(kc_row0 * a.lda_b) + kc_chunk * 16;
+    const int a_step = (int)(4 * RPK * a.lda_b);
+    int b_voff, b_step;
+    if constexpr (KIND == kNN) {
+        // k rows of 512 bytes, 2 per KiB: row 2(4 i + wave) + lane / 32.
+        const int kk0 = 2 * wave + h;
+        const int c = l32 ^ ((kk0 & 3) << 2);
+        b_voff = (int)(kk0 * a.ldb_b) + c * 16;
+        b_step = (int)(8 * a.ldb_b);
+    } else {
+        b_voff = (int)(kc_row0 * a.ldb_b) + kc_chunk * 16;
+        b_step = (int)(4 * RPK * a.ldb_b);
+    }
+    // MX scales: wave w stages the k-tile's scale dwords of rows
+    // 64 w .. 64 w + 63 of both operands (one dword = four 32-blocks).
+    const int sc_voff = (KIND == kMX) ? (64 * wave + lane) * a.sld : 0;
+
+    // ---- per-lane constants of the fragment reads --------------------------
+    // byte offsets in a stage of this lane's A / B chunks at step ks (block
+    // 0); fp8 steps read two chunks (k 16h..16h+15 and 32+16h..32+16h+15)
+    int a_rd[KS][2], b_rd[KS][2];
+    int b_tr[kBlocks];  // NN: offset of block j's transposed read at step 0
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        const int c0 = (KIND == kMX) ? (4 * ks + h) : (2 * ks + h);
+        a_rd[ks][0] = kc_off<RB>(wm * kWaveTile + l32, c0);
+        b_rd[ks][0] = OPB + kc_off<RB>(wn * kWaveTile + l32, c0);
+        a_rd[ks][1] = kc_off<RB>(wm * kWaveTile + l32, c0 + 2);
+        b_rd[ks][1] = OPB + kc_off<RB>(wn * kWaveTile + l32, c0 + 2);
+    }
+    if constexpr (KIND == kNN) {
+        const int g = lane >> 4, li = lane & 15;
+#pragma unroll
+        for (int j = 0; j < kBlocks; ++j) {
+            int n = wn * kWaveTile + j * 32 + 16 * (g & 1) + 4 * (li & 3);
+            int k = 8 * (g >> 1) + (li >> 2);
+            b_tr[j] = OPB + nn_off(k, n);
+        }
+    }
+    // MX: this lane's scale dwords in a stage (row block 0 of A and of B).
+    const int sa_rd = 2 * OPB + 4 * (wm * kWaveTile + l32);
+    const int sb_rd = 2 * OPB + 4 * kTile + 4 * (wn * kWaveTile + l32);
+
+    const int KT = a.kt_full;                // k-tiles holding data
+    const int KTM = (KT + S - 1) / S * S;    // rounded up: the rest are dead (zero) k-tiles
+
+    const int G = gridDim.x;
+    for (int t = logical_block(a); t < a.num_tiles; t += G) {
+        int tm, tn;
+        tile_coords(a, t, tm, tn);
+        const int m0 = tm * kTile, n0 = tn * kTile;
+        const int rows_a = min(kTile, a.M - m0);
+        const int rows_b = min(kTile, a.N - n0);
+
+        // Per-tile buffer descriptors: everything past the last valid row
+        // (or, for row-major B, past the last k row) reads as zero.  The
+        // dead descriptor (size 0) turns the loads of k-tiles past the end
+        // into zero fill without memory traffic.
+        const uint8_t* a_base = a.A + (int64_t)m0 * a.lda_b;
+        const __amdgpu_buffer_rsrc_t ra =
+            make_rsrc(a_base, (int64_t)(rows_a - 1) * a.lda_b + (int64_t)a.K * ESZ);
+        const uint8_t* b_base;
+        __amdgpu_buffer_rsrc_t rb;
+        if constexpr (KIND == kNN) {
+            b_base = a.B + (int64_t)n0 * 2;
+            rb = make_rsrc(b_base, (int64_t)(a.K - 1) * a.ldb_b + (int64_t)(a.N - n0) * 2);
+        } else {
+            b_base = a.B + (int64_t)n0 * a.ldb_b;
+            rb = make_rsrc(b_base, (int64_t)(rows_b - 1) * a.ldb_b + (int64_t)a.K * ESZ);
+        }
+        const __amdgpu_buffer_rsrc_t rdead = make_rsrc(a.A, 0);
+        __amdgpu_buffer_rsrc_t rsa = rdead, rsb = rdead;
+        if constexpr (KIND == kMX) {
+            rsa = make_rsrc(a.SA + (int64_t)m0 * a.sld, (int64_t)rows_a * a.sld);
+            rsb = make_rsrc(a.SB + (int64_t)n0 * a.sld, (int64_t)rows_b * a.sld);
+        }
+
+        // DMA instruction d (0 .. L-1) of k-tile kt into stage s.
+        auto dma = [&](auto sidx, int d, int kt, bool live) {
+            uint8_t FAST_LDS* As = stage_ptr(sidx);
+            if (d < NI) {
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(live ? ra : rdead,
+                                                         (void FAST_LDS*)(As + (4 * d + wave) * 1024), 16,
+                                                         a_voff, kt * RB + d * a_step, 0, 0);
+            } else if (d < 2 * NI) {
+                const int i = d - NI;
+                const int koff = (KIND == kNN) ? kt * BK * (int)a.ldb_b : kt * RB;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(live ? rb : rdead,
+                                                         (void FAST_LDS*)(As + OPB + (4 * i + wave) * 1024), 16,
+                                                         b_voff, koff + i * b_step, 0, 0);
+            } else if constexpr (KIND == kMX) {
+                const bool sb = d > 2 * NI;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    live ? (sb ? rsb : rsa) : rdead,
+                    (void FAST_LDS*)(As + 2 * OPB + (sb ? 4 * kTile : 0) + 256 * wave), 4, sc_voff, kt * 4, 0, 0);
+            }
+        };
+
+        auto read_frags = [&](auto sidx, int ks, Frag* fa, Frag* fb) {
+            const uint8_t FAST_LDS* base = stage_ptr(sidx);
+#pragma unroll
+            for (int i = 0; i < kBlocks; ++i) {
+                if constexpr (KIND == kMX) {
+                    i32x4 lo = *(const i32x4 FAST_LDS*)(base + a_rd[ks][0] + i * 32 * RB);
+                    i32x4 hi = *(const i32x4 FAST_LDS*)(base + a_rd[ks][1] + i * 32 * RB);
+                    fa[i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                } else {
+                    fa[i] = *(const bf16x8 FAST_LDS*)(base + a_rd[ks][0] + i * 32 * RB);
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < kBlocks; ++j) {
+                if constexpr (KIND == kMX) {
+                    i32x4 lo = *(const i32x4 FAST_LDS*)(base + b_rd[ks][0] + j * 32 * RB);
+                    i32x4 hi = *(const i32x4 FAST_LDS*)(base + b_rd[ks][1] + j * 32 * RB);
+                    fb[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                } else if constexpr (KIND == kNN) {
+                    const uint8_t FAST_LDS* p = base + b_tr[j] + ks * 16 * 512;
+                    bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((bf16x4 FAST_LDS*)p);
+                    bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((bf16x4 FAST_LDS*)(p + 4 * 512));
+                    fb[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                } else {
+                    fb[j] = *(const bf16x8 FAST_LDS*)(base + b_rd[ks][0] + j * 32 * RB);
+                }
+            }
+        };
+        // fragment reads per k-step (LDS instructions)
+        constexpr int NR = (KIND == kMX) ? 16 : (KIND == kNN) ? 12 : 8;
+
+        // MX: the scale dwords of the k-tile in stage s, pre-shifted so that
+        // lane half h finds its 32-block (2 ks + h) in byte 2 ks.
+        int sc[2 * kBlocks];
+        auto read_scales = [&](auto sidx) {
+            if constexpr (KIND == kMX) {
+                const uint8_t FAST_LDS* base = stage_ptr(sidx);
+#pragma unroll
+                for (int i = 0; i < kBlocks; ++i) {
+                    uint32_t w = *(const uint32_t FAST_LDS*)(base + sa_rd + 128 * i);
+                    uint32_t v = *(const uint32_t FAST_LDS*)(base + sb_rd + 128 * i);
+                    sc[i] = (int)(w >> (8 * h));
+                    sc[kBlocks + i] = (int)(v >> (8 * h));
+                }
+            }
+        };
+
+        f32x16 acc[kBlocks][kBlocks];
+#pragma unroll
+        for (int i = 0; i < kBlocks; ++i)
+#pragma unroll
+            for (int j = 0; j < kBlocks; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+        auto mfma = [&](int ks, const Frag* fa, const Frag* fb, const int* scl) {
+#pragma unroll
+            for (int i = 0; i < kBlocks; ++i)
+#pragma unroll
+                for (int j = 0; j < kBlocks; ++j) {
+                    if constexpr (KIND == kMX) {
+                        // k-step ks covers 32-blocks 2 ks and 2 ks + 1 of the
+                        // k-tile: byte 2 ks of the (pre-shifted) scale word.
+                        if (ks == 0)
+                            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                                fa[i], fb[j], acc[i][j], 0, 0, 0, scl[i], 0, scl[kBlocks + j]);
+                        else
+                            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                                fa[i], fb[j], acc[i][j], 0, 0, 2, scl[i], 2, scl[kBlocks + j]);
+                    } else {
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+                    }
+                }
+        };
+
+        // ---- prologue: k-tiles 0 .. S-2 into stages 0 .. S-2 --------------
+        [&]<int... Is>(std::integer_sequence<int, Is...>) {
+            ((
+                 [&] {
+#pragma unroll
+                     for (int d = 0; d < L; ++d) dma(std::integral_constant<int, Is>{}, d, Is, Is < KT);
+                 }()),
+             ...);
+        }(std::make_integer_sequence<int, S - 1>{});
+        wait_vm<(S - 2) * L>();
+        barrier();
+
+        Frag F0a[kBlocks], F0b[kBlocks], F1a[kBlocks], F1b[kBlocks];
+        read_frags(std::integral_constant<int, 0>{}, 0, F0a, F0b);
+        read_scales(std::integral_constant<int, 0>{});
+
+        // One k-tile held in stage s; meanwhile the DMA of k-tile kt + S - 1
+        // fills stage s - 1 (freed by the barrier that closed k-tile kt - 1).
+        auto body = [&](auto sidx, int kt) {
+            constexpr int s = decltype(sidx)::value;
+            constexpr int snext = (s + 1) % S;
+            constexpr int sdma = (s + S - 1) % S;
+            const int kd = kt + S - 1;
+            const bool live = kd < KT;
+            int scn[2 * kBlocks];
+            static_for<0, KS>([&](auto ksc) {
+                constexpr int ks = decltype(ksc)::value;
+                Frag* ca = (ks & 1) ? F1a : F0a;
+                Frag* cb = (ks & 1) ? F1b : F0b;
+                Frag* na = (ks & 1) ? F0a : F1a;
+                Frag* nb = (ks & 1) ? F0b : F1b;
+                if constexpr (ks + 1 < KS) {
+                    read_frags(sidx, ks + 1, na, nb);
+                    constexpr int d0 = ks * DPS;
+                    constexpr int d1 = (ks + 1) * DPS < L ? (ks + 1) * DPS : L;
+                    static_for<d0, d1>([&](auto dc) {
+                        dma(std::integral_constant<int, sdma>{}, decltype(dc)::value, kd, live);
+                    });
+                    mfma(ks, ca, cb, sc);
+                    interleave_step<NR, (d1 > d0 ? d1 - d0 : 0)>();
+                } else {
+                    // This k-step's fragments are in registers, so stage s
+                    // is fully read; k-tile kt+1 must have landed while
+                    // kt+2 .. kt+S-1 stay in flight.
+                    wait_lgkm0();
+                    wait_vm<(S - 2) * L>();
+                    barrier();
+                    read_frags(std::integral_constant<int, snext>{}, 0, na, nb);
+                    if constexpr (KIND == kMX) {
+#pragma unroll
+                        for (int q = 0; q < 2 * kBlocks; ++q) scn[q] = sc[q];
+                        read_scales(std::integral_constant<int, snext>{});
+                        mfma(ks, ca, cb, scn);
+                    } else {
+                        mfma(ks, ca, cb, sc);
+                    }
+                    interleave_step<NR, 0>();
+                }
+            });
+        };
+
+        for (int kt0 = 0; kt0 < KTM; kt0 += S) {
+            [&]<int... Is>(std::integer_sequence<int, Is...>) {
+                (body(std::integral_constant<int, Is>{}, kt0 + Is), ...);
+            }(std::make_integer_sequence<int, S>{});
+        }
+
+        // The dead k-tiles still in flight carry no memory traffic; let them
+        // land before the stages are reused.
+        wait_vm<0>();
+
+        // ---- partial last k-tile: predicated register loads, zero past K --
+        if constexpr (TAIL && KIND != kMX) {
+            barrier();  // every wave is done with the pipelined stages
+            uint8_t FAST_LDS* As = stage_ptr(std::integral_constant<int, 0>{});
+            const int kvalid = a.K - KT * BK;
+            load_kc_tail<RB, ESZ>(As, a_base + (int64_t)KT * RB, a.lda_b, rows_a, kvalid * ESZ, tid);
+            if constexpr (KIND == kNN)
+                load_nn_tail<BK>(As + OPB, b_base + (int64_t)KT * BK * a.ldb_b, a.ldb_b, kvalid, a.N - n0,
+                                 tid);
+            else
+                load_kc_tail<RB, ESZ>(As + OPB, b_base + (int64_t)KT * RB, a.ldb_b, rows_b, kvalid * ESZ,
+                                      tid);
+            wait_lgkm0();
+            barrier();
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                read_frags(std::integral_constant<int, 0>{}, ks, F0a, F0b);
+                mfma(ks, F0a, F0b, sc);
+            }
+        }
+
+        // ---- epilogue: fp32 stores straight from the accumulators --------
+        const bool full = (rows_a == kTile) && (rows_b == kTile);
+        float* cbase = a.C + (int64_t)(m0 + wm * kWaveTile) * a.ldc + n0 + wn * kWaveTile + l32;
+        if (full) {
+#pragma unroll
+            for (int i = 0; i < kBlocks; ++i)
+#pragma unroll
+                for (int j = 0; j < kBlocks; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int row = i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+                        cbase[(int64_t)row * a.ldc + j * 32] = acc[i][j][r];
+                    }
+        } else {
+            const int rlim = rows_a - wm * kWaveTile;
+            const int clim = rows_b - wn * kWaveTile - l32;
+#pragma unroll
+            for (int i = 0; i < kBlocks; ++i)
+#pragma unroll
+                for (int j = 0; j < kBlocks; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int row = i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+                        if (row < rlim && j * 32 < clim) cbase[(int64_t)row * a.ldc + j * 32] = acc[i][j][r];
+                    }
+        }
+        // The next tile's prologue overwrites stages 0 .. S-2: every wave
+        // must be done reading them.
+        wait_lgkm0();
+        barrier();
+    }
+}
+
+}  // namespace fast

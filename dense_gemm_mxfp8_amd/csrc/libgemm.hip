@@ -47,10 +47,13 @@
 #include <hip/hip_runtime.h>
 
 #include <mutex>
+#include <stdio.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include "libgemm.h"
+#include "gemm_fast.h"
 
 namespace {
 
@@ -541,6 +544,110 @@ bool use_big_tiles(int64_t M, int64_t N, int cus) {
     return big * 4 >= (int64_t)cus * 3;
 }
 
+// ---------------------------------------------------------------------------
+// Fast path (gemm_fast.h): 256 x 256 tiles, direct-to-LDS buffer loads.
+// ---------------------------------------------------------------------------
+
+// Pipeline variant of the fast kernel: k-tile bytes per operand row and LDS
+// stages.  LIBGEMM_VARIANT=<rb>x<stages> (e.g. 64x4) selects a compiled one
+// for measurements; the default is chosen per kind.
+struct FastVariant {
+    int rb, stages, group;
+};
+
+// LIBGEMM_VARIANT=<rb>x<stages> picks the pipeline; LIBGEMM_GROUP=<n> the
+// number of tile rows per raster band.
+FastVariant env_variant() {
+    static FastVariant v = [] {
+        FastVariant r{0, 0, 0};
+        const char* e = getenv("LIBGEMM_VARIANT");
+        if (e) {
+            int rb = 0, st = 0;
+            if (sscanf(e, "%dx%d", &rb, &st) == 2) {
+                r.rb = rb;
+                r.stages = st;
+            }
+        }
+        const char* g = getenv("LIBGEMM_GROUP");
+        if (g) r.group = atoi(g);
+        return r;
+    }();
+    return v;
+}
+
+template <int KIND, int RB, int S>
+int launch_fast(fast::Args a, int cus, hipStream_t stream, int group_m = 0) {
+    constexpr int BK = RB / (KIND == fast::kMX ? 1 : 2);
+    a.tiles_m = (a.M + fast::kTile - 1) / fast::kTile;
+    a.tiles_n = (a.N + fast::kTile - 1) / fast::kTile;
+    a.num_tiles = a.tiles_m * a.tiles_n;
+    if (group_m <= 0) group_m = 16;
+    a.group_m = a.tiles_m < group_m ? a.tiles_m : group_m;
+    a.kt_full = a.K / BK;
+    a.kt_total = (a.K + BK - 1) / BK;
+    int grid = cus < a.num_tiles ? cus : a.num_tiles;
+    if (grid >= 8) grid -= grid % 8;
+    a.xcd_remap = (grid % 8 == 0) ? 1 : 0;
+    if (a.kt_total > a.kt_full)
+        hipLaunchKernelGGL((fast::gemm_fast_kernel<KIND, RB, S, true>), dim3(grid), dim3(fast::kThreads), 0,
+                           stream, a);
+    else
+        hipLaunchKernelGGL((fast::gemm_fast_kernel<KIND, RB, S, false>), dim3(grid), dim3(fast::kThreads), 0,
+                           stream, a);
+    return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
+}
+
+// Whether the fast kernel's preconditions hold (see gemm_fast.h).
+bool fast_ok(int kind, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+             int64_t ldb, const void* SA, const void* SB) {
+    const int64_t esz = kind == fast::kMX ? 1 : 2;
+    const int64_t lim = (int64_t)1 << 31;
+    if (!aligned16(A) || !aligned16(B)) return false;
+    if ((lda * esz) % 16 || (ldb * esz) % 16) return false;
+    if (256 * lda * esz >= lim) return false;
+    if (kind == fast::kNN) {
+        if (N % 8) return false;
+        if (K * ldb * esz >= lim) return false;
+    } else if (256 * ldb * esz >= lim) {
+        return false;
+    }
+    if (kind == fast::kMX) {
+        if (K % 128) return false;
+        if ((((uintptr_t)SA) & 3) || (((uintptr_t)SB) & 3)) return false;
+    }
+    (void)M;
+    return true;
+}
+
+fast::Args make_fast_args(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                          const void* B, int64_t ldb, float* C, int64_t ldc, int64_t esz) {
+    fast::Args a;
+    memset(&a, 0, sizeof a);
+    a.A = (const uint8_t*)A;
+    a.B = (const uint8_t*)B;
+    a.C = C;
+    a.lda_b = lda * esz;
+    a.ldb_b = ldb * esz;
+    a.ldc = ldc;
+    a.M = (int)M;
+    a.N = (int)N;
+    a.K = (int)K;
+    return a;
+}
+
+int launch_fast_bf16(bool nt, const fast::Args& a, int cus, hipStream_t s) {
+    const FastVariant v = env_variant();
+    const int g = v.group;
+    if (nt) {
+        if (v.rb == 128 && v.stages == 2) return launch_fast<fast::kNT, 128, 2>(a, cus, s, g);
+        if (v.rb == 64 && v.stages == 3) return launch_fast<fast::kNT, 64, 3>(a, cus, s, g);
+        if (v.rb == 64 && v.stages == 5) return launch_fast<fast::kNT, 64, 5>(a, cus, s, g);
+        return launch_fast<fast::kNT, 64, 4>(a, cus, s, g);
+    }
+    if (v.rb == 128 && v.stages == 2) return launch_fast<fast::kNN, 128, 2>(a, cus, s, g);
+    return launch_fast<fast::kNN, 64, 4>(a, cus, s, g);
+}
+
 int bf16_dispatch(bool nt, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
                   const void* B, int64_t ldb, float* C, int64_t ldc, void* stream) {
     int rc = check_common(M, N, K, A, lda, B, ldb, nt ? K : N, C, ldc);
@@ -555,6 +662,8 @@ int bf16_dispatch(bool nt, int64_t M, int64_t N, int64_t K, const void* A, int64
     const bool direct = aligned16(A) && aligned16(B) && (lda % 8 == 0) && (ldb % 8 == 0) &&
                         (nt || (N % 8 == 0));
     const bool big = use_big_tiles(M, N, dev.cus);
+    if (big && fast_ok(nt ? fast::kNT : fast::kNN, M, N, K, A, lda, B, ldb, nullptr, nullptr))
+        return launch_fast_bf16(nt, make_fast_args(M, N, K, A, lda, B, ldb, C, ldc, 2), dev.cus, s);
     if (nt) {
         if (big) return direct ? launch<256, 256, kBf16NT, true>(a, dev.cus, s)
                                : launch<256, 256, kBf16NT, false>(a, dev.cus, s);
@@ -598,6 +707,13 @@ int gemm_mxfp8(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, cons
     a.SA = scaleA;
     a.SB = scaleB;
     a.sld = (int)(K / 32);
+    if (use_big_tiles(M, N, dev.cus) && fast_ok(fast::kMX, M, N, K, A, lda, B, ldb, scaleA, scaleB)) {
+        fast::Args f = make_fast_args(M, N, K, A, lda, B, ldb, C, ldc, 1);
+        f.SA = scaleA;
+        f.SB = scaleB;
+        f.sld = (int)(K / 32);
+        return launch_fast<fast::kMX, 128, 2>(f, dev.cus, s, env_variant().group);
+    }
     const bool direct = aligned16(A) && aligned16(B) && (lda % 16 == 0) && (ldb % 16 == 0);
     if (use_big_tiles(M, N, dev.cus))
         return direct ? launch<256, 256, kMx, true>(a, dev.cus, s)
