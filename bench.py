@@ -40,9 +40,28 @@ def parse():
     ap.add_argument("--workload", default="square8192_nt")
     ap.add_argument("--all", action="store_true", help="also print one line per other workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=256,
+    ap.add_argument("--cpu-rows", type=int, default=1024,
                     help="rows of A in the oracle's timed sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain device copy of COPY_BYTES (for scaling HBM counters)")
     return ap.parse_args()
+
+
+COPY_BYTES = 1 << 30  # 1 GiB read + 1 GiB written per copy launch
+
+
+def copy_calibration(steps: int):
+    """A plain elementwise copy kernel of known size: FETCH_SIZE / WRITE_SIZE of
+    its launches give the scale from counter KiB to bytes."""
+    import torch
+    n = COPY_BYTES // 4
+    src = torch.rand(n, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": True, "bytes_read": COPY_BYTES,
+                      "bytes_written": COPY_BYTES, "launches": steps}), flush=True)
 
 
 def operand_bytes(w) -> int:
@@ -146,18 +165,26 @@ def cpu_baseline(prob, rows: int):
                       f"{dt:.2f} s wall"}
 
 
+def measured_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary of
+    this workload, or None if there is none or the kernels changed since."""
+    from dense_gemm_mxfp8_amd import profiling
+    return profiling.read_traffic(os.path.join(ROOT, "profiles", f"traffic_{workload}.md"))
+
+
 def line(res, steps, warmup, cpu=None, headline=True):
     peak = PEAK_TFLOPS[res["peak_key"]]
+    traffic = measured_traffic(res["workload"])
     achieved = res["flops"] / (res["kernel_ms_mean"] * 1e-3) / 1e12
     ai = res["flops"] / res["bytes"]
     ridge = peak * 1e12 / (PEAK_HBM_GBS * 1e9)
     if ai < ridge:
         gbs = res["bytes"] / (res["kernel_ms_mean"] * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}
+                "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic}
     else:
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak,
-                "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None}
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic}
     out = {
         "metric": METRIC if headline else f"GEMM TFLOP/s ({res['workload']})",
         "value": round(res["tflops"], 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": steps,
@@ -189,6 +216,9 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration:
+        copy_calibration(args.steps)
+        return
     names = [args.workload]
     if args.all:
         from dense_gemm_mxfp8_amd.inputs import WORKLOADS

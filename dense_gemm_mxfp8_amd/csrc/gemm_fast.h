@@ -30,7 +30,9 @@
 //   * the last, partial k-tile (K mod BK != 0) is loaded through registers
 //     with element predicates (zero fill past K).
 //   * epilogue: fp32 stores straight from the accumulators, predicated only
-//     on edge tiles.
+//     on edge tiles, marked non-temporal: C is written once and never read
+//     back, so it should not evict operand lines from L2 and the
+//     Infinity Cache.
 //
 // Fast-path preconditions (checked on the host): 16-byte aligned A and B,
 // leading dimensions that keep every row 16-byte aligned, 256 rows of either
@@ -542,7 +544,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_kernel(Args a) {
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const int row = i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-                        cbase[(int64_t)row * a.ldc + j * 32] = acc[i][j][r];
+                        __builtin_nontemporal_store(acc[i][j][r], &cbase[(int64_t)row * a.ldc + j * 32]);
                     }
         } else {
             const int rlim = rows_a - wm * kWaveTile;
@@ -554,7 +556,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_kernel(Args a) {
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const int row = i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-                        if (row < rlim && j * 32 < clim) cbase[(int64_t)row * a.ldc + j * 32] = acc[i][j][r];
+                        if (row < rlim && j * 32 < clim)
+                            __builtin_nontemporal_store(acc[i][j][r], &cbase[(int64_t)row * a.ldc + j * 32]);
                     }
         }
         // The next tile's prologue overwrites stages 0 .. S-2: every wave

@@ -581,7 +581,7 @@ int launch_fast(fast::Args a, int cus, hipStream_t stream, int group_m = 0) {
     a.tiles_m = (a.M + fast::kTile - 1) / fast::kTile;
     a.tiles_n = (a.N + fast::kTile - 1) / fast::kTile;
     a.num_tiles = a.tiles_m * a.tiles_n;
-    if (group_m <= 0) group_m = 16;
+    if (group_m <= 0) group_m = 8;
     a.group_m = a.tiles_m < group_m ? a.tiles_m : group_m;
     a.kt_full = a.K / BK;
     a.kt_total = (a.K + BK - 1) / BK;
