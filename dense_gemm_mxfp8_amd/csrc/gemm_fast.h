@@ -218,27 +218,53 @@ __device__ __forceinline__ void interleave_step() {
     }
 }
 
-template <int KIND, int RB, int S, bool TAIL>
+// SG (MX only): k-tiles per scale group.  SG == 1 stages each k-tile's scale
+// codes with the tile (one 2- or 4-byte load per row); SG > 1 keeps a
+// double-buffered ring of scale groups in LDS and fetches 4 * SG bytes per
+// row once per group, which cuts the scale loads' L2 requests SG-fold.
+template <int KIND, int RB, int S, bool TAIL, int SG = 1>
 __global__ __launch_bounds__(kThreads, 1) void gemm_fast_kernel(Args a) {
     constexpr int ESZ = (KIND == kMX) ? 1 : 2;  // operand element bytes
     constexpr int BK = RB / ESZ;                // K elements per k-tile
     constexpr int OPB = kTile * RB;             // bytes of one operand in one stage
-    constexpr int SCB = (KIND == kMX) ? 2 * kTile * 4 : 0;  // MX scale bytes per stage
+    // MX: scale bytes per row per k-tile (one E8M0 code per 32 elements).
+    // LDS-DMA narrower than a dword still writes one zero-extended dword per
+    // lane, so every row's scales occupy 4 bytes of LDS either way.
+    constexpr int SPR = (KIND == kMX) ? BK / 32 : 0;
+    constexpr int SCB = (KIND == kMX && SG == 1) ? 2 * kTile * 4 : 0;  // MX scale bytes per stage
+    constexpr int RING = (KIND == kMX && SG > 1) ? 2 * kTile * 4 * SG : 16;  // bytes per ring slot
+    static_assert(SG == 1 || (KIND == kMX && RB == 128 && SG == 4 && S == 2), "scale ring: MX 128x2 only");
     constexpr int STAGE = 2 * OPB + SCB;
     constexpr int NI = RB / 16;                 // DMA instructions per wave per operand
     constexpr int RPK = 1024 / RB;              // K-contiguous rows per KiB
     // MFMA k-steps per k-tile: 16 bf16 or 64 fp8 elements per step
     constexpr int KS = (KIND == kMX) ? BK / 64 : BK / 16;
-    static_assert(KS % 2 == 0, "fragment double-buffering needs an even step count");
+    // Fragments are double-buffered over the global k-step sequence; with an
+    // odd step count per k-tile the buffer parity follows the k-tile parity,
+    // which the S-fold unrolled loop keeps static only for even S.
+    static_assert(KS % 2 == 0 || S % 2 == 0, "odd k-steps per k-tile need an even stage count");
+    static_assert(KIND != kMX || SPR == 2 || SPR == 4, "MX k-tile of 64 or 128 codes");
     static_assert(S >= 2 && S * STAGE <= 160 * 1024, "LDS budget");
     // DMA instructions per wave per k-tile: both operands, plus (MX) one
     // scale instruction per operand.
-    constexpr int L = 2 * NI + (KIND == kMX ? 2 : 0);
-    // The DMA of a k-tile is spread over k-steps 0 .. KS-2 of the previous
-    // k-tile's multiplication (all of it is issued before that k-tile's
-    // closing wait, so the vmcnt bookkeeping stays exact).
-    constexpr int DPS = (L + KS - 2) / (KS - 1);  // DMA instructions per k-step
-    static_assert(KS >= 2, "need a step before the closing wait");
+    constexpr int L = 2 * NI + (KIND == kMX && SG == 1 ? 2 : 0);
+    // the main loop is unrolled by U k-tiles so that the stage and the scale
+    // ring slot of every unrolled k-tile are compile-time constants
+    constexpr int U = SG > 1 ? 2 * SG : S;
+    // The DMA of k-tile kt + S - 1 is issued while k-tile kt is multiplied,
+    // DPS instructions per k-step.  With S >= 3 it is spread over every
+    // k-step (the part issued after the closing wait is simply younger than
+    // what that wait needs); with S == 2 all of it must be issued before
+    // the wait, so it covers k-steps 0 .. KS-2.
+    constexpr int DSTEPS = (S >= 3) ? KS : KS - 1;
+    constexpr int DPS = (L + DSTEPS - 1) / DSTEPS;  // DMA instructions per k-step
+    // DMA instructions of the current k-tile issued before the closing wait
+    constexpr int DBEFORE = (KS - 1) * DPS < L ? (KS - 1) * DPS : L;
+    // Loads younger than k-tile kt+1's when the closing wait of k-tile kt
+    // runs: k-tiles kt+2 .. kt+S-2 in full plus the early part of kt+S-1.
+    constexpr int VM_WAIT = (S >= 3) ? (S - 3) * L + DBEFORE : 0;
+    static_assert(VM_WAIT < 64, "vmcnt range");
+    static_assert(KS >= 2 || S >= 3, "with one k-step per k-tile the DMA goes after the closing wait");
     typedef typename std::conditional<KIND == kMX, i32x8, bf16x8>::type Frag;
 
     __shared__ __attribute__((aligned(1024))) uint8_t st0[STAGE];
@@ -246,6 +272,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_kernel(Args a) {
     __shared__ __attribute__((aligned(1024))) uint8_t st2[S > 2 ? STAGE : 16];
     __shared__ __attribute__((aligned(1024))) uint8_t st3[S > 3 ? STAGE : 16];
     __shared__ __attribute__((aligned(1024))) uint8_t st4[S > 4 ? STAGE : 16];
+    __shared__ __attribute__((aligned(1024))) uint8_t sr0[RING];
+    __shared__ __attribute__((aligned(1024))) uint8_t sr1[RING];
     auto stage_ptr = [&](auto sidx) -> uint8_t FAST_LDS* {
         constexpr int s = decltype(sidx)::value;
         if constexpr (s == 0) return (uint8_t FAST_LDS*)st0;
@@ -312,7 +340,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_kernel(Args a) {
     const int sb_rd = 2 * OPB + 4 * kTile + 4 * (wn * kWaveTile + l32);
 
     const int KT = a.kt_full;                // k-tiles holding data
-    const int KTM = (KT + S - 1) / S * S;    // rounded up: the rest are dead (zero) k-tiles
+    const int KTM = (KT + U - 1) / U * U;    // rounded up: the rest are dead (zero) k-tiles
 
     const int G = gridDim.x;
     for (int t = logical_block(a); t < a.num_tiles; t += G) {
@@ -360,9 +388,26 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_kernel(Args a) {
                                                          b_voff, koff + i * b_step, 0, 0);
             } else if constexpr (KIND == kMX) {
                 const bool sb = d > 2 * NI;
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    live ? (sb ? rsb : rsa) : rdead,
-                    (void FAST_LDS*)(As + 2 * OPB + (sb ? 4 * kTile : 0) + 256 * wave), 4, sc_voff, kt * 4, 0, 0);
+                const __amdgpu_buffer_rsrc_t rs = live ? (sb ? rsb : rsa) : rdead;
+                void FAST_LDS* dst = (void FAST_LDS*)(As + 2 * OPB + (sb ? 4 * kTile : 0) + 256 * wave);
+                // one scale load per row: SPR bytes (the size operand must be a literal)
+                if constexpr (SPR == 2)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 2, sc_voff, kt * SPR, 0, 0);
+                else
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 4, sc_voff, kt * SPR, 0, 0);
+            }
+        };
+
+        // Scale ring: group g (k-tiles SG g .. SG g + SG - 1) into slot g % 2;
+        // wave w loads rows 64 w .. 64 w + 63 of both operands, 4 SG bytes each.
+        auto ring_dma = [&](auto slot, int g, bool live) {
+            if constexpr (KIND == kMX && SG > 1) {
+                uint8_t FAST_LDS* base = decltype(slot)::value ? (uint8_t FAST_LDS*)sr1 : (uint8_t FAST_LDS*)sr0;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(live ? rsa : rdead, (void FAST_LDS*)(base + 1024 * wave),
+                                                         16, sc_voff, g * 16, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(live ? rsb : rdead,
+                                                         (void FAST_LDS*)(base + 4096 + 1024 * wave), 16, sc_voff,
+                                                         g * 16, 0, 0);
             }
         };
 
@@ -400,11 +445,26 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_kernel(Args a) {
         // MX: the scale dwords of the k-tile in stage s, pre-shifted so that
         // lane half h finds its 32-block (2 ks + h) in byte 2 ks.
         int sc[2 * kBlocks];
-        auto read_scales = [&](auto sidx) {
-            if constexpr (KIND == kMX) {
+        // scales of the k-tile in stage sidx (SG == 1) or at position q of
+        // the unrolled loop (SG > 1: ring slot (q / SG) % 2, dword q % SG)
+        auto read_scales = [&](auto sidx, auto qidx) {
+            if constexpr (KIND == kMX && SG > 1) {
+                constexpr int q = decltype(qidx)::value % U;
+                const uint8_t FAST_LDS* base =
+                    ((q / SG) % 2) ? (const uint8_t FAST_LDS*)sr1 : (const uint8_t FAST_LDS*)sr0;
+#pragma unroll
+                for (int i = 0; i < kBlocks; ++i) {
+                    uint32_t w = *(const uint32_t FAST_LDS*)(base + 16 * (wm * kWaveTile + l32 + 32 * i) + 4 * (q % SG));
+                    uint32_t v = *(const uint32_t FAST_LDS*)(base + 4096 + 16 * (wn * kWaveTile + l32 + 32 * i) +
+                                                             4 * (q % SG));
+                    sc[i] = (int)(w >> (8 * h));
+                    sc[kBlocks + i] = (int)(v >> (8 * h));
+                }
+            } else if constexpr (KIND == kMX) {
                 const uint8_t FAST_LDS* base = stage_ptr(sidx);
 #pragma unroll
                 for (int i = 0; i < kBlocks; ++i) {
+                    // low SPR bytes: the codes of 32-blocks SPR*kt .. SPR*kt+SPR-1
                     uint32_t w = *(const uint32_t FAST_LDS*)(base + sa_rd + 128 * i);
                     uint32_t v = *(const uint32_t FAST_LDS*)(base + sb_rd + 128 * i);
                     sc[i] = (int)(w >> (8 * h));
@@ -450,17 +510,20 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_kernel(Args a) {
                  }()),
              ...);
         }(std::make_integer_sequence<int, S - 1>{});
-        wait_vm<(S - 2) * L>();
+        ring_dma(std::integral_constant<int, 0>{}, 0, 0 < KT);
+        wait_vm<(SG > 1) ? 0 : (S - 2) * L>();
         barrier();
 
         Frag F0a[kBlocks], F0b[kBlocks], F1a[kBlocks], F1b[kBlocks];
         read_frags(std::integral_constant<int, 0>{}, 0, F0a, F0b);
-        read_scales(std::integral_constant<int, 0>{});
+        read_scales(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
 
         // One k-tile held in stage s; meanwhile the DMA of k-tile kt + S - 1
         // fills stage s - 1 (freed by the barrier that closed k-tile kt - 1).
-        auto body = [&](auto sidx, int kt) {
-            constexpr int s = decltype(sidx)::value;
+        auto body = [&](auto qidx, int kt) {
+            constexpr int q = decltype(qidx)::value;  // position in the unrolled loop
+            constexpr int s = q % S;
+            auto sidx = std::integral_constant<int, s>{};
             constexpr int snext = (s + 1) % S;
             constexpr int sdma = (s + S - 1) % S;
             const int kd = kt + S - 1;
@@ -468,44 +531,56 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_kernel(Args a) {
             int scn[2 * kBlocks];
             static_for<0, KS>([&](auto ksc) {
                 constexpr int ks = decltype(ksc)::value;
-                Frag* ca = (ks & 1) ? F1a : F0a;
-                Frag* cb = (ks & 1) ? F1b : F0b;
-                Frag* na = (ks & 1) ? F0a : F1a;
-                Frag* nb = (ks & 1) ? F0b : F1b;
+                constexpr int gp = (s * KS + ks) & 1;  // parity of the global k-step
+                Frag* ca = gp ? F1a : F0a;
+                Frag* cb = gp ? F1b : F0b;
+                Frag* na = gp ? F0a : F1a;
+                Frag* nb = gp ? F0b : F1b;
+                constexpr int d0 = ks * DPS < L ? ks * DPS : L;
+                constexpr int d1 = (ks + 1) * DPS < L ? (ks + 1) * DPS : L;
                 if constexpr (ks + 1 < KS) {
                     read_frags(sidx, ks + 1, na, nb);
-                    constexpr int d0 = ks * DPS;
-                    constexpr int d1 = (ks + 1) * DPS < L ? (ks + 1) * DPS : L;
                     static_for<d0, d1>([&](auto dc) {
                         dma(std::integral_constant<int, sdma>{}, decltype(dc)::value, kd, live);
                     });
+                    if constexpr (SG > 1 && ks == 0 && q % SG == 0) {
+                        // next scale group into the other ring slot (its last
+                        // reader finished before the barrier closing k-tile kt-1)
+                        const int g = kt / SG + 1;
+                        ring_dma(std::integral_constant<int, (q / SG + 1) % 2>{}, g, g * SG < KT);
+                    }
                     mfma(ks, ca, cb, sc);
-                    interleave_step<NR, (d1 > d0 ? d1 - d0 : 0)>();
+                    interleave_step<NR, d1 - d0 + ((SG > 1 && ks == 0 && q % SG == 0) ? 2 : 0)>();
+                    // keep every MFMA of this step ahead of the closing wait
+                    __builtin_amdgcn_sched_barrier(0);
                 } else {
                     // This k-step's fragments are in registers, so stage s
-                    // is fully read; k-tile kt+1 must have landed while
-                    // kt+2 .. kt+S-1 stay in flight.
+                    // is fully read; k-tile kt+1 must have landed.
                     wait_lgkm0();
-                    wait_vm<(S - 2) * L>();
+                    wait_vm<VM_WAIT>();
                     barrier();
                     read_frags(std::integral_constant<int, snext>{}, 0, na, nb);
+                    static_for<d0, d1>([&](auto dc) {
+                        dma(std::integral_constant<int, sdma>{}, decltype(dc)::value, kd, live);
+                    });
                     if constexpr (KIND == kMX) {
 #pragma unroll
                         for (int q = 0; q < 2 * kBlocks; ++q) scn[q] = sc[q];
-                        read_scales(std::integral_constant<int, snext>{});
+                        read_scales(std::integral_constant<int, snext>{}, std::integral_constant<int, q + 1>{});
                         mfma(ks, ca, cb, scn);
                     } else {
                         mfma(ks, ca, cb, sc);
                     }
-                    interleave_step<NR, 0>();
+                    interleave_step<NR, d1 - d0>();
+                    __builtin_amdgcn_sched_barrier(0);
                 }
             });
         };
 
-        for (int kt0 = 0; kt0 < KTM; kt0 += S) {
+        for (int kt0 = 0; kt0 < KTM; kt0 += U) {
             [&]<int... Is>(std::integer_sequence<int, Is...>) {
                 (body(std::integral_constant<int, Is>{}, kt0 + Is), ...);
-            }(std::make_integer_sequence<int, S>{});
+            }(std::make_integer_sequence<int, U>{});
         }
 
         // The dead k-tiles still in flight carry no memory traffic; let them

@@ -550,7 +550,8 @@ bool use_big_tiles(int64_t M, int64_t N, int cus) {
 
 // Pipeline variant of the fast kernel: k-tile bytes per operand row and LDS
 // stages.  LIBGEMM_VARIANT=<rb>x<stages> (e.g. 64x4) selects a compiled one
-// for measurements; the default is chosen per kind.
+// for measurements; the defaults (measured on MI355X at 4096^3 and 8192^3)
+// are 128x2 for bf16 NT, 64x4 for bf16 NN and 64x4 for MX.
 struct FastVariant {
     int rb, stages, group;
 };
@@ -575,7 +576,7 @@ FastVariant env_variant() {
     return v;
 }
 
-template <int KIND, int RB, int S>
+template <int KIND, int RB, int S, int SG = 1>
 int launch_fast(fast::Args a, int cus, hipStream_t stream, int group_m = 0) {
     constexpr int BK = RB / (KIND == fast::kMX ? 1 : 2);
     a.tiles_m = (a.M + fast::kTile - 1) / fast::kTile;
@@ -589,10 +590,10 @@ int launch_fast(fast::Args a, int cus, hipStream_t stream, int group_m = 0) {
     if (grid >= 8) grid -= grid % 8;
     a.xcd_remap = (grid % 8 == 0) ? 1 : 0;
     if (a.kt_total > a.kt_full)
-        hipLaunchKernelGGL((fast::gemm_fast_kernel<KIND, RB, S, true>), dim3(grid), dim3(fast::kThreads), 0,
+        hipLaunchKernelGGL((fast::gemm_fast_kernel<KIND, RB, S, true, SG>), dim3(grid), dim3(fast::kThreads), 0,
                            stream, a);
     else
-        hipLaunchKernelGGL((fast::gemm_fast_kernel<KIND, RB, S, false>), dim3(grid), dim3(fast::kThreads), 0,
+        hipLaunchKernelGGL((fast::gemm_fast_kernel<KIND, RB, S, false, SG>), dim3(grid), dim3(fast::kThreads), 0,
                            stream, a);
     return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
 }
@@ -612,8 +613,10 @@ bool fast_ok(int kind, int64_t M, int64_t N, int64_t K, const void* A, int64_t l
         return false;
     }
     if (kind == fast::kMX) {
-        if (K % 128) return false;
-        if ((((uintptr_t)SA) & 3) || (((uintptr_t)SB) & 3)) return false;
+        // the MX pipeline streams 64 or 128 codes per k-tile and the scale
+        // codes of a k-tile as one 2- or 4-byte load per row
+        if (K % 64) return false;
+        if ((((uintptr_t)SA) & 1) || (((uintptr_t)SB) & 1)) return false;
     }
     (void)M;
     return true;
@@ -639,10 +642,10 @@ int launch_fast_bf16(bool nt, const fast::Args& a, int cus, hipStream_t s) {
     const FastVariant v = env_variant();
     const int g = v.group;
     if (nt) {
-        if (v.rb == 128 && v.stages == 2) return launch_fast<fast::kNT, 128, 2>(a, cus, s, g);
         if (v.rb == 64 && v.stages == 3) return launch_fast<fast::kNT, 64, 3>(a, cus, s, g);
+        if (v.rb == 64 && v.stages == 4) return launch_fast<fast::kNT, 64, 4>(a, cus, s, g);
         if (v.rb == 64 && v.stages == 5) return launch_fast<fast::kNT, 64, 5>(a, cus, s, g);
-        return launch_fast<fast::kNT, 64, 4>(a, cus, s, g);
+        return launch_fast<fast::kNT, 128, 2>(a, cus, s, g);
     }
     if (v.rb == 128 && v.stages == 2) return launch_fast<fast::kNN, 128, 2>(a, cus, s, g);
     return launch_fast<fast::kNN, 64, 4>(a, cus, s, g);
@@ -712,7 +715,16 @@ int gemm_mxfp8(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, cons
         f.SA = scaleA;
         f.SB = scaleB;
         f.sld = (int)(K / 32);
-        return launch_fast<fast::kMX, 128, 2>(f, dev.cus, s, env_variant().group);
+        const FastVariant v = env_variant();
+        const uintptr_t sal = ((uintptr_t)scaleA) | ((uintptr_t)scaleB);
+        // scale ring: one 16-byte load per row per 4 k-tiles of 128 codes
+        const bool ring = (K % 512 == 0) && !(sal & 15);
+        const bool word_scales = (K % 128 == 0) && !(sal & 3);
+        if (v.rb == 64 && v.stages == 4) return launch_fast<fast::kMX, 64, 4>(f, dev.cus, s, v.group);
+        if (ring && !(v.rb == 128 && v.stages == 2))
+            return launch_fast<fast::kMX, 128, 2, 4>(f, dev.cus, s, v.group);
+        if (word_scales) return launch_fast<fast::kMX, 128, 2>(f, dev.cus, s, v.group);
+        return launch_fast<fast::kMX, 64, 4>(f, dev.cus, s, v.group);
     }
     const bool direct = aligned16(A) && aligned16(B) && (lda % 16 == 0) && (ldb % 16 == 0);
     if (use_big_tiles(M, N, dev.cus))

@@ -176,6 +176,63 @@ def test_tensor_helper_layouts():
     P.assert_within_bound(c_nn.cpu().numpy(), want, mag, "helper NN")
 
 
+# ---------------------------------------------------------------- fast (256 x 256) path
+
+def _check_sampled(C, want_fn, M, N, nsample, seed, exact=False, what=""):
+    """Sampled positions (random plus every tile-boundary row / column) against
+    the oracle, computed one by one."""
+    rows, cols = P.sample_positions(M, N, nsample, seed=seed)
+    want, mag = want_fn(rows, cols)
+    if exact:
+        P.assert_exact(C[rows, cols], want, what)
+    P.assert_within_bound(C[rows, cols], want, mag, what)
+
+
+def _freivalds(C, Af, Bmat, seed):
+    x = np.random.default_rng(seed).standard_normal(C.shape[1])
+    lhs = C.astype(np.float64) @ x
+    rhs = Af @ (Bmat @ x)
+    lim = P.BOUND * (np.abs(Af) @ (np.abs(Bmat) @ np.abs(x)))
+    assert np.all(np.abs(lhs - rhs) <= lim), "Freivalds check failed"
+
+
+# Shapes large enough for the 256 x 256 kernel (enough tiles for every CU),
+# with partial tiles in M and N and a partial last k-tile.
+FAST_BF16 = [(4096 + 77, 4096 + 133, 513, True), (4096 + 77, 4096 + 8, 520, False),
+             (4096 + 200, 4096 + 64, 1000, True), (4096, 4096, 256, False)]
+
+
+@pytest.mark.parametrize("case", FAST_BF16, ids=lambda c: f"{c[0]}x{c[1]}x{c[2]}_{'nt' if c[3] else 'nn'}")
+@pytest.mark.parametrize("dist", ["normal", "integer"])
+def test_fast_path_bf16_tails(case, dist):
+    M, N, K, colmajor = case
+    prob = _bf16_case(M, N, K, colmajor, dist, seed=31)
+    P.note(f"fast path bf16 {'NT' if colmajor else 'NN'} {M}x{N}x{K} {dist}")
+    C = P.run_bf16(prob.A.to(DEV), prob.B.to(DEV), colmajor).cpu().numpy()
+    assert np.isfinite(C).all()
+    Ab, Bb = P.bits16(prob.A), P.bits16(prob.B)
+    _check_sampled(C, lambda r, c: P.oracle_bf16_at(Ab, Bb, colmajor, r, c), M, N, 1024, 4,
+                   exact=(dist == "integer"), what=prob.name)
+    Af = prob.A.double().numpy()
+    Bf = prob.B.double().numpy()
+    _freivalds(C, Af, Bf.T if colmajor else Bf, 5)
+
+
+FAST_MX = [(4096 + 40, 4096 + 8, 640), (4096 + 40, 4096 + 200, 1024)]
+
+
+@pytest.mark.parametrize("shape", FAST_MX, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("dist", ["normal", "integer"])
+def test_fast_path_mx_tails(shape, dist):
+    M, N, K = shape
+    prob = inputs.mx_problem(M, N, K, dist=dist, seed=32)
+    P.note(f"fast path mx {M}x{N}x{K} {dist}")
+    C = P.run_mx(prob.A.to(DEV), prob.B.to(DEV), prob.SA.to(DEV), prob.SB.to(DEV)).cpu().numpy()
+    assert np.isfinite(C).all()
+    _check_sampled(C, lambda r, c: P.oracle_mx_at(prob.A, prob.B, prob.SA, prob.SB, r, c), M, N, 1024,
+                   6, exact=(dist == "integer"), what=prob.name)
+
+
 # ---------------------------------------------------------------- full-size workloads
 
 def _check_sampled_bf16(name, nsample=2048):
