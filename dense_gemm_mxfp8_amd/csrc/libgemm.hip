@@ -54,6 +54,7 @@
 
 #include "libgemm.h"
 #include "gemm_fast.h"
+#include "gemm_small.h"
 
 namespace {
 
@@ -651,6 +652,60 @@ int launch_fast_bf16(bool nt, const fast::Args& a, int cus, hipStream_t s) {
     return launch_fast<fast::kNN, 64, 4>(a, cus, s, g);
 }
 
+// ---------------------------------------------------------------------------
+// Small-M path (gemm_small.h): row-major B streamed once, M <= 64.
+// ---------------------------------------------------------------------------
+
+bool small_ok(bool nt, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+              int64_t ldb) {
+    if (nt || M > 64 || K < 1) return false;
+    if (!aligned16(A) || !aligned16(B) || (lda % 8) || (ldb % 8)) return false;
+    const int64_t lim = (int64_t)1 << 31;
+    if (K * ldb * 2 >= lim || M * lda * 2 >= lim) return false;
+    // enough column blocks to occupy the GPU; otherwise the tiled kernels
+    return N >= 2048;
+}
+
+template <int MB, int NP, int COLS, int WAVES>
+int launch_small(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
+                 float* C, int64_t ldc, hipStream_t stream) {
+    small::Args a;
+    a.A = (const uint8_t*)A;
+    a.B = (const uint8_t*)B;
+    a.C = C;
+    a.lda_b = lda * 2;
+    a.ldb_b = ldb * 2;
+    a.ldc = ldc;
+    a.M = (int)M;
+    a.N = (int)N;
+    a.K = (int)K;
+    const int64_t per = (K + WAVES - 1) / WAVES;
+    a.kw = (int)((per + small::kStepK - 1) / small::kStepK * small::kStepK);
+    const int grid = (int)((N + COLS - 1) / COLS);
+    hipLaunchKernelGGL((small::gemm_small_m_nn<MB, NP, COLS, WAVES>), dim3(grid), dim3(64 * WAVES), 0, stream, a);
+    return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
+}
+
+int launch_small_bf16(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
+                      float* C, int64_t ldc, hipStream_t s) {
+    // LIBGEMM_SMALL=<np>x<cols>x<waves> selects a compiled variant for measurements
+    static int sv = [] {
+        const char* e = getenv("LIBGEMM_SMALL");
+        int np = 0, c = 0, w = 0;
+        if (e && sscanf(e, "%dx%dx%d", &np, &c, &w) == 3) return np * 10000 + c * 100 + w;
+        return 0;
+    }();
+    if (M <= 16) {
+        if (sv == 120000 + 3208) return launch_small<1, 12, 32, 8>(M, N, K, A, lda, B, ldb, C, ldc, s);
+        if (sv == 80000 + 3216) return launch_small<1, 8, 32, 16>(M, N, K, A, lda, B, ldb, C, ldc, s);
+        if (sv == 80000 + 6416) return launch_small<1, 8, 64, 16>(M, N, K, A, lda, B, ldb, C, ldc, s);
+        if (sv == 80000 + 3208) return launch_small<1, 8, 32, 8>(M, N, K, A, lda, B, ldb, C, ldc, s);
+        return launch_small<1, 4, 32, 16>(M, N, K, A, lda, B, ldb, C, ldc, s);
+    }
+    if (M <= 32) return launch_small<2, 8, 32, 8>(M, N, K, A, lda, B, ldb, C, ldc, s);
+    return launch_small<4, 4, 32, 8>(M, N, K, A, lda, B, ldb, C, ldc, s);
+}
+
 int bf16_dispatch(bool nt, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
                   const void* B, int64_t ldb, float* C, int64_t ldc, void* stream) {
     int rc = check_common(M, N, K, A, lda, B, ldb, nt ? K : N, C, ldc);
@@ -664,6 +719,8 @@ int bf16_dispatch(bool nt, int64_t M, int64_t N, int64_t K, const void* A, int64
     Args a = make_args(M, N, K, A, lda, B, ldb, C, ldc, 64);
     const bool direct = aligned16(A) && aligned16(B) && (lda % 8 == 0) && (ldb % 8 == 0) &&
                         (nt || (N % 8 == 0));
+    if (small_ok(nt, M, N, K, A, lda, B, ldb))
+        return launch_small_bf16(M, N, K, A, lda, B, ldb, C, ldc, s);
     const bool big = use_big_tiles(M, N, dev.cus);
     if (big && fast_ok(nt ? fast::kNT : fast::kNN, M, N, K, A, lda, B, ldb, nullptr, nullptr))
         return launch_fast_bf16(nt, make_fast_args(M, N, K, A, lda, B, ldb, C, ldc, 2), dev.cus, s);

@@ -233,6 +233,33 @@ def test_fast_path_mx_tails(shape, dist):
                    6, exact=(dist == "integer"), what=prob.name)
 
 
+# ---------------------------------------------------------------- small-M path
+
+# (M, N, K, pad): row-major A and B with padded leading dimensions (multiples
+# of 8 elements, the small-M kernel's alignment), K tails not divisible by 32
+SMALL_M = [(1, 2048, 256, 0), (5, 2056, 1000, 8), (16, 4096, 777, 7), (17, 2048, 300, 4),
+           (33, 2304, 513, 15), (64, 2048, 96, 0), (16, 8192 + 24, 1024, 0)]
+
+
+@pytest.mark.parametrize("case", SMALL_M, ids=lambda c: f"{c[0]}x{c[1]}x{c[2]}")
+@pytest.mark.parametrize("dist", ["normal", "integer"])
+def test_small_m_path(case, dist):
+    M, N, K, pad = case
+    prob = _bf16_case(M, N, K, False, dist, seed=41)
+    lda = (K + pad + 7) // 8 * 8
+    ldb = (N + 7) // 8 * 8
+    Ast = torch.full((M, lda), float("nan"), dtype=torch.bfloat16)
+    Ast[:, :K] = prob.A
+    Bst = torch.full((K, ldb), float("nan"), dtype=torch.bfloat16)
+    Bst[:, :N] = prob.B
+    P.note(f"small-M {M}x{N}x{K} lda {lda} {dist}")
+    C = P.run_bf16(Ast.to(DEV), Bst.to(DEV), False, M=M, N=N, K=K, lda=lda, ldb=ldb).cpu().numpy()
+    want, mag = P.oracle_bf16(P.bits16(prob.A), P.bits16(prob.B), False)
+    if dist == "integer":
+        P.assert_exact(C, want, prob.name)
+    P.assert_within_bound(C, want, mag, prob.name)
+
+
 # ---------------------------------------------------------------- full-size workloads
 
 def _check_sampled_bf16(name, nsample=2048):
