@@ -1,0 +1,280 @@
+// gemm_reg.h -- the 256 x 256 bf16 kernel for operands whose rows are not
+// 16-byte aligned (odd leading dimensions, offset base pointers).
+//
+// Same tile, wave arrangement, LDS layout (XOR-swizzled 64-byte k-rows for
+// K-contiguous operands, 512-byte n-rows for row-major B), MFMA inner loop
+// and epilogue as the direct-load kernel in gemm_fast.h; only the
+// global -> LDS step differs.  LDS-DMA needs dword-aligned sources, so here
+// each thread fetches its 16-byte chunks with buffer loads into registers
+// (gfx950 serves 16-byte loads at any 2-byte alignment), one k-tile ahead,
+// and writes them into the swizzled stage with ds_write_b128:
+//
+//   k-step 0 of k-tile t: store the registers of k-tile t+1 into the other
+//                         stage, issue the loads of k-tile t+2, read the
+//                         fragments of step 1, multiply step 0;
+//   k-step 1:             wait for LDS, barrier (stage t+1 complete, stage t
+//                         fully read), read step 0 of t+1, multiply step 1.
+//
+// Bounds: rows past M / N and k-rows past K (row-major B) lie outside the
+// per-tile buffer descriptors and load as zero.  A descriptor starts at the
+// operand's address rounded down to 4 bytes (the difference goes into the
+// offsets) and ends at the data's end rounded up to 4 bytes, so every dword
+// it admits shares an aligned dword with valid data: nothing past the
+// operand's pages is touched.  Range checks work on the dwords a load
+// actually reads, which at 2-byte alignment need not be aligned ones, so a
+// 16-byte chunk that straddles the end of the data may lose its last valid
+// element; such chunks are only ever loaded element by element.  They occur
+// in the last k-tile of K-contiguous operands (K % 8 != 0, so the tail
+// path), and in the last k-row of row-major B when N % 8 != 0, which the
+// host then also routes through the tail path (one k-tile fewer in the
+// main loop).
+
+#pragma once
+
+namespace regpath {
+
+using namespace fast;
+
+constexpr int RB = 64;            // bytes of K per LDS row (32 bf16)
+constexpr int BK = 32;            // k per k-tile
+constexpr int KS = 2;             // 16-deep MFMA steps per k-tile
+constexpr int OPB = kTile * RB;   // 16 KiB per operand per stage
+constexpr int STAGE = 2 * OPB;
+constexpr int NC = OPB / 16 / kThreads;  // 16-byte chunks per thread per operand (4)
+
+// Descriptor over [p, p + bytes) with its base rounded down to a dword;
+// `shift` receives the byte offset of p from that base.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t span_rsrc(const uint8_t* p, int64_t bytes, int& shift) {
+    shift = (int)((uintptr_t)p & 3);
+    return make_rsrc(p - shift, (shift + bytes + 3) & ~(int64_t)3);
+}
+
+template <int KIND, bool TAIL>
+__global__ __launch_bounds__(kThreads, 1) void gemm_reg_kernel(Args a) {
+    static_assert(KIND == kNT || KIND == kNN, "bf16 only");
+    __shared__ __attribute__((aligned(1024))) uint8_t st0[STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t st1[STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int h = lane >> 5;
+    const int l32 = lane & 31;
+
+    // Chunk i of this thread.  K-contiguous operand: row idx / 4, 16-byte
+    // chunk idx % 4 of the row's 64 bytes.  Row-major B: k-row idx / 32,
+    // columns 8 (idx % 32) .. +7.
+    int a_g[NC], b_g[NC], a_l[NC], b_l[NC];
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+        const int idx = i * kThreads + tid;
+        const int r = idx >> 2, c = idx & 3;
+        a_g[i] = r * (int)a.lda_b + c * 16;
+        a_l[i] = kc_off<RB>(r, c);
+        if constexpr (KIND == kNN) {
+            const int kk = idx >> 5, cn = idx & 31;
+            b_g[i] = kk * (int)a.ldb_b + cn * 16;
+            b_l[i] = OPB + nn_off(kk, cn * 8);
+        } else {
+            b_g[i] = r * (int)a.ldb_b + c * 16;
+            b_l[i] = OPB + kc_off<RB>(r, c);
+        }
+    }
+
+    // fragment read offsets (as in gemm_fast.h)
+    int a_rd[KS], b_rd[KS], b_tr[kBlocks];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        a_rd[ks] = kc_off<RB>(wm * kWaveTile + l32, 2 * ks + h);
+        b_rd[ks] = OPB + kc_off<RB>(wn * kWaveTile + l32, 2 * ks + h);
+    }
+    if constexpr (KIND == kNN) {
+        const int g = lane >> 4, li = lane & 15;
+#pragma unroll
+        for (int j = 0; j < kBlocks; ++j) {
+            int n = wn * kWaveTile + j * 32 + 16 * (g & 1) + 4 * (li & 3);
+            int k = 8 * (g >> 1) + (li >> 2);
+            b_tr[j] = OPB + nn_off(k, n);
+        }
+    }
+
+    const int KT = a.kt_full;
+    const int KTM = (KT + 1) / 2 * 2;
+
+    const int G = gridDim.x;
+    for (int t = logical_block(a); t < a.num_tiles; t += G) {
+        int tm, tn;
+        tile_coords(a, t, tm, tn);
+        const int m0 = tm * kTile, n0 = tn * kTile;
+        const int rows_a = min(kTile, a.M - m0);
+        const int rows_b = min(kTile, a.N - n0);
+        int sa, sb;
+        const __amdgpu_buffer_rsrc_t ra =
+            span_rsrc(a.A + (int64_t)m0 * a.lda_b, (int64_t)(rows_a - 1) * a.lda_b + (int64_t)a.K * 2, sa);
+        __amdgpu_buffer_rsrc_t rb;
+        if constexpr (KIND == kNN)
+            rb = span_rsrc(a.B + (int64_t)n0 * 2, (int64_t)(a.K - 1) * a.ldb_b + (int64_t)(a.N - n0) * 2, sb);
+        else
+            rb = span_rsrc(a.B + (int64_t)n0 * a.ldb_b, (int64_t)(rows_b - 1) * a.ldb_b + (int64_t)a.K * 2, sb);
+        const __amdgpu_buffer_rsrc_t rdead = make_rsrc(a.A, 0);
+
+        i32x4 ra_reg[NC], rb_reg[NC];
+        // k-tile kt into registers (zeros for kt >= KT, without traffic)
+        auto load = [&](int kt, bool live) {
+            const int ka = sa + (live ? kt * RB : 0);
+            const int kb = sb + (live ? ((KIND == kNN) ? kt * BK * (int)a.ldb_b : kt * RB) : 0);
+#pragma unroll
+            for (int i = 0; i < NC; ++i) {
+                ra_reg[i] = __builtin_amdgcn_raw_buffer_load_b128(live ? ra : rdead, a_g[i], ka, 0);
+                rb_reg[i] = __builtin_amdgcn_raw_buffer_load_b128(live ? rb : rdead, b_g[i], kb, 0);
+            }
+        };
+        auto store = [&](auto sidx) {
+            uint8_t FAST_LDS* base = decltype(sidx)::value ? (uint8_t FAST_LDS*)st1 : (uint8_t FAST_LDS*)st0;
+#pragma unroll
+            for (int i = 0; i < NC; ++i) {
+                *(i32x4 FAST_LDS*)(base + a_l[i]) = ra_reg[i];
+                *(i32x4 FAST_LDS*)(base + b_l[i]) = rb_reg[i];
+            }
+        };
+        auto read_frags = [&](auto sidx, int ks, bf16x8* fa, bf16x8* fb) {
+            const uint8_t FAST_LDS* base =
+                decltype(sidx)::value ? (const uint8_t FAST_LDS*)st1 : (const uint8_t FAST_LDS*)st0;
+#pragma unroll
+            for (int i = 0; i < kBlocks; ++i) fa[i] = *(const bf16x8 FAST_LDS*)(base + a_rd[ks] + i * 32 * RB);
+#pragma unroll
+            for (int j = 0; j < kBlocks; ++j) {
+                if constexpr (KIND == kNN) {
+                    const uint8_t FAST_LDS* p = base + b_tr[j] + ks * 16 * 512;
+                    bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((bf16x4 FAST_LDS*)p);
+                    bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((bf16x4 FAST_LDS*)(p + 4 * 512));
+                    fb[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                } else {
+                    fb[j] = *(const bf16x8 FAST_LDS*)(base + b_rd[ks] + j * 32 * RB);
+                }
+            }
+        };
+
+        f32x16 acc[kBlocks][kBlocks];
+#pragma unroll
+        for (int i = 0; i < kBlocks; ++i)
+#pragma unroll
+            for (int j = 0; j < kBlocks; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+        auto mfma = [&](const bf16x8* fa, const bf16x8* fb) {
+#pragma unroll
+            for (int i = 0; i < kBlocks; ++i)
+#pragma unroll
+                for (int j = 0; j < kBlocks; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+        };
+
+        // prologue: k-tile 0 into stage 0, k-tile 1 in flight to registers
+        load(0, 0 < KT);
+        store(std::integral_constant<int, 0>{});
+        load(1, 1 < KT);
+        wait_lgkm0();
+        barrier();
+        bf16x8 F0a[kBlocks], F0b[kBlocks], F1a[kBlocks], F1b[kBlocks];
+        read_frags(std::integral_constant<int, 0>{}, 0, F0a, F0b);
+
+        auto body = [&](auto sidx, int kt) {
+            constexpr int sn = decltype(sidx)::value ^ 1;
+            // k-step 0: stage of k-tile kt+1 <- registers, loads of kt+2,
+            // fragments of step 1
+            store(std::integral_constant<int, sn>{});
+            load(kt + 2, kt + 2 < KT);
+            read_frags(sidx, 1, F1a, F1b);
+            mfma(F0a, F0b);
+            __builtin_amdgcn_sched_barrier(0);
+            // k-step 1
+            wait_lgkm0();
+            barrier();
+            read_frags(std::integral_constant<int, sn>{}, 0, F0a, F0b);
+            mfma(F1a, F1b);
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        for (int kt0 = 0; kt0 < KTM; kt0 += 2) {
+            body(std::integral_constant<int, 0>{}, kt0);
+            body(std::integral_constant<int, 1>{}, kt0 + 1);
+        }
+
+        if constexpr (TAIL) {
+            // Last k-tile KT, holding kvalid (1 .. 32) k.  Chunks lying
+            // wholly inside the data are buffer loads; the chunk that
+            // straddles the end of a row (K-contiguous operands) or of the
+            // last columns (row-major B) is read element by element, so no
+            // load reaches past the operand's last element; the rest is zero.
+            const int kvalid = a.K - KT * BK;
+            const uint16_t* ag = (const uint16_t*)(a.A + (int64_t)m0 * a.lda_b) + KT * BK;
+            const uint16_t* bg = (KIND == kNN) ? (const uint16_t*)(a.B + (int64_t)KT * BK * a.ldb_b) + n0
+                                               : (const uint16_t*)(a.B + (int64_t)n0 * a.ldb_b) + KT * BK;
+            auto gather = [](const uint16_t* p, int n) {
+                i32x4 v = {0, 0, 0, 0};
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (e < n) v[e >> 1] |= (int)((uint32_t)p[e] << (16 * (e & 1)));
+                return v;
+            };
+#pragma unroll
+            for (int i = 0; i < NC; ++i) {
+                const int idx = i * kThreads + tid;
+                const int r = idx >> 2, c8 = 8 * (idx & 3);
+                i32x4 va = {0, 0, 0, 0};
+                if (c8 + 8 <= kvalid)
+                    va = __builtin_amdgcn_raw_buffer_load_b128(ra, a_g[i], sa + KT * RB, 0);
+                else if (c8 < kvalid && r < rows_a)
+                    va = gather(ag + (int64_t)r * (a.lda_b >> 1) + c8, kvalid - c8);
+                ra_reg[i] = va;
+                i32x4 vb = {0, 0, 0, 0};
+                if constexpr (KIND == kNN) {
+                    const int kk = idx >> 5, n8 = 8 * (idx & 31);
+                    if (kk < kvalid) {
+                        if (n8 + 8 <= rows_b)
+                            vb = __builtin_amdgcn_raw_buffer_load_b128(rb, b_g[i], sb + KT * BK * (int)a.ldb_b, 0);
+                        else if (n8 < rows_b)
+                            vb = gather(bg + (int64_t)kk * (a.ldb_b >> 1) + n8, rows_b - n8);
+                    }
+                } else {
+                    if (c8 + 8 <= kvalid)
+                        vb = __builtin_amdgcn_raw_buffer_load_b128(rb, b_g[i], sb + KT * RB, 0);
+                    else if (c8 < kvalid && r < rows_b)
+                        vb = gather(bg + (int64_t)r * (a.ldb_b >> 1) + c8, kvalid - c8);
+                }
+                rb_reg[i] = vb;
+            }
+            // the last body ended with a barrier after every wave's reads of
+            // k-tile data in stage 0 (KTM is even, so stage 0 is free; the
+            // reads that follow that barrier fetch the unused dead k-tile)
+            store(std::integral_constant<int, 0>{});
+            wait_lgkm0();
+            barrier();
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                read_frags(std::integral_constant<int, 0>{}, ks, F0a, F0b);
+                mfma(F0a, F0b);
+            }
+        }
+
+        // epilogue (as in gemm_fast.h)
+        float* cbase = a.C + (int64_t)(m0 + wm * kWaveTile) * a.ldc + n0 + wn * kWaveTile + l32;
+        const int rlim = rows_a - wm * kWaveTile;
+        const int clim = rows_b - wn * kWaveTile - l32;
+#pragma unroll
+        for (int i = 0; i < kBlocks; ++i)
+#pragma unroll
+            for (int j = 0; j < kBlocks; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int row = i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+                    if (row < rlim && j * 32 < clim)
+                        __builtin_nontemporal_store(acc[i][j][r], &cbase[(int64_t)row * a.ldc + j * 32]);
+                }
+        wait_lgkm0();
+        barrier();
+    }
+}
+
+}  // namespace regpath

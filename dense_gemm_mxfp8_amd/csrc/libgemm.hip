@@ -55,6 +55,7 @@
 #include "libgemm.h"
 #include "gemm_fast.h"
 #include "gemm_small.h"
+#include "gemm_reg.h"
 
 namespace {
 
@@ -653,6 +654,47 @@ int launch_fast_bf16(bool nt, const fast::Args& a, int cus, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------
+// Register-load path (gemm_reg.h): 256 x 256 tiles for operands whose rows
+// are only 2-byte aligned.
+// ---------------------------------------------------------------------------
+
+bool reg_ok(bool nt, int64_t K, int64_t lda, int64_t ldb) {
+    const int64_t lim = (int64_t)1 << 31;
+    // 32-bit buffer offsets: 256 rows of A (and of B for NT), all K rows of B
+    // for NN, plus the dword shift of the descriptor base
+    if (256 * lda * 2 + 4 >= lim) return false;
+    if (nt) return 256 * ldb * 2 + 4 < lim;
+    return K * ldb * 2 + 4 < lim;
+}
+
+int launch_reg(bool nt, fast::Args a, int cus, hipStream_t stream) {
+    a.tiles_m = (a.M + fast::kTile - 1) / fast::kTile;
+    a.tiles_n = (a.N + fast::kTile - 1) / fast::kTile;
+    a.num_tiles = a.tiles_m * a.tiles_n;
+    const int g = env_variant().group;
+    const int group_m = g > 0 ? g : 8;
+    a.group_m = a.tiles_m < group_m ? a.tiles_m : group_m;
+    a.kt_full = a.K / regpath::BK;
+    a.kt_total = (a.K + regpath::BK - 1) / regpath::BK;
+    // row-major B with N % 8 != 0: the last k-row ends inside a 16-byte
+    // chunk, which only the tail path reads safely
+    if (!nt && a.N % 8 != 0 && a.kt_full == a.kt_total) a.kt_full -= 1;
+    int grid = cus < a.num_tiles ? cus : a.num_tiles;
+    if (grid >= 8) grid -= grid % 8;
+    a.xcd_remap = (grid % 8 == 0) ? 1 : 0;
+    const bool tail = a.kt_total > a.kt_full;
+    const dim3 blk(fast::kThreads);
+    if (nt) {
+        if (tail) hipLaunchKernelGGL((regpath::gemm_reg_kernel<fast::kNT, true>), dim3(grid), blk, 0, stream, a);
+        else hipLaunchKernelGGL((regpath::gemm_reg_kernel<fast::kNT, false>), dim3(grid), blk, 0, stream, a);
+    } else {
+        if (tail) hipLaunchKernelGGL((regpath::gemm_reg_kernel<fast::kNN, true>), dim3(grid), blk, 0, stream, a);
+        else hipLaunchKernelGGL((regpath::gemm_reg_kernel<fast::kNN, false>), dim3(grid), blk, 0, stream, a);
+    }
+    return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
+}
+
+// ---------------------------------------------------------------------------
 // Small-M path (gemm_small.h): row-major B streamed once, M <= 64.
 // ---------------------------------------------------------------------------
 
@@ -724,6 +766,8 @@ int bf16_dispatch(bool nt, int64_t M, int64_t N, int64_t K, const void* A, int64
     const bool big = use_big_tiles(M, N, dev.cus);
     if (big && fast_ok(nt ? fast::kNT : fast::kNN, M, N, K, A, lda, B, ldb, nullptr, nullptr))
         return launch_fast_bf16(nt, make_fast_args(M, N, K, A, lda, B, ldb, C, ldc, 2), dev.cus, s);
+    if (big && reg_ok(nt, K, lda, ldb))
+        return launch_reg(nt, make_fast_args(M, N, K, A, lda, B, ldb, C, ldc, 2), dev.cus, s);
     if (nt) {
         if (big) return direct ? launch<256, 256, kBf16NT, true>(a, dev.cus, s)
                                : launch<256, 256, kBf16NT, false>(a, dev.cus, s);

@@ -233,6 +233,48 @@ def test_fast_path_mx_tails(shape, dist):
                    6, exact=(dist == "integer"), what=prob.name)
 
 
+# ---------------------------------------------------------------- 2-byte aligned rows
+
+# (M, N, K, b_colmajor, lda pad, ldb pad, element offset of A and B): large
+# enough for 256 x 256 tiles, with leading dimensions and base pointers that
+# keep rows off 16-byte (and, for odd values, off 4-byte) alignment, so the
+# register-load kernel runs; K tails of every kind (none, partial, K < 32).
+REG_BF16 = [(3600 + 17, 3500 + 3, 333, False, 3, 1, 1), (3584 + 1, 3840 + 5, 1001, True, 1, 5, 1),
+            (3584, 3584, 512, False, 1, 3, 0), (3600, 3600, 17, True, 2, 2, 3),
+            (3520 + 9, 3520 + 31, 64 + 2, False, 0, 2, 2), (3600 + 1, 3600 + 5, 512, False, 1, 1, 1)]
+
+
+@pytest.mark.parametrize("case", REG_BF16, ids=lambda c: f"{c[0]}x{c[1]}x{c[2]}_{'nt' if c[3] else 'nn'}")
+@pytest.mark.parametrize("dist", ["normal", "integer"])
+def test_unaligned_rows_big_tiles(case, dist):
+    M, N, K, colmajor, pa, pb, off = case
+    prob = _bf16_case(M, N, K, colmajor, dist, seed=51)
+    nan = float("nan")
+    lda = K + pa
+    rows_b, cols_b = prob.B.shape
+    ldb = cols_b + pb
+    # the padding and the elements around each operand hold NaN
+    Ast = torch.full((M * lda + off + 8,), nan, dtype=torch.bfloat16)
+    Ast[off:off + M * lda].view(M, lda)[:, :K] = prob.A
+    Bst = torch.full((rows_b * ldb + off + 8,), nan, dtype=torch.bfloat16)
+    Bst[off:off + rows_b * ldb].view(rows_b, ldb)[:, :cols_b] = prob.B
+    Ad, Bd = Ast.to(DEV), Bst.to(DEV)
+    ldc = N + 3
+    Cst = torch.full((M, ldc), -12345.0, dtype=torch.float32, device=DEV)
+    P.note(f"unaligned rows {'NT' if colmajor else 'NN'} {M}x{N}x{K} lda {lda} ldb {ldb} off {off} {dist}")
+    P.run_bf16(Ad[off:], Bd[off:], colmajor, out=Cst, lda=lda, ldb=ldb, ldc=ldc, M=M, N=N, K=K)
+    Cfull = Cst.cpu().numpy()
+    assert (Cfull[:, N:] == -12345.0).all(), "C written outside M x N"
+    C = np.ascontiguousarray(Cfull[:, :N])
+    assert np.isfinite(C).all()
+    Ab, Bb = P.bits16(prob.A), P.bits16(prob.B)
+    _check_sampled(C, lambda r, c: P.oracle_bf16_at(Ab, Bb, colmajor, r, c), M, N, 1024, 9,
+                   exact=(dist == "integer"), what=prob.name)
+    Af = prob.A.double().numpy()
+    Bf = prob.B.double().numpy()
+    _freivalds(C, Af, Bf.T if colmajor else Bf, 10)
+
+
 # ---------------------------------------------------------------- small-M path
 
 # (M, N, K, pad): row-major A and B with padded leading dimensions (multiples
