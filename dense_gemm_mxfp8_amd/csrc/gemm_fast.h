@@ -28,11 +28,9 @@
 //   * MFMA fragments are double-buffered across k-steps: the LDS reads of
 //     step s + 1 are in flight while step s's MFMAs run.
 //   * the last, partial k-tile (K mod BK != 0) is loaded through registers
-//     with element predicates (zero fill past K).
-//   * epilogue: fp32 stores straight from the accumulators, predicated only
-//     on edge tiles, marked non-temporal: C is written once and never read
-//     back, so it should not evict operand lines from L2 and the
-//     Infinity Cache.
+//     with buffer loads, its bytes past K zeroed.
+//   * epilogue: fp32 buffer stores straight from the
+//     accumulators (store_c).
 //
 // Fast-path preconditions (checked on the host): 16-byte aligned A and B,
 // leading dimensions that keep every row 16-byte aligned, 256 rows of either
@@ -69,6 +67,7 @@ struct Args {
     int kt_full;   // number of k-tiles lying entirely inside K
     int sld;       // MX scale bytes per row (K / 32)
     int xcd_remap;
+    int c_nt;      // C stores non-temporal (1) or cached (0)
 };
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -140,55 +139,102 @@ __device__ __forceinline__ void tile_coords(const Args& a, int t, int& tm, int& 
     tn = r / gsz;
 }
 
-// Predicated register load of the partial last k-tile of a K-contiguous
-// operand (256 rows x RB bytes): element k is read only when k < K, rows past
-// `rows` are zero.
-template <int RB, int ESZ>
-__device__ __forceinline__ void load_kc_tail(uint8_t FAST_LDS* dst, const uint8_t* g, int64_t ld_b,
-                                             int rows, int kvalid_b, int tid) {
+// Number of bytes rounded up to whole dwords (buffer range checks work on
+// dwords: a range ending inside the last valid element's dword would drop it).
+__device__ __forceinline__ int64_t round4(int64_t bytes) { return (bytes + 3) & ~(int64_t)3; }
+
+// Keep the first nb bytes (0 .. 16) of a 16-byte chunk, zero the rest.
+__device__ __forceinline__ i32x4 keep_bytes(i32x4 v, int nb) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const int b = nb - 4 * w;
+        if (b <= 0) v[w] = 0;
+        else if (b < 4) v[w] = (int)((uint32_t)v[w] & ((1u << (8 * b)) - 1u));
+    }
+    return v;
+}
+
+// Partial last k-tile of a K-contiguous operand (256 rows x RB bytes) into
+// a stage: buffer loads at byte soff of each row through `rs` (rows past the
+// operand lie outside it and read as zero), bytes at or past kvalid_b zeroed.
+// The rows are 16-byte aligned, so the loads read aligned dwords and a range
+// rounded up to a dword touches nothing past the operand's last dword.
+template <int RB>
+__device__ __forceinline__ void tail_kc(uint8_t FAST_LDS* dst, __amdgpu_buffer_rsrc_t rs, int ld_b, int soff,
+                                        int kvalid_b, int tid) {
     constexpr int CPR = RB / 16;
 #pragma unroll
     for (int i = 0; i < kTile * CPR / kThreads; ++i) {
-        int idx = i * kThreads + tid;
-        int r = idx / CPR, c = idx % CPR;
+        const int idx = i * kThreads + tid;
+        const int r = idx / CPR, c = idx % CPR;
         i32x4 v = {0, 0, 0, 0};
-        if (r < rows) {
-            const uint8_t* src = g + (int64_t)r * ld_b + c * 16;
-            if (c * 16 + 16 <= kvalid_b) {
-                v = *(const i32x4*)src;
-            } else if (c * 16 < kvalid_b) {
-                // the chunk straddles K: assemble its valid bytes (K * ESZ is
-                // a multiple of ESZ, so whole elements are taken)
-                const int nb = kvalid_b - c * 16;
-#pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    uint32_t word = 0;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (4 * w + e < nb) word |= (uint32_t)src[4 * w + e] << (8 * e);
-                    v[w] = (int)word;
-                }
-            }
-        }
+        if (c * 16 < kvalid_b)
+            v = keep_bytes(__builtin_amdgcn_raw_buffer_load_b128(rs, r * ld_b + c * 16, soff, 0), kvalid_b - c * 16);
         *(i32x4 FAST_LDS*)(dst + kc_off<RB>(r, c)) = v;
     }
 }
 
-// Predicated register load of a partial k-tile of row-major B (k rows of 256
-// bf16): rows k >= kvalid are zero.  Columns are in range by the N % 8 == 0
-// precondition except past N, which only feed discarded outputs and are
-// zero-filled here.
+// Partial k-tile of row-major B (k rows of 256 bf16) into a stage: k-rows at
+// or past kvalid and 8-column chunks at or past ncols are zero (N % 8 == 0,
+// so a chunk is either wholly inside N or wholly outside).
 template <int BK>
-__device__ __forceinline__ void load_nn_tail(uint8_t FAST_LDS* dst, const uint8_t* g, int64_t ldb_b,
-                                             int kvalid, int ncols, int tid) {
+__device__ __forceinline__ void tail_nn(uint8_t FAST_LDS* dst, __amdgpu_buffer_rsrc_t rs, int ldb_b, int soff,
+                                        int kvalid, int ncols, int tid) {
 #pragma unroll
     for (int i = 0; i < BK * 32 / kThreads; ++i) {
-        int idx = i * kThreads + tid;
-        int kk = idx >> 5, c = idx & 31;
+        const int idx = i * kThreads + tid;
+        const int kk = idx >> 5, c = idx & 31;
         i32x4 v = {0, 0, 0, 0};
-        if (kk < kvalid && c * 8 < ncols) v = *(const i32x4*)(g + (int64_t)kk * ldb_b + c * 16);
+        if (kk < kvalid && c * 8 < ncols) v = __builtin_amdgcn_raw_buffer_load_b128(rs, kk * ldb_b + c * 16, soff, 0);
         *(i32x4 FAST_LDS*)(dst + nn_off(kk, c * 8)) = v;
     }
+}
+
+// Epilogue of one wave: its 128 x 128 fp32 accumulators to C at rows
+// m0w.., columns n0w..  Accumulator register r of block (i, j) holds
+// C[32 i + 8 (r / 4) + 4 h + r % 4][32 j + l32].  Buffer stores against a
+// descriptor that ends at the wave tile's last element inside C: rows past M
+// fall outside it and are dropped by the hardware, columns past N are
+// predicated (one branch per 32-column block).  Offsets are 32-bit (the
+// host keeps 256 rows of C below 2 GiB), so no 64-bit address per element
+// is formed.  With whole 128-byte lines per 32-column segment the stores are
+// non-temporal (C is written once and never read back, so it should not
+// evict operand lines from L2 and the Infinity Cache); otherwise they are
+// cached so that L2 merges the two halves of each line.
+template <int AUX>
+__device__ __forceinline__ void store_c_aux(const Args& a, const f32x16 (&acc)[kBlocks][kBlocks], int m0w, int n0w,
+                                            int h, int l32) {
+    const int rlim = a.M - m0w;
+    const int clim = a.N - n0w;
+    if (rlim <= 0 || clim <= 0) return;
+    const int rows = rlim < kWaveTile ? rlim : kWaveTile;
+    const int cols = clim < kWaveTile ? clim : kWaveTile;
+    const int ldc4 = (int)a.ldc * 4;
+    const __amdgpu_buffer_rsrc_t rc =
+        make_rsrc(a.C + (int64_t)m0w * a.ldc + n0w, ((int64_t)(rows - 1) * a.ldc + cols) * 4);
+    const int voff = 4 * h * ldc4 + 4 * l32;
+#pragma unroll
+    for (int j = 0; j < kBlocks; ++j) {
+        if (32 * j + l32 < cols) {
+#pragma unroll
+            for (int i = 0; i < kBlocks; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int row = 32 * i + 8 * (r >> 2) + (r & 3);
+                    // copy the element out first: a bit cast applied to a
+                    // vector element directly is compiled as one of element 0
+                    const float v = acc[i][j][r];
+                    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rc, voff + 128 * j,
+                                                          row * ldc4, AUX);
+                }
+        }
+    }
+}
+
+__device__ __forceinline__ void store_c(const Args& a, const f32x16 (&acc)[kBlocks][kBlocks], int m0w, int n0w,
+                                        int h, int l32) {
+    if (a.c_nt) store_c_aux<2>(a, acc, m0w, n0w, h, l32);
+    else store_c_aux<0>(a, acc, m0w, n0w, h, l32);
 }
 
 // Compile-time loop: f(integral_constant<int, B>), ..., f(integral_constant<int, E-1>).
@@ -356,7 +402,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_kernel(Args a) {
         // into zero fill without memory traffic.
         const uint8_t* a_base = a.A + (int64_t)m0 * a.lda_b;
         const __amdgpu_buffer_rsrc_t ra =
-            make_rsrc(a_base, (int64_t)(rows_a - 1) * a.lda_b + (int64_t)a.K * ESZ);
+            make_rsrc(a_base, round4((int64_t)(rows_a - 1) * a.lda_b + (int64_t)a.K * ESZ));
         const uint8_t* b_base;
         __amdgpu_buffer_rsrc_t rb;
         if constexpr (KIND == kNN) {
@@ -364,7 +410,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_kernel(Args a) {
             rb = make_rsrc(b_base, (int64_t)(a.K - 1) * a.ldb_b + (int64_t)(a.N - n0) * 2);
         } else {
             b_base = a.B + (int64_t)n0 * a.ldb_b;
-            rb = make_rsrc(b_base, (int64_t)(rows_b - 1) * a.ldb_b + (int64_t)a.K * ESZ);
+            rb = make_rsrc(b_base, round4((int64_t)(rows_b - 1) * a.ldb_b + (int64_t)a.K * ESZ));
         }
         const __amdgpu_buffer_rsrc_t rdead = make_rsrc(a.A, 0);
         __amdgpu_buffer_rsrc_t rsa = rdead, rsb = rdead;
@@ -592,13 +638,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_kernel(Args a) {
             barrier();  // every wave is done with the pipelined stages
             uint8_t FAST_LDS* As = stage_ptr(std::integral_constant<int, 0>{});
             const int kvalid = a.K - KT * BK;
-            load_kc_tail<RB, ESZ>(As, a_base + (int64_t)KT * RB, a.lda_b, rows_a, kvalid * ESZ, tid);
+            tail_kc<RB>(As, ra, (int)a.lda_b, KT * RB, kvalid * ESZ, tid);
             if constexpr (KIND == kNN)
-                load_nn_tail<BK>(As + OPB, b_base + (int64_t)KT * BK * a.ldb_b, a.ldb_b, kvalid, a.N - n0,
-                                 tid);
+                tail_nn<BK>(As + OPB, rb, (int)a.ldb_b, KT * BK * (int)a.ldb_b, kvalid, a.N - n0, tid);
             else
-                load_kc_tail<RB, ESZ>(As + OPB, b_base + (int64_t)KT * RB, a.ldb_b, rows_b, kvalid * ESZ,
-                                      tid);
+                tail_kc<RB>(As + OPB, rb, (int)a.ldb_b, KT * RB, kvalid * ESZ, tid);
             wait_lgkm0();
             barrier();
 #pragma unroll
@@ -609,32 +653,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_kernel(Args a) {
         }
 
         // ---- epilogue: fp32 stores straight from the accumulators --------
-        const bool full = (rows_a == kTile) && (rows_b == kTile);
-        float* cbase = a.C + (int64_t)(m0 + wm * kWaveTile) * a.ldc + n0 + wn * kWaveTile + l32;
-        if (full) {
-#pragma unroll
-            for (int i = 0; i < kBlocks; ++i)
-#pragma unroll
-                for (int j = 0; j < kBlocks; ++j)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int row = i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-                        __builtin_nontemporal_store(acc[i][j][r], &cbase[(int64_t)row * a.ldc + j * 32]);
-                    }
-        } else {
-            const int rlim = rows_a - wm * kWaveTile;
-            const int clim = rows_b - wn * kWaveTile - l32;
-#pragma unroll
-            for (int i = 0; i < kBlocks; ++i)
-#pragma unroll
-                for (int j = 0; j < kBlocks; ++j)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int row = i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-                        if (row < rlim && j * 32 < clim)
-                            __builtin_nontemporal_store(acc[i][j][r], &cbase[(int64_t)row * a.ldc + j * 32]);
-                    }
-        }
+        store_c(a, acc, m0 + wm * kWaveTile, n0 + wn * kWaveTile, h, l32);
         // The next tile's prologue overwrites stages 0 .. S-2: every wave
         // must be done reading them.
         wait_lgkm0();

@@ -6,12 +6,14 @@
 // and epilogue as the direct-load kernel in gemm_fast.h; only the
 // global -> LDS step differs.  LDS-DMA needs dword-aligned sources, so here
 // each thread fetches its 16-byte chunks with buffer loads into registers
-// (gfx950 serves 16-byte loads at any 2-byte alignment), one k-tile ahead,
-// and writes them into the swizzled stage with ds_write_b128:
+// (gfx950 serves 16-byte loads at any 2-byte alignment), PF k-tiles ahead of
+// the stage being filled, and writes them into the swizzled stage with
+// ds_write_b128:
 //
 //   k-step 0 of k-tile t: store the registers of k-tile t+1 into the other
-//                         stage, issue the loads of k-tile t+2, read the
-//                         fragments of step 1, multiply step 0;
+//                         stage, issue the loads of k-tile t+1+PF into the
+//                         freed registers, read the fragments of step 1,
+//                         multiply step 0;
 //   k-step 1:             wait for LDS, barrier (stage t+1 complete, stage t
 //                         fully read), read step 0 of t+1, multiply step 1.
 //
@@ -49,9 +51,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t span_rsrc(const uint8_t* p, in
     return make_rsrc(p - shift, (shift + bytes + 3) & ~(int64_t)3);
 }
 
-template <int KIND, bool TAIL>
+// PF: k-tiles held in registers ahead of the stage being filled (1 or 2
+// register sets of 8 x 16 bytes per thread).
+template <int KIND, bool TAIL, int PF = 2>
 __global__ __launch_bounds__(kThreads, 1) void gemm_reg_kernel(Args a) {
     static_assert(KIND == kNT || KIND == kNN, "bf16 only");
+    static_assert(PF == 1 || PF == 2, "one or two register sets");
     __shared__ __attribute__((aligned(1024))) uint8_t st0[STAGE];
     __shared__ __attribute__((aligned(1024))) uint8_t st1[STAGE];
 
@@ -119,23 +124,26 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_reg_kernel(Args a) {
             rb = span_rsrc(a.B + (int64_t)n0 * a.ldb_b, (int64_t)(rows_b - 1) * a.ldb_b + (int64_t)a.K * 2, sb);
         const __amdgpu_buffer_rsrc_t rdead = make_rsrc(a.A, 0);
 
-        i32x4 ra_reg[NC], rb_reg[NC];
-        // k-tile kt into registers (zeros for kt >= KT, without traffic)
-        auto load = [&](int kt, bool live) {
+        // k-tile j lives in register set j % PF
+        i32x4 ra_reg[PF][NC], rb_reg[PF][NC];
+        // k-tile kt into register set q (zeros for kt >= KT, without traffic)
+        auto load = [&](auto qidx, int kt, bool live) {
+            constexpr int q = decltype(qidx)::value;
             const int ka = sa + (live ? kt * RB : 0);
             const int kb = sb + (live ? ((KIND == kNN) ? kt * BK * (int)a.ldb_b : kt * RB) : 0);
 #pragma unroll
             for (int i = 0; i < NC; ++i) {
-                ra_reg[i] = __builtin_amdgcn_raw_buffer_load_b128(live ? ra : rdead, a_g[i], ka, 0);
-                rb_reg[i] = __builtin_amdgcn_raw_buffer_load_b128(live ? rb : rdead, b_g[i], kb, 0);
+                ra_reg[q][i] = __builtin_amdgcn_raw_buffer_load_b128(live ? ra : rdead, a_g[i], ka, 0);
+                rb_reg[q][i] = __builtin_amdgcn_raw_buffer_load_b128(live ? rb : rdead, b_g[i], kb, 0);
             }
         };
-        auto store = [&](auto sidx) {
+        auto store = [&](auto qidx, auto sidx) {
+            constexpr int q = decltype(qidx)::value;
             uint8_t FAST_LDS* base = decltype(sidx)::value ? (uint8_t FAST_LDS*)st1 : (uint8_t FAST_LDS*)st0;
 #pragma unroll
             for (int i = 0; i < NC; ++i) {
-                *(i32x4 FAST_LDS*)(base + a_l[i]) = ra_reg[i];
-                *(i32x4 FAST_LDS*)(base + b_l[i]) = rb_reg[i];
+                *(i32x4 FAST_LDS*)(base + a_l[i]) = ra_reg[q][i];
+                *(i32x4 FAST_LDS*)(base + b_l[i]) = rb_reg[q][i];
             }
         };
         auto read_frags = [&](auto sidx, int ks, bf16x8* fa, bf16x8* fb) {
@@ -171,10 +179,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_reg_kernel(Args a) {
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
         };
 
-        // prologue: k-tile 0 into stage 0, k-tile 1 in flight to registers
-        load(0, 0 < KT);
-        store(std::integral_constant<int, 0>{});
-        load(1, 1 < KT);
+        // prologue: k-tile 0 into stage 0, k-tiles 1 .. PF in flight to registers
+        using Z = std::integral_constant<int, 0>;
+        using O = std::integral_constant<int, PF - 1>;
+        load(Z{}, 0, 0 < KT);
+        if constexpr (PF == 2) load(O{}, 1, 1 < KT);
+        store(Z{}, Z{});
+        load(Z{}, PF, PF < KT);
         wait_lgkm0();
         barrier();
         bf16x8 F0a[kBlocks], F0b[kBlocks], F1a[kBlocks], F1b[kBlocks];
@@ -184,8 +195,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_reg_kernel(Args a) {
             constexpr int sn = decltype(sidx)::value ^ 1;
             // k-step 0: stage of k-tile kt+1 <- registers, loads of kt+2,
             // fragments of step 1
-            store(std::integral_constant<int, sn>{});
-            load(kt + 2, kt + 2 < KT);
+            // k-tile kt+1 sits in set (kt+1) % PF; kt+1+PF goes there next
+            using Q = std::integral_constant<int, PF == 2 ? sn : 0>;
+            store(Q{}, std::integral_constant<int, sn>{});
+            load(Q{}, kt + 1 + PF, kt + 1 + PF < KT);
             read_frags(sidx, 1, F1a, F1b);
             mfma(F0a, F0b);
             __builtin_amdgcn_sched_barrier(0);
@@ -203,52 +216,55 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_reg_kernel(Args a) {
 
         if constexpr (TAIL) {
             // Last k-tile KT, holding kvalid (1 .. 32) k.  Chunks lying
-            // wholly inside the data are buffer loads; the chunk that
+            // wholly inside the data are 16-byte loads; the chunk that
             // straddles the end of a row (K-contiguous operands) or of the
-            // last columns (row-major B) is read element by element, so no
+            // last columns (row-major B) is read as 2-byte elements, so no
             // load reaches past the operand's last element; the rest is zero.
+            // Rows past M / N read as zero through the descriptors.
             const int kvalid = a.K - KT * BK;
-            const uint16_t* ag = (const uint16_t*)(a.A + (int64_t)m0 * a.lda_b) + KT * BK;
-            const uint16_t* bg = (KIND == kNN) ? (const uint16_t*)(a.B + (int64_t)KT * BK * a.ldb_b) + n0
-                                               : (const uint16_t*)(a.B + (int64_t)n0 * a.ldb_b) + KT * BK;
-            auto gather = [](const uint16_t* p, int n) {
+            // 8 elements from byte offset voff + soff, element e kept if e < n;
+            // 2-byte loads never straddle the end of the data
+            auto gather = [](__amdgpu_buffer_rsrc_t rs, int voff, int soff, int n) {
                 i32x4 v = {0, 0, 0, 0};
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    if (e < n) v[e >> 1] |= (int)((uint32_t)p[e] << (16 * (e & 1)));
+                for (int e = 0; e < 8; ++e) {
+                    const uint32_t x = __builtin_amdgcn_raw_buffer_load_b16(rs, voff + 2 * e, soff, 0);
+                    if (e < n) v[e >> 1] |= (int)(x << (16 * (e & 1)));
+                }
                 return v;
             };
 #pragma unroll
             for (int i = 0; i < NC; ++i) {
                 const int idx = i * kThreads + tid;
-                const int r = idx >> 2, c8 = 8 * (idx & 3);
+                const int c8 = 8 * (idx & 3);
                 i32x4 va = {0, 0, 0, 0};
                 if (c8 + 8 <= kvalid)
                     va = __builtin_amdgcn_raw_buffer_load_b128(ra, a_g[i], sa + KT * RB, 0);
-                else if (c8 < kvalid && r < rows_a)
-                    va = gather(ag + (int64_t)r * (a.lda_b >> 1) + c8, kvalid - c8);
-                ra_reg[i] = va;
+                else if (c8 < kvalid)
+                    va = gather(ra, a_g[i], sa + KT * RB, kvalid - c8);
+                ra_reg[0][i] = va;
                 i32x4 vb = {0, 0, 0, 0};
                 if constexpr (KIND == kNN) {
                     const int kk = idx >> 5, n8 = 8 * (idx & 31);
+                    const int soff = sb + KT * BK * (int)a.ldb_b;
                     if (kk < kvalid) {
                         if (n8 + 8 <= rows_b)
-                            vb = __builtin_amdgcn_raw_buffer_load_b128(rb, b_g[i], sb + KT * BK * (int)a.ldb_b, 0);
+                            vb = __builtin_amdgcn_raw_buffer_load_b128(rb, b_g[i], soff, 0);
                         else if (n8 < rows_b)
-                            vb = gather(bg + (int64_t)kk * (a.ldb_b >> 1) + n8, rows_b - n8);
+                            vb = gather(rb, b_g[i], soff, rows_b - n8);
                     }
                 } else {
                     if (c8 + 8 <= kvalid)
                         vb = __builtin_amdgcn_raw_buffer_load_b128(rb, b_g[i], sb + KT * RB, 0);
-                    else if (c8 < kvalid && r < rows_b)
-                        vb = gather(bg + (int64_t)r * (a.ldb_b >> 1) + c8, kvalid - c8);
+                    else if (c8 < kvalid)
+                        vb = gather(rb, b_g[i], sb + KT * RB, kvalid - c8);
                 }
-                rb_reg[i] = vb;
+                rb_reg[0][i] = vb;
             }
             // the last body ended with a barrier after every wave's reads of
             // k-tile data in stage 0 (KTM is even, so stage 0 is free; the
             // reads that follow that barrier fetch the unused dead k-tile)
-            store(std::integral_constant<int, 0>{});
+            store(Z{}, Z{});
             wait_lgkm0();
             barrier();
 #pragma unroll
@@ -258,20 +274,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_reg_kernel(Args a) {
             }
         }
 
-        // epilogue (as in gemm_fast.h)
-        float* cbase = a.C + (int64_t)(m0 + wm * kWaveTile) * a.ldc + n0 + wn * kWaveTile + l32;
-        const int rlim = rows_a - wm * kWaveTile;
-        const int clim = rows_b - wn * kWaveTile - l32;
-#pragma unroll
-        for (int i = 0; i < kBlocks; ++i)
-#pragma unroll
-            for (int j = 0; j < kBlocks; ++j)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int row = i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-                    if (row < rlim && j * 32 < clim)
-                        __builtin_nontemporal_store(acc[i][j][r], &cbase[(int64_t)row * a.ldc + j * 32]);
-                }
+        store_c(a, acc, m0 + wm * kWaveTile, n0 + wn * kWaveTile, h, l32);
         wait_lgkm0();
         barrier();
     }

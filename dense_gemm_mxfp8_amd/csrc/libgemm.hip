@@ -546,6 +546,10 @@ bool use_big_tiles(int64_t M, int64_t N, int cus) {
     return big * 4 >= (int64_t)cus * 3;
 }
 
+// The 256 x 256 kernels store C with 32-bit buffer offsets: 256 rows of C
+// must span less than 2 GiB.
+bool c_ok(int64_t ldc) { return ldc < ((int64_t)1 << 21); }
+
 // ---------------------------------------------------------------------------
 // Fast path (gemm_fast.h): 256 x 256 tiles, direct-to-LDS buffer loads.
 // ---------------------------------------------------------------------------
@@ -637,6 +641,18 @@ fast::Args make_fast_args(int64_t M, int64_t N, int64_t K, const void* A, int64_
     a.M = (int)M;
     a.N = (int)N;
     a.K = (int)K;
+    // C stores bypass the caches' retention (non-temporal) only when every
+    // 32-column segment a wave stores is a whole 128-byte line; otherwise
+    // each line is written in two parts by two stores, and caching lets L2
+    // merge them instead of sending partial lines to memory (measured on
+    // MI355X: 4001 x 3003 x 2050 with ldc = 3003, 112 -> 92 us).
+    // LIBGEMM_C_NT=0|1 overrides the choice (measurement switch).
+    static int c_nt_env = [] {
+        const char* e = getenv("LIBGEMM_C_NT");
+        return e ? atoi(e) : -1;
+    }();
+    const bool lines = ((uintptr_t)C % 128 == 0) && (ldc % 32 == 0);
+    a.c_nt = c_nt_env >= 0 ? c_nt_env : (lines ? 1 : 0);
     return a;
 }
 
@@ -667,7 +683,8 @@ bool reg_ok(bool nt, int64_t K, int64_t lda, int64_t ldb) {
     return K * ldb * 2 + 4 < lim;
 }
 
-int launch_reg(bool nt, fast::Args a, int cus, hipStream_t stream) {
+template <int PF>
+int launch_reg_pf(bool nt, fast::Args a, int cus, hipStream_t stream) {
     a.tiles_m = (a.M + fast::kTile - 1) / fast::kTile;
     a.tiles_n = (a.N + fast::kTile - 1) / fast::kTile;
     a.num_tiles = a.tiles_m * a.tiles_n;
@@ -685,13 +702,23 @@ int launch_reg(bool nt, fast::Args a, int cus, hipStream_t stream) {
     const bool tail = a.kt_total > a.kt_full;
     const dim3 blk(fast::kThreads);
     if (nt) {
-        if (tail) hipLaunchKernelGGL((regpath::gemm_reg_kernel<fast::kNT, true>), dim3(grid), blk, 0, stream, a);
-        else hipLaunchKernelGGL((regpath::gemm_reg_kernel<fast::kNT, false>), dim3(grid), blk, 0, stream, a);
+        if (tail) hipLaunchKernelGGL((regpath::gemm_reg_kernel<fast::kNT, true, PF>), dim3(grid), blk, 0, stream, a);
+        else hipLaunchKernelGGL((regpath::gemm_reg_kernel<fast::kNT, false, PF>), dim3(grid), blk, 0, stream, a);
     } else {
-        if (tail) hipLaunchKernelGGL((regpath::gemm_reg_kernel<fast::kNN, true>), dim3(grid), blk, 0, stream, a);
-        else hipLaunchKernelGGL((regpath::gemm_reg_kernel<fast::kNN, false>), dim3(grid), blk, 0, stream, a);
+        if (tail) hipLaunchKernelGGL((regpath::gemm_reg_kernel<fast::kNN, true, PF>), dim3(grid), blk, 0, stream, a);
+        else hipLaunchKernelGGL((regpath::gemm_reg_kernel<fast::kNN, false, PF>), dim3(grid), blk, 0, stream, a);
     }
     return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
+}
+
+// LIBGEMM_REGPF=1|2: register sets of prefetch (measurement switch)
+int launch_reg(bool nt, const fast::Args& a, int cus, hipStream_t stream) {
+    static int pf = [] {
+        const char* e = getenv("LIBGEMM_REGPF");
+        return e ? atoi(e) : 0;
+    }();
+    if (pf == 1) return launch_reg_pf<1>(nt, a, cus, stream);
+    return launch_reg_pf<2>(nt, a, cus, stream);
 }
 
 // ---------------------------------------------------------------------------
@@ -764,9 +791,14 @@ int bf16_dispatch(bool nt, int64_t M, int64_t N, int64_t K, const void* A, int64
     if (small_ok(nt, M, N, K, A, lda, B, ldb))
         return launch_small_bf16(M, N, K, A, lda, B, ldb, C, ldc, s);
     const bool big = use_big_tiles(M, N, dev.cus);
-    if (big && fast_ok(nt ? fast::kNT : fast::kNN, M, N, K, A, lda, B, ldb, nullptr, nullptr))
+    // LIBGEMM_FORCE_REG=1 runs the register-load kernel where the direct-load
+    // one would (measurement switch)
+    static const bool force_reg = getenv("LIBGEMM_FORCE_REG") != nullptr;
+    if (force_reg && big && c_ok(ldc) && reg_ok(nt, K, lda, ldb))
+        return launch_reg(nt, make_fast_args(M, N, K, A, lda, B, ldb, C, ldc, 2), dev.cus, s);
+    if (big && c_ok(ldc) && fast_ok(nt ? fast::kNT : fast::kNN, M, N, K, A, lda, B, ldb, nullptr, nullptr))
         return launch_fast_bf16(nt, make_fast_args(M, N, K, A, lda, B, ldb, C, ldc, 2), dev.cus, s);
-    if (big && reg_ok(nt, K, lda, ldb))
+    if (big && c_ok(ldc) && reg_ok(nt, K, lda, ldb))
         return launch_reg(nt, make_fast_args(M, N, K, A, lda, B, ldb, C, ldc, 2), dev.cus, s);
     if (nt) {
         if (big) return direct ? launch<256, 256, kBf16NT, true>(a, dev.cus, s)
@@ -811,7 +843,7 @@ int gemm_mxfp8(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, cons
     a.SA = scaleA;
     a.SB = scaleB;
     a.sld = (int)(K / 32);
-    if (use_big_tiles(M, N, dev.cus) && fast_ok(fast::kMX, M, N, K, A, lda, B, ldb, scaleA, scaleB)) {
+    if (use_big_tiles(M, N, dev.cus) && c_ok(ldc) && fast_ok(fast::kMX, M, N, K, A, lda, B, ldb, scaleA, scaleB)) {
         fast::Args f = make_fast_args(M, N, K, A, lda, B, ldb, C, ldc, 1);
         f.SA = scaleA;
         f.SB = scaleB;
