@@ -12,6 +12,12 @@ Prints ONE JSON line: TFLOP/s (2 M N K per step / time), the roofline block
 of the GEMM kernel (per-launch duration from HIP events on the launch
 stream, against the MI355X dense MFMA peak) and the CPU oracle timed on a
 bounded row sample of the same workload on this host.
+
+Before the W warm-up steps the step runs untimed for --settle seconds: an
+idle MI355X needs tens of milliseconds of load before its clocks leave the
+idle state, and without this the timed steps measure the ramp.  The shader
+clock and board power are sampled from sysfs during the timed steps and
+reported under "clocks".
 """
 from __future__ import annotations
 
@@ -42,6 +48,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=1024,
                     help="rows of A in the oracle's timed sample")
+    ap.add_argument("--settle", type=float, default=0.3,
+                    help="seconds of untimed steps before the warm-up, so the GPU's clocks "
+                         "leave their idle state (reported as settle_s)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain device copy of COPY_BYTES (for scaling HBM counters)")
     return ap.parse_args()
@@ -72,7 +81,77 @@ def operand_bytes(w) -> int:
     return 2 * (M * K + K * N) + 4 * M * N
 
 
-def bench_workload(name: str, steps: int, warmup: int):
+class ClockSampler:
+    """Samples the GPU's shader clock and board power from sysfs (the amdgpu
+    driver's pp_dpm_sclk and hwmon power1_input) on a background thread while
+    the timed steps run.  Reports None where the files are not readable."""
+
+    def __init__(self, period_s: float = 0.004):
+        import threading
+        self.period = period_s
+        self.sclk, self.power = [], []
+        self.dev = self._device_dir()
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    @staticmethod
+    def _device_dir():
+        try:
+            import torch
+            p = torch.cuda.get_device_properties(0)
+            path = "/sys/bus/pci/devices/%04x:%02x:%02x.0" % (p.pci_domain_id, p.pci_bus_id, p.pci_device_id)
+            return path if os.path.isdir(path) else None
+        except Exception:
+            return None
+
+    def _read(self):
+        try:
+            with open(os.path.join(self.dev, "pp_dpm_sclk")) as fh:
+                for ln in fh:
+                    if ln.startswith("S:") or ln.rstrip().endswith("*"):
+                        self.sclk.append(float(ln.split(":")[1].strip().split("Mhz")[0]))
+                        break
+        except Exception:
+            pass
+        try:
+            import glob
+            for h in glob.glob(os.path.join(self.dev, "hwmon", "hwmon*", "power1_input")):
+                with open(h) as fh:
+                    self.power.append(float(fh.read()) / 1e6)
+                break
+        except Exception:
+            pass
+
+    def _run(self):
+        while not self._stop.is_set():
+            self._read()
+            time.sleep(self.period)
+
+    def __enter__(self):
+        if self.dev:
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self._thread.is_alive():
+            self._thread.join()
+
+    def summary(self):
+        if not self.sclk and not self.power:
+            return None
+        out = {"samples": max(len(self.sclk), len(self.power)),
+               "source": "sysfs pp_dpm_sclk, hwmon power1_input"}
+        if self.sclk:
+            out["sclk_mhz"] = {"median": float(np.median(self.sclk)), "min": min(self.sclk),
+                               "max": max(self.sclk)}
+        if self.power:
+            out["power_w"] = {"median": round(float(np.median(self.power)), 1),
+                              "max": round(max(self.power), 1)}
+        return out
+
+
+def bench_workload(name: str, steps: int, warmup: int, settle: float = 0.0):
     import torch
     import dense_gemm_mxfp8_amd as dg
     from dense_gemm_mxfp8_amd import inputs
@@ -112,30 +191,56 @@ def bench_workload(name: str, steps: int, warmup: int):
                 raise RuntimeError(dg.gemm_strerror(rc))
         dtype, peak_key = "bf16", "bf16"
 
+    # The clocks ramp up from idle over the first tens of milliseconds of
+    # work; settle steps bring them to their loaded state before the warm-up.
+    settle_steps = 0
+    t_settle = time.perf_counter()
+    while time.perf_counter() - t_settle < settle:
+        for _ in range(8):
+            step(settle_steps)
+            settle_steps += 1
+        torch.cuda.synchronize()
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    t0 = time.perf_counter()
-    for i in range(steps):
+    # Timed region: K back-to-back launches between two events on the launch
+    # stream; the mean launch duration is their span over K.  Events between
+    # the launches would add a marker's latency to every launch, which shows
+    # on the short kernels.
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    with ClockSampler() as clocks:
+        t0 = time.perf_counter()
+        ev0.record(stream)
+        for i in range(steps):
+            step(i)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    mean_ms = ev0.elapsed_time(ev1) / steps
+    # Spread of single launches: a separate, untimed pass with events around
+    # each launch (these include the marker latency).
+    nd = min(steps, 50)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(nd)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(nd)]
+    for i in range(nd):
         starts[i].record(stream)
         step(i)
         ends[i].record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     per = np.array([a.elapsed_time(b) for a, b in zip(starts, ends)])  # ms per launch
     flops = 2.0 * M * N * K
     ms_step = wall * 1e3 / steps
     res = {
         "workload": name, "M": M, "N": N, "K": K, "dtype": dtype, "peak_key": peak_key,
         "flops": flops, "bytes": bytes_per_step, "ms_per_step": ms_step,
-        "kernel_ms_mean": float(per.mean()), "kernel_ms_median": float(np.median(per)),
+        "kernel_ms_mean": float(mean_ms), "kernel_ms_median": float(np.median(per)), "single_launches": nd,
         "kernel_ms_p10": float(np.percentile(per, 10)),
         "kernel_ms_p90": float(np.percentile(per, 90)),
         "tflops": flops / (ms_step * 1e-3) / 1e12,
         "layout": ("NT" if getattr(prob, "b_colmajor", True) else "NN"),
         "dist": w.get("dist"), "operand_copies": copies,
+        "settle_s": round(settle, 3), "settle_steps": settle_steps, "clocks": clocks.summary(),
     }
     return res, prob
 
@@ -196,9 +301,14 @@ def line(res, steps, warmup, cpu=None, headline=True):
                    "output": "fp32", "parallelism": "single-gpu"},
         "kernel_ms": {"mean": round(res["kernel_ms_mean"], 5),
                       "median": round(res["kernel_ms_median"], 5),
-                      "p10": round(res["kernel_ms_p10"], 5), "p90": round(res["kernel_ms_p90"], 5)},
+                      "p10": round(res["kernel_ms_p10"], 5), "p90": round(res["kernel_ms_p90"], 5),
+                      "single_launches": res["single_launches"],
+                      "method": "mean: events around the K timed launches / K; median, p10, p90: "
+                                "events around single launches in a separate pass after them"},
         "pct_of_peak": round(100 * achieved / peak, 2),
         "roofline": roof,
+        "settle_s": res["settle_s"],
+        "clocks": res["clocks"],
     }
     if cpu is not None:
         out["cpu_baseline"] = cpu
@@ -226,7 +336,7 @@ def main():
     for i, name in enumerate(names):
         print(f"[bench] {name}: warmup {args.warmup}, steps {args.steps}", file=sys.stderr,
               flush=True)
-        res, prob = bench_workload(name, args.steps, args.warmup)
+        res, prob = bench_workload(name, args.steps, args.warmup, args.settle)
         cpu = None
         if i == 0 and not args.no_cpu_baseline:
             print(f"[bench] oracle on {args.cpu_rows} rows", file=sys.stderr, flush=True)

@@ -268,7 +268,13 @@ __device__ __forceinline__ void interleave_step() {
 // codes with the tile (one 2- or 4-byte load per row); SG > 1 keeps a
 // double-buffered ring of scale groups in LDS and fetches 4 * SG bytes per
 // row once per group, which cuts the scale loads' L2 requests SG-fold.
-template <int KIND, int RB, int S, bool TAIL, int SG = 1>
+// E (two stages only): DMA instructions of k-tile kt + 2 issued in the last
+// k-step of k-tile kt, right after the barrier that frees its stage, instead
+// of in the first k-steps of kt + 1; an earlier start gives the loads more
+// time before the wait that needs them.
+// D (two stages only): k-steps over which the rest of the DMA of k-tile
+// kt + 1 is spread, starting at k-step 0 of kt (0: all but the last).
+template <int KIND, int RB, int S, bool TAIL, int SG = 1, int E = 0, int D = 0>
 __global__ __launch_bounds__(kThreads, 1) void gemm_fast_kernel(Args a) {
     constexpr int ESZ = (KIND == kMX) ? 1 : 2;  // operand element bytes
     constexpr int BK = RB / ESZ;                // K elements per k-tile
@@ -302,8 +308,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_kernel(Args a) {
     // k-step (the part issued after the closing wait is simply younger than
     // what that wait needs); with S == 2 all of it must be issued before
     // the wait, so it covers k-steps 0 .. KS-2.
-    constexpr int DSTEPS = (S >= 3) ? KS : KS - 1;
-    constexpr int DPS = (L + DSTEPS - 1) / DSTEPS;  // DMA instructions per k-step
+    static_assert(E == 0 || (S == 2 && E <= L), "early DMA: two stages");
+    static_assert(D == 0 || (S == 2 && D < KS), "DMA spread: two stages");
+    constexpr int DSTEPS = (S >= 3) ? KS : (D > 0 ? D : KS - 1);
+    constexpr int DPS = (L - E + DSTEPS - 1) / DSTEPS;  // DMA instructions per k-step
     // DMA instructions of the current k-tile issued before the closing wait
     constexpr int DBEFORE = (KS - 1) * DPS < L ? (KS - 1) * DPS : L;
     // Loads younger than k-tile kt+1's when the closing wait of k-tile kt
@@ -557,7 +565,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_kernel(Args a) {
              ...);
         }(std::make_integer_sequence<int, S - 1>{});
         ring_dma(std::integral_constant<int, 0>{}, 0, 0 < KT);
-        wait_vm<(SG > 1) ? 0 : (S - 2) * L>();
+        // early part of k-tile 1 (two stages)
+#pragma unroll
+        for (int d = 0; d < E; ++d) dma(std::integral_constant<int, 1>{}, d, 1, 1 < KT);
+        wait_vm<((SG > 1) ? 0 : (S - 2) * L) + E>();
         barrier();
 
         Frag F0a[kBlocks], F0b[kBlocks], F1a[kBlocks], F1b[kBlocks];
@@ -582,8 +593,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_kernel(Args a) {
                 Frag* cb = gp ? F1b : F0b;
                 Frag* na = gp ? F0a : F1a;
                 Frag* nb = gp ? F0b : F1b;
-                constexpr int d0 = ks * DPS < L ? ks * DPS : L;
-                constexpr int d1 = (ks + 1) * DPS < L ? (ks + 1) * DPS : L;
+                constexpr int d0 = E + ks * DPS < L ? E + ks * DPS : L;
+                constexpr int d1 = E + (ks + 1) * DPS < L ? E + (ks + 1) * DPS : L;
                 if constexpr (ks + 1 < KS) {
                     read_frags(sidx, ks + 1, na, nb);
                     static_for<d0, d1>([&](auto dc) {
@@ -609,6 +620,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_kernel(Args a) {
                     static_for<d0, d1>([&](auto dc) {
                         dma(std::integral_constant<int, sdma>{}, decltype(dc)::value, kd, live);
                     });
+                    // two stages: stage s is free now; start k-tile kt + 2
+                    static_for<0, E>([&](auto dc) {
+                        dma(sidx, decltype(dc)::value, kt + 2, kt + 2 < KT);
+                    });
                     if constexpr (KIND == kMX) {
 #pragma unroll
                         for (int q = 0; q < 2 * kBlocks; ++q) scn[q] = sc[q];
@@ -617,7 +632,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_kernel(Args a) {
                     } else {
                         mfma(ks, ca, cb, sc);
                     }
-                    interleave_step<NR, d1 - d0>();
+                    interleave_step<NR, d1 - d0 + E>();
                     __builtin_amdgcn_sched_barrier(0);
                 }
             });

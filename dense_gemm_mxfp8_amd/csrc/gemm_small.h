@@ -38,6 +38,7 @@ struct Args {
     int64_t lda_b, ldb_b, ldc;
     int M, N, K;
     int kw;   // k-rows per wave (a multiple of kStepK)
+    int pair_xcd;  // map neighbouring column blocks onto one XCD (grid % 16 == 0)
 };
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -75,7 +76,17 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_small_m_nn(Args a) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int n0 = blockIdx.x * kCols;
+    // Workgroups are dispatched round-robin over the 8 XCDs (workgroup b on
+    // XCD b % 8).  With 32-column blocks two neighbouring blocks share every
+    // 128-byte line of B; numbering them b = 8q + x -> block 16 (q / 2) +
+    // 2x + q % 2 puts both halves of each line on XCD x, so its L2 fetches
+    // the line once instead of two L2s fetching it each.
+    int blk = blockIdx.x;
+    if (a.pair_xcd) {
+        const int q = blk >> 3, x = blk & 7;
+        blk = 16 * (q >> 1) + 2 * x + (q & 1);
+    }
+    const int n0 = blk * kCols;
     // wave w takes the 32-row steps w, w + WAVES, w + 2 WAVES, ...: all
     // waves (and all workgroups) sweep one contiguous band of B rows together
     const int steps = a.kw / kStepK;

@@ -554,26 +554,30 @@ bool c_ok(int64_t ldc) { return ldc < ((int64_t)1 << 21); }
 // Fast path (gemm_fast.h): 256 x 256 tiles, direct-to-LDS buffer loads.
 // ---------------------------------------------------------------------------
 
-// Pipeline variant of the fast kernel: k-tile bytes per operand row and LDS
-// stages.  LIBGEMM_VARIANT=<rb>x<stages> (e.g. 64x4) selects a compiled one
-// for measurements; the defaults (measured on MI355X at 4096^3 and 8192^3)
-// are 128x2 for bf16 NT, 64x4 for bf16 NN and 64x4 for MX.
+// Pipeline variant of the fast kernel: k-tile bytes per operand row, LDS
+// stages and the early-DMA split.  The defaults, measured on MI355X at 4096^3
+// and 8192^3, are 128-byte rows x 2 stages for bf16 NT and NN (early 6,
+// spread 2) and for MX (scale ring, early 12).
 struct FastVariant {
-    int rb, stages, group;
+    int rb, stages, group, early, spread;
 };
 
-// LIBGEMM_VARIANT=<rb>x<stages> picks the pipeline; LIBGEMM_GROUP=<n> the
-// number of tile rows per raster band.
+// LIBGEMM_VARIANT=<rb>x<stages>[e<early>[d<spread>]] picks the pipeline (and
+// for two stages the early-DMA split); LIBGEMM_GROUP=<n> the number of tile
+// rows per raster band.
 FastVariant env_variant() {
     static FastVariant v = [] {
-        FastVariant r{0, 0, 0};
+        FastVariant r{0, 0, 0, -1, 0};
         const char* e = getenv("LIBGEMM_VARIANT");
         if (e) {
-            int rb = 0, st = 0;
-            if (sscanf(e, "%dx%d", &rb, &st) == 2) {
+            int rb = 0, st = 0, ea = -1, sp = 0;
+            const int n = sscanf(e, "%dx%de%dd%d", &rb, &st, &ea, &sp);
+            if (n >= 2) {
                 r.rb = rb;
                 r.stages = st;
             }
+            if (n >= 3) r.early = ea;
+            if (n == 4) r.spread = sp;
         }
         const char* g = getenv("LIBGEMM_GROUP");
         if (g) r.group = atoi(g);
@@ -582,7 +586,7 @@ FastVariant env_variant() {
     return v;
 }
 
-template <int KIND, int RB, int S, int SG = 1>
+template <int KIND, int RB, int S, int SG = 1, int E = 0, int D = 0>
 int launch_fast(fast::Args a, int cus, hipStream_t stream, int group_m = 0) {
     constexpr int BK = RB / (KIND == fast::kMX ? 1 : 2);
     a.tiles_m = (a.M + fast::kTile - 1) / fast::kTile;
@@ -596,11 +600,11 @@ int launch_fast(fast::Args a, int cus, hipStream_t stream, int group_m = 0) {
     if (grid >= 8) grid -= grid % 8;
     a.xcd_remap = (grid % 8 == 0) ? 1 : 0;
     if (a.kt_total > a.kt_full)
-        hipLaunchKernelGGL((fast::gemm_fast_kernel<KIND, RB, S, true, SG>), dim3(grid), dim3(fast::kThreads), 0,
+        hipLaunchKernelGGL((fast::gemm_fast_kernel<KIND, RB, S, true, SG, E, D>), dim3(grid), dim3(fast::kThreads), 0,
                            stream, a);
     else
-        hipLaunchKernelGGL((fast::gemm_fast_kernel<KIND, RB, S, false, SG>), dim3(grid), dim3(fast::kThreads), 0,
-                           stream, a);
+        hipLaunchKernelGGL((fast::gemm_fast_kernel<KIND, RB, S, false, SG, E, D>), dim3(grid), dim3(fast::kThreads),
+                           0, stream, a);
     return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
 }
 
@@ -663,10 +667,17 @@ int launch_fast_bf16(bool nt, const fast::Args& a, int cus, hipStream_t s) {
         if (v.rb == 64 && v.stages == 3) return launch_fast<fast::kNT, 64, 3>(a, cus, s, g);
         if (v.rb == 64 && v.stages == 4) return launch_fast<fast::kNT, 64, 4>(a, cus, s, g);
         if (v.rb == 64 && v.stages == 5) return launch_fast<fast::kNT, 64, 5>(a, cus, s, g);
-        return launch_fast<fast::kNT, 128, 2>(a, cus, s, g);
+        if (v.early == 0) return launch_fast<fast::kNT, 128, 2>(a, cus, s, g);
+        // default: 6 DMA instructions of k-tile t+2 right after the barrier
+        // of k-tile t, the other 10 over k-steps 0 and 1 of t+1 (MI355X,
+        // 8192^3, same box: 776.5 -> 746.5 us and 797.6 -> 778.2 us)
+        return launch_fast<fast::kNT, 128, 2, 1, 6, 2>(a, cus, s, g);
     }
-    if (v.rb == 128 && v.stages == 2) return launch_fast<fast::kNN, 128, 2>(a, cus, s, g);
-    return launch_fast<fast::kNN, 64, 4>(a, cus, s, g);
+    if (v.rb == 64 && v.stages == 4) return launch_fast<fast::kNN, 64, 4>(a, cus, s, g);
+    if (v.rb == 128 && v.stages == 2 && v.early == 0) return launch_fast<fast::kNN, 128, 2>(a, cus, s, g);
+    // default: as NT (MI355X, 4096^3: 108.8 -> 105.5 us against 64 x 4;
+    // 8192^3: 801.5 -> 771.2 us)
+    return launch_fast<fast::kNN, 128, 2, 1, 6, 2>(a, cus, s, g);
 }
 
 // ---------------------------------------------------------------------------
@@ -753,6 +764,12 @@ int launch_small(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, co
     const int64_t per = (K + WAVES - 1) / WAVES;
     a.kw = (int)((per + small::kStepK - 1) / small::kStepK * small::kStepK);
     const int grid = (int)((N + COLS - 1) / COLS);
+    static const int pair_env = [] {
+        const char* e = getenv("LIBGEMM_SMALL_PAIR");
+        return e ? atoi(e) : -1;
+    }();
+    a.pair_xcd = (COLS == 32 && grid % 16 == 0) ? 1 : 0;
+    if (pair_env == 0) a.pair_xcd = 0;  // measurement switch
     hipLaunchKernelGGL((small::gemm_small_m_nn<MB, NP, COLS, WAVES>), dim3(grid), dim3(64 * WAVES), 0, stream, a);
     return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
 }
@@ -856,8 +873,14 @@ int gemm_mxfp8(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, cons
         const bool ring = (K % 512 == 0) && !(sal & 15);
         const bool word_scales = (K % 128 == 0) && !(sal & 3);
         if (v.rb == 64 && v.stages == 4) return launch_fast<fast::kMX, 64, 4>(f, dev.cus, s, v.group);
-        if (ring && !(v.rb == 128 && v.stages == 2))
-            return launch_fast<fast::kMX, 128, 2, 4>(f, dev.cus, s, v.group);
+        if (ring && !(v.rb == 128 && v.stages == 2)) {
+            if (v.early == 0) return launch_fast<fast::kMX, 128, 2, 4>(f, dev.cus, s, v.group);
+            if (v.early == 8) return launch_fast<fast::kMX, 128, 2, 4, 8>(f, dev.cus, s, v.group);
+            // default: 12 of the 16 DMA instructions of k-tile t+2 right
+            // after the barrier of k-tile t (MI355X, 8192^3, same box:
+            // 491.5 -> 427.4 us)
+            return launch_fast<fast::kMX, 128, 2, 4, 12>(f, dev.cus, s, v.group);
+        }
         if (word_scales) return launch_fast<fast::kMX, 128, 2>(f, dev.cus, s, v.group);
         return launch_fast<fast::kMX, 64, 4>(f, dev.cus, s, v.group);
     }

@@ -110,28 +110,40 @@ def stats(args) -> None:
         lines.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
                      f"{float(r['Percentage']):.2f} |")
+    bench = None
+    if args.bench_json:
+        import json
+        with open(args.bench_json) as fh:
+            first = fh.readline()
+        if first.strip():
+            bench = json.loads(first)
     if args.trace:
-        # per-dispatch durations of the matching kernel, skipping the first
-        # `skip` launches (the benchmark's warm-up), to compare with the
-        # benchmark's own event timing of the timed launches
+        # per-dispatch durations of the matching kernel.  With the benchmark's
+        # JSON line at hand its timed launches are the `steps` ones before the
+        # final single-launch pass (the settle and warm-up launches come
+        # first); otherwise the first `skip` launches are dropped.
         durs = []
         with open(args.trace) as fh:
             for r in csv.DictReader(fh):
                 if args.match in r["Kernel_Name"]:
                     durs.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
         durs.sort()
-        timed = [d for _, d in durs[args.skip:]]
+        if bench is not None and bench.get("steps"):
+            tail = int(bench.get("kernel_ms", {}).get("single_launches", 0))
+            end = len(durs) - tail
+            timed = [d for _, d in durs[end - int(bench["steps"]):end]]
+            which = f"the benchmark's {len(timed)} timed steps"
+        else:
+            timed = [d for _, d in durs[args.skip:]]
+            which = f"after the first {args.skip}"
         if timed:
             timed_sorted = sorted(timed)
-            lines += ["", f"Timed launches of `{args.match}` (after the first {args.skip}): {len(timed)}, "
+            lines += ["", f"Timed launches of `{args.match}` ({which}): {len(timed)}, "
                       f"average {sum(timed) / len(timed) / 1e3:.2f} us, "
                       f"median {timed_sorted[len(timed) // 2] / 1e3:.2f} us"]
-    if args.bench_json:
-        import json
-        with open(args.bench_json) as fh:
-            first = fh.readline()
-        if first.strip():
-            d = json.loads(first)
+    if bench is not None:
+        if True:
+            d = bench
             km = d.get("kernel_ms", {})
             lines += ["", f"The benchmark's own HIP-event timing of the same launches: mean "
                       f"{km.get('mean', float('nan')) * 1e3:.2f} us, median "
