@@ -201,20 +201,20 @@ __device__ __forceinline__ void tail_nn(uint8_t FAST_LDS* dst, __amdgpu_buffer_r
 // non-temporal (C is written once and never read back, so it should not
 // evict operand lines from L2 and the Infinity Cache); otherwise they are
 // cached so that L2 merges the two halves of each line.
-template <int AUX>
-__device__ __forceinline__ void store_c_aux(const Args& a, const f32x16 (&acc)[kBlocks][kBlocks], int m0w, int n0w,
+template <int AUX, int NBJ>
+__device__ __forceinline__ void store_c_aux(const Args& a, const f32x16 (&acc)[kBlocks][NBJ], int m0w, int n0w,
                                             int h, int l32) {
     const int rlim = a.M - m0w;
     const int clim = a.N - n0w;
     if (rlim <= 0 || clim <= 0) return;
     const int rows = rlim < kWaveTile ? rlim : kWaveTile;
-    const int cols = clim < kWaveTile ? clim : kWaveTile;
+    const int cols = clim < 32 * NBJ ? clim : 32 * NBJ;
     const int ldc4 = (int)a.ldc * 4;
     const __amdgpu_buffer_rsrc_t rc =
         make_rsrc(a.C + (int64_t)m0w * a.ldc + n0w, ((int64_t)(rows - 1) * a.ldc + cols) * 4);
     const int voff = 4 * h * ldc4 + 4 * l32;
 #pragma unroll
-    for (int j = 0; j < kBlocks; ++j) {
+    for (int j = 0; j < NBJ; ++j) {
         if (32 * j + l32 < cols) {
 #pragma unroll
             for (int i = 0; i < kBlocks; ++i)
@@ -231,10 +231,11 @@ __device__ __forceinline__ void store_c_aux(const Args& a, const f32x16 (&acc)[k
     }
 }
 
-__device__ __forceinline__ void store_c(const Args& a, const f32x16 (&acc)[kBlocks][kBlocks], int m0w, int n0w,
-                                        int h, int l32) {
-    if (a.c_nt) store_c_aux<2>(a, acc, m0w, n0w, h, l32);
-    else store_c_aux<0>(a, acc, m0w, n0w, h, l32);
+template <int NBJ = kBlocks>
+__device__ __forceinline__ void store_c(const Args& a, const f32x16 (&acc)[kBlocks][NBJ], int m0w, int n0w, int h,
+                                        int l32) {
+    if (a.c_nt) store_c_aux<2, NBJ>(a, acc, m0w, n0w, h, l32);
+    else store_c_aux<0, NBJ>(a, acc, m0w, n0w, h, l32);
 }
 
 // Compile-time loop: f(integral_constant<int, B>), ..., f(integral_constant<int, E-1>).

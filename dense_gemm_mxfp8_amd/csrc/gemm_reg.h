@@ -42,7 +42,7 @@ constexpr int BK = 32;            // k per k-tile
 constexpr int KS = 2;             // 16-deep MFMA steps per k-tile
 constexpr int OPB = kTile * RB;   // 16 KiB per operand per stage
 constexpr int STAGE = 2 * OPB;
-constexpr int NC = OPB / 16 / kThreads;  // 16-byte chunks per thread per operand (4)
+constexpr int NC = OPB / 16 / kThreads;  // 16-byte chunks of A per thread (4)
 
 // Descriptor over [p, p + bytes) with its base rounded down to a dword;
 // `shift` receives the byte offset of p from that base.
@@ -52,11 +52,17 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t span_rsrc(const uint8_t* p, in
 }
 
 // PF: k-tiles held in registers ahead of the stage being filled (1 or 2
-// register sets of 8 x 16 bytes per thread).
-template <int KIND, bool TAIL, int PF = 2>
+// register sets).  BN: tile columns, 256 or 192 (wave tiles 128 x BN/2); the
+// narrower tile lets the host match the tile count to the CU count.
+template <int KIND, bool TAIL, int PF = 2, int BN = kTile>
 __global__ __launch_bounds__(kThreads, 1) void gemm_reg_kernel(Args a) {
     static_assert(KIND == kNT || KIND == kNN, "bf16 only");
     static_assert(PF == 1 || PF == 2, "one or two register sets");
+    static_assert(BN == 256 || BN == 192, "tile columns");
+    constexpr int NBJ = BN / 64;      // 32-column MFMA blocks per wave tile
+    constexpr int WTN = BN / 2;       // wave tile columns
+    constexpr int CPK = BN / 8;       // row-major B: 16-byte chunks per k-row
+    constexpr int NCB = 4 * BN / kThreads;  // 16-byte chunks of B per thread
     __shared__ __attribute__((aligned(1024))) uint8_t st0[STAGE];
     __shared__ __attribute__((aligned(1024))) uint8_t st1[STAGE];
 
@@ -68,37 +74,42 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_reg_kernel(Args a) {
     const int l32 = lane & 31;
 
     // Chunk i of this thread.  K-contiguous operand: row idx / 4, 16-byte
-    // chunk idx % 4 of the row's 64 bytes.  Row-major B: k-row idx / 32,
-    // columns 8 (idx % 32) .. +7.
-    int a_g[NC], b_g[NC], a_l[NC], b_l[NC];
+    // chunk idx % 4 of the row's 64 bytes.  Row-major B: k-row idx / CPK,
+    // columns 8 (idx % CPK) .. +7 (LDS rows keep the 512-byte pitch).
+    int a_g[NC], b_g[NCB], a_l[NC], b_l[NCB];
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
         const int idx = i * kThreads + tid;
         const int r = idx >> 2, c = idx & 3;
         a_g[i] = r * (int)a.lda_b + c * 16;
         a_l[i] = kc_off<RB>(r, c);
+    }
+#pragma unroll
+    for (int i = 0; i < NCB; ++i) {
+        const int idx = i * kThreads + tid;
         if constexpr (KIND == kNN) {
-            const int kk = idx >> 5, cn = idx & 31;
+            const int kk = idx / CPK, cn = idx % CPK;
             b_g[i] = kk * (int)a.ldb_b + cn * 16;
             b_l[i] = OPB + nn_off(kk, cn * 8);
         } else {
+            const int r = idx >> 2, c = idx & 3;
             b_g[i] = r * (int)a.ldb_b + c * 16;
             b_l[i] = OPB + kc_off<RB>(r, c);
         }
     }
 
     // fragment read offsets (as in gemm_fast.h)
-    int a_rd[KS], b_rd[KS], b_tr[kBlocks];
+    int a_rd[KS], b_rd[KS], b_tr[NBJ];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
         a_rd[ks] = kc_off<RB>(wm * kWaveTile + l32, 2 * ks + h);
-        b_rd[ks] = OPB + kc_off<RB>(wn * kWaveTile + l32, 2 * ks + h);
+        b_rd[ks] = OPB + kc_off<RB>(wn * WTN + l32, 2 * ks + h);
     }
     if constexpr (KIND == kNN) {
         const int g = lane >> 4, li = lane & 15;
 #pragma unroll
-        for (int j = 0; j < kBlocks; ++j) {
-            int n = wn * kWaveTile + j * 32 + 16 * (g & 1) + 4 * (li & 3);
+        for (int j = 0; j < NBJ; ++j) {
+            int n = wn * WTN + j * 32 + 16 * (g & 1) + 4 * (li & 3);
             int k = 8 * (g >> 1) + (li >> 2);
             b_tr[j] = OPB + nn_off(k, n);
         }
@@ -111,9 +122,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_reg_kernel(Args a) {
     for (int t = logical_block(a); t < a.num_tiles; t += G) {
         int tm, tn;
         tile_coords(a, t, tm, tn);
-        const int m0 = tm * kTile, n0 = tn * kTile;
+        const int m0 = tm * kTile, n0 = tn * BN;
         const int rows_a = min(kTile, a.M - m0);
-        const int rows_b = min(kTile, a.N - n0);
+        const int rows_b = min(BN, a.N - n0);
         int sa, sb;
         const __amdgpu_buffer_rsrc_t ra =
             span_rsrc(a.A + (int64_t)m0 * a.lda_b, (int64_t)(rows_a - 1) * a.lda_b + (int64_t)a.K * 2, sa);
@@ -122,29 +133,30 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_reg_kernel(Args a) {
             rb = span_rsrc(a.B + (int64_t)n0 * 2, (int64_t)(a.K - 1) * a.ldb_b + (int64_t)(a.N - n0) * 2, sb);
         else
             rb = span_rsrc(a.B + (int64_t)n0 * a.ldb_b, (int64_t)(rows_b - 1) * a.ldb_b + (int64_t)a.K * 2, sb);
-        const __amdgpu_buffer_rsrc_t rdead = make_rsrc(a.A, 0);
-
         // k-tile j lives in register set j % PF
-        i32x4 ra_reg[PF][NC], rb_reg[PF][NC];
-        // k-tile kt into register set q (zeros for kt >= KT, without traffic)
+        i32x4 ra_reg[PF][NC], rb_reg[PF][NCB];
+        // k-tile kt into register set q.  A dead k-tile (kt >= KT) reads
+        // zeros without traffic: its scalar offset kDead puts every lane
+        // past the descriptor's range (voffset < 2^31 and the range below
+        // 2^31, so the sum cannot wrap).  Selecting the offset rather than a
+        // second descriptor keeps the descriptors in scalar registers.
+        constexpr int kDead = 0x7fffffff;
         auto load = [&](auto qidx, int kt, bool live) {
             constexpr int q = decltype(qidx)::value;
-            const int ka = sa + (live ? kt * RB : 0);
-            const int kb = sb + (live ? ((KIND == kNN) ? kt * BK * (int)a.ldb_b : kt * RB) : 0);
+            const int ka = live ? sa + kt * RB : kDead;
+            const int kb = live ? sb + ((KIND == kNN) ? kt * BK * (int)a.ldb_b : kt * RB) : kDead;
 #pragma unroll
-            for (int i = 0; i < NC; ++i) {
-                ra_reg[q][i] = __builtin_amdgcn_raw_buffer_load_b128(live ? ra : rdead, a_g[i], ka, 0);
-                rb_reg[q][i] = __builtin_amdgcn_raw_buffer_load_b128(live ? rb : rdead, b_g[i], kb, 0);
-            }
+            for (int i = 0; i < NC; ++i) ra_reg[q][i] = __builtin_amdgcn_raw_buffer_load_b128(ra, a_g[i], ka, 0);
+#pragma unroll
+            for (int i = 0; i < NCB; ++i) rb_reg[q][i] = __builtin_amdgcn_raw_buffer_load_b128(rb, b_g[i], kb, 0);
         };
         auto store = [&](auto qidx, auto sidx) {
             constexpr int q = decltype(qidx)::value;
             uint8_t FAST_LDS* base = decltype(sidx)::value ? (uint8_t FAST_LDS*)st1 : (uint8_t FAST_LDS*)st0;
 #pragma unroll
-            for (int i = 0; i < NC; ++i) {
-                *(i32x4 FAST_LDS*)(base + a_l[i]) = ra_reg[q][i];
-                *(i32x4 FAST_LDS*)(base + b_l[i]) = rb_reg[q][i];
-            }
+            for (int i = 0; i < NC; ++i) *(i32x4 FAST_LDS*)(base + a_l[i]) = ra_reg[q][i];
+#pragma unroll
+            for (int i = 0; i < NCB; ++i) *(i32x4 FAST_LDS*)(base + b_l[i]) = rb_reg[q][i];
         };
         auto read_frags = [&](auto sidx, int ks, bf16x8* fa, bf16x8* fb) {
             const uint8_t FAST_LDS* base =
@@ -152,7 +164,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_reg_kernel(Args a) {
 #pragma unroll
             for (int i = 0; i < kBlocks; ++i) fa[i] = *(const bf16x8 FAST_LDS*)(base + a_rd[ks] + i * 32 * RB);
 #pragma unroll
-            for (int j = 0; j < kBlocks; ++j) {
+            for (int j = 0; j < NBJ; ++j) {
                 if constexpr (KIND == kNN) {
                     const uint8_t FAST_LDS* p = base + b_tr[j] + ks * 16 * 512;
                     bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((bf16x4 FAST_LDS*)p);
@@ -164,18 +176,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_reg_kernel(Args a) {
             }
         };
 
-        f32x16 acc[kBlocks][kBlocks];
+        f32x16 acc[kBlocks][NBJ];
 #pragma unroll
         for (int i = 0; i < kBlocks; ++i)
 #pragma unroll
-            for (int j = 0; j < kBlocks; ++j)
+            for (int j = 0; j < NBJ; ++j)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
         auto mfma = [&](const bf16x8* fa, const bf16x8* fb) {
 #pragma unroll
             for (int i = 0; i < kBlocks; ++i)
 #pragma unroll
-                for (int j = 0; j < kBlocks; ++j)
+                for (int j = 0; j < NBJ; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
         };
 
@@ -188,7 +200,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_reg_kernel(Args a) {
         load(Z{}, PF, PF < KT);
         wait_lgkm0();
         barrier();
-        bf16x8 F0a[kBlocks], F0b[kBlocks], F1a[kBlocks], F1b[kBlocks];
+        bf16x8 F0a[kBlocks], F0b[NBJ], F1a[kBlocks], F1b[NBJ];
         read_frags(std::integral_constant<int, 0>{}, 0, F0a, F0b);
 
         auto body = [&](auto sidx, int kt) {
@@ -243,9 +255,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_reg_kernel(Args a) {
                 else if (c8 < kvalid)
                     va = gather(ra, a_g[i], sa + KT * RB, kvalid - c8);
                 ra_reg[0][i] = va;
+            }
+#pragma unroll
+            for (int i = 0; i < NCB; ++i) {
+                const int idx = i * kThreads + tid;
+                const int c8 = 8 * (idx & 3);
                 i32x4 vb = {0, 0, 0, 0};
                 if constexpr (KIND == kNN) {
-                    const int kk = idx >> 5, n8 = 8 * (idx & 31);
+                    const int kk = idx / CPK, n8 = 8 * (idx % CPK);
                     const int soff = sb + KT * BK * (int)a.ldb_b;
                     if (kk < kvalid) {
                         if (n8 + 8 <= rows_b)
@@ -274,7 +291,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_reg_kernel(Args a) {
             }
         }
 
-        store_c(a, acc, m0 + wm * kWaveTile, n0 + wn * kWaveTile, h, l32);
+        store_c<NBJ>(a, acc, m0 + wm * kWaveTile, n0 + wn * WTN, h, l32);
         wait_lgkm0();
         barrier();
     }

@@ -694,10 +694,10 @@ bool reg_ok(bool nt, int64_t K, int64_t lda, int64_t ldb) {
     return K * ldb * 2 + 4 < lim;
 }
 
-template <int PF>
+template <int PF, int BN>
 int launch_reg_pf(bool nt, fast::Args a, int cus, hipStream_t stream) {
     a.tiles_m = (a.M + fast::kTile - 1) / fast::kTile;
-    a.tiles_n = (a.N + fast::kTile - 1) / fast::kTile;
+    a.tiles_n = (a.N + BN - 1) / BN;
     a.num_tiles = a.tiles_m * a.tiles_n;
     const int g = env_variant().group;
     const int group_m = g > 0 ? g : 8;
@@ -713,13 +713,30 @@ int launch_reg_pf(bool nt, fast::Args a, int cus, hipStream_t stream) {
     const bool tail = a.kt_total > a.kt_full;
     const dim3 blk(fast::kThreads);
     if (nt) {
-        if (tail) hipLaunchKernelGGL((regpath::gemm_reg_kernel<fast::kNT, true, PF>), dim3(grid), blk, 0, stream, a);
-        else hipLaunchKernelGGL((regpath::gemm_reg_kernel<fast::kNT, false, PF>), dim3(grid), blk, 0, stream, a);
+        if (tail)
+            hipLaunchKernelGGL((regpath::gemm_reg_kernel<fast::kNT, true, PF, BN>), dim3(grid), blk, 0, stream, a);
+        else
+            hipLaunchKernelGGL((regpath::gemm_reg_kernel<fast::kNT, false, PF, BN>), dim3(grid), blk, 0, stream, a);
     } else {
-        if (tail) hipLaunchKernelGGL((regpath::gemm_reg_kernel<fast::kNN, true, PF>), dim3(grid), blk, 0, stream, a);
-        else hipLaunchKernelGGL((regpath::gemm_reg_kernel<fast::kNN, false, PF>), dim3(grid), blk, 0, stream, a);
+        if (tail)
+            hipLaunchKernelGGL((regpath::gemm_reg_kernel<fast::kNN, true, PF, BN>), dim3(grid), blk, 0, stream, a);
+        else
+            hipLaunchKernelGGL((regpath::gemm_reg_kernel<fast::kNN, false, PF, BN>), dim3(grid), blk, 0, stream, a);
     }
     return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
+}
+
+// Tile width for the register kernel: 192 columns when that needs fewer
+// rounds of tiles over the CUs, weighted by the tile's work (for example
+// 4001 x 3003: 16 x 12 = 192 tiles of 256 columns leave a quarter of the CUs
+// idle, 16 x 16 = 256 tiles of 192 columns fill them).
+int reg_tile_n(int64_t M, int64_t N, int cus) {
+    const int64_t tm = (M + 255) / 256;
+    auto cost = [&](int64_t bn) {
+        const int64_t tiles = tm * ((N + bn - 1) / bn);
+        return ((tiles + cus - 1) / cus) * bn;
+    };
+    return cost(192) < cost(256) ? 192 : 256;
 }
 
 // LIBGEMM_REGPF=1|2: register sets of prefetch (measurement switch)
@@ -730,8 +747,17 @@ int launch_reg(bool nt, const fast::Args& a, int cus, hipStream_t stream) {
     }();
     // one register set measured faster than two on MI355X (4001x3003x2050:
     // 111.6 vs 116.7 us; 4096^3 with odd ld: 149 vs 160 us)
-    if (pf == 2) return launch_reg_pf<2>(nt, a, cus, stream);
-    return launch_reg_pf<1>(nt, a, cus, stream);
+    static int bn_env = [] {
+        const char* e = getenv("LIBGEMM_REG_BN");
+        return e ? atoi(e) : 0;
+    }();
+    const int bn = bn_env == 192 || bn_env == 256 ? bn_env : reg_tile_n(a.M, a.N, cus);
+    if (bn == 192) {
+        if (pf == 2) return launch_reg_pf<2, 192>(nt, a, cus, stream);
+        return launch_reg_pf<1, 192>(nt, a, cus, stream);
+    }
+    if (pf == 2) return launch_reg_pf<2, 256>(nt, a, cus, stream);
+    return launch_reg_pf<1, 256>(nt, a, cus, stream);
 }
 
 // ---------------------------------------------------------------------------

@@ -241,7 +241,12 @@ def test_fast_path_mx_tails(shape, dist):
 # register-load kernel runs; K tails of every kind (none, partial, K < 32).
 REG_BF16 = [(3600 + 17, 3500 + 3, 333, False, 3, 1, 1), (3584 + 1, 3840 + 5, 1001, True, 1, 5, 1),
             (3584, 3584, 512, False, 1, 3, 0), (3600, 3600, 17, True, 2, 2, 3),
-            (3520 + 9, 3520 + 31, 64 + 2, False, 0, 2, 2), (3600 + 1, 3600 + 5, 512, False, 1, 1, 1)]
+            (3520 + 9, 3520 + 31, 64 + 2, False, 0, 2, 2), (3600 + 1, 3600 + 5, 512, False, 1, 1, 1),
+            # 192-column tiles (16 x 16 of them fill 256 CUs where 256-column
+            # tiles would leave a quarter idle)
+            (3900 + 1, 2900 + 3, 333, False, 3, 1, 1), (4000, 3000, 1001, True, 1, 5, 1),
+            (3850, 2890, 17, True, 2, 2, 3), (4001, 3003, 512, False, 1, 1, 1),
+            (4096, 3072, 64 + 2, False, 0, 2, 2)]
 
 
 @pytest.mark.parametrize("case", REG_BF16, ids=lambda c: f"{c[0]}x{c[1]}x{c[2]}_{'nt' if c[3] else 'nn'}")
