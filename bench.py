@@ -245,29 +245,35 @@ def bench_workload(name: str, steps: int, warmup: int, settle: float = 0.0):
     return res, prob
 
 
-def cpu_baseline(prob, rows: int):
-    """The oracle, untouched, on rows [0, rows) of the same product."""
+def cpu_baseline(prob, rows: int, single_rows: int = 32):
+    """The oracle, untouched, on rows [0, rows) of the same product with all
+    the host threads it uses, and on rows [0, single_rows) with one thread."""
     import torch
     import oracle
     from dense_gemm_mxfp8_amd.inputs import MxProblem
 
-    rows = min(rows, prob.M)
-    if isinstance(prob, MxProblem):
-        A = prob.A[:rows].numpy()
-        t0 = time.perf_counter()
-        oracle.gemm_mxfp8(A, prob.B.numpy().T, prob.SA[:rows].numpy(), prob.SB.numpy())
-    else:
-        A = prob.A[:rows].contiguous().view(torch.int16).numpy().view(np.uint16)
-        B = prob.B.view(torch.int16).numpy().view(np.uint16)
-        Bv = B.T if prob.b_colmajor else B
-        t0 = time.perf_counter()
-        oracle.gemm_bf16(A, Bv)
-    dt = time.perf_counter() - t0
-    flops = 2.0 * rows * prob.N * prob.K
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.default_threads(),
-            "kind": "oracle",
-            "sample": f"rows 0..{rows - 1} of A against all of B ({rows}x{prob.N}x{prob.K}), "
-                      f"{dt:.2f} s wall"}
+    def run(nrows, nthreads):
+        nrows = min(nrows, prob.M)
+        if isinstance(prob, MxProblem):
+            A = prob.A[:nrows].numpy()
+            t0 = time.perf_counter()
+            oracle.gemm_mxfp8(A, prob.B.numpy().T, prob.SA[:nrows].numpy(), prob.SB.numpy(), nthreads=nthreads)
+        else:
+            A = prob.A[:nrows].contiguous().view(torch.int16).numpy().view(np.uint16)
+            B = prob.B.view(torch.int16).numpy().view(np.uint16)
+            Bv = B.T if prob.b_colmajor else B
+            t0 = time.perf_counter()
+            oracle.gemm_bf16(A, Bv, nthreads=nthreads)
+        dt = time.perf_counter() - t0
+        return nrows, dt, 2.0 * nrows * prob.N * prob.K / dt / 1e12
+
+    cores = oracle.default_threads()
+    n, dt, tf = run(rows, cores)
+    n1, dt1, tf1 = run(single_rows, 1)
+    return {"value": tf, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"rows 0..{n - 1} of A against all of B ({n}x{prob.N}x{prob.K}), {dt:.2f} s wall",
+            "single_core": {"value": tf1, "unit": "TFLOP/s", "cores": 1,
+                            "sample": f"rows 0..{n1 - 1} ({n1}x{prob.N}x{prob.K}), {dt1:.2f} s wall"}}
 
 
 def measured_traffic(workload: str):
