@@ -159,13 +159,13 @@ __device__ __forceinline__ i32x4 keep_bytes(i32x4 v, int nb) {
 // operand lie outside it and read as zero), bytes at or past kvalid_b zeroed.
 // The rows are 16-byte aligned, so the loads read aligned dwords and a range
 // rounded up to a dword touches nothing past the operand's last dword.
-template <int RB>
+template <int RB, int THREADS = kThreads>
 __device__ __forceinline__ void tail_kc(uint8_t FAST_LDS* dst, __amdgpu_buffer_rsrc_t rs, int ld_b, int soff,
                                         int kvalid_b, int tid) {
     constexpr int CPR = RB / 16;
 #pragma unroll
-    for (int i = 0; i < kTile * CPR / kThreads; ++i) {
-        const int idx = i * kThreads + tid;
+    for (int i = 0; i < kTile * CPR / THREADS; ++i) {
+        const int idx = i * THREADS + tid;
         const int r = idx / CPR, c = idx % CPR;
         i32x4 v = {0, 0, 0, 0};
         if (c * 16 < kvalid_b)
@@ -177,12 +177,12 @@ __device__ __forceinline__ void tail_kc(uint8_t FAST_LDS* dst, __amdgpu_buffer_r
 // Partial k-tile of row-major B (k rows of 256 bf16) into a stage: k-rows at
 // or past kvalid and 8-column chunks at or past ncols are zero (N % 8 == 0,
 // so a chunk is either wholly inside N or wholly outside).
-template <int BK>
+template <int BK, int THREADS = kThreads>
 __device__ __forceinline__ void tail_nn(uint8_t FAST_LDS* dst, __amdgpu_buffer_rsrc_t rs, int ldb_b, int soff,
                                         int kvalid, int ncols, int tid) {
 #pragma unroll
-    for (int i = 0; i < BK * 32 / kThreads; ++i) {
-        const int idx = i * kThreads + tid;
+    for (int i = 0; i < BK * 32 / THREADS; ++i) {
+        const int idx = i * THREADS + tid;
         const int kk = idx >> 5, c = idx & 31;
         i32x4 v = {0, 0, 0, 0};
         if (kk < kvalid && c * 8 < ncols) v = __builtin_amdgcn_raw_buffer_load_b128(rs, kk * ldb_b + c * 16, soff, 0);
@@ -255,10 +255,10 @@ constexpr int kSgDsRead = 0x100;
 // Interleave the 16 MFMAs of one k-step with NR LDS fragment reads and ND
 // DMA instructions so that memory instructions issue while the matrix core
 // is busy instead of in bursts.
-template <int NR, int ND>
+template <int NR, int ND, int NMF = 16>
 __device__ __forceinline__ void interleave_step() {
 #pragma unroll
-    for (int m = 0; m < 16; ++m) {
+    for (int m = 0; m < NMF; ++m) {
         __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
         if (m < NR) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
         if (m < ND) __builtin_amdgcn_sched_group_barrier(kSgVmem, 1, 0);
@@ -275,8 +275,15 @@ __device__ __forceinline__ void interleave_step() {
 // time before the wait that needs them.
 // D (two stages only): k-steps over which the rest of the DMA of k-tile
 // kt + 1 is spread, starting at k-step 0 of kt (0: all but the last).
-template <int KIND, int RB, int S, bool TAIL, int SG = 1, int E = 0, int D = 0>
-__global__ __launch_bounds__(kThreads, 1) void gemm_fast_kernel(Args a) {
+// NW: waves per workgroup.  4 waves hold 128 x 128 wave tiles (one wave per
+// SIMD); 8 waves hold 128 x 64 wave tiles, two per SIMD, so that one wave's
+// MFMAs can run while the other waits (bf16 only).
+template <int KIND, int RB, int S, bool TAIL, int SG = 1, int E = 0, int D = 0, int NW = 4>
+__global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(Args a) {
+    static_assert(NW == 4 || (NW == 8 && KIND != kMX), "8 waves: bf16 only");
+    constexpr int THREADS = 64 * NW;
+    constexpr int NBJ = NW == 8 ? 2 : kBlocks;  // 32-column MFMA blocks per wave tile
+    constexpr int WTN = 32 * NBJ;               // wave tile columns
     constexpr int ESZ = (KIND == kMX) ? 1 : 2;  // operand element bytes
     constexpr int BK = RB / ESZ;                // K elements per k-tile
     constexpr int OPB = kTile * RB;             // bytes of one operand in one stage
@@ -288,7 +295,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_kernel(Args a) {
     constexpr int RING = (KIND == kMX && SG > 1) ? 2 * kTile * 4 * SG : 16;  // bytes per ring slot
     static_assert(SG == 1 || (KIND == kMX && RB == 128 && SG == 4 && S == 2), "scale ring: MX 128x2 only");
     constexpr int STAGE = 2 * OPB + SCB;
-    constexpr int NI = RB / 16;                 // DMA instructions per wave per operand
+    constexpr int NI = RB * kTile / 1024 / NW;  // DMA instructions per wave per operand
     constexpr int RPK = 1024 / RB;              // K-contiguous rows per KiB
     // MFMA k-steps per k-tile: 16 bf16 or 64 fp8 elements per step
     constexpr int KS = (KIND == kMX) ? BK / 64 : BK / 16;
@@ -341,28 +348,29 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_kernel(Args a) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = NW == 8 ? wave >> 2 : wave >> 1;
+    const int wn = NW == 8 ? wave & 3 : wave & 1;
     const int h = lane >> 5;
     const int l32 = lane & 31;
 
     // ---- per-lane constants of the DMA loads ------------------------------
-    // K-contiguous operand: instruction i of this wave fills KiB (4 i + wave)
+    // K-contiguous operand: instruction i of this wave fills KiB (NW i + wave)
     // of the operand's stage area; the swizzle of its rows does not depend
     // on i, so one lane offset plus a scalar row step covers all of them.
     const int kc_row0 = wave * RPK + lane / (RB / 16);
     const int kc_chunk = (lane % (RB / 16)) ^ swz<RB>(kc_row0);
     const int a_voff = (int)(kc_row0 * a.lda_b) + kc_chunk * 16;
-    const int a_step = (int)(4 * RPK * a.lda_b);
+    const int a_step = (int)(NW * RPK * a.lda_b);
     int b_voff, b_step;
     if constexpr (KIND == kNN) {
-        // k rows of 512 bytes, 2 per KiB: row 2(4 i + wave) + lane / 32.
+        // k rows of 512 bytes, 2 per KiB: row 2(NW i + wave) + lane / 32.
         const int kk0 = 2 * wave + h;
         const int c = l32 ^ ((kk0 & 3) << 2);
         b_voff = (int)(kk0 * a.ldb_b) + c * 16;
-        b_step = (int)(8 * a.ldb_b);
+        b_step = (int)(2 * NW * a.ldb_b);
     } else {
         b_voff = (int)(kc_row0 * a.ldb_b) + kc_chunk * 16;
-        b_step = (int)(4 * RPK * a.ldb_b);
+        b_step = (int)(NW * RPK * a.ldb_b);
     }
     // MX scales: wave w stages the k-tile's scale dwords of rows
     // 64 w .. 64 w + 63 of both operands (one dword = four 32-blocks).
@@ -372,20 +380,20 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_kernel(Args a) {
     // byte offsets in a stage of this lane's A / B chunks at step ks (block
     // 0); fp8 steps read two chunks (k 16h..16h+15 and 32+16h..32+16h+15)
     int a_rd[KS][2], b_rd[KS][2];
-    int b_tr[kBlocks];  // NN: offset of block j's transposed read at step 0
+    int b_tr[NBJ];  // NN: offset of block j's transposed read at step 0
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
         const int c0 = (KIND == kMX) ? (4 * ks + h) : (2 * ks + h);
         a_rd[ks][0] = kc_off<RB>(wm * kWaveTile + l32, c0);
-        b_rd[ks][0] = OPB + kc_off<RB>(wn * kWaveTile + l32, c0);
+        b_rd[ks][0] = OPB + kc_off<RB>(wn * WTN + l32, c0);
         a_rd[ks][1] = kc_off<RB>(wm * kWaveTile + l32, c0 + 2);
-        b_rd[ks][1] = OPB + kc_off<RB>(wn * kWaveTile + l32, c0 + 2);
+        b_rd[ks][1] = OPB + kc_off<RB>(wn * WTN + l32, c0 + 2);
     }
     if constexpr (KIND == kNN) {
         const int g = lane >> 4, li = lane & 15;
 #pragma unroll
-        for (int j = 0; j < kBlocks; ++j) {
-            int n = wn * kWaveTile + j * 32 + 16 * (g & 1) + 4 * (li & 3);
+        for (int j = 0; j < NBJ; ++j) {
+            int n = wn * WTN + j * 32 + 16 * (g & 1) + 4 * (li & 3);
             int k = 8 * (g >> 1) + (li >> 2);
             b_tr[j] = OPB + nn_off(k, n);
         }
@@ -433,13 +441,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_kernel(Args a) {
             uint8_t FAST_LDS* As = stage_ptr(sidx);
             if (d < NI) {
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(live ? ra : rdead,
-                                                         (void FAST_LDS*)(As + (4 * d + wave) * 1024), 16,
+                                                         (void FAST_LDS*)(As + (NW * d + wave) * 1024), 16,
                                                          a_voff, kt * RB + d * a_step, 0, 0);
             } else if (d < 2 * NI) {
                 const int i = d - NI;
                 const int koff = (KIND == kNN) ? kt * BK * (int)a.ldb_b : kt * RB;
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(live ? rb : rdead,
-                                                         (void FAST_LDS*)(As + OPB + (4 * i + wave) * 1024), 16,
+                                                         (void FAST_LDS*)(As + OPB + (NW * i + wave) * 1024), 16,
                                                          b_voff, koff + i * b_step, 0, 0);
             } else if constexpr (KIND == kMX) {
                 const bool sb = d > 2 * NI;
@@ -479,7 +487,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_kernel(Args a) {
                 }
             }
 #pragma unroll
-            for (int j = 0; j < kBlocks; ++j) {
+            for (int j = 0; j < NBJ; ++j) {
                 if constexpr (KIND == kMX) {
                     i32x4 lo = *(const i32x4 FAST_LDS*)(base + b_rd[ks][0] + j * 32 * RB);
                     i32x4 hi = *(const i32x4 FAST_LDS*)(base + b_rd[ks][1] + j * 32 * RB);
@@ -495,7 +503,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_kernel(Args a) {
             }
         };
         // fragment reads per k-step (LDS instructions)
-        constexpr int NR = (KIND == kMX) ? 16 : (KIND == kNN) ? 12 : 8;
+        constexpr int NR = (KIND == kMX) ? 16 : (KIND == kNN) ? 4 + 2 * NBJ : 4 + NBJ;
+        constexpr int NMF = kBlocks * NBJ;  // MFMAs per k-step
 
         // MX: the scale dwords of the k-tile in stage s, pre-shifted so that
         // lane half h finds its 32-block (2 ks + h) in byte 2 ks.
@@ -528,11 +537,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_kernel(Args a) {
             }
         };
 
-        f32x16 acc[kBlocks][kBlocks];
+        f32x16 acc[kBlocks][NBJ];
 #pragma unroll
         for (int i = 0; i < kBlocks; ++i)
 #pragma unroll
-            for (int j = 0; j < kBlocks; ++j)
+            for (int j = 0; j < NBJ; ++j)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
@@ -540,7 +549,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_kernel(Args a) {
 #pragma unroll
             for (int i = 0; i < kBlocks; ++i)
 #pragma unroll
-                for (int j = 0; j < kBlocks; ++j) {
+                for (int j = 0; j < NBJ; ++j) {
                     if constexpr (KIND == kMX) {
                         // k-step ks covers 32-blocks 2 ks and 2 ks + 1 of the
                         // k-tile: byte 2 ks of the (pre-shifted) scale word.
@@ -572,7 +581,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_kernel(Args a) {
         wait_vm<((SG > 1) ? 0 : (S - 2) * L) + E>();
         barrier();
 
-        Frag F0a[kBlocks], F0b[kBlocks], F1a[kBlocks], F1b[kBlocks];
+        Frag F0a[kBlocks], F0b[NBJ], F1a[kBlocks], F1b[NBJ];
         read_frags(std::integral_constant<int, 0>{}, 0, F0a, F0b);
         read_scales(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
 
@@ -608,7 +617,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_kernel(Args a) {
                         ring_dma(std::integral_constant<int, (q / SG + 1) % 2>{}, g, g * SG < KT);
                     }
                     mfma(ks, ca, cb, sc);
-                    interleave_step<NR, d1 - d0 + ((SG > 1 && ks == 0 && q % SG == 0) ? 2 : 0)>();
+                    interleave_step<NR, d1 - d0 + ((SG > 1 && ks == 0 && q % SG == 0) ? 2 : 0), NMF>();
                     // keep every MFMA of this step ahead of the closing wait
                     __builtin_amdgcn_sched_barrier(0);
                 } else {
@@ -633,7 +642,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_kernel(Args a) {
                     } else {
                         mfma(ks, ca, cb, sc);
                     }
-                    interleave_step<NR, d1 - d0 + E>();
+                    interleave_step<NR, d1 - d0 + E, NMF>();
                     __builtin_amdgcn_sched_barrier(0);
                 }
             });
@@ -654,11 +663,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_kernel(Args a) {
             barrier();  // every wave is done with the pipelined stages
             uint8_t FAST_LDS* As = stage_ptr(std::integral_constant<int, 0>{});
             const int kvalid = a.K - KT * BK;
-            tail_kc<RB>(As, ra, (int)a.lda_b, KT * RB, kvalid * ESZ, tid);
+            tail_kc<RB, THREADS>(As, ra, (int)a.lda_b, KT * RB, kvalid * ESZ, tid);
             if constexpr (KIND == kNN)
-                tail_nn<BK>(As + OPB, rb, (int)a.ldb_b, KT * BK * (int)a.ldb_b, kvalid, a.N - n0, tid);
+                tail_nn<BK, THREADS>(As + OPB, rb, (int)a.ldb_b, KT * BK * (int)a.ldb_b, kvalid, a.N - n0, tid);
             else
-                tail_kc<RB>(As + OPB, rb, (int)a.ldb_b, KT * RB, kvalid * ESZ, tid);
+                tail_kc<RB, THREADS>(As + OPB, rb, (int)a.ldb_b, KT * RB, kvalid * ESZ, tid);
             wait_lgkm0();
             barrier();
 #pragma unroll
@@ -669,7 +678,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_kernel(Args a) {
         }
 
         // ---- epilogue: fp32 stores straight from the accumulators --------
-        store_c(a, acc, m0 + wm * kWaveTile, n0 + wn * kWaveTile, h, l32);
+        store_c<NBJ>(a, acc, m0 + wm * kWaveTile, n0 + wn * WTN, h, l32);
         // The next tile's prologue overwrites stages 0 .. S-2: every wave
         // must be done reading them.
         wait_lgkm0();
