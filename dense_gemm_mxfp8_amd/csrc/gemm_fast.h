@@ -509,21 +509,33 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(Args a) {
         // MX: the scale dwords of the k-tile in stage s, pre-shifted so that
         // lane half h finds its 32-block (2 ks + h) in byte 2 ks.
         int sc[2 * kBlocks];
+        // scale ring (SG > 1): raw scale dwords of the next k-tile, read one
+        // k-step ahead so that their LDS latency is hidden
+        int scr[2 * kBlocks];
         // scales of the k-tile in stage sidx (SG == 1) or at position q of
         // the unrolled loop (SG > 1: ring slot (q / SG) % 2, dword q % SG)
-        auto read_scales = [&](auto sidx, auto qidx) {
+        // ring: the raw dwords of k-tile position q into out (unshifted)
+        auto read_ring = [&](auto qidx, int* out) {
             if constexpr (KIND == kMX && SG > 1) {
                 constexpr int q = decltype(qidx)::value % U;
                 const uint8_t FAST_LDS* base =
                     ((q / SG) % 2) ? (const uint8_t FAST_LDS*)sr1 : (const uint8_t FAST_LDS*)sr0;
 #pragma unroll
                 for (int i = 0; i < kBlocks; ++i) {
-                    uint32_t w = *(const uint32_t FAST_LDS*)(base + 16 * (wm * kWaveTile + l32 + 32 * i) + 4 * (q % SG));
-                    uint32_t v = *(const uint32_t FAST_LDS*)(base + 4096 + 16 * (wn * kWaveTile + l32 + 32 * i) +
-                                                             4 * (q % SG));
-                    sc[i] = (int)(w >> (8 * h));
-                    sc[kBlocks + i] = (int)(v >> (8 * h));
+                    out[i] = *(const int FAST_LDS*)(base + 16 * (wm * kWaveTile + l32 + 32 * i) + 4 * (q % SG));
+                    out[kBlocks + i] =
+                        *(const int FAST_LDS*)(base + 4096 + 16 * (wn * kWaveTile + l32 + 32 * i) + 4 * (q % SG));
                 }
+            }
+        };
+        auto shift_scales = [&](const int* raw) {
+#pragma unroll
+            for (int i = 0; i < 2 * kBlocks; ++i) sc[i] = (int)((uint32_t)raw[i] >> (8 * h));
+        };
+        auto read_scales = [&](auto sidx, auto qidx) {
+            if constexpr (KIND == kMX && SG > 1) {
+                read_ring(qidx, scr);
+                shift_scales(scr);
             } else if constexpr (KIND == kMX) {
                 const uint8_t FAST_LDS* base = stage_ptr(sidx);
 #pragma unroll
@@ -607,6 +619,11 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(Args a) {
                 constexpr int d1 = E + (ks + 1) * DPS < L ? E + (ks + 1) * DPS : L;
                 if constexpr (ks + 1 < KS) {
                     read_frags(sidx, ks + 1, na, nb);
+                    if constexpr (KIND == kMX && SG > 1 && ks == 0) {
+                        // scales of k-tile kt + 1: its ring slot landed before
+                        // the barrier closing the k-tile that requested it
+                        read_ring(std::integral_constant<int, q + 1>{}, scr);
+                    }
                     static_for<d0, d1>([&](auto dc) {
                         dma(std::integral_constant<int, sdma>{}, decltype(dc)::value, kd, live);
                     });
@@ -634,7 +651,10 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(Args a) {
                     static_for<0, E>([&](auto dc) {
                         dma(sidx, decltype(dc)::value, kt + 2, kt + 2 < KT);
                     });
-                    if constexpr (KIND == kMX) {
+                    if constexpr (KIND == kMX && SG > 1) {
+                        mfma(ks, ca, cb, sc);
+                        shift_scales(scr);  // k-tile kt + 1's scales, read at k-step 0
+                    } else if constexpr (KIND == kMX) {
 #pragma unroll
                         for (int q = 0; q < 2 * kBlocks; ++q) scn[q] = sc[q];
                         read_scales(std::integral_constant<int, snext>{}, std::integral_constant<int, q + 1>{});
