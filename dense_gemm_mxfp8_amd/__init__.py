@@ -21,6 +21,8 @@ GEMM_OK = 0
 GEMM_ERR_INVALID_ARG = -1
 GEMM_ERR_UNSUPPORTED = -2
 GEMM_ERR_LAUNCH = -3
+GEMM_OUT_F32 = 0
+GEMM_OUT_BF16 = 1
 
 _lib = None
 _i64 = ctypes.c_int64
@@ -42,6 +44,12 @@ def library() -> ctypes.CDLL:
             fn.argtypes = sig
         lib.gemm_mxfp8.restype = ctypes.c_int
         lib.gemm_mxfp8.argtypes = [_i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _i64, _vp]
+        lib.gemm_bf16_fused.restype = ctypes.c_int
+        lib.gemm_bf16_fused.argtypes = [_i64, _i64, _i64, _vp, _i64, _vp, _i64, ctypes.c_int, _vp, _i64,
+                                        ctypes.c_int, _vp, _vp, _vp, _vp]
+        lib.gemm_mxfp8_fused.restype = ctypes.c_int
+        lib.gemm_mxfp8_fused.argtypes = [_i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _i64,
+                                         ctypes.c_int, _vp, _vp, _vp, _vp]
         lib.gemm_strerror.restype = ctypes.c_char_p
         lib.gemm_strerror.argtypes = [ctypes.c_int]
         lib.gemm_version.restype = ctypes.c_int
@@ -62,6 +70,18 @@ def gemm_bf16_nt(M, N, K, A, lda, B, ldb, C, ldc, stream) -> int:
 
 def gemm_mxfp8(M, N, K, A, lda, B, ldb, scaleA, scaleB, C, ldc, stream) -> int:
     return library().gemm_mxfp8(M, N, K, A, lda, B, ldb, scaleA, scaleB, C, ldc, stream)
+
+
+def gemm_bf16_fused(M, N, K, A, lda, B, ldb, b_colmajor, C, ldc, out_type, row_scale, col_scale, bias,
+                    stream) -> int:
+    return library().gemm_bf16_fused(M, N, K, A, lda, B, ldb, int(b_colmajor), C, ldc, out_type, row_scale,
+                                     col_scale, bias, stream)
+
+
+def gemm_mxfp8_fused(M, N, K, A, lda, B, ldb, scaleA, scaleB, C, ldc, out_type, row_scale, col_scale, bias,
+                     stream) -> int:
+    return library().gemm_mxfp8_fused(M, N, K, A, lda, B, ldb, scaleA, scaleB, C, ldc, out_type, row_scale,
+                                      col_scale, bias, stream)
 
 
 def gemm_strerror(code: int) -> str:
@@ -90,21 +110,43 @@ def _stream(device):
     return torch.cuda.current_stream(device).cuda_stream
 
 
-def _out(out, M, N, device):
+def _out(out, M, N, device, dtype=None):
     import torch
+    dtype = torch.float32 if dtype is None else dtype
     if out is None:
-        return torch.empty((M, N), dtype=torch.float32, device=device)
-    if out.shape != (M, N) or out.dtype != torch.float32 or (N > 1 and out.stride(1) != 1):
-        raise ValueError("out must be a float32 (M, N) tensor with unit column stride")
+        return torch.empty((M, N), dtype=dtype, device=device)
+    if out.shape != (M, N) or out.dtype != dtype or (N > 1 and out.stride(1) != 1):
+        raise ValueError(f"out must be a {dtype} (M, N) tensor with unit column stride")
     return out
 
 
-def bf16(A, B, out=None):
+def _epilogue(out_dtype, row_scale, col_scale, bias, M, N):
+    """(fused?, out_type, pointers) of the optional epilogue arguments."""
+    import torch
+    fused = out_dtype is not None or row_scale is not None or col_scale is not None or bias is not None
+    if out_dtype not in (None, torch.float32, torch.bfloat16):
+        raise TypeError("out_dtype must be torch.float32 or torch.bfloat16")
+    ptrs = []
+    for v, n, name in ((row_scale, M, "row_scale"), (col_scale, N, "col_scale"), (bias, N, "bias")):
+        if v is None:
+            ptrs.append(None)
+            continue
+        if v.dtype != torch.float32 or v.dim() != 1 or v.shape[0] != n or (n > 1 and v.stride(0) != 1):
+            raise ValueError(f"{name} must be a contiguous float32 vector of length {n}")
+        ptrs.append(v.data_ptr())
+    out_type = GEMM_OUT_BF16 if out_dtype == torch.bfloat16 else GEMM_OUT_F32
+    return fused, out_type, ptrs
+
+
+def bf16(A, B, out=None, *, out_dtype=None, row_scale=None, col_scale=None, bias=None):
     """C = A @ B in fp32 from bf16 CUDA tensors.
 
     A: (M, K), row-major rows (unit column stride).  B: a (K, N) tensor that is
     either row-major (unit column stride: ``gemm_bf16``) or column-major
-    (unit row stride, e.g. ``Bt.t()`` of an (N, K) tensor: ``gemm_bf16_nt``)."""
+    (unit row stride, e.g. ``Bt.t()`` of an (N, K) tensor: ``gemm_bf16_nt``).
+    With any of out_dtype (float32 or bfloat16), row_scale (M), col_scale (N)
+    or bias (N) the fused epilogue applies: C = A @ B * row_scale[:, None] *
+    col_scale[None, :] + bias[None, :] (``gemm_bf16_fused``)."""
     import torch
     if A.dtype != torch.bfloat16 or B.dtype != torch.bfloat16:
         raise TypeError("A and B must be bfloat16")
@@ -115,27 +157,31 @@ def bf16(A, B, out=None):
     if M > 0 and K > 1 and A.stride(1) != 1:
         raise ValueError("A needs unit column stride")
     lda = A.stride(0) if M > 1 else max(K, 1)
-    C = _out(out, M, N, A.device)
+    fused, out_type, (rs, cs, bs) = _epilogue(out_dtype, row_scale, col_scale, bias, M, N)
+    C = _out(out, M, N, A.device, out_dtype)
     ldc = C.stride(0) if M > 1 else max(N, 1)
     if N <= 1 or B.stride(1) == 1:
         ldb = B.stride(0) if K > 1 else max(N, 1)
-        fn = gemm_bf16
+        colmajor, fn = False, gemm_bf16
     elif B.stride(0) == 1:
         ldb = B.stride(1)
-        fn = gemm_bf16_nt
+        colmajor, fn = True, gemm_bf16_nt
     else:
         raise ValueError("B must have a unit stride along N (row-major) or K (column-major)")
-    _check(fn(M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, C.data_ptr(), ldc,
-              _stream(A.device)))
+    if fused:
+        _check(gemm_bf16_fused(M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, colmajor, C.data_ptr(), ldc,
+                               out_type, rs, cs, bs, _stream(A.device)))
+    else:
+        _check(fn(M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, C.data_ptr(), ldc, _stream(A.device)))
     return C
 
 
-def mxfp8(A, SA, B, SB, out=None):
+def mxfp8(A, SA, B, SB, out=None, *, out_dtype=None, row_scale=None, col_scale=None, bias=None):
     """MX block-scaled fp8 GEMM from uint8 CUDA tensors.
 
     A: (M, K) E4M3 codes, row-major.  B: (N, K) E4M3 codes, i.e. the K x N
     operand stored column-major.  SA: (M, K/32) and SB: (N, K/32) E8M0 codes,
-    dense row-major."""
+    dense row-major.  The epilogue arguments are those of ``bf16``."""
     import torch
     for t, name in ((A, "A"), (B, "B"), (SA, "SA"), (SB, "SB")):
         if t.dtype != torch.uint8 or t.dim() != 2:
@@ -152,8 +198,13 @@ def mxfp8(A, SA, B, SB, out=None):
         raise ValueError("A and B need unit stride along K")
     lda = A.stride(0) if M > 1 else max(K, 1)
     ldb = B.stride(0) if N > 1 else max(K, 1)
-    C = _out(out, M, N, A.device)
+    fused, out_type, (rs, cs, bs) = _epilogue(out_dtype, row_scale, col_scale, bias, M, N)
+    C = _out(out, M, N, A.device, out_dtype)
     ldc = C.stride(0) if M > 1 else max(N, 1)
-    _check(gemm_mxfp8(M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, SA.data_ptr(),
-                      SB.data_ptr(), C.data_ptr(), ldc, _stream(A.device)))
+    if fused:
+        _check(gemm_mxfp8_fused(M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, SA.data_ptr(), SB.data_ptr(),
+                                C.data_ptr(), ldc, out_type, rs, cs, bs, _stream(A.device)))
+    else:
+        _check(gemm_mxfp8(M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, SA.data_ptr(),
+                          SB.data_ptr(), C.data_ptr(), ldc, _stream(A.device)))
     return C

@@ -42,6 +42,8 @@
 #include <type_traits>
 #include <utility>
 
+#include "gemm_epi.h"
+
 namespace fast {
 
 constexpr int kTile = 256;      // BM = BN
@@ -68,6 +70,7 @@ struct Args {
     int sld;       // MX scale bytes per row (K / 32)
     int xcd_remap;
     int c_nt;      // C stores non-temporal (1) or cached (0)
+    epi::Params epi;  // fused epilogue (C is bf16 when epi.out_bf16)
 };
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -231,11 +234,76 @@ __device__ __forceinline__ void store_c_aux(const Args& a, const f32x16 (&acc)[k
     }
 }
 
-template <int NBJ = kBlocks>
+// Fused epilogue (gemm_epi.h): t = acc * rs[row] * cs[col] + bias[col] in
+// fp32, stored as fp32 or bf16, with the descriptor scheme of store_c_aux.
+// The scale and bias vectors are read only inside M x N.
+template <int AUX, int NBJ, bool BF16>
+__device__ __forceinline__ void store_c_fused(const Args& a, const f32x16 (&acc)[kBlocks][NBJ], int m0w, int n0w,
+                                              int h, int l32) {
+    const int rlim = a.M - m0w;
+    const int clim = a.N - n0w;
+    if (rlim <= 0 || clim <= 0) return;
+    const int rows = rlim < kWaveTile ? rlim : kWaveTile;
+    const int cols = clim < 32 * NBJ ? clim : 32 * NBJ;
+    constexpr int ESZ = BF16 ? 2 : 4;
+    const int ldcb = (int)a.ldc * ESZ;
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc((const uint8_t*)a.C + ((int64_t)m0w * a.ldc + n0w) * ESZ,
+                                                ((int64_t)(rows - 1) * a.ldc + cols) * ESZ);
+    const int voff = 4 * h * ldcb + ESZ * l32;
+    const epi::Params& e = a.epi;
+    float cf[NBJ], cb[NBJ];
+#pragma unroll
+    for (int j = 0; j < NBJ; ++j) {
+        const int col = 32 * j + l32;
+        const bool ok = col < cols;
+        cf[j] = (e.cs && ok) ? e.cs[n0w + col] : 1.0f;
+        cb[j] = (e.bias && ok) ? e.bias[n0w + col] : 0.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < kBlocks; ++i) {
+        // one 32-row block at a time, so that its 16 row factors are the only
+        // ones live
+        float rf[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int lrow = 32 * i + 8 * (r >> 2) + (r & 3) + 4 * h;
+            rf[r] = (e.rs && lrow < rows) ? e.rs[m0w + lrow] : 1.0f;
+        }
+#pragma unroll
+        for (int j = 0; j < NBJ; ++j) {
+            if (32 * j + l32 < cols) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int row = 32 * i + 8 * (r >> 2) + (r & 3);
+                    float t = acc[i][j][r];
+                    if (e.rs) t *= rf[r];
+                    if (e.cs) t *= cf[j];
+                    if (e.bias) t += cb[j];
+                    if constexpr (BF16)
+                        __builtin_amdgcn_raw_buffer_store_b16(epi::to_bf16(t), rc, voff + 64 * j, row * ldcb, AUX);
+                    else
+                        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, t), rc, voff + 128 * j,
+                                                              row * ldcb, AUX);
+                }
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// FUSED: the kernel instance carries the fused epilogue (a.epi.on); plain
+// instances keep the lean store path.
+template <int NBJ = kBlocks, bool FUSED = false>
 __device__ __forceinline__ void store_c(const Args& a, const f32x16 (&acc)[kBlocks][NBJ], int m0w, int n0w, int h,
                                         int l32) {
-    if (a.c_nt) store_c_aux<2, NBJ>(a, acc, m0w, n0w, h, l32);
-    else store_c_aux<0, NBJ>(a, acc, m0w, n0w, h, l32);
+    if constexpr (FUSED) {
+        if (a.epi.out_bf16) store_c_fused<0, NBJ, true>(a, acc, m0w, n0w, h, l32);
+        else if (a.c_nt) store_c_fused<2, NBJ, false>(a, acc, m0w, n0w, h, l32);
+        else store_c_fused<0, NBJ, false>(a, acc, m0w, n0w, h, l32);
+    } else {
+        if (a.c_nt) store_c_aux<2, NBJ>(a, acc, m0w, n0w, h, l32);
+        else store_c_aux<0, NBJ>(a, acc, m0w, n0w, h, l32);
+    }
 }
 
 // Compile-time loop: f(integral_constant<int, B>), ..., f(integral_constant<int, E-1>).
@@ -278,7 +346,8 @@ __device__ __forceinline__ void interleave_step() {
 // NW: waves per workgroup.  4 waves hold 128 x 128 wave tiles (one wave per
 // SIMD); 8 waves hold 128 x 64 wave tiles, two per SIMD, so that one wave's
 // MFMAs can run while the other waits (bf16 only).
-template <int KIND, int RB, int S, bool TAIL, int SG = 1, int E = 0, int D = 0, int NW = 4>
+// FUSED: the fused epilogue of gemm_epi.h instead of the plain fp32 store.
+template <int KIND, int RB, int S, bool TAIL, int SG = 1, int E = 0, int D = 0, int NW = 4, bool FUSED = false>
 __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(Args a) {
     static_assert(NW == 4 || (NW == 8 && KIND != kMX), "8 waves: bf16 only");
     constexpr int THREADS = 64 * NW;
@@ -698,7 +767,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(Args a) {
         }
 
         // ---- epilogue: fp32 stores straight from the accumulators --------
-        store_c<NBJ>(a, acc, m0 + wm * kWaveTile, n0 + wn * WTN, h, l32);
+        store_c<NBJ, FUSED>(a, acc, m0 + wm * kWaveTile, n0 + wn * WTN, h, l32);
         // The next tile's prologue overwrites stages 0 .. S-2: every wave
         // must be done reading them.
         wait_lgkm0();

@@ -54,7 +54,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t span_rsrc(const uint8_t* p, in
 // PF: k-tiles held in registers ahead of the stage being filled (1 or 2
 // register sets).  BN: tile columns, 256 or 192 (wave tiles 128 x BN/2); the
 // narrower tile lets the host match the tile count to the CU count.
-template <int KIND, bool TAIL, int PF = 2, int BN = kTile>
+// FUSED: the fused epilogue of gemm_epi.h instead of the plain fp32 store.
+template <int KIND, bool TAIL, int PF = 2, int BN = kTile, bool FUSED = false>
 __global__ __launch_bounds__(kThreads, 1) void gemm_reg_kernel(Args a) {
     static_assert(KIND == kNT || KIND == kNN, "bf16 only");
     static_assert(PF == 1 || PF == 2, "one or two register sets");
@@ -291,7 +292,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_reg_kernel(Args a) {
             }
         }
 
-        store_c<NBJ>(a, acc, m0 + wm * kWaveTile, n0 + wn * WTN, h, l32);
+        store_c<NBJ, FUSED>(a, acc, m0 + wm * kWaveTile, n0 + wn * WTN, h, l32);
         wait_lgkm0();
         barrier();
     }

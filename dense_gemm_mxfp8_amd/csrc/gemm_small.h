@@ -26,6 +26,8 @@
 
 #pragma once
 
+#include "gemm_epi.h"
+
 namespace small {
 
 constexpr int kStepK = 32;     // k-rows per step (one 16x16x32 MFMA depth)
@@ -34,11 +36,12 @@ constexpr int kRsrcWord3 = 0x00020000;
 struct Args {
     const uint8_t* A;
     const uint8_t* B;
-    float* C;
+    void* C;             // fp32, or bf16 when epi.out_bf16
     int64_t lda_b, ldb_b, ldc;
     int M, N, K;
     int kw;   // k-rows per wave (a multiple of kStepK)
     int pair_xcd;  // map neighbouring column blocks onto one XCD (grid % 16 == 0)
+    epi::Params epi;  // fused epilogue
 };
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -211,7 +214,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_small_m_nn(Args a) {
         float s = 0.f;
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) s += red[(w * MB * 16 + row) * kCols + col];
-        if (row < a.M && n0 + col < a.N) a.C[(int64_t)row * a.ldc + n0 + col] = s;
+        if (row < a.M && n0 + col < a.N) epi::store(a.C, a.ldc, a.epi, row, n0 + col, s);
     }
 }
 

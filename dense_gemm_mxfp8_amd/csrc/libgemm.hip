@@ -53,6 +53,7 @@
 #include <string.h>
 
 #include "libgemm.h"
+#include "gemm_epi.h"
 #include "gemm_fast.h"
 #include "gemm_small.h"
 #include "gemm_reg.h"
@@ -86,6 +87,7 @@ struct Args {
     int kt_total;  // kt_full, plus one if K leaves a partial tile
     int sld;       // scale codes per row: K / 32
     int xcd_remap; // 1: grid is a multiple of 8, spread tiles per XCD
+    epi::Params epi;  // fused epilogue (C is bf16 when epi.out_bf16)
 };
 
 // ---------------------------------------------------------------------------
@@ -429,19 +431,19 @@ __global__ __launch_bounds__(kThreads, (BM * BN >= 256 * 256) ? 1 : 2) void gemm
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int row = m0 + wm * WTM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                    if (row < a.M && col < a.N) a.C[(int64_t)row * a.ldc + col] = acc[i][j][r];
+                    if (row < a.M && col < a.N) epi::store(a.C, a.ldc, a.epi, row, col, acc[i][j][r]);
                 }
             }
     }
 }
 
-// C[0:M, 0:N] := 0 (the K == 0 product).
-__global__ void zero_fill_kernel(float* C, int64_t ldc, int M, int N) {
+// C[0:M, 0:N] := the K == 0 product (zero, through the epilogue if any).
+__global__ void zero_fill_kernel(void* C, int64_t ldc, int M, int N, epi::Params e) {
     int64_t total = (int64_t)M * N;
     for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
          idx += (int64_t)gridDim.x * blockDim.x) {
         int64_t r = idx / N, c = idx - r * N;
-        C[r * ldc + c] = 0.0f;
+        epi::store(C, ldc, e, (int)r, (int)c, 0.0f);
     }
 }
 
@@ -498,18 +500,18 @@ int launch(Args a, int cus, hipStream_t stream) {
     return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
 }
 
-int zero_fill(float* C, int64_t ldc, int64_t M, int64_t N, hipStream_t stream) {
+int zero_fill(void* C, int64_t ldc, int64_t M, int64_t N, const epi::Params& e, hipStream_t stream) {
     int64_t total = M * N;
     int64_t blocks = (total + 255) / 256;
     if (blocks > 4096) blocks = 4096;
     hipLaunchKernelGGL(zero_fill_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, C, ldc, (int)M,
-                       (int)N);
+                       (int)N, e);
     return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
 }
 
 // Common argument checks; returns GEMM_OK to proceed, 1 for "nothing to do".
 int check_common(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
-                 int64_t ldb, int64_t ldb_min, const float* C, int64_t ldc) {
+                 int64_t ldb, int64_t ldb_min, const void* C, int64_t ldc) {
     if (M < 0 || N < 0 || K < 0) return GEMM_ERR_INVALID_ARG;
     if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return GEMM_ERR_INVALID_ARG;
     if (M == 0 || N == 0) return 1;
@@ -522,12 +524,13 @@ int check_common(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, co
 }
 
 Args make_args(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
-               int64_t ldb, float* C, int64_t ldc, int bk) {
+               int64_t ldb, void* C, int64_t ldc, int bk, const epi::Params& e) {
     Args a;
     memset(&a, 0, sizeof a);
     a.A = (const uint8_t*)A;
     a.B = (const uint8_t*)B;
-    a.C = C;
+    a.C = (float*)C;
+    a.epi = e;
     a.lda = lda;
     a.ldb = ldb;
     a.ldc = ldc;
@@ -587,7 +590,7 @@ FastVariant env_variant() {
     return v;
 }
 
-template <int KIND, int RB, int S, int SG = 1, int E = 0, int D = 0, int NW = 4>
+template <int KIND, int RB, int S, int SG = 1, int E = 0, int D = 0, int NW = 4, bool FUSED = false>
 int launch_fast(fast::Args a, int cus, hipStream_t stream, int group_m = 0) {
     constexpr int BK = RB / (KIND == fast::kMX ? 1 : 2);
     a.tiles_m = (a.M + fast::kTile - 1) / fast::kTile;
@@ -601,11 +604,11 @@ int launch_fast(fast::Args a, int cus, hipStream_t stream, int group_m = 0) {
     if (grid >= 8) grid -= grid % 8;
     a.xcd_remap = (grid % 8 == 0) ? 1 : 0;
     if (a.kt_total > a.kt_full)
-        hipLaunchKernelGGL((fast::gemm_fast_kernel<KIND, RB, S, true, SG, E, D, NW>), dim3(grid), dim3(64 * NW), 0,
-                           stream, a);
+        hipLaunchKernelGGL((fast::gemm_fast_kernel<KIND, RB, S, true, SG, E, D, NW, FUSED>), dim3(grid),
+                           dim3(64 * NW), 0, stream, a);
     else
-        hipLaunchKernelGGL((fast::gemm_fast_kernel<KIND, RB, S, false, SG, E, D, NW>), dim3(grid), dim3(64 * NW), 0,
-                           stream, a);
+        hipLaunchKernelGGL((fast::gemm_fast_kernel<KIND, RB, S, false, SG, E, D, NW, FUSED>), dim3(grid),
+                           dim3(64 * NW), 0, stream, a);
     return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
 }
 
@@ -634,12 +637,12 @@ bool fast_ok(int kind, int64_t M, int64_t N, int64_t K, const void* A, int64_t l
 }
 
 fast::Args make_fast_args(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
-                          const void* B, int64_t ldb, float* C, int64_t ldc, int64_t esz) {
+                          const void* B, int64_t ldb, void* C, int64_t ldc, int64_t esz, const epi::Params& e) {
     fast::Args a;
     memset(&a, 0, sizeof a);
     a.A = (const uint8_t*)A;
     a.B = (const uint8_t*)B;
-    a.C = C;
+    a.C = (float*)C;
     a.lda_b = lda * esz;
     a.ldb_b = ldb * esz;
     a.ldc = ldc;
@@ -656,18 +659,24 @@ fast::Args make_fast_args(int64_t M, int64_t N, int64_t K, const void* A, int64_
         const char* e = getenv("LIBGEMM_C_NT");
         return e ? atoi(e) : -1;
     }();
-    const bool lines = ((uintptr_t)C % 128 == 0) && (ldc % 32 == 0);
+    // bf16 output: a 32-column segment is 64 bytes, half a line
+    const bool lines = !e.out_bf16 && ((uintptr_t)C % 128 == 0) && (ldc % 32 == 0);
     a.c_nt = c_nt_env >= 0 ? c_nt_env : (lines ? 1 : 0);
+    a.epi = e;
     return a;
 }
 
 int launch_fast_bf16(bool nt, const fast::Args& a, int cus, hipStream_t s) {
     const FastVariant v = env_variant();
     const int g = v.group;
+    // fused epilogue: the default pipelines only (the variants below are
+    // measurement switches of the plain product)
+    if (a.epi.on) {
+        if (nt) return launch_fast<fast::kNT, 128, 2, 1, 6, 2, 4, true>(a, cus, s, g);
+        return launch_fast<fast::kNN, 128, 2, 1, 6, 2, 4, true>(a, cus, s, g);
+    }
     if (nt) {
-        if (v.rb == 64 && v.stages == 3) return launch_fast<fast::kNT, 64, 3>(a, cus, s, g);
         if (v.rb == 64 && v.stages == 4) return launch_fast<fast::kNT, 64, 4>(a, cus, s, g);
-        if (v.rb == 64 && v.stages == 5) return launch_fast<fast::kNT, 64, 5>(a, cus, s, g);
         // 8 waves (two per SIMD, 128 x 64 wave tiles): measured 1% slower
         // than 4 waves at 8192^3 on MI355X; kept for measurements
         if (v.waves == 8) return launch_fast<fast::kNT, 128, 2, 1, 4, 2, 8>(a, cus, s, g);
@@ -698,7 +707,7 @@ bool reg_ok(bool nt, int64_t K, int64_t lda, int64_t ldb) {
     return K * ldb * 2 + 4 < lim;
 }
 
-template <int PF, int BN>
+template <int PF, int BN, bool FUSED = false>
 int launch_reg_pf(bool nt, fast::Args a, int cus, hipStream_t stream) {
     a.tiles_m = (a.M + fast::kTile - 1) / fast::kTile;
     a.tiles_n = (a.N + BN - 1) / BN;
@@ -718,14 +727,14 @@ int launch_reg_pf(bool nt, fast::Args a, int cus, hipStream_t stream) {
     const dim3 blk(fast::kThreads);
     if (nt) {
         if (tail)
-            hipLaunchKernelGGL((regpath::gemm_reg_kernel<fast::kNT, true, PF, BN>), dim3(grid), blk, 0, stream, a);
+            hipLaunchKernelGGL((regpath::gemm_reg_kernel<fast::kNT, true, PF, BN, FUSED>), dim3(grid), blk, 0, stream, a);
         else
-            hipLaunchKernelGGL((regpath::gemm_reg_kernel<fast::kNT, false, PF, BN>), dim3(grid), blk, 0, stream, a);
+            hipLaunchKernelGGL((regpath::gemm_reg_kernel<fast::kNT, false, PF, BN, FUSED>), dim3(grid), blk, 0, stream, a);
     } else {
         if (tail)
-            hipLaunchKernelGGL((regpath::gemm_reg_kernel<fast::kNN, true, PF, BN>), dim3(grid), blk, 0, stream, a);
+            hipLaunchKernelGGL((regpath::gemm_reg_kernel<fast::kNN, true, PF, BN, FUSED>), dim3(grid), blk, 0, stream, a);
         else
-            hipLaunchKernelGGL((regpath::gemm_reg_kernel<fast::kNN, false, PF, BN>), dim3(grid), blk, 0, stream, a);
+            hipLaunchKernelGGL((regpath::gemm_reg_kernel<fast::kNN, false, PF, BN, FUSED>), dim3(grid), blk, 0, stream, a);
     }
     return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
 }
@@ -756,6 +765,10 @@ int launch_reg(bool nt, const fast::Args& a, int cus, hipStream_t stream) {
         return e ? atoi(e) : 0;
     }();
     const int bn = bn_env == 192 || bn_env == 256 ? bn_env : reg_tile_n(a.M, a.N, cus);
+    if (a.epi.on) {
+        if (bn == 192) return launch_reg_pf<1, 192, true>(nt, a, cus, stream);
+        return launch_reg_pf<1, 256, true>(nt, a, cus, stream);
+    }
     if (bn == 192) {
         if (pf == 2) return launch_reg_pf<2, 192>(nt, a, cus, stream);
         return launch_reg_pf<1, 192>(nt, a, cus, stream);
@@ -780,11 +793,12 @@ bool small_ok(bool nt, int64_t M, int64_t N, int64_t K, const void* A, int64_t l
 
 template <int MB, int NP, int COLS, int WAVES>
 int launch_small(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
-                 float* C, int64_t ldc, hipStream_t stream) {
+                 void* C, int64_t ldc, const epi::Params& e, hipStream_t stream) {
     small::Args a;
     a.A = (const uint8_t*)A;
     a.B = (const uint8_t*)B;
     a.C = C;
+    a.epi = e;
     a.lda_b = lda * 2;
     a.ldb_b = ldb * 2;
     a.ldc = ldc;
@@ -805,7 +819,7 @@ int launch_small(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, co
 }
 
 int launch_small_bf16(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
-                      float* C, int64_t ldc, hipStream_t s) {
+                      void* C, int64_t ldc, const epi::Params& e, hipStream_t s) {
     // LIBGEMM_SMALL=<np>x<cols>x<waves> selects a compiled variant for measurements
     static int sv = [] {
         const char* e = getenv("LIBGEMM_SMALL");
@@ -814,18 +828,18 @@ int launch_small_bf16(int64_t M, int64_t N, int64_t K, const void* A, int64_t ld
         return 0;
     }();
     if (M <= 16) {
-        if (sv == 120000 + 3208) return launch_small<1, 12, 32, 8>(M, N, K, A, lda, B, ldb, C, ldc, s);
-        if (sv == 80000 + 3216) return launch_small<1, 8, 32, 16>(M, N, K, A, lda, B, ldb, C, ldc, s);
-        if (sv == 80000 + 6416) return launch_small<1, 8, 64, 16>(M, N, K, A, lda, B, ldb, C, ldc, s);
-        if (sv == 80000 + 3208) return launch_small<1, 8, 32, 8>(M, N, K, A, lda, B, ldb, C, ldc, s);
-        return launch_small<1, 4, 32, 16>(M, N, K, A, lda, B, ldb, C, ldc, s);
+        if (sv == 120000 + 3208) return launch_small<1, 12, 32, 8>(M, N, K, A, lda, B, ldb, C, ldc, e, s);
+        if (sv == 80000 + 3216) return launch_small<1, 8, 32, 16>(M, N, K, A, lda, B, ldb, C, ldc, e, s);
+        if (sv == 80000 + 6416) return launch_small<1, 8, 64, 16>(M, N, K, A, lda, B, ldb, C, ldc, e, s);
+        if (sv == 80000 + 3208) return launch_small<1, 8, 32, 8>(M, N, K, A, lda, B, ldb, C, ldc, e, s);
+        return launch_small<1, 4, 32, 16>(M, N, K, A, lda, B, ldb, C, ldc, e, s);
     }
-    if (M <= 32) return launch_small<2, 8, 32, 8>(M, N, K, A, lda, B, ldb, C, ldc, s);
-    return launch_small<4, 4, 32, 8>(M, N, K, A, lda, B, ldb, C, ldc, s);
+    if (M <= 32) return launch_small<2, 8, 32, 8>(M, N, K, A, lda, B, ldb, C, ldc, e, s);
+    return launch_small<4, 4, 32, 8>(M, N, K, A, lda, B, ldb, C, ldc, e, s);
 }
 
 int bf16_dispatch(bool nt, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
-                  const void* B, int64_t ldb, float* C, int64_t ldc, void* stream) {
+                  const void* B, int64_t ldb, void* C, int64_t ldc, const epi::Params& e, void* stream) {
     int rc = check_common(M, N, K, A, lda, B, ldb, nt ? K : N, C, ldc);
     if (rc == 1) return GEMM_OK;
     if (rc != GEMM_OK) return rc;
@@ -833,22 +847,22 @@ int bf16_dispatch(bool nt, int64_t M, int64_t N, int64_t K, const void* A, int64
     rc = device_info(&dev);
     if (rc != GEMM_OK) return rc;
     hipStream_t s = (hipStream_t)stream;
-    if (K == 0) return zero_fill(C, ldc, M, N, s);
-    Args a = make_args(M, N, K, A, lda, B, ldb, C, ldc, 64);
+    if (K == 0) return zero_fill(C, ldc, M, N, e, s);
+    Args a = make_args(M, N, K, A, lda, B, ldb, C, ldc, 64, e);
     const bool direct = aligned16(A) && aligned16(B) && (lda % 8 == 0) && (ldb % 8 == 0) &&
                         (nt || (N % 8 == 0));
     if (small_ok(nt, M, N, K, A, lda, B, ldb))
-        return launch_small_bf16(M, N, K, A, lda, B, ldb, C, ldc, s);
+        return launch_small_bf16(M, N, K, A, lda, B, ldb, C, ldc, e, s);
     const bool big = use_big_tiles(M, N, dev.cus);
     // LIBGEMM_FORCE_REG=1 runs the register-load kernel where the direct-load
     // one would (measurement switch)
     static const bool force_reg = getenv("LIBGEMM_FORCE_REG") != nullptr;
     if (force_reg && big && c_ok(ldc) && reg_ok(nt, K, lda, ldb))
-        return launch_reg(nt, make_fast_args(M, N, K, A, lda, B, ldb, C, ldc, 2), dev.cus, s);
+        return launch_reg(nt, make_fast_args(M, N, K, A, lda, B, ldb, C, ldc, 2, e), dev.cus, s);
     if (big && c_ok(ldc) && fast_ok(nt ? fast::kNT : fast::kNN, M, N, K, A, lda, B, ldb, nullptr, nullptr))
-        return launch_fast_bf16(nt, make_fast_args(M, N, K, A, lda, B, ldb, C, ldc, 2), dev.cus, s);
+        return launch_fast_bf16(nt, make_fast_args(M, N, K, A, lda, B, ldb, C, ldc, 2, e), dev.cus, s);
     if (big && c_ok(ldc) && reg_ok(nt, K, lda, ldb))
-        return launch_reg(nt, make_fast_args(M, N, K, A, lda, B, ldb, C, ldc, 2), dev.cus, s);
+        return launch_reg(nt, make_fast_args(M, N, K, A, lda, B, ldb, C, ldc, 2, e), dev.cus, s);
     if (nt) {
         if (big) return direct ? launch<256, 256, kBf16NT, true>(a, dev.cus, s)
                                : launch<256, 256, kBf16NT, false>(a, dev.cus, s);
@@ -861,23 +875,25 @@ int bf16_dispatch(bool nt, int64_t M, int64_t N, int64_t K, const void* A, int64
                   : launch<128, 128, kBf16NN, false>(a, dev.cus, s);
 }
 
-}  // namespace
-
-extern "C" {
-
-int gemm_bf16(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
-              int64_t ldb, float* C, int64_t ldc, void* stream) {
-    return bf16_dispatch(false, M, N, K, A, lda, B, ldb, C, ldc, stream);
+// Epilogue parameters of a fused call; GEMM_ERR_INVALID_ARG for an unknown
+// output type or a C pointer not aligned to its element.
+int fused_params(int out_type, const void* C, const float* rs, const float* cs, const float* bias,
+                 epi::Params* e) {
+    if (out_type != GEMM_OUT_F32 && out_type != GEMM_OUT_BF16) return GEMM_ERR_INVALID_ARG;
+    if (((uintptr_t)C) & (out_type == GEMM_OUT_BF16 ? 1 : 3)) return GEMM_ERR_INVALID_ARG;
+    e->rs = rs;
+    e->cs = cs;
+    e->bias = bias;
+    e->on = 1;
+    e->out_bf16 = out_type == GEMM_OUT_BF16;
+    return GEMM_OK;
 }
 
-int gemm_bf16_nt(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
-                 int64_t ldb, float* C, int64_t ldc, void* stream) {
-    return bf16_dispatch(true, M, N, K, A, lda, B, ldb, C, ldc, stream);
-}
+const epi::Params kPlain = {nullptr, nullptr, nullptr, 0, 0};
 
-int gemm_mxfp8(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
-               int64_t ldb, const uint8_t* scaleA, const uint8_t* scaleB, float* C, int64_t ldc,
-               void* stream) {
+int mx_dispatch(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+                int64_t ldb, const uint8_t* scaleA, const uint8_t* scaleB, void* C, int64_t ldc,
+                const epi::Params& e, void* stream) {
     int rc = check_common(M, N, K, A, lda, B, ldb, K, C, ldc);
     if (rc == 1) return GEMM_OK;
     if (rc != GEMM_OK) return rc;
@@ -887,13 +903,13 @@ int gemm_mxfp8(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, cons
     rc = device_info(&dev);
     if (rc != GEMM_OK) return rc;
     hipStream_t s = (hipStream_t)stream;
-    if (K == 0) return zero_fill(C, ldc, M, N, s);
-    Args a = make_args(M, N, K, A, lda, B, ldb, C, ldc, 128);
+    if (K == 0) return zero_fill(C, ldc, M, N, e, s);
+    Args a = make_args(M, N, K, A, lda, B, ldb, C, ldc, 128, e);
     a.SA = scaleA;
     a.SB = scaleB;
     a.sld = (int)(K / 32);
     if (use_big_tiles(M, N, dev.cus) && c_ok(ldc) && fast_ok(fast::kMX, M, N, K, A, lda, B, ldb, scaleA, scaleB)) {
-        fast::Args f = make_fast_args(M, N, K, A, lda, B, ldb, C, ldc, 1);
+        fast::Args f = make_fast_args(M, N, K, A, lda, B, ldb, C, ldc, 1, e);
         f.SA = scaleA;
         f.SB = scaleB;
         f.sld = (int)(K / 32);
@@ -902,10 +918,14 @@ int gemm_mxfp8(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, cons
         // scale ring: one 16-byte load per row per 4 k-tiles of 128 codes
         const bool ring = (K % 512 == 0) && !(sal & 15);
         const bool word_scales = (K % 128 == 0) && !(sal & 3);
+        if (e.on) {
+            if (ring) return launch_fast<fast::kMX, 128, 2, 4, 12, 0, 4, true>(f, dev.cus, s, v.group);
+            if (word_scales) return launch_fast<fast::kMX, 128, 2, 1, 0, 0, 4, true>(f, dev.cus, s, v.group);
+            return launch_fast<fast::kMX, 64, 4, 1, 0, 0, 4, true>(f, dev.cus, s, v.group);
+        }
         if (v.rb == 64 && v.stages == 4) return launch_fast<fast::kMX, 64, 4>(f, dev.cus, s, v.group);
         if (ring && !(v.rb == 128 && v.stages == 2)) {
             if (v.early == 0) return launch_fast<fast::kMX, 128, 2, 4>(f, dev.cus, s, v.group);
-            if (v.early == 8) return launch_fast<fast::kMX, 128, 2, 4, 8>(f, dev.cus, s, v.group);
             // default: 12 of the 16 DMA instructions of k-tile t+2 right
             // after the barrier of k-tile t (MI355X, 8192^3, same box:
             // 491.5 -> 427.4 us)
@@ -920,6 +940,44 @@ int gemm_mxfp8(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, cons
                       : launch<256, 256, kMx, false>(a, dev.cus, s);
     return direct ? launch<128, 128, kMx, true>(a, dev.cus, s)
                   : launch<128, 128, kMx, false>(a, dev.cus, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+int gemm_bf16(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+              int64_t ldb, float* C, int64_t ldc, void* stream) {
+    return bf16_dispatch(false, M, N, K, A, lda, B, ldb, C, ldc, kPlain, stream);
+}
+
+int gemm_bf16_nt(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+                 int64_t ldb, float* C, int64_t ldc, void* stream) {
+    return bf16_dispatch(true, M, N, K, A, lda, B, ldb, C, ldc, kPlain, stream);
+}
+
+int gemm_mxfp8(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+               int64_t ldb, const uint8_t* scaleA, const uint8_t* scaleB, float* C, int64_t ldc,
+               void* stream) {
+    return mx_dispatch(M, N, K, A, lda, B, ldb, scaleA, scaleB, C, ldc, kPlain, stream);
+}
+
+int gemm_bf16_fused(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
+                    int b_colmajor, void* C, int64_t ldc, int out_type, const float* row_scale,
+                    const float* col_scale, const float* bias, void* stream) {
+    epi::Params e;
+    const int rc = fused_params(out_type, C, row_scale, col_scale, bias, &e);
+    if (rc != GEMM_OK) return rc;
+    return bf16_dispatch(b_colmajor != 0, M, N, K, A, lda, B, ldb, C, ldc, e, stream);
+}
+
+int gemm_mxfp8_fused(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
+                     const uint8_t* scaleA, const uint8_t* scaleB, void* C, int64_t ldc, int out_type,
+                     const float* row_scale, const float* col_scale, const float* bias, void* stream) {
+    epi::Params e;
+    const int rc = fused_params(out_type, C, row_scale, col_scale, bias, &e);
+    if (rc != GEMM_OK) return rc;
+    return mx_dispatch(M, N, K, A, lda, B, ldb, scaleA, scaleB, C, ldc, e, stream);
 }
 
 const char* gemm_strerror(int code) {

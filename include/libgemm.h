@@ -93,6 +93,46 @@ int gemm_mxfp8(int64_t M, int64_t N, int64_t K,
                float* C, int64_t ldc,
                void* stream);
 
+/* ---- fused epilogue ------------------------------------------------------
+ *
+ * The writeback role of "Modern GPU Programming For MLSys - 书籍总结", section
+ * 4.3 (Step 7), and the fusion model of "GPU 执行模型", section "Fusion 的收益
+ * 与上限": the elementwise work that would otherwise read C back is applied to
+ * the fp32 accumulator before the single store:
+ *
+ *     t(i, j) = acc(i, j) * row_scale[i] * col_scale[j] + bias[j]
+ *     C[i*ldc + j] = t rounded to the output type
+ *
+ * evaluated in fp32 in that order (the products may be fused into one
+ * multiply-add).  row_scale (M floats), col_scale (N floats) and bias
+ * (N floats) are device pointers; each may be NULL, meaning 1, 1 and 0.
+ * out_type GEMM_OUT_F32 stores fp32 (C is float*); GEMM_OUT_BF16 stores bf16
+ * rounded to nearest even (C is a 2-byte element array; NaN stays NaN).
+ * ldc counts elements of the output type.  K == 0 stores t with acc = 0.
+ * Every other convention is that of the entry points above; the accuracy
+ * bound applies to acc, and t adds the fp32 rounding of the epilogue and,
+ * for bf16, the final rounding. */
+#define GEMM_OUT_F32 0
+#define GEMM_OUT_BF16 1
+
+/* bf16 operands, B row-major (b_colmajor == 0, as gemm_bf16) or column-major
+ * (b_colmajor != 0, as gemm_bf16_nt). */
+int gemm_bf16_fused(int64_t M, int64_t N, int64_t K,
+                    const void* A, int64_t lda,
+                    const void* B, int64_t ldb, int b_colmajor,
+                    void* C, int64_t ldc, int out_type,
+                    const float* row_scale, const float* col_scale, const float* bias,
+                    void* stream);
+
+/* MX-fp8 operands, as gemm_mxfp8. */
+int gemm_mxfp8_fused(int64_t M, int64_t N, int64_t K,
+                     const void* A, int64_t lda,
+                     const void* B, int64_t ldb,
+                     const uint8_t* scaleA, const uint8_t* scaleB,
+                     void* C, int64_t ldc, int out_type,
+                     const float* row_scale, const float* col_scale, const float* bias,
+                     void* stream);
+
 /* Static text for a return code (never NULL). */
 const char* gemm_strerror(int code);
 

@@ -251,3 +251,60 @@ def gemm_mxfp8(*args, **kw):
 
 def gemm_mxfp8_at(*args, **kw):
     return default().gemm_mxfp8_at(*args, **kw)
+
+
+# ---------------------------------------------------------------- epilogue
+#
+# The fused epilogue is the writeback role ("Modern GPU Programming For MLSys
+# - 书籍总结", section 4.3, Step 7) with the elementwise work of the fusion
+# model ("GPU 执行模型", section "Fusion 的收益与上限") applied before the one
+# store: t(i, j) = acc(i, j) * row_scale[i] * col_scale[j] + bias[j].  Here it
+# is evaluated in binary64 on the oracle's exact product; rounding to the
+# output type is a separate step.  Parity unpinned beyond the special cases
+# the tests check (unit scales reduce it to the plain product; power-of-two
+# scales and integer biases keep every step exact).
+
+def epilogue(acc, mag, row_scale=None, col_scale=None, bias=None, rows=None, cols=None):
+    """(t, m): t as above in float64 and m = |row_scale[i] col_scale[j]| mag,
+    the magnitude the product's accuracy bound scales with.  acc and mag are
+    the oracle's product and sum |a||b|, either full (M, N) arrays or values
+    at the positions (rows, cols)."""
+    t = np.asarray(acc, dtype=np.float64).copy()
+    m = np.asarray(mag, dtype=np.float64).copy()
+    full = rows is None
+    if row_scale is not None:
+        r = np.asarray(row_scale, dtype=np.float64)
+        r = r[:, None] if full else r[rows]
+        t = t * r
+        m = m * np.abs(r)
+    if col_scale is not None:
+        c = np.asarray(col_scale, dtype=np.float64)
+        c = c[None, :] if full else c[cols]
+        t = t * c
+        m = m * np.abs(c)
+    if bias is not None:
+        b = np.asarray(bias, dtype=np.float64)
+        b = b[None, :] if full else b[cols]
+        t = t + b
+    return t, m
+
+
+def round_bf16(x):
+    """Round float64 values to bfloat16 (8 significant bits, exponent range of
+    binary32), nearest even, returned as float64.  Overflow gives +-inf, NaN
+    stays NaN.  Written from the format's definition: the quantum of a value
+    in [2^e, 2^(e+1)) is 2^(e-7), and 2^-133 below the normal range."""
+    x = np.asarray(x, dtype=np.float64)
+    out = np.array(x, dtype=np.float64, copy=True)
+    fin = np.isfinite(x) & (x != 0)
+    v = x[fin]
+    e = np.floor(np.log2(np.abs(v)))
+    # log2 can be off by one next to powers of two: correct the exponent
+    e = np.where(np.abs(v) >= np.exp2(e + 1), e + 1, e)
+    e = np.where(np.abs(v) < np.exp2(e), e - 1, e)
+    q = np.exp2(np.maximum(e, -126.0) - 7.0)
+    r = np.rint(v / q) * q  # np.rint rounds half to even
+    big = (2.0 - 2.0 ** -7) * 2.0 ** 127
+    r = np.where(np.abs(r) > big, np.copysign(np.inf, v), r)
+    out[fin] = r
+    return out

@@ -74,3 +74,15 @@ def test_empty_extents_are_a_no_op():
     assert dg.gemm_bf16(0, 8, 16, 0, 16, 0, 8, 0, 8, 0) == dg.GEMM_OK
     assert dg.gemm_bf16_nt(4, 0, 16, 0, 16, 0, 16, 0, 1, 0) == dg.GEMM_OK
     assert dg.gemm_mxfp8(0, 0, 64, 0, 64, 0, 64, 0, 0, 0, 1, 0) == dg.GEMM_OK
+
+
+def test_fused_entry_points_reject_bad_epilogue_arguments():
+    # checked before any device call
+    assert dg.gemm_bf16_fused(4, 4, 4, 16, 4, 16, 4, 0, 16, 4, 7, None, None, None, None) == dg.GEMM_ERR_INVALID_ARG
+    # fp32 output needs a 4-byte aligned C, bf16 a 2-byte aligned one
+    assert dg.gemm_bf16_fused(4, 4, 4, 16, 4, 16, 4, 1, 18, 4, dg.GEMM_OUT_F32, None, None, None,
+                              None) == dg.GEMM_ERR_INVALID_ARG
+    assert dg.gemm_mxfp8_fused(4, 4, 32, 16, 32, 16, 32, 16, 16, 17, 4, dg.GEMM_OUT_BF16, None, None, None,
+                               None) == dg.GEMM_ERR_INVALID_ARG
+    # empty extents are still a no-op
+    assert dg.gemm_bf16_fused(0, 4, 4, 0, 4, 0, 4, 0, 0, 4, dg.GEMM_OUT_BF16, None, None, None, None) == dg.GEMM_OK
