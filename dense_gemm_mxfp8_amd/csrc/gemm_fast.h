@@ -236,10 +236,14 @@ __device__ __forceinline__ void store_c_aux(const Args& a, const f32x16 (&acc)[k
 
 // Fused epilogue (gemm_epi.h): t = acc * rs[row] * cs[col] + bias[col] in
 // fp32, stored as fp32 or bf16, with the descriptor scheme of store_c_aux.
-// The scale and bias vectors are read only inside M x N.
+// The tile's scale and bias values were loaded into registers when the tile
+// started (epi_prefetch) and staged in LDS before the epilogue (epi_stage),
+// so no global load latency shows here: ev points at 3 x 256 floats (row
+// scales, column scales, biases of the tile), evr / evc are this wave's
+// first row / column within the tile.
 template <int AUX, int NBJ, bool BF16>
 __device__ __forceinline__ void store_c_fused(const Args& a, const f32x16 (&acc)[kBlocks][NBJ], int m0w, int n0w,
-                                              int h, int l32) {
+                                              int h, int l32, const float FAST_LDS* ev, int evr, int evc) {
     const int rlim = a.M - m0w;
     const int clim = a.N - n0w;
     if (rlim <= 0 || clim <= 0) return;
@@ -250,25 +254,18 @@ __device__ __forceinline__ void store_c_fused(const Args& a, const f32x16 (&acc)
     const __amdgpu_buffer_rsrc_t rc = make_rsrc((const uint8_t*)a.C + ((int64_t)m0w * a.ldc + n0w) * ESZ,
                                                 ((int64_t)(rows - 1) * a.ldc + cols) * ESZ);
     const int voff = 4 * h * ldcb + ESZ * l32;
-    const epi::Params& e = a.epi;
+    const bool has_r = a.epi.rs != nullptr, has_c = a.epi.cs != nullptr, has_b = a.epi.bias != nullptr;
     float cf[NBJ], cb[NBJ];
 #pragma unroll
     for (int j = 0; j < NBJ; ++j) {
-        const int col = 32 * j + l32;
-        const bool ok = col < cols;
-        cf[j] = (e.cs && ok) ? e.cs[n0w + col] : 1.0f;
-        cb[j] = (e.bias && ok) ? e.bias[n0w + col] : 0.0f;
+        cf[j] = ev[256 + evc + 32 * j + l32];
+        cb[j] = ev[512 + evc + 32 * j + l32];
     }
 #pragma unroll
     for (int i = 0; i < kBlocks; ++i) {
-        // one 32-row block at a time, so that its 16 row factors are the only
-        // ones live
         float rf[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int lrow = 32 * i + 8 * (r >> 2) + (r & 3) + 4 * h;
-            rf[r] = (e.rs && lrow < rows) ? e.rs[m0w + lrow] : 1.0f;
-        }
+        for (int r = 0; r < 16; ++r) rf[r] = ev[evr + 32 * i + 8 * (r >> 2) + (r & 3) + 4 * h];
 #pragma unroll
         for (int j = 0; j < NBJ; ++j) {
             if (32 * j + l32 < cols) {
@@ -276,9 +273,9 @@ __device__ __forceinline__ void store_c_fused(const Args& a, const f32x16 (&acc)
                 for (int r = 0; r < 16; ++r) {
                     const int row = 32 * i + 8 * (r >> 2) + (r & 3);
                     float t = acc[i][j][r];
-                    if (e.rs) t *= rf[r];
-                    if (e.cs) t *= cf[j];
-                    if (e.bias) t += cb[j];
+                    if (has_r) t *= rf[r];
+                    if (has_c) t *= cf[j];
+                    if (has_b) t += cb[j];
                     if constexpr (BF16)
                         __builtin_amdgcn_raw_buffer_store_b16(epi::to_bf16(t), rc, voff + 64 * j, row * ldcb, AUX);
                     else
@@ -291,15 +288,39 @@ __device__ __forceinline__ void store_c_fused(const Args& a, const f32x16 (&acc)
     }
 }
 
+// The fused epilogue's values for one tile, one row, one column and one bias
+// per thread (256 threads cover 256 rows and up to 256 columns), loaded when
+// the tile starts so that their latency hides under the K loop.
+struct EpiRegs {
+    float r, c, b;
+};
+
+__device__ __forceinline__ EpiRegs epi_prefetch(const Args& a, int m0, int n0, int bn, int tid) {
+    EpiRegs v{1.0f, 1.0f, 0.0f};
+    const epi::Params& e = a.epi;
+    if (e.rs && m0 + tid < a.M) v.r = e.rs[m0 + tid];
+    if (tid < bn && n0 + tid < a.N) {
+        if (e.cs) v.c = e.cs[n0 + tid];
+        if (e.bias) v.b = e.bias[n0 + tid];
+    }
+    return v;
+}
+
+__device__ __forceinline__ void epi_stage(float FAST_LDS* ev, const EpiRegs& v, int tid) {
+    ev[tid] = v.r;
+    ev[256 + tid] = v.c;
+    ev[512 + tid] = v.b;
+}
+
 // FUSED: the kernel instance carries the fused epilogue (a.epi.on); plain
 // instances keep the lean store path.
 template <int NBJ = kBlocks, bool FUSED = false>
 __device__ __forceinline__ void store_c(const Args& a, const f32x16 (&acc)[kBlocks][NBJ], int m0w, int n0w, int h,
-                                        int l32) {
+                                        int l32, const float FAST_LDS* ev = nullptr, int evr = 0, int evc = 0) {
     if constexpr (FUSED) {
-        if (a.epi.out_bf16) store_c_fused<0, NBJ, true>(a, acc, m0w, n0w, h, l32);
-        else if (a.c_nt) store_c_fused<2, NBJ, false>(a, acc, m0w, n0w, h, l32);
-        else store_c_fused<0, NBJ, false>(a, acc, m0w, n0w, h, l32);
+        if (a.epi.out_bf16) store_c_fused<0, NBJ, true>(a, acc, m0w, n0w, h, l32, ev, evr, evc);
+        else if (a.c_nt) store_c_fused<2, NBJ, false>(a, acc, m0w, n0w, h, l32, ev, evr, evc);
+        else store_c_fused<0, NBJ, false>(a, acc, m0w, n0w, h, l32, ev, evr, evc);
     } else {
         if (a.c_nt) store_c_aux<2, NBJ>(a, acc, m0w, n0w, h, l32);
         else store_c_aux<0, NBJ>(a, acc, m0w, n0w, h, l32);
@@ -405,6 +426,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(Args a) {
     __shared__ __attribute__((aligned(1024))) uint8_t st4[S > 4 ? STAGE : 16];
     __shared__ __attribute__((aligned(1024))) uint8_t sr0[RING];
     __shared__ __attribute__((aligned(1024))) uint8_t sr1[RING];
+    __shared__ float evl[FUSED ? 3 * 256 : 1];  // fused epilogue: the tile's scales and biases
     auto stage_ptr = [&](auto sidx) -> uint8_t FAST_LDS* {
         constexpr int s = decltype(sidx)::value;
         if constexpr (s == 0) return (uint8_t FAST_LDS*)st0;
@@ -481,6 +503,8 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(Args a) {
         const int m0 = tm * kTile, n0 = tn * kTile;
         const int rows_a = min(kTile, a.M - m0);
         const int rows_b = min(kTile, a.N - n0);
+        EpiRegs epv{};
+        if constexpr (FUSED) epv = epi_prefetch(a, m0, n0, kTile, tid);
 
         // Per-tile buffer descriptors: everything past the last valid row
         // (or, for row-major B, past the last k row) reads as zero.  The
@@ -767,7 +791,14 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(Args a) {
         }
 
         // ---- epilogue: fp32 stores straight from the accumulators --------
-        store_c<NBJ, FUSED>(a, acc, m0 + wm * kWaveTile, n0 + wn * WTN, h, l32);
+        if constexpr (FUSED) {
+            static_assert(NW == 4, "fused epilogue: one row, column and bias per thread");
+            epi_stage((float FAST_LDS*)evl, epv, tid);
+            wait_lgkm0();
+            barrier();
+        }
+        store_c<NBJ, FUSED>(a, acc, m0 + wm * kWaveTile, n0 + wn * WTN, h, l32, (const float FAST_LDS*)evl,
+                            wm * kWaveTile, wn * WTN);
         // The next tile's prologue overwrites stages 0 .. S-2: every wave
         // must be done reading them.
         wait_lgkm0();

@@ -66,6 +66,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_reg_kernel(Args a) {
     constexpr int NCB = 4 * BN / kThreads;  // 16-byte chunks of B per thread
     __shared__ __attribute__((aligned(1024))) uint8_t st0[STAGE];
     __shared__ __attribute__((aligned(1024))) uint8_t st1[STAGE];
+    __shared__ float evl[FUSED ? 3 * 256 : 1];  // fused epilogue: the tile's scales and biases
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -126,6 +127,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_reg_kernel(Args a) {
         const int m0 = tm * kTile, n0 = tn * BN;
         const int rows_a = min(kTile, a.M - m0);
         const int rows_b = min(BN, a.N - n0);
+        EpiRegs epv{};
+        if constexpr (FUSED) epv = epi_prefetch(a, m0, n0, BN, tid);
         int sa, sb;
         const __amdgpu_buffer_rsrc_t ra =
             span_rsrc(a.A + (int64_t)m0 * a.lda_b, (int64_t)(rows_a - 1) * a.lda_b + (int64_t)a.K * 2, sa);
@@ -292,7 +295,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_reg_kernel(Args a) {
             }
         }
 
-        store_c<NBJ, FUSED>(a, acc, m0 + wm * kWaveTile, n0 + wn * WTN, h, l32);
+        if constexpr (FUSED) {
+            epi_stage((float FAST_LDS*)evl, epv, tid);
+            wait_lgkm0();
+            barrier();
+        }
+        store_c<NBJ, FUSED>(a, acc, m0 + wm * kWaveTile, n0 + wn * WTN, h, l32, (const float FAST_LDS*)evl,
+                            wm * kWaveTile, wn * WTN);
         wait_lgkm0();
         barrier();
     }
