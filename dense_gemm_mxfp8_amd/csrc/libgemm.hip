@@ -983,13 +983,14 @@ int gemm_mxfp8_fused(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda
 const char* gemm_strerror(int code) {
     switch (code) {
         case GEMM_OK: return "success";
-        case GEMM_ERR_INVALID_ARG: return "invalid argument (size, leading dimension, pointer or K alignment)";
+        case GEMM_ERR_INVALID_ARG:
+            return "invalid argument (size, leading dimension, pointer, K alignment or output type)";
         case GEMM_ERR_UNSUPPORTED: return "unsupported device (a gfx950 GPU is required)";
         case GEMM_ERR_LAUNCH: return "kernel launch failed";
         default: return "unknown error code";
     }
 }
 
-int gemm_version(void) { return 100; }
+int gemm_version(void) { return 200; }
 
 }  // extern "C"

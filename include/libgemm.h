@@ -57,7 +57,8 @@ extern "C" {
 
 #define GEMM_OK 0
 /* a size is negative, a leading dimension too small, a pointer NULL with a
- * non-empty extent, or (MX) K not a multiple of 32 */
+ * non-empty extent, (MX) K not a multiple of 32, or (fused entry points) an
+ * unknown output type or a C pointer not aligned to its element */
 #define GEMM_ERR_INVALID_ARG (-1)
 /* the current device is not a gfx950 (MI355X-class) GPU, or no device */
 #define GEMM_ERR_UNSUPPORTED (-2)
