@@ -50,6 +50,12 @@ def library() -> ctypes.CDLL:
         lib.gemm_mxfp8_fused.restype = ctypes.c_int
         lib.gemm_mxfp8_fused.argtypes = [_i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _i64,
                                          ctypes.c_int, _vp, _vp, _vp, _vp]
+        lib.gemm_bf16_splitk.restype = ctypes.c_int
+        lib.gemm_bf16_splitk.argtypes = [_i64, _i64, _i64, _vp, _i64, _vp, _i64, ctypes.c_int, _vp, _i64,
+                                         ctypes.c_int, _vp, _vp, _vp, ctypes.c_int, _vp, ctypes.c_size_t, _vp]
+        lib.gemm_bf16_splitk_plan.restype = ctypes.c_int
+        lib.gemm_bf16_splitk_plan.argtypes = [_i64, _i64, _i64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                              ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_size_t)]
         lib.gemm_strerror.restype = ctypes.c_char_p
         lib.gemm_strerror.argtypes = [ctypes.c_int]
         lib.gemm_version.restype = ctypes.c_int
@@ -82,6 +88,21 @@ def gemm_mxfp8_fused(M, N, K, A, lda, B, ldb, scaleA, scaleB, C, ldc, out_type, 
                      stream) -> int:
     return library().gemm_mxfp8_fused(M, N, K, A, lda, B, ldb, scaleA, scaleB, C, ldc, out_type, row_scale,
                                       col_scale, bias, stream)
+
+
+def gemm_bf16_splitk(M, N, K, A, lda, B, ldb, b_colmajor, C, ldc, out_type, row_scale, col_scale, bias,
+                     splits, workspace, workspace_bytes, stream) -> int:
+    return library().gemm_bf16_splitk(M, N, K, A, lda, B, ldb, int(b_colmajor), C, ldc, out_type, row_scale,
+                                      col_scale, bias, splits, workspace, workspace_bytes, stream)
+
+
+def gemm_bf16_splitk_plan(M, N, K, b_colmajor, splits=0, cus=0):
+    """(return code, K ranges used, workspace bytes) of the split-K plan."""
+    used = ctypes.c_int(0)
+    ws = ctypes.c_size_t(0)
+    rc = library().gemm_bf16_splitk_plan(M, N, K, int(b_colmajor), splits, cus, ctypes.byref(used),
+                                         ctypes.byref(ws))
+    return rc, used.value, ws.value
 
 
 def gemm_strerror(code: int) -> str:
@@ -138,15 +159,8 @@ def _epilogue(out_dtype, row_scale, col_scale, bias, M, N):
     return fused, out_type, ptrs
 
 
-def bf16(A, B, out=None, *, out_dtype=None, row_scale=None, col_scale=None, bias=None):
-    """C = A @ B in fp32 from bf16 CUDA tensors.
-
-    A: (M, K), row-major rows (unit column stride).  B: a (K, N) tensor that is
-    either row-major (unit column stride: ``gemm_bf16``) or column-major
-    (unit row stride, e.g. ``Bt.t()`` of an (N, K) tensor: ``gemm_bf16_nt``).
-    With any of out_dtype (float32 or bfloat16), row_scale (M), col_scale (N)
-    or bias (N) the fused epilogue applies: C = A @ B * row_scale[:, None] *
-    col_scale[None, :] + bias[None, :] (``gemm_bf16_fused``)."""
+def _bf16_operands(A, B):
+    """(M, N, K, lda, ldb, b_colmajor) of bf16 operands A (M, K) and B (K, N)."""
     import torch
     if A.dtype != torch.bfloat16 or B.dtype != torch.bfloat16:
         raise TypeError("A and B must be bfloat16")
@@ -157,22 +171,53 @@ def bf16(A, B, out=None, *, out_dtype=None, row_scale=None, col_scale=None, bias
     if M > 0 and K > 1 and A.stride(1) != 1:
         raise ValueError("A needs unit column stride")
     lda = A.stride(0) if M > 1 else max(K, 1)
+    if N <= 1 or B.stride(1) == 1:
+        return M, N, K, lda, (B.stride(0) if K > 1 else max(N, 1)), False
+    if B.stride(0) == 1:
+        return M, N, K, lda, B.stride(1), True
+    raise ValueError("B must have a unit stride along N (row-major) or K (column-major)")
+
+
+def bf16(A, B, out=None, *, out_dtype=None, row_scale=None, col_scale=None, bias=None):
+    """C = A @ B in fp32 from bf16 CUDA tensors.
+
+    A: (M, K), row-major rows (unit column stride).  B: a (K, N) tensor that is
+    either row-major (unit column stride: ``gemm_bf16``) or column-major
+    (unit row stride, e.g. ``Bt.t()`` of an (N, K) tensor: ``gemm_bf16_nt``).
+    With any of out_dtype (float32 or bfloat16), row_scale (M), col_scale (N)
+    or bias (N) the fused epilogue applies: C = A @ B * row_scale[:, None] *
+    col_scale[None, :] + bias[None, :] (``gemm_bf16_fused``)."""
+    M, N, K, lda, ldb, colmajor = _bf16_operands(A, B)
+    fn = gemm_bf16_nt if colmajor else gemm_bf16
     fused, out_type, (rs, cs, bs) = _epilogue(out_dtype, row_scale, col_scale, bias, M, N)
     C = _out(out, M, N, A.device, out_dtype)
     ldc = C.stride(0) if M > 1 else max(N, 1)
-    if N <= 1 or B.stride(1) == 1:
-        ldb = B.stride(0) if K > 1 else max(N, 1)
-        colmajor, fn = False, gemm_bf16
-    elif B.stride(0) == 1:
-        ldb = B.stride(1)
-        colmajor, fn = True, gemm_bf16_nt
-    else:
-        raise ValueError("B must have a unit stride along N (row-major) or K (column-major)")
     if fused:
         _check(gemm_bf16_fused(M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, colmajor, C.data_ptr(), ldc,
                                out_type, rs, cs, bs, _stream(A.device)))
     else:
         _check(fn(M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, C.data_ptr(), ldc, _stream(A.device)))
+    return C
+
+
+def bf16_splitk(A, B, out=None, *, splits=0, workspace=None, out_dtype=None, row_scale=None, col_scale=None,
+                bias=None):
+    """``bf16`` through ``gemm_bf16_splitk``: K cut into `splits` ranges (0:
+    the library's plan) whose fp32 partial products are added in range
+    order.  workspace: a CUDA tensor of at least the planned bytes (16-byte
+    aligned); None allocates one with torch for this call."""
+    import torch
+    M, N, K, lda, ldb, colmajor = _bf16_operands(A, B)
+    _, out_type, (rs, cs, bs) = _epilogue(out_dtype, row_scale, col_scale, bias, M, N)
+    C = _out(out, M, N, A.device, out_dtype)
+    ldc = C.stride(0) if M > 1 else max(N, 1)
+    if workspace is None:
+        rc, _, nbytes = gemm_bf16_splitk_plan(M, N, K, colmajor, splits)
+        _check(rc)
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=A.device)
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(gemm_bf16_splitk(M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, colmajor, C.data_ptr(), ldc, out_type,
+                            rs, cs, bs, splits, workspace.data_ptr(), nbytes, _stream(A.device)))
     return C
 
 

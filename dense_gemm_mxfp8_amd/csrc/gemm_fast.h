@@ -71,6 +71,10 @@ struct Args {
     int xcd_remap;
     int c_nt;      // C stores non-temporal (1) or cached (0)
     epi::Params epi;  // fused epilogue (C is bf16 when epi.out_bf16)
+    // split-K instances: work unit u is tile u % tiles_per_split of K range
+    // u / tiles_per_split ([ks kslice, min(K, (ks + 1) kslice)), kslice a
+    // multiple of the k-tile); its fp32 partial sums go to rows ks M .. of C
+    int tiles_per_split, kslice;
 };
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -206,7 +210,7 @@ __device__ __forceinline__ void tail_nn(uint8_t FAST_LDS* dst, __amdgpu_buffer_r
 // cached so that L2 merges the two halves of each line.
 template <int AUX, int NBJ>
 __device__ __forceinline__ void store_c_aux(const Args& a, const f32x16 (&acc)[kBlocks][NBJ], int m0w, int n0w,
-                                            int h, int l32) {
+                                            int h, int l32, int crow) {
     const int rlim = a.M - m0w;
     const int clim = a.N - n0w;
     if (rlim <= 0 || clim <= 0) return;
@@ -214,7 +218,7 @@ __device__ __forceinline__ void store_c_aux(const Args& a, const f32x16 (&acc)[k
     const int cols = clim < 32 * NBJ ? clim : 32 * NBJ;
     const int ldc4 = (int)a.ldc * 4;
     const __amdgpu_buffer_rsrc_t rc =
-        make_rsrc(a.C + (int64_t)m0w * a.ldc + n0w, ((int64_t)(rows - 1) * a.ldc + cols) * 4);
+        make_rsrc(a.C + (int64_t)(m0w + crow) * a.ldc + n0w, ((int64_t)(rows - 1) * a.ldc + cols) * 4);
     const int voff = 4 * h * ldc4 + 4 * l32;
 #pragma unroll
     for (int j = 0; j < NBJ; ++j) {
@@ -313,17 +317,19 @@ __device__ __forceinline__ void epi_stage(float FAST_LDS* ev, const EpiRegs& v, 
 }
 
 // FUSED: the kernel instance carries the fused epilogue (a.epi.on); plain
-// instances keep the lean store path.
+// instances keep the lean store path.  crow: rows of C skipped before row 0
+// of the product (a split-K partial's block of the workspace; plain only).
 template <int NBJ = kBlocks, bool FUSED = false>
 __device__ __forceinline__ void store_c(const Args& a, const f32x16 (&acc)[kBlocks][NBJ], int m0w, int n0w, int h,
-                                        int l32, const float FAST_LDS* ev = nullptr, int evr = 0, int evc = 0) {
+                                        int l32, const float FAST_LDS* ev = nullptr, int evr = 0, int evc = 0,
+                                        int crow = 0) {
     if constexpr (FUSED) {
         if (a.epi.out_bf16) store_c_fused<0, NBJ, true>(a, acc, m0w, n0w, h, l32, ev, evr, evc);
         else if (a.c_nt) store_c_fused<2, NBJ, false>(a, acc, m0w, n0w, h, l32, ev, evr, evc);
         else store_c_fused<0, NBJ, false>(a, acc, m0w, n0w, h, l32, ev, evr, evc);
     } else {
-        if (a.c_nt) store_c_aux<2, NBJ>(a, acc, m0w, n0w, h, l32);
-        else store_c_aux<0, NBJ>(a, acc, m0w, n0w, h, l32);
+        if (a.c_nt) store_c_aux<2, NBJ>(a, acc, m0w, n0w, h, l32, crow);
+        else store_c_aux<0, NBJ>(a, acc, m0w, n0w, h, l32, crow);
     }
 }
 
@@ -368,9 +374,13 @@ __device__ __forceinline__ void interleave_step() {
 // SIMD); 8 waves hold 128 x 64 wave tiles, two per SIMD, so that one wave's
 // MFMAs can run while the other waits (bf16 only).
 // FUSED: the fused epilogue of gemm_epi.h instead of the plain fp32 store.
-template <int KIND, int RB, int S, bool TAIL, int SG = 1, int E = 0, int D = 0, int NW = 4, bool FUSED = false>
+// SPLIT: split-K work units (Args::tiles_per_split, Args::kslice); each unit
+// stores its fp32 partial sums, which a separate pass adds in a fixed order.
+template <int KIND, int RB, int S, bool TAIL, int SG = 1, int E = 0, int D = 0, int NW = 4, bool FUSED = false,
+          bool SPLIT = false>
 __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(Args a) {
     static_assert(NW == 4 || (NW == 8 && KIND != kMX), "8 waves: bf16 only");
+    static_assert(!SPLIT || (KIND != kMX && !FUSED && NW == 4), "split-K: plain bf16 only");
     constexpr int THREADS = 64 * NW;
     constexpr int NBJ = NW == 8 ? 2 : kBlocks;  // 32-column MFMA blocks per wave tile
     constexpr int WTN = 32 * NBJ;               // wave tile columns
@@ -493,13 +503,22 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(Args a) {
     const int sa_rd = 2 * OPB + 4 * (wm * kWaveTile + l32);
     const int sb_rd = 2 * OPB + 4 * kTile + 4 * (wn * kWaveTile + l32);
 
-    const int KT = a.kt_full;                // k-tiles holding data
-    const int KTM = (KT + U - 1) / U * U;    // rounded up: the rest are dead (zero) k-tiles
-
     const int G = gridDim.x;
     for (int t = logical_block(a); t < a.num_tiles; t += G) {
+        // split-K: unit t is tile tt of K range ks; K ranges are the slow
+        // index, so concurrently running units read the same k columns
+        int tt = t, k0 = 0, Kl = a.K, crow = 0;
+        if constexpr (SPLIT) {
+            const int ks = t / a.tiles_per_split;
+            tt = t - ks * a.tiles_per_split;
+            k0 = ks * a.kslice;
+            Kl = min(a.K - k0, a.kslice);
+            crow = ks * a.M;
+        }
+        const int KT = SPLIT ? Kl / BK : a.kt_full;  // k-tiles holding data
+        const int KTM = (KT + U - 1) / U * U;        // rounded up: the rest are dead (zero) k-tiles
         int tm, tn;
-        tile_coords(a, t, tm, tn);
+        tile_coords(a, tt, tm, tn);
         const int m0 = tm * kTile, n0 = tn * kTile;
         const int rows_a = min(kTile, a.M - m0);
         const int rows_b = min(kTile, a.N - n0);
@@ -510,17 +529,17 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(Args a) {
         // (or, for row-major B, past the last k row) reads as zero.  The
         // dead descriptor (size 0) turns the loads of k-tiles past the end
         // into zero fill without memory traffic.
-        const uint8_t* a_base = a.A + (int64_t)m0 * a.lda_b;
+        const uint8_t* a_base = a.A + (int64_t)m0 * a.lda_b + (int64_t)k0 * ESZ;
         const __amdgpu_buffer_rsrc_t ra =
-            make_rsrc(a_base, round4((int64_t)(rows_a - 1) * a.lda_b + (int64_t)a.K * ESZ));
+            make_rsrc(a_base, round4((int64_t)(rows_a - 1) * a.lda_b + (int64_t)Kl * ESZ));
         const uint8_t* b_base;
         __amdgpu_buffer_rsrc_t rb;
         if constexpr (KIND == kNN) {
-            b_base = a.B + (int64_t)n0 * 2;
-            rb = make_rsrc(b_base, (int64_t)(a.K - 1) * a.ldb_b + (int64_t)(a.N - n0) * 2);
+            b_base = a.B + (int64_t)n0 * 2 + (int64_t)k0 * a.ldb_b;
+            rb = make_rsrc(b_base, (int64_t)(Kl - 1) * a.ldb_b + (int64_t)(a.N - n0) * 2);
         } else {
-            b_base = a.B + (int64_t)n0 * a.ldb_b;
-            rb = make_rsrc(b_base, round4((int64_t)(rows_b - 1) * a.ldb_b + (int64_t)a.K * ESZ));
+            b_base = a.B + (int64_t)n0 * a.ldb_b + (int64_t)k0 * ESZ;
+            rb = make_rsrc(b_base, round4((int64_t)(rows_b - 1) * a.ldb_b + (int64_t)Kl * ESZ));
         }
         const __amdgpu_buffer_rsrc_t rdead = make_rsrc(a.A, 0);
         __amdgpu_buffer_rsrc_t rsa = rdead, rsb = rdead;
@@ -775,7 +794,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(Args a) {
         if constexpr (TAIL && KIND != kMX) {
             barrier();  // every wave is done with the pipelined stages
             uint8_t FAST_LDS* As = stage_ptr(std::integral_constant<int, 0>{});
-            const int kvalid = a.K - KT * BK;
+            const int kvalid = Kl - KT * BK;  // 0 for a split-K unit before the last
             tail_kc<RB, THREADS>(As, ra, (int)a.lda_b, KT * RB, kvalid * ESZ, tid);
             if constexpr (KIND == kNN)
                 tail_nn<BK, THREADS>(As + OPB, rb, (int)a.ldb_b, KT * BK * (int)a.ldb_b, kvalid, a.N - n0, tid);
@@ -798,7 +817,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(Args a) {
             barrier();
         }
         store_c<NBJ, FUSED>(a, acc, m0 + wm * kWaveTile, n0 + wn * WTN, h, l32, (const float FAST_LDS*)evl,
-                            wm * kWaveTile, wn * WTN);
+                            wm * kWaveTile, wn * WTN, crow);
         // The next tile's prologue overwrites stages 0 .. S-2: every wave
         // must be done reading them.
         wait_lgkm0();

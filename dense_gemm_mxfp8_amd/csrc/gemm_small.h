@@ -18,6 +18,11 @@
 //   * the 8 per-wave partial sums are added in LDS in wave order (a fixed
 //     order, so results are deterministic) and written as fp32.
 //
+// Split-K: blockIdx.y selects the K range [y kslice, min(K, (y+1) kslice)),
+// and the workgroup writes its fp32 partial sums to C + y c_split (plain
+// store); a separate pass adds the partials in range order.  Without a
+// split, gridDim.y == 1 and kslice == K.
+//
 // Bounds: B and A are read through buffer descriptors, so rows past K (B)
 // and past M (A) read as zero; A's elements past K inside a valid row are
 // masked in registers on the last step.  Columns past N only feed outputs
@@ -42,6 +47,8 @@ struct Args {
     int kw;   // k-rows per wave (a multiple of kStepK)
     int pair_xcd;  // map neighbouring column blocks onto one XCD (grid % 16 == 0)
     epi::Params epi;  // fused epilogue
+    int kslice;       // K range per blockIdx.y (a multiple of kStepK)
+    int64_t c_split;  // fp32 elements between the partial sums of two K ranges
 };
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -90,6 +97,12 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_small_m_nn(Args a) {
         blk = 16 * (q >> 1) + 2 * x + (q & 1);
     }
     const int n0 = blk * kCols;
+    // this workgroup's K range (the whole of K without a split)
+    const int k0 = blockIdx.y * a.kslice;
+    const int K = min(a.K - k0, a.kslice);
+    const uint8_t* const A = a.A + (int64_t)k0 * 2;
+    const uint8_t* const B = a.B + (int64_t)k0 * a.ldb_b;
+    void* const C = (float*)a.C + blockIdx.y * a.c_split;
     // wave w takes the 32-row steps w, w + WAVES, w + 2 WAVES, ...: all
     // waves (and all workgroups) sweep one contiguous band of B rows together
     const int steps = a.kw / kStepK;
@@ -101,10 +114,10 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_small_m_nn(Args a) {
     // masked (A) or feed only columns that are not stored (B).
     // B descriptor from column n0: rows past K read as zero.
     const __amdgpu_buffer_rsrc_t rb =
-        make_rsrc(a.B + (int64_t)n0 * 2, ((int64_t)(a.K - 1) * a.ldb_b + (int64_t)(a.N - n0) * 2 + 3) & ~(int64_t)3);
+        make_rsrc(B + (int64_t)n0 * 2, ((int64_t)(K - 1) * a.ldb_b + (int64_t)(a.N - n0) * 2 + 3) & ~(int64_t)3);
     // A descriptor: rows past M read as zero.
     const __amdgpu_buffer_rsrc_t ra =
-        make_rsrc(a.A, ((int64_t)(a.M - 1) * a.lda_b + (int64_t)a.K * 2 + 3) & ~(int64_t)3);
+        make_rsrc(A, ((int64_t)(a.M - 1) * a.lda_b + (int64_t)K * 2 + 3) & ~(int64_t)3);
 
     // B loads: lane l covers k-row (l / LPR) (+ RPI per further load) and
     // bytes 16 (l % LPR) .. +15 of the block's row segment.
@@ -127,7 +140,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_small_m_nn(Args a) {
         for (int c = 0; c < CB; ++c) acc[b][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     // zero-size descriptor: loads of steps past the wave's range are zero
-    const __amdgpu_buffer_rsrc_t rdead = make_rsrc(a.B, 0);
+    const __amdgpu_buffer_rsrc_t rdead = make_rsrc(B, 0);
     i32x4 rB[NP][NL];
     i32x4 rA[NP][MB];
     auto issue = [&](int slot, int st) {
@@ -160,16 +173,16 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_small_m_nn(Args a) {
                 *(i32x4 SMALL_LDS*)(buf + (h * RPI + lane / LPR) * (kCols * 2) + (lane % LPR) * 16) = rB[p][h];
             // A past K inside a valid row must not reach the sum
             const int kfirst = kstep(st) + 8 * ag;
-            if (kfirst + 8 > a.K) {
+            if (kfirst + 8 > K) {
 #pragma unroll
                 for (int b = 0; b < MB; ++b) {
                     i32x4 v = rA[p][b];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        const int k0 = kfirst + 2 * e;
+                        const int kk = kfirst + 2 * e;
                         uint32_t w = (uint32_t)v[e];
-                        if (k0 >= a.K) w = 0;
-                        else if (k0 + 1 >= a.K) w &= 0xffffu;
+                        if (kk >= K) w = 0;
+                        else if (kk + 1 >= K) w &= 0xffffu;
                         v[e] = (int)w;
                     }
                     rA[p][b] = v;
@@ -214,7 +227,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_small_m_nn(Args a) {
         float s = 0.f;
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) s += red[(w * MB * 16 + row) * kCols + col];
-        if (row < a.M && n0 + col < a.N) epi::store(a.C, a.ldc, a.epi, row, n0 + col, s);
+        if (row < a.M && n0 + col < a.N) epi::store(C, a.ldc, a.epi, row, n0 + col, s);
     }
 }
 

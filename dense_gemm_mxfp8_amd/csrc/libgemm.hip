@@ -447,6 +447,39 @@ __global__ void zero_fill_kernel(void* C, int64_t ldc, int M, int N, epi::Params
     }
 }
 
+// Split-K reduction: C(i, j) = epilogue(W[0](i, j) + W[1](i, j) + ... +
+// W[splits-1](i, j)), the partial sums of the K ranges added in range order,
+// so the result does not depend on how the ranges were scheduled.  W holds
+// `splits` dense M x N fp32 planes.  With N % 4 == 0 (and W 16-byte
+// aligned) each thread adds 4 consecutive elements of one row with 16-byte
+// loads.  Bound by HBM: splits M N 4 bytes read, M N (4 or 2) written.
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ W, int splits, int M, int N,
+                                                            void* C, int64_t ldc, epi::Params e) {
+    const int64_t plane = (int64_t)M * N;
+    const int64_t step = (int64_t)gridDim.x * blockDim.x;
+    if ((N & 3) == 0) {
+        typedef float f32x4 __attribute__((ext_vector_type(4)));
+        for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < plane / 4; q += step) {
+            f32x4 acc = *(const f32x4*)(W + 4 * q);
+            for (int r = 1; r < splits; ++r) acc += *(const f32x4*)(W + r * plane + 4 * q);
+            const int row = (int)(4 * q / N);
+            const int col = (int)(4 * q - (int64_t)row * N);
+            const float v0 = acc[0], v1 = acc[1], v2 = acc[2], v3 = acc[3];
+            epi::store(C, ldc, e, row, col, v0);
+            epi::store(C, ldc, e, row, col + 1, v1);
+            epi::store(C, ldc, e, row, col + 2, v2);
+            epi::store(C, ldc, e, row, col + 3, v3);
+        }
+        return;
+    }
+    for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < plane; q += step) {
+        float acc = W[q];
+        for (int r = 1; r < splits; ++r) acc += W[r * plane + q];
+        const int row = (int)(q / N);
+        epi::store(C, ldc, e, row, (int)(q - (int64_t)row * N), acc);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Host side.
 // ---------------------------------------------------------------------------
@@ -553,6 +586,9 @@ bool use_big_tiles(int64_t M, int64_t N, int cus) {
 // must span less than 2 GiB.
 bool c_ok(int64_t ldc) { return ldc < ((int64_t)1 << 21); }
 
+// Most K ranges a split-K call uses.
+constexpr int kMaxSplits = 32;
+
 // ---------------------------------------------------------------------------
 // Fast path (gemm_fast.h): 256 x 256 tiles, direct-to-LDS buffer loads.
 // ---------------------------------------------------------------------------
@@ -590,12 +626,17 @@ FastVariant env_variant() {
     return v;
 }
 
-template <int KIND, int RB, int S, int SG = 1, int E = 0, int D = 0, int NW = 4, bool FUSED = false>
-int launch_fast(fast::Args a, int cus, hipStream_t stream, int group_m = 0) {
+// SPLIT: split-K units (a.kslice set, `splits` K ranges): the partial sums
+// go to `splits` stacked M x N planes of C.
+template <int KIND, int RB, int S, int SG = 1, int E = 0, int D = 0, int NW = 4, bool FUSED = false,
+          bool SPLIT = false>
+int launch_fast(fast::Args a, int cus, hipStream_t stream, int group_m = 0, int splits = 1) {
     constexpr int BK = RB / (KIND == fast::kMX ? 1 : 2);
     a.tiles_m = (a.M + fast::kTile - 1) / fast::kTile;
     a.tiles_n = (a.N + fast::kTile - 1) / fast::kTile;
     a.num_tiles = a.tiles_m * a.tiles_n;
+    a.tiles_per_split = a.num_tiles;
+    if (SPLIT) a.num_tiles *= splits;
     if (group_m <= 0) group_m = 8;
     a.group_m = a.tiles_m < group_m ? a.tiles_m : group_m;
     a.kt_full = a.K / BK;
@@ -604,10 +645,10 @@ int launch_fast(fast::Args a, int cus, hipStream_t stream, int group_m = 0) {
     if (grid >= 8) grid -= grid % 8;
     a.xcd_remap = (grid % 8 == 0) ? 1 : 0;
     if (a.kt_total > a.kt_full)
-        hipLaunchKernelGGL((fast::gemm_fast_kernel<KIND, RB, S, true, SG, E, D, NW, FUSED>), dim3(grid),
+        hipLaunchKernelGGL((fast::gemm_fast_kernel<KIND, RB, S, true, SG, E, D, NW, FUSED, SPLIT>), dim3(grid),
                            dim3(64 * NW), 0, stream, a);
     else
-        hipLaunchKernelGGL((fast::gemm_fast_kernel<KIND, RB, S, false, SG, E, D, NW, FUSED>), dim3(grid),
+        hipLaunchKernelGGL((fast::gemm_fast_kernel<KIND, RB, S, false, SG, E, D, NW, FUSED, SPLIT>), dim3(grid),
                            dim3(64 * NW), 0, stream, a);
     return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
 }
@@ -791,9 +832,12 @@ bool small_ok(bool nt, int64_t M, int64_t N, int64_t K, const void* A, int64_t l
     return N >= 2048;
 }
 
+// splits > 1: K ranges of kslice rows (a multiple of small::kStepK), fp32
+// partial sums to `splits` stacked M x N planes at C (ldc == N, plain e).
 template <int MB, int NP, int COLS, int WAVES>
 int launch_small(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
-                 void* C, int64_t ldc, const epi::Params& e, hipStream_t stream) {
+                 void* C, int64_t ldc, const epi::Params& e, hipStream_t stream, int splits = 1,
+                 int64_t kslice = 0) {
     small::Args a;
     a.A = (const uint8_t*)A;
     a.B = (const uint8_t*)B;
@@ -805,7 +849,10 @@ int launch_small(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, co
     a.M = (int)M;
     a.N = (int)N;
     a.K = (int)K;
-    const int64_t per = (K + WAVES - 1) / WAVES;
+    if (splits <= 1) kslice = K;
+    a.kslice = (int)kslice;
+    a.c_split = splits > 1 ? M * N : 0;
+    const int64_t per = (kslice + WAVES - 1) / WAVES;
     a.kw = (int)((per + small::kStepK - 1) / small::kStepK * small::kStepK);
     const int grid = (int)((N + COLS - 1) / COLS);
     static const int pair_env = [] {
@@ -814,12 +861,14 @@ int launch_small(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, co
     }();
     a.pair_xcd = (COLS == 32 && grid % 16 == 0) ? 1 : 0;
     if (pair_env == 0) a.pair_xcd = 0;  // measurement switch
-    hipLaunchKernelGGL((small::gemm_small_m_nn<MB, NP, COLS, WAVES>), dim3(grid), dim3(64 * WAVES), 0, stream, a);
+    hipLaunchKernelGGL((small::gemm_small_m_nn<MB, NP, COLS, WAVES>), dim3(grid, splits > 1 ? splits : 1),
+                       dim3(64 * WAVES), 0, stream, a);
     return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
 }
 
 int launch_small_bf16(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
-                      void* C, int64_t ldc, const epi::Params& e, hipStream_t s) {
+                      void* C, int64_t ldc, const epi::Params& e, hipStream_t s, int splits = 1,
+                      int64_t kslice = 0) {
     // LIBGEMM_SMALL=<np>x<cols>x<waves> selects a compiled variant for measurements
     static int sv = [] {
         const char* e = getenv("LIBGEMM_SMALL");
@@ -828,14 +877,18 @@ int launch_small_bf16(int64_t M, int64_t N, int64_t K, const void* A, int64_t ld
         return 0;
     }();
     if (M <= 16) {
-        if (sv == 120000 + 3208) return launch_small<1, 12, 32, 8>(M, N, K, A, lda, B, ldb, C, ldc, e, s);
-        if (sv == 80000 + 3216) return launch_small<1, 8, 32, 16>(M, N, K, A, lda, B, ldb, C, ldc, e, s);
-        if (sv == 80000 + 6416) return launch_small<1, 8, 64, 16>(M, N, K, A, lda, B, ldb, C, ldc, e, s);
-        if (sv == 80000 + 3208) return launch_small<1, 8, 32, 8>(M, N, K, A, lda, B, ldb, C, ldc, e, s);
-        return launch_small<1, 4, 32, 16>(M, N, K, A, lda, B, ldb, C, ldc, e, s);
+        if (sv == 120000 + 3208)
+            return launch_small<1, 12, 32, 8>(M, N, K, A, lda, B, ldb, C, ldc, e, s, splits, kslice);
+        if (sv == 80000 + 3216)
+            return launch_small<1, 8, 32, 16>(M, N, K, A, lda, B, ldb, C, ldc, e, s, splits, kslice);
+        if (sv == 80000 + 6416)
+            return launch_small<1, 8, 64, 16>(M, N, K, A, lda, B, ldb, C, ldc, e, s, splits, kslice);
+        if (sv == 80000 + 3208)
+            return launch_small<1, 8, 32, 8>(M, N, K, A, lda, B, ldb, C, ldc, e, s, splits, kslice);
+        return launch_small<1, 4, 32, 16>(M, N, K, A, lda, B, ldb, C, ldc, e, s, splits, kslice);
     }
-    if (M <= 32) return launch_small<2, 8, 32, 8>(M, N, K, A, lda, B, ldb, C, ldc, e, s);
-    return launch_small<4, 4, 32, 8>(M, N, K, A, lda, B, ldb, C, ldc, e, s);
+    if (M <= 32) return launch_small<2, 8, 32, 8>(M, N, K, A, lda, B, ldb, C, ldc, e, s, splits, kslice);
+    return launch_small<4, 4, 32, 8>(M, N, K, A, lda, B, ldb, C, ldc, e, s, splits, kslice);
 }
 
 int bf16_dispatch(bool nt, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
@@ -875,6 +928,101 @@ int bf16_dispatch(bool nt, int64_t M, int64_t N, int64_t K, const void* A, int64
                   : launch<128, 128, kBf16NN, false>(a, dev.cus, s);
 }
 
+const epi::Params kPlain = {nullptr, nullptr, nullptr, 0, 0};
+
+// ---------------------------------------------------------------------------
+// Split-K: the K extent cut into ranges computed by separate work units,
+// whose fp32 partial sums a second pass adds in range order.
+// ---------------------------------------------------------------------------
+
+enum SplitKernel { kSplitNone = 0, kSplitFast = 1, kSplitSmall = 2 };
+
+struct SplitPlan {
+    int kernel;      // SplitKernel
+    int splits;      // K ranges (1: no split)
+    int64_t kslice;  // K elements per range, the last range takes the rest
+};
+
+// Which kernel would compute the partial sums of this problem.  `aligned`:
+// the operand pointers are 16-byte aligned (the query entry point assumes
+// they are).
+int split_kernel(bool nt, int64_t M, int64_t N, int64_t K, bool aligned, int64_t lda, int64_t ldb) {
+    const int64_t lim = (int64_t)1 << 31;
+    if (!aligned || (lda % 8) || (ldb % 8)) return kSplitNone;
+    // the stacked partial planes are addressed with 32-bit offsets per 256 rows
+    if (!c_ok(N)) return kSplitNone;
+    if (!nt && M <= 64 && N >= 2048 && K * ldb * 2 < lim && M * lda * 2 < lim) return kSplitSmall;
+    if (256 * lda * 2 >= lim) return kSplitNone;
+    if (nt ? 256 * ldb * 2 >= lim : (N % 8 || K * ldb * 2 >= lim)) return kSplitNone;
+    return kSplitFast;
+}
+
+// The split plan.  requested > 0 asks for that many ranges (fewer when K is
+// too short); 0 lets the shape decide:
+//   - 256 x 256 tiles (fast kernel): when the tiles give the CUs less than
+//     3/4 of a round, cut K so that tiles x ranges fills about one round,
+//     each range at least 8 k-tiles (512) long;
+//   - small M (small kernel): when its 32-column blocks give fewer
+//     workgroups than CUs, the same with ranges of at least 1024.
+SplitPlan plan_split(bool nt, int64_t M, int64_t N, int64_t K, bool aligned, int64_t lda, int64_t ldb, int cus,
+                     int requested) {
+    SplitPlan p{split_kernel(nt, M, N, K, aligned, lda, ldb), 1, K};
+    if (p.kernel == kSplitNone || K <= 0) return p;
+    const int64_t gran = p.kernel == kSplitFast ? 64 : small::kStepK;  // k-tile of the partial kernel
+    int64_t want = requested;
+    if (want <= 0) {
+        const int64_t units = p.kernel == kSplitFast ? ((M + 255) / 256) * ((N + 255) / 256) : (N + 31) / 32;
+        const int64_t min_range = p.kernel == kSplitFast ? 512 : 1024;
+        if (units * 4 >= (int64_t)cus * 3) return p;
+        want = cus / units;
+        if (want > K / min_range) want = K / min_range;
+        if (want > kMaxSplits) want = kMaxSplits;
+    }
+    if (want > kMaxSplits) want = kMaxSplits;
+    if (want <= 1) return p;
+    int64_t kslice = (K + want - 1) / want;
+    kslice = (kslice + gran - 1) / gran * gran;
+    const int64_t splits = (K + kslice - 1) / kslice;
+    if (splits <= 1) return p;
+    p.splits = (int)splits;
+    p.kslice = kslice;
+    return p;
+}
+
+int splitk_dispatch(bool nt, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+                    int64_t ldb, void* C, int64_t ldc, const epi::Params& e, int splits, void* ws,
+                    size_t ws_bytes, void* stream) {
+    if (splits < 0) return GEMM_ERR_INVALID_ARG;
+    int rc = check_common(M, N, K, A, lda, B, ldb, nt ? K : N, C, ldc);
+    if (rc == 1) return GEMM_OK;
+    if (rc != GEMM_OK) return rc;
+    DeviceInfo dev;
+    rc = device_info(&dev);
+    if (rc != GEMM_OK) return rc;
+    const SplitPlan p = plan_split(nt, M, N, K, aligned16(A) && aligned16(B), lda, ldb, dev.cus, splits);
+    if (p.splits <= 1) return bf16_dispatch(nt, M, N, K, A, lda, B, ldb, C, ldc, e, stream);
+    const int64_t need = (int64_t)p.splits * M * N * 4;
+    if (ws == nullptr || (int64_t)ws_bytes < need || ((uintptr_t)ws & 15)) return GEMM_ERR_INVALID_ARG;
+    hipStream_t s = (hipStream_t)stream;
+    if (p.kernel == kSplitSmall) {
+        rc = launch_small_bf16(M, N, K, A, lda, B, ldb, ws, N, kPlain, s, p.splits, p.kslice);
+    } else {
+        fast::Args a = make_fast_args(M, N, K, A, lda, B, ldb, ws, N, 2, kPlain);
+        a.kslice = (int)p.kslice;
+        a.c_nt = 0;  // the partial sums are read back at once: keep them cached
+        const int g = env_variant().group;
+        rc = nt ? launch_fast<fast::kNT, 128, 2, 1, 6, 2, 4, false, true>(a, dev.cus, s, g, p.splits)
+                : launch_fast<fast::kNN, 128, 2, 1, 6, 2, 4, false, true>(a, dev.cus, s, g, p.splits);
+    }
+    if (rc != GEMM_OK) return rc;
+    int64_t blocks = (M * N / 4 + 255) / 256;
+    if (blocks > (int64_t)dev.cus * 8) blocks = (int64_t)dev.cus * 8;
+    if (blocks < 1) blocks = 1;
+    hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, s, (const float*)ws, p.splits,
+                       (int)M, (int)N, C, ldc, e);
+    return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
+}
+
 // Epilogue parameters of a fused call; GEMM_ERR_INVALID_ARG for an unknown
 // output type or a C pointer not aligned to its element.
 int fused_params(int out_type, const void* C, const float* rs, const float* cs, const float* bias,
@@ -889,7 +1037,6 @@ int fused_params(int out_type, const void* C, const float* rs, const float* cs, 
     return GEMM_OK;
 }
 
-const epi::Params kPlain = {nullptr, nullptr, nullptr, 0, 0};
 
 int mx_dispatch(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
                 int64_t ldb, const uint8_t* scaleA, const uint8_t* scaleB, void* C, int64_t ldc,
@@ -978,6 +1125,36 @@ int gemm_mxfp8_fused(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda
     const int rc = fused_params(out_type, C, row_scale, col_scale, bias, &e);
     if (rc != GEMM_OK) return rc;
     return mx_dispatch(M, N, K, A, lda, B, ldb, scaleA, scaleB, C, ldc, e, stream);
+}
+
+int gemm_bf16_splitk(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
+                     int b_colmajor, void* C, int64_t ldc, int out_type, const float* row_scale,
+                     const float* col_scale, const float* bias, int splits, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+    epi::Params e;
+    const int rc = fused_params(out_type, C, row_scale, col_scale, bias, &e);
+    if (rc != GEMM_OK) return rc;
+    return splitk_dispatch(b_colmajor != 0, M, N, K, A, lda, B, ldb, C, ldc, e, splits, workspace,
+                           workspace_bytes, stream);
+}
+
+int gemm_bf16_splitk_plan(int64_t M, int64_t N, int64_t K, int b_colmajor, int splits, int cus,
+                          int* splits_used, size_t* workspace_bytes) {
+    if (M < 0 || N < 0 || K < 0 || splits < 0 || cus < 0 || M > INT32_MAX || N > INT32_MAX || K > INT32_MAX)
+        return GEMM_ERR_INVALID_ARG;
+    if (cus == 0) {
+        DeviceInfo dev;
+        const int rc = device_info(&dev);
+        if (rc != GEMM_OK) return rc;
+        cus = dev.cus;
+    }
+    const bool nt = b_colmajor != 0;
+    // operands assumed 16-byte aligned with dense leading dimensions
+    SplitPlan p{kSplitNone, 1, K};
+    if (M > 0 && N > 0) p = plan_split(nt, M, N, K, true, K, nt ? K : N, cus, splits);
+    if (splits_used) *splits_used = p.splits;
+    if (workspace_bytes) *workspace_bytes = p.splits > 1 ? (size_t)p.splits * (size_t)M * (size_t)N * 4 : 0;
+    return GEMM_OK;
 }
 
 const char* gemm_strerror(int code) {

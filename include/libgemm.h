@@ -49,6 +49,7 @@
 #ifndef LIBGEMM_H
 #define LIBGEMM_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -133,6 +134,57 @@ int gemm_mxfp8_fused(int64_t M, int64_t N, int64_t K,
                      void* C, int64_t ldc, int out_type,
                      const float* row_scale, const float* col_scale, const float* bias,
                      void* stream);
+
+/* ---- split-K --------------------------------------------------------------
+ *
+ * "GPU 执行模型", section "编译与 autotune", lists split-K among the
+ * strategies a GEMM chooses per shape, with a bounded choice for shapes not
+ * seen before.  Here the K extent is cut into `splits` ranges of kslice
+ * elements (a multiple of the partial kernel's k-tile; the last range takes
+ * the rest).  Each range's fp32 partial product is written to its own dense
+ * M x N plane of the caller's workspace, and a second kernel adds the planes
+ * in range order (0, 1, 2, ...) and applies the epilogue:
+ *
+ *     acc(i, j) = P_0(i, j) + P_1(i, j) + ... + P_{s-1}(i, j)
+ *
+ * so results are deterministic for a given plan.  This fills the GPU when the
+ * output has too few tiles for its compute units (a short, wide product or a
+ * small M x N with a long K).
+ *
+ * gemm_bf16_splitk: arguments as gemm_bf16_fused, plus
+ *   splits          K ranges wanted; 0 lets the library decide from the shape
+ *                   (its plan is gemm_bf16_splitk_plan's).  Fewer ranges are
+ *                   used when K is too short; with 1 range, or when no
+ *                   split-capable kernel applies (operands not 16-byte
+ *                   aligned, leading dimensions not multiples of 8 elements),
+ *                   the product runs unsplit as gemm_bf16_fused and the
+ *                   workspace is not touched.
+ *   workspace       device memory owned by the caller, 16-byte aligned, at
+ *                   least splits_used * M * N * 4 bytes (gemm_bf16_splitk_plan
+ *                   reports the figure); its contents on entry do not matter
+ *                   and are overwritten.  Calls that share a workspace must
+ *                   be ordered on one stream.
+ *   workspace_bytes its size.
+ * Errors: GEMM_ERR_INVALID_ARG as gemm_bf16_fused, or splits < 0, or a split
+ * plan whose workspace is NULL, too small or not 16-byte aligned.  The
+ * accuracy bound is that of the other entry points (every K range is summed
+ * in fp32 and the ranges are added in fp32). */
+int gemm_bf16_splitk(int64_t M, int64_t N, int64_t K,
+                     const void* A, int64_t lda,
+                     const void* B, int64_t ldb, int b_colmajor,
+                     void* C, int64_t ldc, int out_type,
+                     const float* row_scale, const float* col_scale, const float* bias,
+                     int splits, void* workspace, size_t workspace_bytes,
+                     void* stream);
+
+/* The split plan of gemm_bf16_splitk for 16-byte aligned operands with dense
+ * leading dimensions (lda = K; ldb = N, or K when b_colmajor): the number of
+ * K ranges it uses (*splits_used, 1 = unsplit) and the workspace bytes they
+ * need (*workspace_bytes, 0 when unsplit).  splits as in gemm_bf16_splitk;
+ * cus: compute units to plan for, 0 = those of the current device.  Either
+ * output pointer may be NULL.  Runs on the host only (no device work). */
+int gemm_bf16_splitk_plan(int64_t M, int64_t N, int64_t K, int b_colmajor, int splits, int cus,
+                          int* splits_used, size_t* workspace_bytes);
 
 /* Static text for a return code (never NULL). */
 const char* gemm_strerror(int code);

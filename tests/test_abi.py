@@ -86,3 +86,44 @@ def test_fused_entry_points_reject_bad_epilogue_arguments():
                                None) == dg.GEMM_ERR_INVALID_ARG
     # empty extents are still a no-op
     assert dg.gemm_bf16_fused(0, 4, 4, 0, 4, 0, 4, 0, 0, 4, dg.GEMM_OUT_BF16, None, None, None, None) == dg.GEMM_OK
+
+
+def test_splitk_rejects_negative_splits():
+    # checked before any device call
+    args = (4, 4, 64, 16, 64, 16, 64, 1, 16, 4, dg.GEMM_OUT_F32, None, None, None)
+    assert dg.gemm_bf16_splitk(*args, -1, None, 0, None) == dg.GEMM_ERR_INVALID_ARG
+    assert dg.gemm_bf16_splitk_plan(4, 4, 64, 1, -1, 256)[0] == dg.GEMM_ERR_INVALID_ARG
+    assert dg.gemm_bf16_splitk_plan(-4, 4, 64, 1, 0, 256)[0] == dg.GEMM_ERR_INVALID_ARG
+    assert dg.gemm_bf16_splitk_plan(4, 4, 64, 1, 0, -1)[0] == dg.GEMM_ERR_INVALID_ARG
+
+
+# (M, N, K, b_colmajor, splits asked, compute units) -> K ranges planned.
+# Planned ranges (splits 0): 256 x 256 tiles that give the CUs under 3/4 of
+# a round get K cut into about CUs / tiles ranges of at least 512; small-M
+# products (row-major B, M <= 64, N >= 2048) the same per 32-column block with
+# ranges of at least 1024.  Asked counts are honoured up to 32, with the range
+# length rounded up to the partial kernel's k-tile (64, or 32 for small M).
+SPLIT_PLANS = [
+    ((8192, 8192, 8192, 1, 0, 256), 1),     # 1024 tiles: the GPU is full
+    ((4096, 4096, 4096, 0, 0, 256), 1),     # 256 tiles
+    ((2048, 2048, 16384, 1, 0, 256), 4),    # 64 tiles x 4 ranges of 4096
+    ((2048, 2048, 1024, 1, 0, 256), 2),     # ranges of at least 512
+    ((2048, 2048, 16384, 1, 0, 128), 2),    # fewer CUs, fewer ranges
+    ((16, 2048, 8192, 0, 0, 256), 4),       # small M: 64 column blocks
+    ((16, 8192, 8192, 0, 0, 256), 1),       # small M: 256 column blocks
+    ((16, 8192, 8192, 1, 0, 256), 8),       # column-major B: 32 tiles
+    ((1000, 777, 4104, 1, 5, 256), 5),
+    ((1000, 1000, 1000, 1, 5, 256), 4),     # 200 -> 256 per range: 4 ranges
+    ((1000, 1000, 1000, 1, 100, 256), 16),  # capped at 32, then 64-element ranges
+    ((1000, 1000, 1002, 1, 4, 256), 1),     # lda = 1002: rows not 16-byte aligned
+    ((0, 1000, 1000, 1, 4, 256), 1),
+]
+
+
+@pytest.mark.parametrize("case,want", SPLIT_PLANS, ids=lambda c: "x".join(map(str, c)) if isinstance(c, tuple) else str(c))
+def test_splitk_plan(case, want):
+    M, N, K, colmajor, splits, cus = case
+    rc, used, nbytes = dg.gemm_bf16_splitk_plan(M, N, K, colmajor, splits, cus)
+    assert rc == dg.GEMM_OK
+    assert used == want
+    assert nbytes == (used * M * N * 4 if used > 1 else 0)

@@ -1,0 +1,192 @@
+"""GPU parity of split-K (gemm_bf16_splitk) through the C ABI.
+
+The K extent is cut into ranges whose fp32 partial products land in the
+caller's workspace and are added in range order by a second kernel.  Cases
+reach both partial kernels: the 256 x 256 direct-load kernel (NT and NN, with
+partial tiles, a partial last k-tile inside the last range, explicit and
+planned range counts) and the small-M kernel (planned and explicit counts, a
+K that ends inside a 32-row step), plus the fused epilogue after the
+reduction, an unsplit fallback that must leave the workspace alone, a
+workspace that is too small, and determinism.
+
+Reference: the oracle's exact product (binary64).  Tolerance: the acceptance
+bound |C - exact| <= 1e-3 sum_k |a||b|; every range is summed in fp32 and the
+ranges are added in fp32, so the total rounding stays within
+gamma_(K + splits) sum|a||b|, below the bound for these K.  Integer operands
+keep every partial sum below 2^24 and must match bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+import dense_gemm_mxfp8_amd as dg
+import oracle
+from dense_gemm_mxfp8_amd import inputs
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _plan(M, N, K, colmajor, splits):
+    rc, used, nbytes = dg.gemm_bf16_splitk_plan(M, N, K, colmajor, splits)
+    assert rc == dg.GEMM_OK, dg.gemm_strerror(rc)
+    return used, nbytes
+
+
+def _run(prob, splits, *, ldc_pad=3, out_bf16=False, vecs=(None, None, None), ws=None, ws_fill=float("nan")):
+    """gemm_bf16_splitk on the problem's operands; returns (C as float64,
+    splits the plan uses, workspace tensor)."""
+    M, N, K = prob.M, prob.N, prob.K
+    A, B = prob.A.to(DEV), prob.B.to(DEV)
+    ldb = K if prob.b_colmajor else N
+    used, nbytes = _plan(M, N, K, prob.b_colmajor, splits)
+    if ws is None:
+        # contents on entry must not matter: start from NaN
+        ws = torch.full((max(nbytes, 16) // 4,), ws_fill, dtype=torch.float32, device=DEV)
+    odt = torch.bfloat16 if out_bf16 else torch.float32
+    ldc = N + ldc_pad
+    Cst = torch.full((M, ldc), -7.0, dtype=odt, device=DEV)
+    rs, cs, bias = (None if v is None else torch.from_numpy(v).to(DEV) for v in vecs)
+    ptr = lambda t: 0 if t is None else t.data_ptr()
+    out_type = dg.GEMM_OUT_BF16 if out_bf16 else dg.GEMM_OUT_F32
+    rc = dg.gemm_bf16_splitk(M, N, K, A.data_ptr(), K, B.data_ptr(), ldb, prob.b_colmajor, Cst.data_ptr(), ldc,
+                             out_type, ptr(rs), ptr(cs), ptr(bias), splits, ws.data_ptr(), ws.numel() * 4,
+                             P.stream())
+    assert rc == dg.GEMM_OK, dg.gemm_strerror(rc)
+    torch.cuda.synchronize()
+    C = Cst.float().cpu().numpy()
+    assert (C[:, N:] == -7.0).all(), "C written outside M x N"
+    return np.ascontiguousarray(C[:, :N]).astype(np.float64), used, ws
+
+
+def _check(prob, got, exact, sample=None):
+    Ab, Bb = P.bits16(prob.A), P.bits16(prob.B)
+    if sample is None:
+        want, mag = P.oracle_bf16(Ab, Bb, prob.b_colmajor)
+        g = got
+    else:
+        rows, cols = sample
+        want, mag = P.oracle_bf16_at(Ab, Bb, prob.b_colmajor, rows, cols)
+        g = got[rows, cols]
+    if exact:
+        P.assert_exact(g, want, prob.name)
+    else:
+        P.assert_within_bound(g, want, mag, prob.name)
+
+
+def _prob(M, N, K, colmajor, exact, seed):
+    return inputs.bf16_problem(M, N, K, dist="integer" if exact else "normal", b_colmajor=colmajor, seed=seed)
+
+
+# (M, N, K, b_colmajor, splits): 256 x 256 partial kernel.  K = 4104 and 3000 end
+# inside a k-tile (the last range carries the partial k-tile); 0 = the plan.
+FAST = [(1000, 777, 4104, True, 0), (1000, 777, 4104, True, 3), (513, 1032, 3000, False, 0),
+        (513, 1032, 3000, False, 5), (300, 520, 1024, True, 2), (256, 256, 640, False, 7)]
+
+
+@pytest.mark.parametrize("case", FAST, ids=lambda c: f"{c[0]}x{c[1]}x{c[2]}_{'nt' if c[3] else 'nn'}_s{c[4]}")
+@pytest.mark.parametrize("exact", [True, False], ids=["integer", "normal"])
+def test_splitk_fast_kernel(case, exact):
+    M, N, K, colmajor, splits = case
+    prob = _prob(M, N, K, colmajor, exact, seed=81)
+    P.note(f"splitk fast {prob.name} splits={splits}")
+    got, used, _ = _run(prob, splits)
+    assert used > 1, "the plan should split this shape"
+    _check(prob, got, exact)
+
+
+# small-M partial kernel (row-major B, M <= 64, N >= 2048): 64 column
+# blocks (the plan splits), K ending inside a 32-row step, 48 rows
+SMALL = [(16, 2048, 8192, 0), (16, 2048, 1000, 3), (48, 4096, 2056, 4), (1, 2048, 4096, 0), (16, 8192, 8192, 2)]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: f"{c[0]}x{c[1]}x{c[2]}_s{c[3]}")
+@pytest.mark.parametrize("exact", [True, False], ids=["integer", "normal"])
+def test_splitk_small_m(case, exact):
+    M, N, K, splits = case
+    prob = _prob(M, N, K, False, exact, seed=82)
+    P.note(f"splitk small {prob.name} splits={splits}")
+    got, used, _ = _run(prob, splits)
+    assert used > 1
+    sample = P.sample_positions(M, N, 2048, seed=83) if K >= 8192 else None
+    _check(prob, got, exact, sample)
+
+
+def test_splitk_long_k_sampled():
+    """2048 x 2048 x 16384 NT: 64 tiles, the plan fills the GPU with K ranges."""
+    prob = _prob(2048, 2048, 16384, True, False, seed=84)
+    P.note(f"splitk sampled {prob.name}")
+    got, used, _ = _run(prob, 0, ldc_pad=0)
+    assert used >= 2
+    _check(prob, got, False, P.sample_positions(2048, 2048, 1024, seed=85))
+
+
+@pytest.mark.parametrize("out_bf16", [False, True], ids=["f32", "bf16"])
+def test_splitk_fused_epilogue(out_bf16):
+    M, N, K = 700, 600, 2048
+    prob = _prob(M, N, K, True, True, seed=86)
+    g = np.random.default_rng(87)
+    rs = np.exp2(g.integers(-2, 3, size=M)).astype(np.float32)
+    cs = np.exp2(g.integers(-2, 3, size=N)).astype(np.float32)
+    bias = g.integers(-8, 9, size=N).astype(np.float32)
+    P.note(f"splitk fused {prob.name} out {'bf16' if out_bf16 else 'f32'}")
+    got, used, _ = _run(prob, 4, out_bf16=out_bf16, vecs=(rs, cs, bias))
+    assert used == 4
+    acc, mag = P.oracle_bf16(P.bits16(prob.A), P.bits16(prob.B), True)
+    t, _ = oracle.epilogue(acc, mag, rs, cs, bias)
+    P.assert_exact(got, oracle.round_bf16(t) if out_bf16 else t, prob.name)
+
+
+def test_splitk_unsplit_fallback_leaves_workspace():
+    """Operands that are not 16-byte aligned run unsplit; the workspace is not touched."""
+    M, N, K = 200, 300, 1000
+    prob = _prob(M, N, K, True, True, seed=88)
+    Ast = torch.zeros(M * K + 8, dtype=torch.bfloat16, device=DEV)
+    Ast[1:1 + M * K] = prob.A.reshape(-1).to(DEV)
+    B = prob.B.to(DEV)
+    C = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    ws = torch.full((4 * M * N,), 12345.0, dtype=torch.float32, device=DEV)
+    P.note("splitk fallback (A offset by one element)")
+    rc = dg.gemm_bf16_splitk(M, N, K, Ast.data_ptr() + 2, K, B.data_ptr(), K, 1, C.data_ptr(), N, dg.GEMM_OUT_F32,
+                             0, 0, 0, 4, ws.data_ptr(), ws.numel() * 4, P.stream())
+    assert rc == dg.GEMM_OK, dg.gemm_strerror(rc)
+    torch.cuda.synchronize()
+    assert (ws == 12345.0).all().item(), "an unsplit call wrote the workspace"
+    want, _ = P.oracle_bf16(P.bits16(prob.A), P.bits16(prob.B), True)
+    P.assert_exact(C.cpu().numpy().astype(np.float64), want, "fallback")
+
+
+def test_splitk_rejects_short_workspace():
+    M, N, K = 512, 512, 4096
+    prob = _prob(M, N, K, True, True, seed=89)
+    A, B = prob.A.to(DEV), prob.B.to(DEV)
+    used, nbytes = _plan(M, N, K, True, 4)
+    assert used == 4 and nbytes == 4 * M * N * 4
+    C = torch.full((M, N), -7.0, dtype=torch.float32, device=DEV)
+    ws = torch.empty(nbytes // 4, dtype=torch.float32, device=DEV)
+    P.note("splitk short workspace")
+    args = (M, N, K, A.data_ptr(), K, B.data_ptr(), K, 1, C.data_ptr(), N, dg.GEMM_OUT_F32, 0, 0, 0, 4)
+    assert dg.gemm_bf16_splitk(*args, ws.data_ptr(), nbytes - 4, P.stream()) == dg.GEMM_ERR_INVALID_ARG
+    assert dg.gemm_bf16_splitk(*args, 0, nbytes, P.stream()) == dg.GEMM_ERR_INVALID_ARG
+    assert dg.gemm_bf16_splitk(*args, ws.data_ptr() + 4, nbytes - 4, P.stream()) == dg.GEMM_ERR_INVALID_ARG
+    torch.cuda.synchronize()
+    assert (C == -7.0).all().item(), "C changed by a rejected call"
+
+
+def test_splitk_deterministic():
+    prob = _prob(1000, 777, 4104, True, False, seed=90)
+    P.note(f"splitk determinism {prob.name}")
+    a, _, _ = _run(prob, 6)
+    b, _, _ = _run(prob, 6, ws_fill=0.0)
+    assert np.array_equal(a, b)
+
+
+def test_splitk_tensor_helper():
+    prob = _prob(16, 2048, 4096, False, True, seed=91)
+    A, B = prob.A.to(DEV), prob.B.to(DEV)
+    P.note("splitk tensor helper")
+    C = dg.bf16_splitk(A, B)
+    torch.cuda.synchronize()
+    want, _ = P.oracle_bf16(P.bits16(prob.A), P.bits16(prob.B), False)
+    P.assert_exact(C.cpu().numpy().astype(np.float64), want, "bf16_splitk")
