@@ -168,6 +168,7 @@ def bench_workload(name: str, steps: int, warmup: int, settle: float = 0.0):
     # from HBM.
     bytes_per_step = operand_bytes(w)
     copies = 4 if bytes_per_step < 512 * 2**20 and 2 * M * N * K / bytes_per_step < 300 else 1
+    splits = 1
     if w["kind"] == "mx":
         ops = [(prob.A.to(dev), prob.B.to(dev), prob.SA.to(dev), prob.SB.to(dev))
                for _ in range(copies)]
@@ -183,12 +184,28 @@ def bench_workload(name: str, steps: int, warmup: int, settle: float = 0.0):
         ops = [(prob.A.to(dev), prob.B.to(dev)) for _ in range(copies)]
         fn = dg.gemm_bf16_nt if prob.b_colmajor else dg.gemm_bf16
         ldb = K if prob.b_colmajor else N
-
-        def step(i):
-            A, B = ops[i % copies]
-            rc = fn(M, N, K, A.data_ptr(), K, B.data_ptr(), ldb, C.data_ptr(), N, s)
+        if w.get("splitk"):
+            # split-K: the library's plan, with its workspace allocated once
+            rc, splits, nbytes = dg.gemm_bf16_splitk_plan(M, N, K, prob.b_colmajor, 0)
             if rc:
                 raise RuntimeError(dg.gemm_strerror(rc))
+            ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+
+            def step(i):
+                A, B = ops[i % copies]
+                rc = dg.gemm_bf16_splitk(M, N, K, A.data_ptr(), K, B.data_ptr(), ldb, prob.b_colmajor,
+                                         C.data_ptr(), N, dg.GEMM_OUT_F32, None, None, None, 0, ws.data_ptr(),
+                                         ws.numel(), s)
+                if rc:
+                    raise RuntimeError(dg.gemm_strerror(rc))
+        else:
+            splits = 1
+
+            def step(i):
+                A, B = ops[i % copies]
+                rc = fn(M, N, K, A.data_ptr(), K, B.data_ptr(), ldb, C.data_ptr(), N, s)
+                if rc:
+                    raise RuntimeError(dg.gemm_strerror(rc))
         dtype, peak_key = "bf16", "bf16"
 
     # The clocks ramp up from idle over the first tens of milliseconds of
@@ -239,7 +256,7 @@ def bench_workload(name: str, steps: int, warmup: int, settle: float = 0.0):
         "kernel_ms_p90": float(np.percentile(per, 90)),
         "tflops": flops / (ms_step * 1e-3) / 1e12,
         "layout": ("NT" if getattr(prob, "b_colmajor", True) else "NN"),
-        "dist": w.get("dist"), "operand_copies": copies,
+        "dist": w.get("dist"), "operand_copies": copies, "splitk": splits,
         "settle_s": round(settle, 3), "settle_steps": settle_steps, "clocks": clocks.summary(),
     }
     return res, prob
@@ -304,7 +321,8 @@ def line(res, steps, warmup, cpu=None, headline=True):
         "dtype": res["dtype"], "data": "synthetic",
         "config": {"workload": res["workload"], "M": res["M"], "N": res["N"], "K": res["K"],
                    "layout": res["layout"], "dist": res["dist"], "seed": 0,
-                   "output": "fp32", "parallelism": "single-gpu"},
+                   "output": "fp32", "parallelism": "single-gpu",
+                   **({"splitk_ranges": res["splitk"]} if res.get("splitk", 1) > 1 else {})},
         "kernel_ms": {"mean": round(res["kernel_ms_mean"], 5),
                       "median": round(res["kernel_ms_median"], 5),
                       "p10": round(res["kernel_ms_p10"], 5), "p90": round(res["kernel_ms_p90"], 5),

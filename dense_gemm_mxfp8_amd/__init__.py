@@ -23,6 +23,7 @@ GEMM_ERR_UNSUPPORTED = -2
 GEMM_ERR_LAUNCH = -3
 GEMM_OUT_F32 = 0
 GEMM_OUT_BF16 = 1
+GEMM_DYNAMIC_WORKSPACE_BYTES = 1024
 
 _lib = None
 _i64 = ctypes.c_int64
@@ -56,6 +57,9 @@ def library() -> ctypes.CDLL:
         lib.gemm_bf16_splitk_plan.restype = ctypes.c_int
         lib.gemm_bf16_splitk_plan.argtypes = [_i64, _i64, _i64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                               ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_size_t)]
+        lib.gemm_bf16_dynamic.restype = ctypes.c_int
+        lib.gemm_bf16_dynamic.argtypes = [_i64, _i64, _i64, _vp, _i64, _vp, _i64, ctypes.c_int, _vp, _i64, _vp,
+                                          ctypes.c_size_t, _vp]
         lib.gemm_strerror.restype = ctypes.c_char_p
         lib.gemm_strerror.argtypes = [ctypes.c_int]
         lib.gemm_version.restype = ctypes.c_int
@@ -103,6 +107,11 @@ def gemm_bf16_splitk_plan(M, N, K, b_colmajor, splits=0, cus=0):
     rc = library().gemm_bf16_splitk_plan(M, N, K, int(b_colmajor), splits, cus, ctypes.byref(used),
                                          ctypes.byref(ws))
     return rc, used.value, ws.value
+
+
+def gemm_bf16_dynamic(M, N, K, A, lda, B, ldb, b_colmajor, C, ldc, workspace, workspace_bytes, stream) -> int:
+    return library().gemm_bf16_dynamic(M, N, K, A, lda, B, ldb, int(b_colmajor), C, ldc, workspace,
+                                       workspace_bytes, stream)
 
 
 def gemm_strerror(code: int) -> str:

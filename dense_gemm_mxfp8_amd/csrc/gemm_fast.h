@@ -75,6 +75,9 @@ struct Args {
     // u / tiles_per_split ([ks kslice, min(K, (ks + 1) kslice)), kslice a
     // multiple of the k-tile); its fp32 partial sums go to rows ks M .. of C
     int tiles_per_split, kslice;
+    // dynamic-schedule instances: 8 tile counters, one per XCD, 32 ints
+    // apart (zero when the launch starts)
+    int* tile_ctr;
 };
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -144,6 +147,32 @@ __device__ __forceinline__ void tile_coords(const Args& a, int t, int& tm, int& 
     int r = t - g * per_group;
     tm = first + r % gsz;
     tn = r / gsz;
+}
+
+// Dynamic schedule (the atomic tile counter): tile number of position idx in
+// XCD x's queue.  The static walk gives the workgroups on XCD x (grid G,
+// P = G / 8 per XCD) the tiles r G + x P + j of every round r; the dynamic
+// walk keeps that split into 8 per-XCD queues, so neighbouring tiles still
+// share an L2, but hands the positions out through a counter per queue.
+// Round 0 (idx < P) is each workgroup's first tile, taken without a counter.
+__device__ __forceinline__ int queue_tile(int x, int idx, int P, int G) {
+    return (idx / P) * G + x * P + idx % P;
+}
+
+// The next tile of a workgroup on XCD x whose own queue handed it position
+// idx: that tile if it exists, else one taken from the other XCDs' queues in
+// turn (work stealing), else num_tiles (every queue is empty).  Positions
+// grow with each grab and tile numbers grow with positions, so a tile past
+// the end means the queue is exhausted.
+__device__ __forceinline__ int next_tile(const Args& a, int x, int idx, int P, int G) {
+    int t = queue_tile(x, idx, P, G);
+    if (t < a.num_tiles) return t;
+    for (int q = 1; q < 8; ++q) {
+        const int xq = (x + q) & 7;
+        t = queue_tile(xq, P + atomicAdd(a.tile_ctr + 32 * xq, 1), P, G);
+        if (t < a.num_tiles) return t;
+    }
+    return a.num_tiles;
 }
 
 // Number of bytes rounded up to whole dwords (buffer range checks work on
@@ -376,11 +405,15 @@ __device__ __forceinline__ void interleave_step() {
 // FUSED: the fused epilogue of gemm_epi.h instead of the plain fp32 store.
 // SPLIT: split-K work units (Args::tiles_per_split, Args::kslice); each unit
 // stores its fp32 partial sums, which a separate pass adds in a fixed order.
+// DYN: tiles after the first are taken from per-XCD atomic counters
+// (Args::tile_ctr, next_tile) instead of the static strided walk; the grid
+// must be a multiple of 8.
 template <int KIND, int RB, int S, bool TAIL, int SG = 1, int E = 0, int D = 0, int NW = 4, bool FUSED = false,
-          bool SPLIT = false>
+          bool SPLIT = false, bool DYN = false>
 __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(Args a) {
     static_assert(NW == 4 || (NW == 8 && KIND != kMX), "8 waves: bf16 only");
     static_assert(!SPLIT || (KIND != kMX && !FUSED && NW == 4), "split-K: plain bf16 only");
+    static_assert(!DYN || (!SPLIT && NW == 4), "dynamic schedule: whole tiles, 4 waves");
     constexpr int THREADS = 64 * NW;
     constexpr int NBJ = NW == 8 ? 2 : kBlocks;  // 32-column MFMA blocks per wave tile
     constexpr int WTN = 32 * NBJ;               // wave tile columns
@@ -437,6 +470,10 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(Args a) {
     __shared__ __attribute__((aligned(1024))) uint8_t sr0[RING];
     __shared__ __attribute__((aligned(1024))) uint8_t sr1[RING];
     __shared__ float evl[FUSED ? 3 * 256 : 1];  // fused epilogue: the tile's scales and biases
+    // dynamic schedule: the next tile, handed from thread 0 to the workgroup
+    // through two alternating slots (a slot is rewritten only after the
+    // barrier that follows every wave's read of it)
+    __shared__ int tile_slot[2];
     auto stage_ptr = [&](auto sidx) -> uint8_t FAST_LDS* {
         constexpr int s = decltype(sidx)::value;
         if constexpr (s == 0) return (uint8_t FAST_LDS*)st0;
@@ -504,7 +541,16 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(Args a) {
     const int sb_rd = 2 * OPB + 4 * kTile + 4 * (wn * kWaveTile + l32);
 
     const int G = gridDim.x;
-    for (int t = logical_block(a); t < a.num_tiles; t += G) {
+    const int P = G >> 3;              // workgroups per XCD
+    const int xcd = blockIdx.x & 7;    // workgroup b runs on XCD b % 8
+    int slot = 0;
+    for (int t = logical_block(a); t < a.num_tiles;) {
+        // dynamic schedule: claim the next position of this XCD's queue now;
+        // the value is needed only when the tile ends
+        int claim = 0;
+        if constexpr (DYN) {
+            if (tid == 0) claim = P + atomicAdd(a.tile_ctr + 32 * xcd, 1);
+        }
         // split-K: unit t is tile tt of K range ks; K ranges are the slow
         // index, so concurrently running units read the same k columns
         int tt = t, k0 = 0, Kl = a.K, crow = 0;
@@ -818,10 +864,19 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(Args a) {
         }
         store_c<NBJ, FUSED>(a, acc, m0 + wm * kWaveTile, n0 + wn * WTN, h, l32, (const float FAST_LDS*)evl,
                             wm * kWaveTile, wn * WTN, crow);
+        if constexpr (DYN) {
+            if (tid == 0) tile_slot[slot] = next_tile(a, xcd, claim, P, G);
+        }
         // The next tile's prologue overwrites stages 0 .. S-2: every wave
         // must be done reading them.
         wait_lgkm0();
         barrier();
+        if constexpr (DYN) {
+            t = __builtin_amdgcn_readfirstlane(tile_slot[slot]);
+            slot ^= 1;
+        } else {
+            t += G;
+        }
     }
 }
 

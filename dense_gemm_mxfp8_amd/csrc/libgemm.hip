@@ -480,6 +480,12 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
     }
 }
 
+// Zero n ints (the dynamic schedule's tile counters) with vector stores; a
+// kernel rather than a memset so that the call stays capturable as kernels.
+__global__ __launch_bounds__(256) void zero_words_kernel(int* p, int n) {
+    for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0;
+}
+
 // ---------------------------------------------------------------------------
 // Host side.
 // ---------------------------------------------------------------------------
@@ -628,8 +634,11 @@ FastVariant env_variant() {
 
 // SPLIT: split-K units (a.kslice set, `splits` K ranges): the partial sums
 // go to `splits` stacked M x N planes of C.
+// DYN: the dynamic tile schedule; a.tile_ctr holds 256 ints that are zeroed
+// on the stream first (falls back to the static walk when the grid is not a
+// multiple of 8).
 template <int KIND, int RB, int S, int SG = 1, int E = 0, int D = 0, int NW = 4, bool FUSED = false,
-          bool SPLIT = false>
+          bool SPLIT = false, bool DYN = false>
 int launch_fast(fast::Args a, int cus, hipStream_t stream, int group_m = 0, int splits = 1) {
     constexpr int BK = RB / (KIND == fast::kMX ? 1 : 2);
     a.tiles_m = (a.M + fast::kTile - 1) / fast::kTile;
@@ -644,12 +653,25 @@ int launch_fast(fast::Args a, int cus, hipStream_t stream, int group_m = 0, int 
     int grid = cus < a.num_tiles ? cus : a.num_tiles;
     if (grid >= 8) grid -= grid % 8;
     a.xcd_remap = (grid % 8 == 0) ? 1 : 0;
-    if (a.kt_total > a.kt_full)
+    if constexpr (DYN) {
+        if (a.xcd_remap) {
+            hipLaunchKernelGGL(zero_words_kernel, dim3(1), dim3(256), 0, stream, a.tile_ctr, 256);
+            if (a.kt_total > a.kt_full)
+                hipLaunchKernelGGL((fast::gemm_fast_kernel<KIND, RB, S, true, SG, E, D, NW, FUSED, false, true>),
+                                   dim3(grid), dim3(64 * NW), 0, stream, a);
+            else
+                hipLaunchKernelGGL((fast::gemm_fast_kernel<KIND, RB, S, false, SG, E, D, NW, FUSED, false, true>),
+                                   dim3(grid), dim3(64 * NW), 0, stream, a);
+            return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
+        }
+    }
+    if (a.kt_total > a.kt_full) {
         hipLaunchKernelGGL((fast::gemm_fast_kernel<KIND, RB, S, true, SG, E, D, NW, FUSED, SPLIT>), dim3(grid),
                            dim3(64 * NW), 0, stream, a);
-    else
+    } else {
         hipLaunchKernelGGL((fast::gemm_fast_kernel<KIND, RB, S, false, SG, E, D, NW, FUSED, SPLIT>), dim3(grid),
                            dim3(64 * NW), 0, stream, a);
+    }
     return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
 }
 
@@ -1023,6 +1045,33 @@ int splitk_dispatch(bool nt, int64_t M, int64_t N, int64_t K, const void* A, int
     return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
 }
 
+// ---------------------------------------------------------------------------
+// Dynamic tile schedule (gemm_bf16_dynamic).
+// ---------------------------------------------------------------------------
+
+constexpr size_t kDynWorkspace = 1024;  // 8 counters, 128 bytes apart
+
+int dynamic_dispatch(bool nt, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+                     int64_t ldb, float* C, int64_t ldc, void* ws, size_t ws_bytes, void* stream) {
+    if (ws == nullptr || ws_bytes < kDynWorkspace || ((uintptr_t)ws & 15)) return GEMM_ERR_INVALID_ARG;
+    int rc = check_common(M, N, K, A, lda, B, ldb, nt ? K : N, C, ldc);
+    if (rc == 1) return GEMM_OK;
+    if (rc != GEMM_OK) return rc;
+    DeviceInfo dev;
+    rc = device_info(&dev);
+    if (rc != GEMM_OK) return rc;
+    if (K > 0 && use_big_tiles(M, N, dev.cus) && c_ok(ldc) &&
+        fast_ok(nt ? fast::kNT : fast::kNN, M, N, K, A, lda, B, ldb, nullptr, nullptr)) {
+        fast::Args a = make_fast_args(M, N, K, A, lda, B, ldb, C, ldc, 2, kPlain);
+        a.tile_ctr = (int*)ws;
+        hipStream_t s = (hipStream_t)stream;
+        const int g = env_variant().group;
+        return nt ? launch_fast<fast::kNT, 128, 2, 1, 6, 2, 4, false, false, true>(a, dev.cus, s, g)
+                  : launch_fast<fast::kNN, 128, 2, 1, 6, 2, 4, false, false, true>(a, dev.cus, s, g);
+    }
+    return bf16_dispatch(nt, M, N, K, A, lda, B, ldb, C, ldc, kPlain, stream);
+}
+
 // Epilogue parameters of a fused call; GEMM_ERR_INVALID_ARG for an unknown
 // output type or a C pointer not aligned to its element.
 int fused_params(int out_type, const void* C, const float* rs, const float* cs, const float* bias,
@@ -1136,6 +1185,12 @@ int gemm_bf16_splitk(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda
     if (rc != GEMM_OK) return rc;
     return splitk_dispatch(b_colmajor != 0, M, N, K, A, lda, B, ldb, C, ldc, e, splits, workspace,
                            workspace_bytes, stream);
+}
+
+int gemm_bf16_dynamic(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
+                      int b_colmajor, float* C, int64_t ldc, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+    return dynamic_dispatch(b_colmajor != 0, M, N, K, A, lda, B, ldb, C, ldc, workspace, workspace_bytes, stream);
 }
 
 int gemm_bf16_splitk_plan(int64_t M, int64_t N, int64_t K, int b_colmajor, int splits, int cus,

@@ -142,12 +142,19 @@ WORKLOADS = {
     "skinny16x8192x8192_nn": dict(kind="bf16", M=16, N=8192, K=8192, dist="normal",
                                   b_colmajor=False),
     "mx8192": dict(kind="mx", M=8192, N=8192, K=8192, dist="normal"),
+    # split-K (K ranges planned by the library): a small output with a long K,
+    # and the skinny product with column-major B
+    "longk1024x1024x32768_nt": dict(kind="bf16", M=1024, N=1024, K=32768, dist="normal", b_colmajor=True,
+                                    splitk=True),
+    "skinny16x8192x8192_nt": dict(kind="bf16", M=16, N=8192, K=8192, dist="normal", b_colmajor=True,
+                                  splitk=True),
 }
 
 
 def workload(name: str, seed: int = 0):
     w = dict(WORKLOADS[name])
     kind = w.pop("kind")
+    w.pop("splitk", None)
     if kind == "bf16":
         return bf16_problem(seed=seed, name=name, **w)
     return mx_problem(seed=seed, name=name, **w)

@@ -186,6 +186,39 @@ int gemm_bf16_splitk(int64_t M, int64_t N, int64_t K,
 int gemm_bf16_splitk_plan(int64_t M, int64_t N, int64_t K, int b_colmajor, int splits, int cus,
                           int* splits_used, size_t* workspace_bytes);
 
+/* ---- dynamic tile schedule -----------------------------------------------
+ *
+ * "Modern GPU Programming For MLSys - 书籍总结", section 2.9 (Cluster Launch
+ * Control) and section 4.2 (Step 6, the persistent kernel with a tile
+ * scheduler): resident workgroups ask for their next tile at run time, so a
+ * workgroup that finishes early takes more work instead of idling at the
+ * tail.  Here that request is an atomic increment of a tile counter in the
+ * caller's workspace: 8 queues, one per XCD, each holding the tiles the
+ * static walk would give that XCD's workgroups (neighbouring tiles, which
+ * share the XCD's L2), and a workgroup whose queue is empty takes tiles from
+ * the other queues.  Every tile is still computed by exactly one workgroup
+ * with the same arithmetic, so C is bitwise identical to gemm_bf16's.
+ *
+ * Arguments as gemm_bf16_fused without the epilogue (fp32 C), plus
+ *   workspace        device memory owned by the caller, 16-byte aligned, at
+ *                    least GEMM_DYNAMIC_WORKSPACE_BYTES; the counters are
+ *                    zeroed on the stream by the call itself, so its contents
+ *                    on entry do not matter.  Calls that share a workspace
+ *                    must be ordered on one stream.
+ *   workspace_bytes  its size.
+ * Products that the 256 x 256 direct-load kernel does not take run as
+ * gemm_bf16 / gemm_bf16_nt, and the workspace is not touched.
+ * Errors: as gemm_bf16, or a workspace that is NULL, too small or not 16-byte
+ * aligned (GEMM_ERR_INVALID_ARG). */
+#define GEMM_DYNAMIC_WORKSPACE_BYTES 1024
+
+int gemm_bf16_dynamic(int64_t M, int64_t N, int64_t K,
+                      const void* A, int64_t lda,
+                      const void* B, int64_t ldb, int b_colmajor,
+                      float* C, int64_t ldc,
+                      void* workspace, size_t workspace_bytes,
+                      void* stream);
+
 /* Static text for a return code (never NULL). */
 const char* gemm_strerror(int code);
 

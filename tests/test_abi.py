@@ -127,3 +127,13 @@ def test_splitk_plan(case, want):
     assert rc == dg.GEMM_OK
     assert used == want
     assert nbytes == (used * M * N * 4 if used > 1 else 0)
+
+
+def test_dynamic_rejects_bad_workspace_before_any_device_call():
+    args = (4, 4, 64, FAKE, 64, FAKE, 64, 1, FAKE, 4)
+    W = dg.GEMM_DYNAMIC_WORKSPACE_BYTES
+    assert dg.gemm_bf16_dynamic(*args, None, W, None) == dg.GEMM_ERR_INVALID_ARG
+    assert dg.gemm_bf16_dynamic(*args, FAKE, W - 1, None) == dg.GEMM_ERR_INVALID_ARG
+    assert dg.gemm_bf16_dynamic(*args, FAKE + 4, W, None) == dg.GEMM_ERR_INVALID_ARG
+    # empty extents: a no-op
+    assert dg.gemm_bf16_dynamic(0, 4, 64, 0, 64, 0, 64, 1, 0, 4, FAKE, W, None) == dg.GEMM_OK

@@ -190,3 +190,18 @@ def test_splitk_tensor_helper():
     torch.cuda.synchronize()
     want, _ = P.oracle_bf16(P.bits16(prob.A), P.bits16(prob.B), False)
     P.assert_exact(C.cpu().numpy().astype(np.float64), want, "bf16_splitk")
+
+
+@pytest.mark.parametrize("name,ranges", [("longk1024x1024x32768_nt", 16), ("skinny16x8192x8192_nt", 8)])
+def test_splitk_bench_workloads(name, ranges):
+    """The split-K workloads at full size, in the launch configuration the
+    benchmark times (the library's plan, ldc = N), on sampled outputs.  With
+    K = 32768 the unsplit fp32 sum would not be inside the 1e-3 bound in
+    general; each of the 16 ranges sums 2048 products (gamma < 1.3e-4) and the
+    16 partials add at most gamma_16 more, so the bound holds."""
+    prob = inputs.workload(name, seed=0)
+    P.note(f"splitk workload {name}")
+    got, used, _ = _run(prob, 0, ldc_pad=0)
+    assert used == ranges
+    assert np.isfinite(got).all()
+    _check(prob, got, False, P.sample_positions(prob.M, prob.N, 2048, seed=92))
