@@ -97,7 +97,7 @@ def stats(args) -> None:
     rows = []
     with open(args.csv) as fh:
         for r in csv.DictReader(fh):
-            if args.match and args.match not in r["Name"]:
+            if args.match and args.match not in r["Name"] and not any(x in r["Name"] for x in args.also):
                 continue
             rows.append(r)
     lines = [f"# rocprofv3 kernel statistics{': ' + args.title if args.title else ''}", "",
@@ -177,6 +177,8 @@ def main():
     s.add_argument("--cmd", required=True)
     s.add_argument("--match", default="")
     s.add_argument("--title", default="")
+    s.add_argument("--also", action="append", default=[],
+                   help="further kernel names to list in the table (e.g. a second kernel of each step)")
     s.add_argument("--trace", default="", help="run_kernel_trace.csv of the same run")
     s.add_argument("--skip", type=int, default=0, help="leading launches to leave out (warm-up)")
     s.add_argument("--bench-json", default="", help="the JSON line bench.py printed in the same run")
