@@ -71,10 +71,14 @@ struct Args {
     int xcd_remap;
     int c_nt;      // C stores non-temporal (1) or cached (0)
     epi::Params epi;  // fused epilogue (C is bf16 when epi.out_bf16)
-    // split-K instances: work unit u is tile u % tiles_per_split of K range
-    // u / tiles_per_split ([ks kslice, min(K, (ks + 1) kslice)), kslice a
-    // multiple of the k-tile); its fp32 partial sums go to rows ks M .. of C
-    int tiles_per_split, kslice;
+    // split-K instances: units 0 .. dp_units-1 are whole tiles 0 .. dp_units-1
+    // (stored to C); unit dp_units + u is tile tile0 + u % tiles_per_split of
+    // K range ks = u / tiles_per_split ([ks kslice, min(K, (ks + 1) kslice)),
+    // kslice a multiple of the k-tile).  Its fp32 partial sums go either to
+    // rows ks M .. of C (part == null: stacked dense M x N planes) or to the
+    // 256 x 256 block (ks tiles_per_split + u % tiles_per_split) of `part`.
+    int tiles_per_split, kslice, dp_units, tile0;
+    float* part;
     // dynamic-schedule instances: 8 tile counters, one per XCD, 32 ints
     // apart (zero when the launch starts)
     int* tile_ctr;
@@ -237,17 +241,20 @@ __device__ __forceinline__ void tail_nn(uint8_t FAST_LDS* dst, __amdgpu_buffer_r
 // non-temporal (C is written once and never read back, so it should not
 // evict operand lines from L2 and the Infinity Cache); otherwise they are
 // cached so that L2 merges the two halves of each line.
-template <int AUX, int NBJ>
+// AT: cw is where output (m0w, n0w) goes and ldc its row pitch in floats
+// (a split-K partial); otherwise C at (m0w, n0w) with pitch a.ldc.
+template <int AUX, int NBJ, bool AT = false>
 __device__ __forceinline__ void store_c_aux(const Args& a, const f32x16 (&acc)[kBlocks][NBJ], int m0w, int n0w,
-                                            int h, int l32, int crow) {
+                                            int h, int l32, float* cw = nullptr, int ldc = 0) {
     const int rlim = a.M - m0w;
     const int clim = a.N - n0w;
     if (rlim <= 0 || clim <= 0) return;
     const int rows = rlim < kWaveTile ? rlim : kWaveTile;
     const int cols = clim < 32 * NBJ ? clim : 32 * NBJ;
-    const int ldc4 = (int)a.ldc * 4;
+    const int ldc4 = (int)(AT ? ldc : a.ldc) * 4;
     const __amdgpu_buffer_rsrc_t rc =
-        make_rsrc(a.C + (int64_t)(m0w + crow) * a.ldc + n0w, ((int64_t)(rows - 1) * a.ldc + cols) * 4);
+        AT ? make_rsrc(cw, ((int64_t)(rows - 1) * ldc + cols) * 4)
+           : make_rsrc(a.C + (int64_t)m0w * a.ldc + n0w, ((int64_t)(rows - 1) * a.ldc + cols) * 4);
     const int voff = 4 * h * ldc4 + 4 * l32;
 #pragma unroll
     for (int j = 0; j < NBJ; ++j) {
@@ -346,19 +353,21 @@ __device__ __forceinline__ void epi_stage(float FAST_LDS* ev, const EpiRegs& v, 
 }
 
 // FUSED: the kernel instance carries the fused epilogue (a.epi.on); plain
-// instances keep the lean store path.  crow: rows of C skipped before row 0
-// of the product (a split-K partial's block of the workspace; plain only).
+// instances keep the lean store path.  cw / cld (plain only): where output
+// (m0w, n0w) goes and the row pitch there, for a split-K partial (null: C);
+// nt: non-temporal stores allowed (a partial is read back at once).
 template <int NBJ = kBlocks, bool FUSED = false>
 __device__ __forceinline__ void store_c(const Args& a, const f32x16 (&acc)[kBlocks][NBJ], int m0w, int n0w, int h,
                                         int l32, const float FAST_LDS* ev = nullptr, int evr = 0, int evc = 0,
-                                        int crow = 0) {
+                                        float* cw = nullptr, int cld = 0, bool nt = true) {
     if constexpr (FUSED) {
         if (a.epi.out_bf16) store_c_fused<0, NBJ, true>(a, acc, m0w, n0w, h, l32, ev, evr, evc);
         else if (a.c_nt) store_c_fused<2, NBJ, false>(a, acc, m0w, n0w, h, l32, ev, evr, evc);
         else store_c_fused<0, NBJ, false>(a, acc, m0w, n0w, h, l32, ev, evr, evc);
     } else {
-        if (a.c_nt) store_c_aux<2, NBJ>(a, acc, m0w, n0w, h, l32, crow);
-        else store_c_aux<0, NBJ>(a, acc, m0w, n0w, h, l32, crow);
+        if (cw != nullptr) store_c_aux<0, NBJ, true>(a, acc, m0w, n0w, h, l32, cw, cld);
+        else if (a.c_nt && nt) store_c_aux<2, NBJ>(a, acc, m0w, n0w, h, l32);
+        else store_c_aux<0, NBJ>(a, acc, m0w, n0w, h, l32);
     }
 }
 
@@ -553,13 +562,25 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(Args a) {
         }
         // split-K: unit t is tile tt of K range ks; K ranges are the slow
         // index, so concurrently running units read the same k columns
-        int tt = t, k0 = 0, Kl = a.K, crow = 0;
+        int tt = t, k0 = 0, Kl = a.K;
+        float* pw = nullptr;  // split-K partial: where output (m0, n0) goes
+        int pld = 0;          // and its row pitch
         if constexpr (SPLIT) {
-            const int ks = t / a.tiles_per_split;
-            tt = t - ks * a.tiles_per_split;
-            k0 = ks * a.kslice;
-            Kl = min(a.K - k0, a.kslice);
-            crow = ks * a.M;
+            if (t >= a.dp_units) {
+                const int u = t - a.dp_units;
+                const int ks = u / a.tiles_per_split;
+                const int i = u - ks * a.tiles_per_split;
+                tt = a.tile0 + i;
+                k0 = ks * a.kslice;
+                Kl = min(a.K - k0, a.kslice);
+                if (a.part != nullptr) {
+                    pw = a.part + (int64_t)(ks * a.tiles_per_split + i) * (kTile * kTile);
+                    pld = kTile;
+                } else {
+                    pw = nullptr;  // set below, once m0 and n0 are known
+                    pld = -1 - ks;
+                }
+            }
         }
         const int KT = SPLIT ? Kl / BK : a.kt_full;  // k-tiles holding data
         const int KTM = (KT + U - 1) / U * U;        // rounded up: the rest are dead (zero) k-tiles
@@ -862,8 +883,23 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(Args a) {
             wait_lgkm0();
             barrier();
         }
-        store_c<NBJ, FUSED>(a, acc, m0 + wm * kWaveTile, n0 + wn * WTN, h, l32, (const float FAST_LDS*)evl,
-                            wm * kWaveTile, wn * WTN, crow);
+        if constexpr (SPLIT) {
+            float* cw = nullptr;
+            int cld = 0;
+            if (pld > 0) {
+                cw = pw + wm * kWaveTile * kTile + wn * WTN;
+                cld = pld;
+            } else if (pld < 0) {
+                // stacked dense planes: plane ks = -1 - pld, row pitch ldc
+                cw = a.C + (int64_t)(m0 + wm * kWaveTile + (-1 - pld) * a.M) * a.ldc + n0 + wn * WTN;
+                cld = (int)a.ldc;
+            }
+            store_c<NBJ, false>(a, acc, m0 + wm * kWaveTile, n0 + wn * WTN, h, l32, nullptr, 0, 0, cw, cld,
+                                pld == 0);
+        } else {
+            store_c<NBJ, FUSED>(a, acc, m0 + wm * kWaveTile, n0 + wn * WTN, h, l32, (const float FAST_LDS*)evl,
+                                wm * kWaveTile, wn * WTN);
+        }
         if constexpr (DYN) {
             if (tid == 0) tile_slot[slot] = next_tile(a, xcd, claim, P, G);
         }

@@ -486,6 +486,36 @@ __global__ __launch_bounds__(256) void zero_words_kernel(int* p, int n) {
     for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0;
 }
 
+// Split tiles of the stream-K style plan: the ranges' partial tiles of split
+// tile i are 256 x 256 blocks r T + i of a.part (T = a.tiles_per_split), and
+// C's tile a.tile0 + i = epilogue(block 0 + block T + ... + block (s-1) T),
+// added in range order.  Sixteen workgroups per tile, 16 rows each; only
+// elements inside M x N are read back into C (the rest of a block was never
+// written).
+__global__ __launch_bounds__(256) void tile_reduce_kernel(fast::Args a, int splits, void* C, int64_t ldc,
+                                                          epi::Params e) {
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    constexpr int kT = fast::kTile;
+    const int i = blockIdx.x >> 4, q = blockIdx.x & 15;
+    int tm, tn;
+    fast::tile_coords(a, a.tile0 + i, tm, tn);
+    const int m0 = tm * kT, n0 = tn * kT;
+    const int64_t plane = (int64_t)a.tiles_per_split * kT * kT;
+    const float* blk = a.part + (int64_t)i * kT * kT;
+    for (int v = threadIdx.x; v < 16 * kT / 4; v += blockDim.x) {
+        const int row = 16 * q + v / (kT / 4), col = 4 * (v % (kT / 4));
+        if (m0 + row >= a.M || n0 + col >= a.N) continue;
+        const int64_t off = (int64_t)row * kT + col;
+        f32x4 acc = *(const f32x4*)(blk + off);
+        for (int r = 1; r < splits; ++r) acc += *(const f32x4*)(blk + r * plane + off);
+        const float v0 = acc[0], v1 = acc[1], v2 = acc[2], v3 = acc[3];
+        epi::store(C, ldc, e, m0 + row, n0 + col, v0);
+        if (n0 + col + 1 < a.N) epi::store(C, ldc, e, m0 + row, n0 + col + 1, v1);
+        if (n0 + col + 2 < a.N) epi::store(C, ldc, e, m0 + row, n0 + col + 2, v2);
+        if (n0 + col + 3 < a.N) epi::store(C, ldc, e, m0 + row, n0 + col + 3, v3);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Host side.
 // ---------------------------------------------------------------------------
@@ -644,8 +674,14 @@ int launch_fast(fast::Args a, int cus, hipStream_t stream, int group_m = 0, int 
     a.tiles_m = (a.M + fast::kTile - 1) / fast::kTile;
     a.tiles_n = (a.N + fast::kTile - 1) / fast::kTile;
     a.num_tiles = a.tiles_m * a.tiles_n;
-    a.tiles_per_split = a.num_tiles;
-    if (SPLIT) a.num_tiles *= splits;
+    if (SPLIT) {
+        if (a.part == nullptr) {  // every tile split, stacked dense planes
+            a.dp_units = 0;
+            a.tile0 = 0;
+            a.tiles_per_split = a.num_tiles;
+        }
+        a.num_tiles = a.dp_units + a.tiles_per_split * splits;
+    }
     if (group_m <= 0) group_m = 8;
     a.group_m = a.tiles_m < group_m ? a.tiles_m : group_m;
     a.kt_full = a.K / BK;
@@ -963,7 +999,16 @@ struct SplitPlan {
     int kernel;      // SplitKernel
     int splits;      // K ranges (1: no split)
     int64_t kslice;  // K elements per range, the last range takes the rest
+    int64_t dp;      // stream-K style: whole tiles computed first (0: every tile split)
+    int64_t rem;     // stream-K style: tiles split after them
 };
+
+// Workspace bytes of a plan.
+int64_t plan_bytes(const SplitPlan& p, int64_t M, int64_t N) {
+    if (p.splits <= 1) return 0;
+    if (p.rem > 0) return (int64_t)p.splits * p.rem * fast::kTile * fast::kTile * 4;
+    return (int64_t)p.splits * M * N * 4;
+}
 
 // Which kernel would compute the partial sums of this problem.  `aligned`:
 // the operand pointers are 16-byte aligned (the query entry point assumes
@@ -985,17 +1030,41 @@ int split_kernel(bool nt, int64_t M, int64_t N, int64_t K, bool aligned, int64_t
 //     3/4 of a round, cut K so that tiles x ranges fills about one round,
 //     each range at least 8 k-tiles (512) long;
 //   - small M (small kernel): when its 32-column blocks give fewer
-//     workgroups than CUs, the same with ranges of at least 1024.
+//     workgroups than CUs, the same with ranges of at least 1024;
+//   - 256 x 256 tiles filling more than one round with a last round at most
+//     half full (stream-K style): the full rounds run whole tiles, and only
+//     the last round's tiles are split, into about CUs / (those tiles)
+//     ranges of at least 512, so that the last round takes a fraction of a
+//     round.  Its partial tiles go to compact 256 x 256 blocks.  A round is
+//     the 256 x 256 kernel's persistent grid: the CUs rounded down to a
+//     multiple of 8.
 SplitPlan plan_split(bool nt, int64_t M, int64_t N, int64_t K, bool aligned, int64_t lda, int64_t ldb, int cus,
                      int requested) {
-    SplitPlan p{split_kernel(nt, M, N, K, aligned, lda, ldb), 1, K};
+    SplitPlan p{split_kernel(nt, M, N, K, aligned, lda, ldb), 1, K, 0, 0};
     if (p.kernel == kSplitNone || K <= 0) return p;
     const int64_t gran = p.kernel == kSplitFast ? 64 : small::kStepK;  // k-tile of the partial kernel
     int64_t want = requested;
     if (want <= 0) {
         const int64_t units = p.kernel == kSplitFast ? ((M + 255) / 256) * ((N + 255) / 256) : (N + 31) / 32;
         const int64_t min_range = p.kernel == kSplitFast ? 512 : 1024;
-        if (units * 4 >= (int64_t)cus * 3) return p;
+        if (units * 4 >= (int64_t)cus * 3) {
+            const int64_t grid = cus - cus % 8;
+            const int64_t rem = grid > 0 ? units % grid : 0;
+            if (p.kernel != kSplitFast || units <= grid || rem == 0 || rem * 2 > grid) return p;
+            int64_t s = grid / rem;
+            if (s > K / min_range) s = K / min_range;
+            if (s > kMaxSplits) s = kMaxSplits;
+            if (s < 2) return p;
+            int64_t kslice = (K + s - 1) / s;
+            kslice = (kslice + gran - 1) / gran * gran;
+            const int64_t splits = (K + kslice - 1) / kslice;
+            if (splits <= 1) return p;
+            p.splits = (int)splits;
+            p.kslice = kslice;
+            p.dp = units - rem;
+            p.rem = rem;
+            return p;
+        }
         want = cus / units;
         if (want > K / min_range) want = K / min_range;
         if (want > kMaxSplits) want = kMaxSplits;
@@ -1021,11 +1090,34 @@ int splitk_dispatch(bool nt, int64_t M, int64_t N, int64_t K, const void* A, int
     DeviceInfo dev;
     rc = device_info(&dev);
     if (rc != GEMM_OK) return rc;
-    const SplitPlan p = plan_split(nt, M, N, K, aligned16(A) && aligned16(B), lda, ldb, dev.cus, splits);
+    SplitPlan p = plan_split(nt, M, N, K, aligned16(A) && aligned16(B), lda, ldb, dev.cus, splits);
+    // the stream-K style plan stores whole tiles straight to C with the plain
+    // fp32 epilogue (the split kernel has no fused store)
+    const bool plain = !e.out_bf16 && !e.rs && !e.cs && !e.bias;
+    if (p.rem > 0 && (!plain || !c_ok(ldc))) p.splits = 1;
     if (p.splits <= 1) return bf16_dispatch(nt, M, N, K, A, lda, B, ldb, C, ldc, e, stream);
-    const int64_t need = (int64_t)p.splits * M * N * 4;
+    const int64_t need = plan_bytes(p, M, N);
     if (ws == nullptr || (int64_t)ws_bytes < need || ((uintptr_t)ws & 15)) return GEMM_ERR_INVALID_ARG;
     hipStream_t s = (hipStream_t)stream;
+    if (p.rem > 0) {
+        fast::Args a = make_fast_args(M, N, K, A, lda, B, ldb, C, ldc, 2, kPlain);
+        a.kslice = (int)p.kslice;
+        a.part = (float*)ws;
+        a.dp_units = (int)p.dp;
+        a.tile0 = (int)p.dp;
+        a.tiles_per_split = (int)p.rem;
+        const int g = env_variant().group;
+        rc = nt ? launch_fast<fast::kNT, 128, 2, 1, 6, 2, 4, false, true>(a, dev.cus, s, g, p.splits)
+                : launch_fast<fast::kNN, 128, 2, 1, 6, 2, 4, false, true>(a, dev.cus, s, g, p.splits);
+        if (rc != GEMM_OK) return rc;
+        // the same tile geometry as launch_fast's
+        a.tiles_m = (a.M + fast::kTile - 1) / fast::kTile;
+        a.tiles_n = (a.N + fast::kTile - 1) / fast::kTile;
+        a.group_m = a.tiles_m < (g > 0 ? g : 8) ? a.tiles_m : (g > 0 ? g : 8);
+        hipLaunchKernelGGL(tile_reduce_kernel, dim3((unsigned)(p.rem * 16)), dim3(256), 0, s, a, p.splits, C, ldc,
+                           e);
+        return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
+    }
     if (p.kernel == kSplitSmall) {
         rc = launch_small_bf16(M, N, K, A, lda, B, ldb, ws, N, kPlain, s, p.splits, p.kslice);
     } else {
@@ -1073,7 +1165,8 @@ int dynamic_dispatch(bool nt, int64_t M, int64_t N, int64_t K, const void* A, in
 }
 
 // Epilogue parameters of a fused call; GEMM_ERR_INVALID_ARG for an unknown
-// output type or a C pointer not aligned to its element.
+// output type or a C pointer not aligned to its element.  fp32 output with
+// no vectors is the plain store (the lean kernel instances).
 int fused_params(int out_type, const void* C, const float* rs, const float* cs, const float* bias,
                  epi::Params* e) {
     if (out_type != GEMM_OUT_F32 && out_type != GEMM_OUT_BF16) return GEMM_ERR_INVALID_ARG;
@@ -1081,8 +1174,8 @@ int fused_params(int out_type, const void* C, const float* rs, const float* cs, 
     e->rs = rs;
     e->cs = cs;
     e->bias = bias;
-    e->on = 1;
     e->out_bf16 = out_type == GEMM_OUT_BF16;
+    e->on = (e->out_bf16 || rs || cs || bias) ? 1 : 0;
     return GEMM_OK;
 }
 
@@ -1205,10 +1298,10 @@ int gemm_bf16_splitk_plan(int64_t M, int64_t N, int64_t K, int b_colmajor, int s
     }
     const bool nt = b_colmajor != 0;
     // operands assumed 16-byte aligned with dense leading dimensions
-    SplitPlan p{kSplitNone, 1, K};
+    SplitPlan p{kSplitNone, 1, K, 0, 0};
     if (M > 0 && N > 0) p = plan_split(nt, M, N, K, true, K, nt ? K : N, cus, splits);
     if (splits_used) *splits_used = p.splits;
-    if (workspace_bytes) *workspace_bytes = p.splits > 1 ? (size_t)p.splits * (size_t)M * (size_t)N * 4 : 0;
+    if (workspace_bytes) *workspace_bytes = (size_t)plan_bytes(p, M, N);
     return GEMM_OK;
 }
 

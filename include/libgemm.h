@@ -151,6 +151,16 @@ int gemm_mxfp8_fused(int64_t M, int64_t N, int64_t K,
  * output has too few tiles for its compute units (a short, wide product or a
  * small M x N with a long K).
  *
+ * Products whose 256 x 256 tiles fill more than one round of the compute
+ * units, with a last round at most half full, get a stream-K style plan from
+ * the library (splits == 0): the whole rounds compute their tiles unsplit,
+ * straight into C, and only the last round's tiles are split over K, so that
+ * round takes a fraction of a round's time.  Their partial products go to
+ * compact 256 x 256 fp32 blocks (splits_used * left-over tiles * 256 KiB of
+ * workspace) and are added per tile in range order.  This plan stores C with
+ * the plain fp32 epilogue only; with another epilogue such products run
+ * unsplit.
+ *
  * gemm_bf16_splitk: arguments as gemm_bf16_fused, plus
  *   splits          K ranges wanted; 0 lets the library decide from the shape
  *                   (its plan is gemm_bf16_splitk_plan's).  Fewer ranges are
@@ -160,8 +170,9 @@ int gemm_mxfp8_fused(int64_t M, int64_t N, int64_t K,
  *                   the product runs unsplit as gemm_bf16_fused and the
  *                   workspace is not touched.
  *   workspace       device memory owned by the caller, 16-byte aligned, at
- *                   least splits_used * M * N * 4 bytes (gemm_bf16_splitk_plan
- *                   reports the figure); its contents on entry do not matter
+ *                   least the bytes gemm_bf16_splitk_plan reports
+ *                   (splits_used * M * N * 4 when every tile is split); its
+ *                   contents on entry do not matter
  *                   and are overwritten.  Calls that share a workspace must
  *                   be ordered on one stream.
  *   workspace_bytes its size.

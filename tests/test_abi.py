@@ -117,7 +117,16 @@ SPLIT_PLANS = [
     ((1000, 1000, 1000, 1, 100, 256), 16),  # capped at 32, then 64-element ranges
     ((1000, 1000, 1002, 1, 4, 256), 1),     # lda = 1002: rows not 16-byte aligned
     ((0, 1000, 1000, 1, 4, 256), 1),
+    # stream-K style: whole rounds unsplit, a last round at most half full split
+    ((4352, 4352, 4096, 1, 0, 256), 7),     # 289 tiles: 33 left over, 7 ranges of 640
+    ((4096, 6144, 4096, 0, 0, 256), 2),     # 384 tiles: 128 left over
+    ((8448, 8192, 8192, 1, 0, 256), 8),     # 1056 tiles: 32 left over, 8 ranges
+    ((4352, 4352, 512, 1, 0, 256), 1),      # K too short for two ranges of 512
+    ((6656, 4096, 4096, 1, 0, 256), 1),     # 416 tiles: the last round is over half full
 ]
+
+# tiles left over after the whole rounds of the stream-K style plans above
+LEFT_OVER = {(4352, 4352, 4096): 33, (4096, 6144, 4096): 128, (8448, 8192, 8192): 32}
 
 
 @pytest.mark.parametrize("case,want", SPLIT_PLANS, ids=lambda c: "x".join(map(str, c)) if isinstance(c, tuple) else str(c))
@@ -126,7 +135,13 @@ def test_splitk_plan(case, want):
     rc, used, nbytes = dg.gemm_bf16_splitk_plan(M, N, K, colmajor, splits, cus)
     assert rc == dg.GEMM_OK
     assert used == want
-    assert nbytes == (used * M * N * 4 if used > 1 else 0)
+    if used == 1:
+        assert nbytes == 0
+    elif (M, N, K) in LEFT_OVER:
+        # compact 256 x 256 fp32 partial tiles of the left-over tiles only
+        assert nbytes == used * LEFT_OVER[(M, N, K)] * 256 * 256 * 4
+    else:
+        assert nbytes == used * M * N * 4
 
 
 def test_dynamic_rejects_bad_workspace_before_any_device_call():

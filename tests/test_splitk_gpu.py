@@ -205,3 +205,37 @@ def test_splitk_bench_workloads(name, ranges):
     assert used == ranges
     assert np.isfinite(got).all()
     _check(prob, got, False, P.sample_positions(prob.M, prob.N, 2048, seed=92))
+
+
+# Stream-K style plans: products that fill more than one round of the 256 x
+# 256 kernel with a last round at most half full.  The whole rounds store
+# straight to C with the arithmetic of the plain entry points; only the last
+# round's tiles are split over K (compact partial tiles, tile-wise reduction).
+# 4173 x 4360: 17 x 18 = 306 tiles, 50 left over in 4 ranges, the last range
+# with a partial k-tile; the left-over tiles include the bottom and right
+# edges.  4352 x 4352: 289 tiles, 33 left over.
+STREAMK = [(4096 + 77, 4096 + 264, 2056, False, 4), (4352, 4352, 1024, True, 2), (4352, 4352, 4096, True, 7)]
+
+
+@pytest.mark.parametrize("case", STREAMK, ids=lambda c: f"{c[0]}x{c[1]}x{c[2]}_{'nt' if c[3] else 'nn'}")
+@pytest.mark.parametrize("exact", [True, False], ids=["integer", "normal"])
+def test_splitk_stream_k_style(case, exact):
+    M, N, K, colmajor, ranges = case
+    prob = _prob(M, N, K, colmajor, exact, seed=98)
+    P.note(f"splitk stream-K style {prob.name} {'NT' if colmajor else 'NN'}")
+    got, used, _ = _run(prob, 0, ldc_pad=0)
+    assert used == ranges
+    plain = P.run_bf16(prob.A.to(DEV), prob.B.to(DEV), colmajor).cpu().numpy().astype(np.float64)
+    if exact:
+        assert np.array_equal(got, plain)
+    else:
+        # whole tiles are computed as by the plain call, bit for bit; at most
+        # the left-over tiles (under half a round of 256 x 256) may differ
+        differ = np.count_nonzero(got != plain)
+        assert differ <= 128 * 256 * 256, differ
+    rows, cols = P.sample_positions(M, N, 2048, seed=99)
+    want, mag = P.oracle_bf16_at(P.bits16(prob.A), P.bits16(prob.B), colmajor, rows, cols)
+    if exact:
+        P.assert_exact(got[rows, cols], want, prob.name)
+    else:
+        P.assert_within_bound(got[rows, cols], want, mag, prob.name)
