@@ -84,6 +84,14 @@ class Oracle:
         lib.oracle_gemm_mxfp8_at.argtypes = ([_i64] * 3 + [_vp, _i64, _i64] * 2
                                              + [_vp, _i64] * 2
                                              + [_vp, _vp, _i64, _vp, _vp, ctypes.c_int])
+        lib.oracle_attention_fwd.restype = ctypes.c_int
+        lib.oracle_attention_fwd.argtypes = ([_i64] * 6 + [_vp, _vp] * 3
+                                             + [ctypes.c_double, ctypes.c_int, _vp, _vp, _vp,
+                                                ctypes.c_int])
+        lib.oracle_attention_fwd_at.restype = ctypes.c_int
+        lib.oracle_attention_fwd_at.argtypes = ([_i64] * 6 + [_vp, _vp] * 3
+                                                + [ctypes.c_double, ctypes.c_int, _vp, _i64,
+                                                   _vp, _vp, _vp, ctypes.c_int])
         self.lib = lib
         self.path = path
 
@@ -208,6 +216,64 @@ class Oracle:
         return out, absout
 
 
+    # --------------------------------------------------------------- attention
+    @staticmethod
+    def _attn_args(Q, K, V):
+        for x, name in ((Q, "Q"), (K, "K"), (V, "V")):
+            if not isinstance(x, np.ndarray) or x.ndim != 4 or x.dtype != np.uint16:
+                raise TypeError(f"{name} must be a 4-D numpy array of uint16 (bf16 bits)")
+        B, Hq, Sq, D = Q.shape
+        Bk, Hkv, Sk, Dk = K.shape
+        if K.shape != V.shape or Bk != B or Dk != D:
+            raise ValueError("K and V must be [B][Hkv][Sk][D] with Q's B and D")
+        st = [np.ascontiguousarray(_strides(x), np.int64) for x in (Q, K, V)]
+        return (B, Hq, Hkv, Sq, Sk, D), st
+
+    def attention_fwd(self, Q, K, V, scale: float, causal: bool = False,
+                      nthreads: int | None = None):
+        """Softmax attention of bf16 bit arrays Q [B,Hq,Sq,D], K and V
+        [B,Hkv,Sk,D] (any strides).  Returns (O, Omag, lse): O and Omag float64
+        [B,Hq,Sq,D] (Omag = sum_j p_j |v(j,d)|), lse float64 [B,Hq,Sq]."""
+        dims, st = self._attn_args(Q, K, V)
+        B, Hq, Hkv, Sq, Sk, D = dims
+        O = np.zeros((B, Hq, Sq, D), np.float64)
+        Om = np.zeros_like(O)
+        lse = np.zeros((B, Hq, Sq), np.float64)
+        rc = self.lib.oracle_attention_fwd(B, Hq, Hkv, Sq, Sk, D,
+                                           Q.ctypes.data, st[0].ctypes.data,
+                                           K.ctypes.data, st[1].ctypes.data,
+                                           V.ctypes.data, st[2].ctypes.data,
+                                           float(scale), int(bool(causal)), O.ctypes.data,
+                                           Om.ctypes.data, lse.ctypes.data,
+                                           nthreads or default_threads())
+        if rc != 0:
+            raise ValueError(f"oracle_attention_fwd rejected its arguments ({rc})")
+        return O, Om, lse
+
+    def attention_fwd_at(self, Q, K, V, scale: float, causal: bool, rows,
+                         nthreads: int | None = None):
+        """The same for sampled rows: rows is an (n, 3) array of (b, h, i).
+        Returns O, Omag of shape (n, D) and lse of shape (n,)."""
+        dims, st = self._attn_args(Q, K, V)
+        B, Hq, Hkv, Sq, Sk, D = dims
+        rows = np.ascontiguousarray(rows, np.int64).reshape(-1, 3)
+        n = rows.shape[0]
+        O = np.zeros((n, D), np.float64)
+        Om = np.zeros_like(O)
+        lse = np.zeros(n, np.float64)
+        rc = self.lib.oracle_attention_fwd_at(B, Hq, Hkv, Sq, Sk, D,
+                                              Q.ctypes.data, st[0].ctypes.data,
+                                              K.ctypes.data, st[1].ctypes.data,
+                                              V.ctypes.data, st[2].ctypes.data,
+                                              float(scale), int(bool(causal)),
+                                              rows.ctypes.data, n, O.ctypes.data,
+                                              Om.ctypes.data, lse.ctypes.data,
+                                              nthreads or default_threads())
+        if rc != 0:
+            raise ValueError(f"oracle_attention_fwd_at rejected its arguments ({rc})")
+        return O, Om, lse
+
+
 _default: Oracle | None = None
 
 
@@ -251,6 +317,14 @@ def gemm_mxfp8(*args, **kw):
 
 def gemm_mxfp8_at(*args, **kw):
     return default().gemm_mxfp8_at(*args, **kw)
+
+
+def attention_fwd(*args, **kw):
+    return default().attention_fwd(*args, **kw)
+
+
+def attention_fwd_at(*args, **kw):
+    return default().attention_fwd_at(*args, **kw)
 
 
 # ---------------------------------------------------------------- epilogue

@@ -368,3 +368,201 @@ int oracle_gemm_mxfp8_at(int64_t M, int64_t N, int64_t K,
     J.out = out; J.absout = absout;
     return run_split(&J, nsample, nthreads, run_sample_mx);
 }
+
+/* ------------------------------------------------------------------------ */
+/* Attention forward (the second workload of "Modern GPU Programming For     */
+/* MLSys - 书籍总结", part IV, sections 5.1-5.3).                            */
+/* ------------------------------------------------------------------------ */
+
+/* What is computed, per batch b, query head h and query row i:
+ *
+ *   s_j   = scale * sum_d q(i,d) k(j,d)            (the score MMA, 5.1)
+ *   keys  : j in [0, Sk); with the causal mask only j <= i + (Sk - Sq)
+ *           (5.3 names causal masking; the pages fix no alignment, and the
+ *           bottom-right one keeps the last query row seeing every key)
+ *   e_j   = exp(s_j - max_j s_j),  p_j = e_j / sum_j e_j          (softmax)
+ *   o(i,d)= sum_j p_j v(j,d) = (sum_j e_j v(j,d)) / sum_j e_j  (value MMA, 5.1)
+ *   lse_i = max_j s_j + log(sum_j exp(s_j - max_j s_j))
+ *
+ * Grouped-query attention (5.3): query head h reads key/value head
+ * h / (Hq / Hkv).  This is the plain definition of softmax attention; the
+ * online (running-max, rescaled) form of section 5.2 reaches the same value
+ * up to rounding, so the oracle does not follow it.  A row with no allowed
+ * key (causal, Sq > Sk) has no softmax: its output is 0 and its lse -inf.
+ *
+ * Arithmetic: bf16 inputs decoded exactly, every sum in binary64 in
+ * ascending index order, exp and log from the C library in binary64.
+ * Alongside o(i,d) the oracle returns sum_j p_j |v(j,d)|, which scales the
+ * elementwise acceptance bound. */
+typedef struct {
+    int64_t Hq, Hkv, Sq, Sk, D;
+    const uint16_t *Q, *K, *V;
+    int64_t qs[4], ks[4], vs[4];  /* element strides: batch, head, seq, dim */
+    double scale;
+    int causal;
+    const int64_t* rows;          /* sampled rows as (b, h, i) triples, or NULL */
+    double *O, *Omag, *lse;       /* outputs, dense [row][D] and [row] */
+    double* work;                 /* per-thread scratch of Sk doubles */
+    int64_t lo, hi;
+} attn_job_t;
+
+static void attn_row(const attn_job_t* J, int64_t b, int64_t h, int64_t i,
+                     double* o, double* omag, double* lse, double* s) {
+    const int64_t g = J->Hq / J->Hkv;
+    const int64_t hk = h / g;
+    const uint16_t* q = J->Q + b * J->qs[0] + h * J->qs[1] + i * J->qs[2];
+    const uint16_t* kb = J->K + b * J->ks[0] + hk * J->ks[1];
+    const uint16_t* vb = J->V + b * J->vs[0] + hk * J->vs[1];
+    int64_t nkeys = J->Sk;
+    if (J->causal) {
+        int64_t last = i + (J->Sk - J->Sq);  /* largest allowed key */
+        nkeys = last + 1 < J->Sk ? last + 1 : J->Sk;
+        if (nkeys < 0) nkeys = 0;
+    }
+    for (int64_t d = 0; d < J->D; ++d) {
+        o[d] = 0.0;
+        omag[d] = 0.0;
+    }
+    if (nkeys == 0) {
+        *lse = -INFINITY;
+        return;
+    }
+    double mx = -INFINITY;
+    for (int64_t j = 0; j < nkeys; ++j) {
+        const uint16_t* k = kb + j * J->ks[2];
+        double dot = 0.0;
+        for (int64_t d = 0; d < J->D; ++d)
+            dot += oracle_bf16_value(q[d * J->qs[3]]) * oracle_bf16_value(k[d * J->ks[3]]);
+        s[j] = J->scale * dot;
+        if (s[j] > mx || j == 0) mx = s[j];
+    }
+    double l = 0.0;
+    for (int64_t j = 0; j < nkeys; ++j) {
+        s[j] = exp(s[j] - mx);
+        l += s[j];
+    }
+    /* softmax(s) V = (sum_j e_j v(j)) / (sum_j e_j): sum, then divide once */
+    for (int64_t j = 0; j < nkeys; ++j) {
+        const uint16_t* v = vb + j * J->vs[2];
+        for (int64_t d = 0; d < J->D; ++d) {
+            double x = oracle_bf16_value(v[d * J->vs[3]]);
+            o[d] += s[j] * x;
+            omag[d] += s[j] * fabs(x);
+        }
+    }
+    for (int64_t d = 0; d < J->D; ++d) {
+        o[d] /= l;
+        omag[d] /= l;
+    }
+    *lse = mx + log(l);
+}
+
+static void* run_attn(void* p) {
+    attn_job_t* J = (attn_job_t*)p;
+    double* s = (double*)malloc(sizeof(double) * (size_t)(J->Sk > 0 ? J->Sk : 1));
+    if (!s) return NULL;
+    for (int64_t t = J->lo; t < J->hi; ++t) {
+        int64_t b, h, i;
+        if (J->rows) {
+            b = J->rows[3 * t];
+            h = J->rows[3 * t + 1];
+            i = J->rows[3 * t + 2];
+        } else {
+            i = t % J->Sq;
+            h = (t / J->Sq) % J->Hq;
+            b = t / (J->Sq * J->Hq);
+        }
+        attn_row(J, b, h, i, J->O + t * J->D, J->Omag + t * J->D, J->lse + t, s);
+    }
+    free(s);
+    return NULL;
+}
+
+static int run_attn_split(attn_job_t* proto, int64_t total, int nthreads) {
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    if ((int64_t)nthreads > total) nthreads = total > 0 ? (int)total : 1;
+    pthread_t th[256];
+    attn_job_t jobs[256];
+    int started = 0;
+    for (int t = 0; t < nthreads; ++t) {
+        jobs[t] = *proto;
+        jobs[t].lo = total * t / nthreads;
+        jobs[t].hi = total * (t + 1) / nthreads;
+    }
+    if (nthreads == 1) {
+        run_attn(&jobs[0]);
+        return 0;
+    }
+    for (int t = 0; t < nthreads; ++t) {
+        if (pthread_create(&th[t], NULL, run_attn, &jobs[t]) != 0) {
+            for (int u = t; u < nthreads; ++u) run_attn(&jobs[u]);
+            break;
+        }
+        ++started;
+    }
+    for (int t = 0; t < started; ++t) pthread_join(th[t], NULL);
+    return 0;
+}
+
+static int attn_setup(attn_job_t* J, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Sk,
+                      int64_t D, const uint16_t* Q, const int64_t* qs, const uint16_t* K,
+                      const int64_t* ks, const uint16_t* V, const int64_t* vs, double scale,
+                      int causal) {
+    if (B < 0 || Hq < 1 || Hkv < 1 || Sq < 0 || Sk < 0 || D < 1 || Hq % Hkv != 0) return -1;
+    memset(J, 0, sizeof *J);
+    J->Hq = Hq;
+    J->Hkv = Hkv;
+    J->Sq = Sq;
+    J->Sk = Sk;
+    J->D = D;
+    J->Q = Q;
+    J->K = K;
+    J->V = V;
+    for (int t = 0; t < 4; ++t) {
+        J->qs[t] = qs[t];
+        J->ks[t] = ks[t];
+        J->vs[t] = vs[t];
+    }
+    J->scale = scale;
+    J->causal = causal ? 1 : 0;
+    return 0;
+}
+
+/* Attention forward over every row.  Q is [B][Hq][Sq][D], K and V are
+ * [B][Hkv][Sk][D] (bf16 bits), addressed through the element strides
+ * qs/ks/vs = (batch, head, seq, dim).  O and Omag are dense binary64
+ * [B][Hq][Sq][D]; lse is dense [B][Hq][Sq].  Returns 0, or -1 on bad sizes
+ * (Hq not a multiple of Hkv included). */
+int oracle_attention_fwd(int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Sk, int64_t D,
+                         const uint16_t* Q, const int64_t* qs, const uint16_t* K,
+                         const int64_t* ks, const uint16_t* V, const int64_t* vs,
+                         double scale, int causal, double* O, double* Omag, double* lse,
+                         int nthreads) {
+    attn_job_t J;
+    if (attn_setup(&J, B, Hq, Hkv, Sq, Sk, D, Q, qs, K, ks, V, vs, scale, causal)) return -1;
+    J.O = O;
+    J.Omag = Omag;
+    J.lse = lse;
+    return run_attn_split(&J, B * Hq * Sq, nthreads);
+}
+
+/* The same for a sample of rows: rows holds n triples (b, h, i); row t of
+ * the dense outputs O/Omag [n][D] and lse [n] belongs to triple t. */
+int oracle_attention_fwd_at(int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Sk, int64_t D,
+                            const uint16_t* Q, const int64_t* qs, const uint16_t* K,
+                            const int64_t* ks, const uint16_t* V, const int64_t* vs,
+                            double scale, int causal, const int64_t* rows, int64_t n,
+                            double* O, double* Omag, double* lse, int nthreads) {
+    attn_job_t J;
+    if (attn_setup(&J, B, Hq, Hkv, Sq, Sk, D, Q, qs, K, ks, V, vs, scale, causal)) return -1;
+    for (int64_t t = 0; t < n; ++t)
+        if (rows[3 * t] < 0 || rows[3 * t] >= B || rows[3 * t + 1] < 0 || rows[3 * t + 1] >= Hq ||
+            rows[3 * t + 2] < 0 || rows[3 * t + 2] >= Sq)
+            return -1;
+    J.rows = rows;
+    J.O = O;
+    J.Omag = Omag;
+    J.lse = lse;
+    return run_attn_split(&J, n, nthreads);
+}

@@ -372,3 +372,9 @@ ALL_PINS = [
     pin_bf16_freivalds, pin_bf16_strided_views, pin_bf16_special_values,
     pin_mx_bruteforce, pin_mx_unit_scales, pin_mx_scale_algebra, pin_mx_integer_exact, pin_mx_nan,
 ]
+
+
+# the attention oracle's pins (part IV of the MLSys book summary) run with these
+from tests.oracle_attn_pins import ATTN_PINS  # noqa: E402
+
+ALL_PINS = ALL_PINS + ATTN_PINS

@@ -38,6 +38,22 @@ MUTATIONS = {
     "ledger_stages_fixed": ("int64_t smem = stages * hbm;", "int64_t smem = 2 * hbm;"),
     "ledger_flops_single": ("int64_t flops = 2 * m * n * k;", "int64_t flops = m * n * k;"),
     "ledger_fits_strict": ("out[3] = smem <= smem_limit ? 1 : 0;", "out[3] = smem < smem_limit ? 1 : 0;"),
+    # attention (part IV of the MLSys book summary)
+    "attn_scale_dropped": ("s[j] = J->scale * dot;", "s[j] = dot;"),
+    "attn_causal_top_left": ("int64_t last = i + (J->Sk - J->Sq);", "int64_t last = i;"),
+    "attn_causal_strict": ("nkeys = last + 1 < J->Sk ? last + 1 : J->Sk;",
+                           "nkeys = last < J->Sk ? last : J->Sk;"),
+    "attn_no_max_shift": ("s[j] = exp(s[j] - mx);", "s[j] = exp(s[j]);"),
+    "attn_gqa_modulo": ("const int64_t hk = h / g;", "const int64_t hk = h % J->Hkv;"),
+    "attn_v_from_k": ("const uint16_t* v = vb + j * J->vs[2];", "const uint16_t* v = kb + j * J->ks[2];"),
+    "attn_lse_no_log": ("*lse = mx + log(l);", "*lse = mx + l;"),
+    "attn_not_normalised": ("        o[d] /= l;\n", ""),
+    "attn_omag_signed": ("omag[d] += s[j] * fabs(x);", "omag[d] += s[j] * x;"),
+    "attn_dim_stride_lost": ("oracle_bf16_value(q[d * J->qs[3]])", "oracle_bf16_value(q[d])"),
+    "attn_dropped_last_d": ("for (int64_t d = 0; d < J->D; ++d)\n            dot +=",
+                            "for (int64_t d = 0; d + 1 < J->D; ++d)\n            dot +="),
+    "attn_first_key_dropped": ("o[d] += s[j] * x;", "o[d] += j ? s[j] * x : 0.0;"),
+    "attn_empty_rows_nan": ("    if (nkeys == 0) {\n        *lse = -INFINITY;\n        return;\n    }\n", ""),
 }
 
 
