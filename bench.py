@@ -34,6 +34,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "GEMM TFLOP/s at 8192³ bf16 + % of MI355X dense MFMA peak (1 GPU)"
+HEADLINE = "square8192_nt"
 PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}   # MI355X dense MFMA
 PEAK_HBM_GBS = 8000.0
 
@@ -43,7 +44,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="square8192_nt")
+    ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--all", action="store_true", help="also print one line per other workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=1024,
@@ -157,6 +158,8 @@ def bench_workload(name: str, steps: int, warmup: int, settle: float = 0.0):
     from dense_gemm_mxfp8_amd import inputs
 
     dev = torch.device("cuda:0")
+    if name in inputs.ATTN_WORKLOADS:
+        return bench_attention(name, steps, warmup, settle)
     w = inputs.WORKLOADS[name]
     prob = inputs.workload(name, seed=0)
     M, N, K = prob.M, prob.N, prob.K
@@ -208,6 +211,21 @@ def bench_workload(name: str, steps: int, warmup: int, settle: float = 0.0):
                     raise RuntimeError(dg.gemm_strerror(rc))
         dtype, peak_key = "bf16", "bf16"
 
+    timing = time_steps(step, stream, steps, warmup, settle)
+    flops = 2.0 * M * N * K
+    config = {"workload": name, "M": M, "N": N, "K": K,
+              "layout": ("NT" if getattr(prob, "b_colmajor", True) else "NN"), "dist": w.get("dist"),
+              "seed": 0, "output": "fp32", "parallelism": "single-gpu",
+              **({"splitk_ranges": splits} if splits > 1 else {})}
+    res = {"workload": name, "dtype": dtype, "peak_key": peak_key, "flops": flops, "bytes": bytes_per_step,
+           "operand_copies": copies, "config": config, **timing}
+    res["tflops"] = flops / (res["ms_per_step"] * 1e-3) / 1e12
+    return res, prob
+
+
+def time_steps(step, stream, steps: int, warmup: int, settle: float):
+    """Settle, warm up and time `steps` launches of step(i) on `stream`."""
+    import torch
     # The clocks ramp up from idle over the first tens of milliseconds of
     # work; settle steps bring them to their loaded state before the warm-up.
     settle_steps = 0
@@ -246,20 +264,60 @@ def bench_workload(name: str, steps: int, warmup: int, settle: float = 0.0):
         ends[i].record(stream)
     torch.cuda.synchronize()
     per = np.array([a.elapsed_time(b) for a, b in zip(starts, ends)])  # ms per launch
-    flops = 2.0 * M * N * K
     ms_step = wall * 1e3 / steps
-    res = {
-        "workload": name, "M": M, "N": N, "K": K, "dtype": dtype, "peak_key": peak_key,
-        "flops": flops, "bytes": bytes_per_step, "ms_per_step": ms_step,
-        "kernel_ms_mean": float(mean_ms), "kernel_ms_median": float(np.median(per)), "single_launches": nd,
-        "kernel_ms_p10": float(np.percentile(per, 10)),
-        "kernel_ms_p90": float(np.percentile(per, 90)),
-        "tflops": flops / (ms_step * 1e-3) / 1e12,
-        "layout": ("NT" if getattr(prob, "b_colmajor", True) else "NN"),
-        "dist": w.get("dist"), "operand_copies": copies, "splitk": splits,
-        "settle_s": round(settle, 3), "settle_steps": settle_steps, "clocks": clocks.summary(),
-    }
-    return res, prob
+    return {"ms_per_step": ms_step, "kernel_ms_mean": float(mean_ms),
+            "kernel_ms_median": float(np.median(per)), "single_launches": nd,
+            "kernel_ms_p10": float(np.percentile(per, 10)), "kernel_ms_p90": float(np.percentile(per, 90)),
+            "settle_s": round(settle, 3), "settle_steps": settle_steps, "clocks": clocks.summary()}
+
+
+def attention_pairs(p) -> int:
+    """(query, key) pairs the softmax covers, summed over batch and heads."""
+    if not p.causal:
+        return p.B * p.Hq * p.Sq * p.Sk
+    off = p.Sk - p.Sq
+    per_head = sum(min(p.Sk, max(0, i + off + 1)) for i in range(p.Sq))
+    return p.B * p.Hq * per_head
+
+
+def attention_flops(p) -> float:
+    """Two products of 2 FLOPs per multiply-add over head_dim per visible pair."""
+    return 4.0 * p.D * attention_pairs(p)
+
+
+def attention_bytes(p) -> int:
+    """Q, K, V read once (bf16), O (fp32) and lse written once."""
+    return 2 * (p.B * p.Hq * p.Sq * p.D + 2 * p.B * p.Hkv * p.Sk * p.D) + 4 * p.B * p.Hq * p.Sq * (p.D + 1)
+
+
+def bench_attention(name: str, steps: int, warmup: int, settle: float):
+    import torch
+    import dense_gemm_mxfp8_amd as dg
+    from dense_gemm_mxfp8_amd import inputs
+
+    dev = torch.device("cuda:0")
+    p = inputs.workload(name, seed=0)
+    stream = torch.cuda.current_stream(dev)
+    s = stream.cuda_stream
+    Q, K, V = p.Q.to(dev), p.K.to(dev), p.V.to(dev)
+    O = torch.empty((p.B, p.Hq, p.Sq, p.D), dtype=torch.float32, device=dev)
+    L = torch.empty((p.B, p.Hq, p.Sq), dtype=torch.float32, device=dev)
+
+    def step(i):
+        rc = dg.attn_fwd_bf16(p.B, p.Hq, p.Hkv, p.Sq, p.Sk, p.D, Q.data_ptr(), None, K.data_ptr(), None,
+                              V.data_ptr(), None, O.data_ptr(), None, L.data_ptr(), p.scale, p.causal, s)
+        if rc:
+            raise RuntimeError(dg.gemm_strerror(rc))
+
+    timing = time_steps(step, stream, steps, warmup, settle)
+    flops = attention_flops(p)
+    config = {"workload": name, "batch": p.B, "heads_q": p.Hq, "heads_kv": p.Hkv, "seq_q": p.Sq,
+              "seq_k": p.Sk, "head_dim": p.D, "causal": p.causal, "layout": "BHSD", "dist": "normal",
+              "seed": 0, "output": "fp32 O + fp32 lse", "parallelism": "single-gpu"}
+    res = {"workload": name, "dtype": "bf16", "peak_key": "bf16", "flops": flops, "bytes": attention_bytes(p),
+           "operand_copies": 1, "config": config, **timing}
+    res["tflops"] = flops / (res["ms_per_step"] * 1e-3) / 1e12
+    return res, p
 
 
 def cpu_baseline(prob, rows: int, single_rows: int = 32):
@@ -293,6 +351,28 @@ def cpu_baseline(prob, rows: int, single_rows: int = 32):
                             "sample": f"rows 0..{n1 - 1} ({n1}x{prob.N}x{prob.K}), {dt1:.2f} s wall"}}
 
 
+def cpu_baseline_attention(p, rows: int = 65536):
+    """The attention oracle, untouched, on the first `rows` query rows of head
+    (0, 0) onward (all the host threads it uses), scaled by the rows' own
+    algorithmic FLOPs."""
+    import torch
+    import oracle
+    bits = lambda t: t.contiguous().view(torch.int16).numpy().view(np.uint16)
+    n = min(rows, p.B * p.Hq * p.Sq)
+    idx = np.arange(n)
+    sel = np.stack([idx // (p.Hq * p.Sq), (idx // p.Sq) % p.Hq, idx % p.Sq], axis=1).astype(np.int64)
+    Qb, Kb, Vb = bits(p.Q), bits(p.K), bits(p.V)
+    t0 = time.perf_counter()
+    oracle.attention_fwd_at(Qb, Kb, Vb, p.scale, p.causal, sel)
+    dt = time.perf_counter() - t0
+    off = p.Sk - p.Sq
+    pairs = sum(min(p.Sk, max(0, int(i) + off + 1)) if p.causal else p.Sk for i in sel[:, 2])
+    cores = oracle.default_threads()
+    return {"value": 4.0 * p.D * pairs / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"query rows 0..{n - 1} in (batch, head, row) order ({pairs} query-key pairs), "
+                      f"{dt:.2f} s wall"}
+
+
 def measured_traffic(workload: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary of
     this workload, or None if there is none or the kernels changed since."""
@@ -313,16 +393,14 @@ def line(res, steps, warmup, cpu=None, headline=True):
     else:
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic}
+    kind = "attention forward" if "heads_q" in res["config"] else "GEMM"
     out = {
-        "metric": METRIC if headline else f"GEMM TFLOP/s ({res['workload']})",
+        "metric": METRIC if headline else f"{kind} TFLOP/s ({res['workload']})",
         "value": round(res["tflops"], 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": steps,
         "warmup": warmup, "ms_per_step": round(res["ms_per_step"], 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": res["dtype"], "data": "synthetic",
-        "config": {"workload": res["workload"], "M": res["M"], "N": res["N"], "K": res["K"],
-                   "layout": res["layout"], "dist": res["dist"], "seed": 0,
-                   "output": "fp32", "parallelism": "single-gpu",
-                   **({"splitk_ranges": res["splitk"]} if res.get("splitk", 1) > 1 else {})},
+        "config": res["config"],
         "kernel_ms": {"mean": round(res["kernel_ms_mean"], 5),
                       "median": round(res["kernel_ms_median"], 5),
                       "p10": round(res["kernel_ms_p10"], 5), "p90": round(res["kernel_ms_p90"], 5),
@@ -356,7 +434,8 @@ def main():
     names = [args.workload]
     if args.all:
         from dense_gemm_mxfp8_amd.inputs import WORKLOADS
-        names += [n for n in WORKLOADS if n != args.workload]
+        from dense_gemm_mxfp8_amd.inputs import ATTN_WORKLOADS
+        names += [n for n in list(WORKLOADS) + list(ATTN_WORKLOADS) if n != args.workload]
     for i, name in enumerate(names):
         print(f"[bench] {name}: warmup {args.warmup}, steps {args.steps}", file=sys.stderr,
               flush=True)
@@ -364,8 +443,11 @@ def main():
         cpu = None
         if i == 0 and not args.no_cpu_baseline:
             print(f"[bench] oracle on {args.cpu_rows} rows", file=sys.stderr, flush=True)
-            cpu = cpu_baseline(prob, args.cpu_rows)
-        print(json.dumps(line(res, args.steps, args.warmup, cpu, headline=(i == 0))), flush=True)
+            if name.startswith("attn"):
+                cpu = cpu_baseline_attention(prob)
+            else:
+                cpu = cpu_baseline(prob, args.cpu_rows)
+        print(json.dumps(line(res, args.steps, args.warmup, cpu, headline=(name == HEADLINE))), flush=True)
         del prob
         torch.cuda.empty_cache()
 

@@ -4,10 +4,11 @@ The binding only marshals arguments: every step of the product runs in the
 HIP kernels of ``libgemm.so``.  PyTorch provides device memory and the current
 stream.  If the library is missing the calls raise; there is no fallback.
 
-Raw entry points mirror the C ABI of include/libgemm.h one to one
-(``gemm_bf16``, ``gemm_bf16_nt``, ``gemm_mxfp8``, ``gemm_strerror``,
-``gemm_version``) and take integers for pointers and the stream.  The tensor
-helpers ``bf16`` and ``mxfp8`` build those arguments from torch tensors.
+Raw entry points mirror the C ABI of include/libgemm.h and
+include/attention.h one to one (``gemm_bf16``, ``gemm_bf16_nt``,
+``gemm_mxfp8``, ..., ``attn_fwd_bf16``, ``gemm_strerror``, ``gemm_version``)
+and take integers for pointers and the stream.  The tensor helpers ``bf16``,
+``mxfp8`` and ``attention`` build those arguments from torch tensors.
 """
 from __future__ import annotations
 
@@ -60,6 +61,8 @@ def library() -> ctypes.CDLL:
         lib.gemm_bf16_dynamic.restype = ctypes.c_int
         lib.gemm_bf16_dynamic.argtypes = [_i64, _i64, _i64, _vp, _i64, _vp, _i64, ctypes.c_int, _vp, _i64, _vp,
                                           ctypes.c_size_t, _vp]
+        lib.attn_fwd_bf16.restype = ctypes.c_int
+        lib.attn_fwd_bf16.argtypes = [_i64] * 6 + [_vp, _vp] * 4 + [_vp, ctypes.c_float, ctypes.c_int, _vp]
         lib.gemm_strerror.restype = ctypes.c_char_p
         lib.gemm_strerror.argtypes = [ctypes.c_int]
         lib.gemm_version.restype = ctypes.c_int
@@ -112,6 +115,20 @@ def gemm_bf16_splitk_plan(M, N, K, b_colmajor, splits=0, cus=0):
 def gemm_bf16_dynamic(M, N, K, A, lda, B, ldb, b_colmajor, C, ldc, workspace, workspace_bytes, stream) -> int:
     return library().gemm_bf16_dynamic(M, N, K, A, lda, B, ldb, int(b_colmajor), C, ldc, workspace,
                                        workspace_bytes, stream)
+
+
+def attn_fwd_bf16(batch, heads_q, heads_kv, seq_q, seq_k, head_dim, Q, q_strides, K, k_strides, V,
+                  v_strides, O, o_strides, lse, scale, causal, stream) -> int:
+    """Strides: None (dense [B][H][S][D]) or a sequence of 3 element strides
+    (batch, head, sequence), passed to the library as a host int64 array."""
+    def arr(s):
+        if s is None:
+            return None
+        a = (ctypes.c_int64 * 3)(*[int(x) for x in s])
+        return ctypes.cast(a, _vp)
+    qa, ka, va, oa = (arr(s) for s in (q_strides, k_strides, v_strides, o_strides))
+    return library().attn_fwd_bf16(batch, heads_q, heads_kv, seq_q, seq_k, head_dim, Q, qa, K, ka, V, va, O,
+                                   oa, lse, float(scale), int(bool(causal)), stream)
 
 
 def gemm_strerror(code: int) -> str:
@@ -262,3 +279,36 @@ def mxfp8(A, SA, B, SB, out=None, *, out_dtype=None, row_scale=None, col_scale=N
         _check(gemm_mxfp8(M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, SA.data_ptr(),
                           SB.data_ptr(), C.data_ptr(), ldc, _stream(A.device)))
     return C
+
+
+def attention(Q, K, V, *, causal=False, scale=None, out=None, lse=False):
+    """Fused attention forward (``attn_fwd_bf16``) of bf16 CUDA tensors.
+
+    Q: (B, Hq, Sq, D); K, V: (B, Hkv, Sk, D), Hq a multiple of Hkv, D 64 or
+    128, any strides with a contiguous last dimension (so [B][S][H][D]
+    storage viewed as (B, H, S, D) works).  Returns the fp32 output
+    (B, Hq, Sq, D), and with lse=True also the fp32 log-sum-exp (B, Hq, Sq).
+    scale defaults to 1/sqrt(D)."""
+    import math
+    import torch
+    for t, name in ((Q, "Q"), (K, "K"), (V, "V")):
+        if t.dtype != torch.bfloat16 or t.dim() != 4:
+            raise TypeError(f"{name} must be a 4-D bfloat16 tensor")
+        if t.shape[3] > 1 and t.stride(3) != 1:
+            raise ValueError(f"{name} needs a contiguous last dimension")
+    B, Hq, Sq, D = Q.shape
+    Hkv, Sk = K.shape[1], K.shape[2]
+    if K.shape != V.shape or K.shape[0] != B or K.shape[3] != D:
+        raise ValueError("K and V must be (B, Hkv, Sk, D) with Q's B and D")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((B, Hq, Sq, D), dtype=torch.float32, device=Q.device)
+    elif out.shape != (B, Hq, Sq, D) or out.dtype != torch.float32 or (D > 1 and out.stride(3) != 1):
+        raise ValueError("out must be a float32 (B, Hq, Sq, D) tensor with a contiguous last dimension")
+    L = torch.empty((B, Hq, Sq), dtype=torch.float32, device=Q.device) if lse else None
+    st = lambda t: (t.stride(0), t.stride(1), t.stride(2))
+    _check(attn_fwd_bf16(B, Hq, Hkv, Sq, Sk, D, Q.data_ptr(), st(Q), K.data_ptr(), st(K), V.data_ptr(), st(V),
+                         out.data_ptr(), st(out), L.data_ptr() if lse else None, scale, causal,
+                         _stream(Q.device)))
+    return (out, L) if lse else out

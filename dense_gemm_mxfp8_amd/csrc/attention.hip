@@ -1,0 +1,471 @@
+// attention.hip -- fused attention forward for gfx950 and its C ABI
+// (include/attention.h).
+//
+// "Modern GPU Programming For MLSys - 书籍总结", part IV (5.1-5.3): attention
+// is two matrix products with a softmax between them; the running maximum of
+// each row changes as key blocks arrive, so the partial output is rescaled
+// before the next value product adds to it; causal masking and grouped-query
+// heads are part of the kernel.  The pages build it for Blackwell (TMEM
+// accumulators, warp roles); here it is one gfx950 workgroup per block of
+// 128 query rows of one head, four waves of 32 rows each, streaming blocks of
+// 64 keys through LDS:
+//
+//   * scores are computed transposed, S^T = K Q^T, with
+//     v_mfma_f32_32x32x16_bf16: K rows come from LDS as the A operand and the
+//     wave's 32 query rows stay in registers as the B operand for the whole
+//     kernel.  Accumulator register r of lane l then holds one query
+//     (l % 32) and key row 8 (r/4) + 4 (l/32) + r % 4 of the 32-key tile.
+//   * the K rows are fed to the MFMA in a permuted order (bits 2 and 3 of the
+//     row index swapped), so that register r of lane l holds key
+//     16 (r/8) + 8 (l/32) + r % 8: registers 8u .. 8u+7 are then exactly the
+//     8 consecutive keys the B operand of a 16-key MFMA step wants from that
+//     lane.  The probabilities go from the score accumulators into the value
+//     product as bf16 with no data movement between lanes.
+//   * the value product is computed transposed too, O^T = V^T P^T: V^T
+//     fragments are read from the row-major V tile with ds_read_b64_tr_b16,
+//     and the O accumulators keep the query in the lane, like the softmax
+//     state (running max, running sum), so rescaling O is a multiply by a
+//     per-lane scalar.  Rescaling is skipped when no row's maximum moved
+//     (the factor is then exactly 1).
+//   * the two halves of the wave hold different keys of the same query; the
+//     row maximum is combined across them with a cross-lane exchange, and the
+//     row sums are kept per lane and combined once at the end.
+//   * K/V tiles are double-buffered: the 16-byte buffer loads of block t+1
+//     are issued before block t is multiplied, and written to the other LDS
+//     buffer after it; one barrier per block.  Rows past seq_k lie outside
+//     the tile's buffer descriptor and load as zero (and are masked).
+//   * LDS rows are XOR-swizzled in 16-byte chunks so that both the K
+//     fragment reads (16 rows, one chunk) and the transposing V reads
+//     (4 rows x 4 chunks per 32 lanes) hit distinct banks.
+//   * two workgroups per CU: while one wave runs its softmax (VALU), the
+//     other wave on the SIMD keeps the matrix core busy.
+//   * workgroup ids are remapped so that the query blocks of one head run on
+//     one XCD and share its L2; for causal masks the blocks with the most
+//     keys start first.
+
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <mutex>
+#include <stdint.h>
+#include <string.h>
+
+#include "attention.h"
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+#define ALDS __attribute__((address_space(3)))
+
+constexpr int kThreads = 256;  // 4 waves
+constexpr int kQW = 32;        // query rows per wave
+constexpr int kQB = 128;       // query rows per workgroup
+constexpr int kKB = 64;        // keys per block
+constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
+
+struct Params {
+    const uint8_t* Q;
+    const uint8_t* K;
+    const uint8_t* V;
+    float* O;
+    float* lse;
+    int64_t q_b, q_h, k_b, k_h, v_b, v_h, o_b, o_h;  // batch / head strides, elements
+    int q_s, k_s, v_s, o_s;                          // sequence strides, elements
+    int Hq, group, Sq, Sk, qblocks, off;             // off = Sk - Sq
+    float c;      // scale * log2(e)
+    float scale;
+    int xcd_remap;
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+    int n = bytes > 0x7fffffff ? 0x7fffffff : (bytes < 0 ? 0 : (int)bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, kRsrcWord3);
+}
+
+// Chunk swizzles (16-byte chunks, rows of 2 D bytes).
+template <int D>
+__device__ __forceinline__ int kswz(int row) {
+    if constexpr (D == 128) return row & 15;
+    else return (row >> 1) & 7;
+}
+template <int D>
+__device__ __forceinline__ int vswz(int row) {
+    if constexpr (D == 128) return (row & 3) << 2;
+    else return ((row >> 1) & 1) << 2;
+}
+
+// K row fed to MFMA A-row m: bits 2 and 3 of m swapped.
+__device__ __forceinline__ int perm_row(int m) {
+    return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
+}
+
+// The value of the lane 32 away (the other half of the wave holds the other
+// keys of the same query).  Both halves combine (own, partner) with a
+// symmetric operation, so they end with the same result.
+__device__ __forceinline__ float partner(float x) { return __shfl_xor(x, 32); }
+__device__ __forceinline__ float half_max(float x) { return fmaxf(x, partner(x)); }
+__device__ __forceinline__ float half_sum(float x) { return x + partner(x); }
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(Params p) {
+    constexpr int RB = 2 * D;                  // bytes per LDS row
+    constexpr int NCH = D / 8;                 // 16-byte chunks per row
+    constexpr int KT = kKB * RB;               // bytes of one K or V tile
+    constexpr int DS = D / 16;                 // MFMA steps over d
+    constexpr int DT = D / 32;                 // 32-row d tiles of O^T
+    constexpr int RPP = kThreads / NCH;        // tile rows per load pass
+    constexpr int LPT = kKB / RPP;             // 16-byte loads per thread per tensor
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2][2][KT];
+
+    // ---- (batch, head, query block) of this workgroup
+    int bid = blockIdx.x;
+    if (p.xcd_remap) bid = (bid & 7) * (int)(gridDim.x >> 3) + (bid >> 3);
+    const int bh = bid / p.qblocks;
+    const int qb = p.qblocks - 1 - (bid - bh * p.qblocks);
+    const int b = bh / p.Hq;
+    const int h = bh - b * p.Hq;
+    const int hk = h / p.group;
+    const int q0 = qb * kQB;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31;
+    const int hh = lane >> 5;
+    const int qw0 = q0 + wave * kQW;   // first query row of this wave
+    const int myq = qw0 + l32;         // this lane's query row
+
+    // keys any row of the workgroup / of this wave can see
+    int kend = p.Sk, wend = p.Sk;
+    if constexpr (CAUSAL) {
+        const int qlast = min(q0 + kQB, p.Sq);
+        kend = min(p.Sk, qlast + p.off);
+        wend = min(p.Sk, min(qw0 + kQW, p.Sq) + p.off);
+    }
+    const int nt = kend > 0 ? (kend + kKB - 1) / kKB : 0;
+    const bool wave_rows = qw0 < p.Sq;
+
+    const uint8_t* qbase = p.Q + 2 * (b * p.q_b + h * p.q_h);
+    const uint8_t* kbase = p.K + 2 * (b * p.k_b + hk * p.k_h);
+    const uint8_t* vbase = p.V + 2 * (b * p.v_b + hk * p.v_h);
+    const int64_t qbytes = p.Sq > 0 ? 2 * ((int64_t)(p.Sq - 1) * p.q_s + D) : 0;
+    const int64_t kbytes = p.Sk > 0 ? 2 * ((int64_t)(p.Sk - 1) * p.k_s + D) : 0;
+    const int64_t vbytes = p.Sk > 0 ? 2 * ((int64_t)(p.Sk - 1) * p.v_s + D) : 0;
+
+    // ---- this wave's query rows, resident as the B operand of S^T = K Q^T
+    bf16x8 qf[DS];
+    {
+        const auto rq = make_rsrc(qbase, qbytes);
+        const int voff = myq * p.q_s * 2 + 16 * hh;
+#pragma unroll
+        for (int s = 0; s < DS; ++s)
+            qf[s] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rq, voff + 32 * s, 0, 0));
+    }
+
+    // ---- per-thread constants of the tile loads and LDS writes
+    const int ld_row = tid / NCH;      // + RPP * i
+    const int ld_ch = tid % NCH;
+    const int k_voff = ld_row * p.k_s * 2 + 16 * ld_ch;
+    const int v_voff = ld_row * p.v_s * 2 + 16 * ld_ch;
+    const int k_wr = ld_row * RB + ((ld_ch ^ kswz<D>(ld_row)) << 4);
+    const int v_wr = ld_row * RB + ((ld_ch ^ vswz<D>(ld_row)) << 4);
+    const int k_rstep = RPP * p.k_s * 2;
+    const int v_rstep = RPP * p.v_s * 2;
+
+    // ---- per-lane constants of the fragment reads
+    // K: A-row m = l32 reads key row perm_row(l32) (+32 for the second tile),
+    // 16-byte chunk 2 s + hh at step s
+    int k_rd[DS];
+    {
+        const int r = perm_row(l32);
+#pragma unroll
+        for (int s = 0; s < DS; ++s) k_rd[s] = r * RB + (((2 * s + hh) ^ kswz<D>(r)) << 4);
+    }
+    // V^T: ds_read_b64_tr_b16 groups of 16 lanes read 4 key rows x 16 d
+    int v_rd[DT];
+    {
+        const int g = lane >> 4, li = lane & 15;
+        const int row = 8 * (g >> 1) + (li >> 2);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            const int d = 32 * dt + 16 * (g & 1) + 4 * (li & 3);
+            v_rd[dt] = row * RB + ((((d >> 3)) ^ vswz<D>(row)) << 4) + ((d & 7) << 1);
+        }
+    }
+
+    i32x4 kreg[LPT], vreg[LPT];
+    auto issue_loads = [&](int t) {
+        const int64_t kofs = (int64_t)t * kKB * p.k_s * 2;
+        const int64_t vofs = (int64_t)t * kKB * p.v_s * 2;
+        const auto rk = make_rsrc(kbase + kofs, kbytes - kofs);
+        const auto rv = make_rsrc(vbase + vofs, vbytes - vofs);
+#pragma unroll
+        for (int i = 0; i < LPT; ++i) {
+            kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, k_voff + i * k_rstep, 0, 0);
+            vreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, v_voff + i * v_rstep, 0, 0);
+        }
+    };
+    auto write_tile = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < LPT; ++i) {
+            *(i32x4 ALDS*)(&lds[buf][0][0] + k_wr + i * RPP * RB) = kreg[i];
+            *(i32x4 ALDS*)(&lds[buf][1][0] + v_wr + i * RPP * RB) = vreg[i];
+        }
+    };
+
+    f32x16 oacc[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+        for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.0f;
+    float m_run = -INFINITY;  // running max of the raw scores q.k of this lane's row
+    float l_run = 0.0f;       // this lane's part of the running sum
+
+    if (nt > 0) {
+        issue_loads(0);
+        write_tile(0);
+    }
+    __syncthreads();
+
+    for (int t = 0; t < nt; ++t) {
+        const int buf = t & 1;
+        const int k0 = t * kKB;
+        if (t + 1 < nt) issue_loads(t + 1);
+
+        if (wave_rows && k0 < wend) {
+            const uint8_t ALDS* kt = (const uint8_t ALDS*)&lds[buf][0][0];
+            const uint8_t ALDS* vt = (const uint8_t ALDS*)&lds[buf][1][0];
+            // ---- S^T = K Q^T over the 64 keys (two 32-key tiles)
+            f32x16 sacc[2];
+#pragma unroll
+            for (int st = 0; st < 2; ++st)
+                for (int r = 0; r < 16; ++r) sacc[st][r] = 0.0f;
+#pragma unroll
+            for (int s = 0; s < DS; ++s) {
+#pragma unroll
+                for (int st = 0; st < 2; ++st) {
+                    const bf16x8 kf = *(const bf16x8 ALDS*)(kt + k_rd[s] + st * 32 * RB);
+                    sacc[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc[st], 0, 0, 0);
+                }
+            }
+            // ---- mask: keys past seq_k, and (causal) keys after the row's limit
+            const bool need_mask = (k0 + kKB > p.Sk) || (CAUSAL && k0 + kKB - 1 > qw0 + p.off);
+            if (need_mask) {
+                const int lim = CAUSAL ? min(p.Sk - 1, myq + p.off) : p.Sk - 1;
+#pragma unroll
+                for (int st = 0; st < 2; ++st)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int key = k0 + 32 * st + 16 * (r >> 3) + 8 * hh + (r & 7);
+                        if (key > lim) sacc[st][r] = -INFINITY;
+                    }
+            }
+            // ---- online softmax (running max, rescale)
+            float mx = sacc[0][0];
+#pragma unroll
+            for (int st = 0; st < 2; ++st)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[st][r]);
+            mx = half_max(mx);
+            const float m_new = fmaxf(m_run, mx);
+            const float alpha = (m_run == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f((m_run - m_new) * p.c);
+            const float mc = (m_new == -INFINITY) ? 0.0f : m_new * p.c;
+            m_run = m_new;
+            float psum = 0.0f;
+#pragma unroll
+            for (int st = 0; st < 2; ++st)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[st][r], p.c, -mc));
+                    sacc[st][r] = e;
+                    psum += e;
+                }
+            l_run = l_run * alpha + psum;
+            if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+            }
+            // ---- O^T += V^T P^T, 16 keys per MFMA step
+#pragma unroll
+            for (int st = 0; st < 2; ++st) {
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    bf16x8 pf;
+#pragma unroll
+                    for (int x = 0; x < 8; ++x) pf[x] = (__bf16)sacc[st][8 * u + x];
+                    const int krow = 32 * st + 16 * u;
+#pragma unroll
+                    for (int dt = 0; dt < DT; ++dt) {
+                        const uint8_t ALDS* pv = vt + v_rd[dt] + krow * RB;
+                        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((bf16x4 ALDS*)pv);
+                        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((bf16x4 ALDS*)(pv + 4 * RB));
+                        const bf16x8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, oacc[dt], 0, 0, 0);
+                    }
+                }
+            }
+        }
+
+        if (t + 1 < nt) write_tile(buf ^ 1);
+        __syncthreads();
+    }
+
+    // ---- normalise and store
+    if (!wave_rows) return;
+    const float l_tot = half_sum(l_run);
+    if (myq < p.Sq) {
+        float* orow = p.O + (b * p.o_b + h * p.o_h) + (int64_t)myq * p.o_s;
+        // no visible key: every weight was 0 (a visible row has one weight of exactly 1)
+        const bool empty = l_tot == 0.0f;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                f32x4 v;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) v[j] = empty ? 0.0f : oacc[dt][4 * i + j] / l_tot;
+                *(f32x4*)(orow + 32 * dt + 8 * i + 4 * hh) = v;
+            }
+        if (p.lse && hh == 0)
+            p.lse[((int64_t)b * p.Hq + h) * p.Sq + myq] = empty ? -INFINITY : m_run * p.scale + logf(l_tot);
+    }
+}
+
+struct DeviceInfo {
+    int checked;
+    int supported;
+};
+
+constexpr int kMaxDevices = 64;
+DeviceInfo g_devices[kMaxDevices];
+std::mutex g_devices_mutex;
+
+int device_supported() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return GEMM_ERR_UNSUPPORTED;
+    }
+    std::lock_guard<std::mutex> lock(g_devices_mutex);
+    DeviceInfo& d = g_devices[dev];
+    if (!d.checked) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+            (void)hipGetLastError();
+            return GEMM_ERR_UNSUPPORTED;
+        }
+        d.supported = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+        d.checked = 1;
+    }
+    return d.supported ? GEMM_OK : GEMM_ERR_UNSUPPORTED;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (((uintptr_t)p) & (a - 1)) == 0; }
+
+// Strides (batch, head, seq) of a tensor, defaulting to dense [B][H][S][D].
+void strides_of(const int64_t* given, int64_t H, int64_t S, int64_t D, int64_t out[3]) {
+    if (given) {
+        out[0] = given[0];
+        out[1] = given[1];
+        out[2] = given[2];
+    } else {
+        out[2] = D;
+        out[1] = S * D;
+        out[0] = H * S * D;
+    }
+}
+
+bool strides_ok(const int64_t s[3], int64_t mult) {
+    for (int i = 0; i < 3; ++i)
+        if (s[i] < 0 || s[i] % mult) return false;
+    return true;
+}
+
+// rows * stride elements of esize bytes (plus one row of D) fit a 31-bit offset
+bool span_ok(int64_t rows, int64_t stride, int64_t D, int64_t esize) {
+    return (rows * stride + D) * esize <= (int64_t)0x7fffffff;
+}
+
+template <int D, bool CAUSAL>
+int launch(const Params& p, int grid, hipStream_t stream) {
+    hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL>), dim3(grid), dim3(kThreads), 0, stream, p);
+    return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" int attn_fwd_bf16(int64_t batch, int64_t heads_q, int64_t heads_kv,
+                             int64_t seq_q, int64_t seq_k, int64_t head_dim,
+                             const void* Q, const int64_t* q_strides,
+                             const void* K, const int64_t* k_strides,
+                             const void* V, const int64_t* v_strides,
+                             float* O, const int64_t* o_strides,
+                             float* lse, float scale, int causal, void* stream) {
+    if (batch < 0 || seq_q < 0 || seq_k < 0 || heads_q < 1 || heads_kv < 1) return GEMM_ERR_INVALID_ARG;
+    if (heads_q % heads_kv != 0) return GEMM_ERR_INVALID_ARG;
+    if (head_dim != 64 && head_dim != 128) return GEMM_ERR_INVALID_ARG;
+    if (!(scale > 0.0f) || !isfinite(scale)) return GEMM_ERR_INVALID_ARG;
+    if (batch > INT32_MAX || heads_q > INT32_MAX || seq_q > INT32_MAX - 256 || seq_k > INT32_MAX - 256)
+        return GEMM_ERR_INVALID_ARG;
+    int64_t qs[3], ks[3], vs[3], os[3];
+    strides_of(q_strides, heads_q, seq_q, head_dim, qs);
+    strides_of(k_strides, heads_kv, seq_k, head_dim, ks);
+    strides_of(v_strides, heads_kv, seq_k, head_dim, vs);
+    strides_of(o_strides, heads_q, seq_q, head_dim, os);
+    if (!strides_ok(qs, 8) || !strides_ok(ks, 8) || !strides_ok(vs, 8) || !strides_ok(os, 4))
+        return GEMM_ERR_INVALID_ARG;
+    if (qs[2] < head_dim || ks[2] < head_dim || vs[2] < head_dim || os[2] < head_dim)
+        return GEMM_ERR_INVALID_ARG;
+    if (!span_ok(seq_q + kQB, qs[2], head_dim, 2) || !span_ok(seq_q + kQB, os[2], head_dim, 4) ||
+        !span_ok(seq_k + kKB, ks[2], head_dim, 2) || !span_ok(seq_k + kKB, vs[2], head_dim, 2))
+        return GEMM_ERR_INVALID_ARG;
+    const bool rows = batch > 0 && seq_q > 0;
+    if (rows && (Q == nullptr || O == nullptr)) return GEMM_ERR_INVALID_ARG;
+    if (rows && seq_k > 0 && (K == nullptr || V == nullptr)) return GEMM_ERR_INVALID_ARG;
+    if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16) || !aligned(lse, 4))
+        return GEMM_ERR_INVALID_ARG;
+    const int rc = device_supported();
+    if (rc != GEMM_OK) return rc;
+    if (!rows) return GEMM_OK;
+
+    Params p;
+    p.Q = (const uint8_t*)Q;
+    p.K = (const uint8_t*)K;
+    p.V = (const uint8_t*)V;
+    p.O = O;
+    p.lse = lse;
+    p.q_b = qs[0];
+    p.q_h = qs[1];
+    p.q_s = (int)qs[2];
+    p.k_b = ks[0];
+    p.k_h = ks[1];
+    p.k_s = (int)ks[2];
+    p.v_b = vs[0];
+    p.v_h = vs[1];
+    p.v_s = (int)vs[2];
+    p.o_b = os[0];
+    p.o_h = os[1];
+    p.o_s = (int)os[2];
+    p.Hq = (int)heads_q;
+    p.group = (int)(heads_q / heads_kv);
+    p.Sq = (int)seq_q;
+    p.Sk = (int)seq_k;
+    p.qblocks = (int)((seq_q + kQB - 1) / kQB);
+    p.off = (int)(seq_k - seq_q);
+    p.scale = scale;
+    p.c = (float)((double)scale * 1.4426950408889634);  // log2(e)
+    const int64_t grid = batch * heads_q * p.qblocks;
+    if (grid > INT32_MAX) return GEMM_ERR_INVALID_ARG;
+    p.xcd_remap = (grid % 8 == 0) ? 1 : 0;
+    hipStream_t st = (hipStream_t)stream;
+    const bool c = causal != 0;
+    if (head_dim == 128)
+        return c ? launch<128, true>(p, (int)grid, st) : launch<128, false>(p, (int)grid, st);
+    return c ? launch<64, true>(p, (int)grid, st) : launch<64, false>(p, (int)grid, st);
+}

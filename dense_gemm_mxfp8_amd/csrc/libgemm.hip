@@ -1309,13 +1309,14 @@ const char* gemm_strerror(int code) {
     switch (code) {
         case GEMM_OK: return "success";
         case GEMM_ERR_INVALID_ARG:
-            return "invalid argument (size, leading dimension, pointer, K alignment or output type)";
+            return "invalid argument (size, leading dimension or stride, pointer, alignment, output type, "
+                   "head dimension or scale)";
         case GEMM_ERR_UNSUPPORTED: return "unsupported device (a gfx950 GPU is required)";
         case GEMM_ERR_LAUNCH: return "kernel launch failed";
         default: return "unknown error code";
     }
 }
 
-int gemm_version(void) { return 200; }
+int gemm_version(void) { return 300; }
 
 }  // extern "C"

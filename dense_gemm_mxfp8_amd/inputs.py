@@ -1,4 +1,4 @@
-"""Seeded synthetic inputs for the GEMM workloads.
+"""Seeded synthetic inputs for the GEMM and attention workloads.
 
 This module only draws random numbers and encodes them (bf16 rounding, the
 MX e4m3 / e8m0 quantiser that prepares block-scaled operands).  It performs
@@ -6,7 +6,8 @@ no part of the matrix product; the HIP library and the CPU oracle both take
 its bytes as given.
 
 All generation happens on the CPU with a ``torch.Generator`` seeded per
-workload: A is drawn first, then B, so one seed fixes both operands.
+workload: A is drawn first, then B, so one seed fixes both operands
+(attention: Q, then K, then V).
 
 MX encoding (input preparation, not the product).  The pages name
 block-scaled MMA ("Modern GPU Programming For MLSys - 书籍总结", sections
@@ -151,7 +152,48 @@ WORKLOADS = {
 }
 
 
+@dataclass
+class AttnProblem:
+    """Q (B, Hq, Sq, D), K and V (B, Hkv, Sk, D), bf16, dense [B][H][S][D]."""
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    Sq: int
+    Sk: int
+    D: int
+    causal: bool
+    Q: torch.Tensor
+    K: torch.Tensor
+    V: torch.Tensor
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / float(self.D) ** 0.5
+
+
+def attn_problem(B: int, Hq: int, Hkv: int, Sq: int, Sk: int, D: int, causal: bool = False,
+                 dist: str = "normal", seed: int = 0, name: str | None = None) -> AttnProblem:
+    g = generator(seed)
+    draw = {"normal": normal_bf16, "uniform": uniform_bf16, "integer": integer_bf16}[dist]
+    Q = draw((B, Hq, Sq, D), g)
+    K = draw((B, Hkv, Sk, D), g)
+    V = draw((B, Hkv, Sk, D), g)
+    return AttnProblem(name or f"attn_{B}x{Hq}x{Hkv}x{Sq}x{Sk}x{D}_{dist}", B, Hq, Hkv, Sq, Sk, D, causal,
+                       Q.contiguous(), K.contiguous(), V.contiguous())
+
+
+# Attention forward workloads: 16 heads of dimension 128 (hidden size 2048)
+# at sequence length 4096 and batch 4 (16k tokens), unmasked and causal.
+ATTN_WORKLOADS = {
+    "attn4x16x4096_d128": dict(B=4, Hq=16, Hkv=16, Sq=4096, Sk=4096, D=128, causal=False),
+    "attn4x16x4096_d128_causal": dict(B=4, Hq=16, Hkv=16, Sq=4096, Sk=4096, D=128, causal=True),
+}
+
+
 def workload(name: str, seed: int = 0):
+    if name in ATTN_WORKLOADS:
+        return attn_problem(seed=seed, name=name, **ATTN_WORKLOADS[name])
     w = dict(WORKLOADS[name])
     kind = w.pop("kind")
     w.pop("splitk", None)

@@ -11,17 +11,22 @@ import dense_gemm_mxfp8_amd as dg
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "libgemm.h")
+HEADERS = [HEADER, os.path.join(ROOT, "include", "attention.h")]
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return re.findall(r"^\s*(?:const\s+)?\w+\s*\**\s*(gemm_\w+)\s*\(", text, flags=re.M)
+    names = []
+    for path in HEADERS:
+        text = open(path).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names += re.findall(r"^\s*(?:const\s+)?\w+\s*\**\s*((?:gemm|attn)_\w+)\s*\(", text, flags=re.M)
+    return names
 
 
 def test_header_declares_the_entry_points():
     names = set(declared_functions())
-    assert {"gemm_bf16", "gemm_bf16_nt", "gemm_mxfp8", "gemm_strerror", "gemm_version"} <= names
+    assert {"gemm_bf16", "gemm_bf16_nt", "gemm_mxfp8", "gemm_strerror", "gemm_version",
+            "attn_fwd_bf16"} <= names
 
 
 def test_library_exports_every_declared_symbol():
@@ -152,3 +157,26 @@ def test_dynamic_rejects_bad_workspace_before_any_device_call():
     assert dg.gemm_bf16_dynamic(*args, FAKE + 4, W, None) == dg.GEMM_ERR_INVALID_ARG
     # empty extents: a no-op
     assert dg.gemm_bf16_dynamic(0, 4, 64, 0, 64, 0, 64, 1, 0, 4, FAKE, W, None) == dg.GEMM_OK
+
+
+def test_attention_rejects_bad_arguments():
+    """Argument checks of attn_fwd_bf16 fail before any device call."""
+    F = FAKE * 16  # 16-byte aligned, never dereferenced
+    ok = dict(batch=2, heads_q=4, heads_kv=2, seq_q=100, seq_k=90, head_dim=128, Q=F, q_strides=None, K=F,
+              k_strides=None, V=F, v_strides=None, O=F, o_strides=None, lse=None, scale=0.1, causal=1, stream=0)
+    bad = [
+        dict(batch=-1), dict(seq_q=-1), dict(seq_k=-1), dict(heads_q=0), dict(heads_kv=0),
+        dict(heads_q=5),                       # not a multiple of heads_kv
+        dict(head_dim=96), dict(head_dim=0),   # 64 and 128 only
+        dict(scale=0.0), dict(scale=-0.5), dict(scale=float("inf")), dict(scale=float("nan")),
+        dict(Q=0), dict(K=0), dict(V=0), dict(O=0),
+        dict(Q=F + 2), dict(K=F + 8), dict(V=F + 4), dict(O=F + 4), dict(lse=F + 2),
+        dict(q_strides=(0, 0, 129)),           # not a multiple of 8
+        dict(k_strides=(0, 0, 64)),            # sequence stride below head_dim
+        dict(o_strides=(0, 0, 130)),           # O strides: multiples of 4
+        dict(v_strides=(0, -8, 128)),
+        dict(seq_k=1 << 23),                   # (seq_k + 64) rows of 256 B pass 2 GiB
+    ]
+    for change in bad:
+        args = dict(ok, **change)
+        assert dg.attn_fwd_bf16(**args) == dg.GEMM_ERR_INVALID_ARG, change
