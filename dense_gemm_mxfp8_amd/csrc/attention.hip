@@ -25,15 +25,18 @@
 //     fragments are read from the row-major V tile with ds_read_b64_tr_b16,
 //     and the O accumulators keep the query in the lane, like the softmax
 //     state (running max, running sum), so rescaling O is a multiply by a
-//     per-lane scalar.  Rescaling is skipped when no row's maximum moved
-//     (the factor is then exactly 1).
+//     per-lane scalar.  A row's reference maximum moves only when a block's
+//     maximum passes it by more than 8 (log2 units), so weights stay below
+//     2^8 and the rescale of O (skipped when no row of the wave moved, its
+//     factor then being exactly 1) is rare after the first block.
 //   * the two halves of the wave hold different keys of the same query; the
 //     row maximum is combined across them with a cross-lane exchange, and the
 //     row sums are kept per lane and combined once at the end.
-//   * K/V tiles are double-buffered: the 16-byte buffer loads of block t+1
-//     are issued before block t is multiplied, and written to the other LDS
-//     buffer after it; one barrier per block.  Rows past seq_k lie outside
-//     the tile's buffer descriptor and load as zero (and are masked).
+//   * K/V tiles are double-buffered in LDS: the DMA of block t+1
+//     (buffer_load ... lds, 16 bytes per lane, no VGPR round trip) is issued
+//     into the other buffer before block t is multiplied; one wait and one
+//     barrier per block.  Rows past seq_k lie outside the tile's buffer
+//     descriptor and load as zero (and are masked).
 //   * LDS rows are XOR-swizzled in 16-byte chunks so that both the K
 //     fragment reads (16 rows, one chunk) and the transposing V reads
 //     (4 rows x 4 chunks per 32 lanes) hit distinct banks.
@@ -67,6 +70,7 @@ constexpr int kQW = 32;        // query rows per wave
 constexpr int kQB = 128;       // query rows per workgroup
 constexpr int kKB = 64;        // keys per block
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
+constexpr float kLazy = 8.0f;  // log2 headroom of the lazily moved row maximum
 
 struct Params {
     const uint8_t* Q;
@@ -99,6 +103,20 @@ __device__ __forceinline__ int vswz(int row) {
     else return ((row >> 1) & 1) << 2;
 }
 
+// s_waitcnt vmcnt(0), leaving the other counters alone.
+__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8)); }
+
+// This wave's DMA instructions of one K or V tile: instruction n = 4 i + wave
+// fills LDS bytes [1024 n, 1024 n + 1024) from the lane offsets off[i].
+template <int NDMA>
+__device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t rs, uint8_t ALDS* dst, const int (&off)[NDMA],
+                                         int wave) {
+#pragma unroll
+    for (int i = 0; i < NDMA; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (void ALDS*)(dst + (4 * i + wave) * 1024), 16, off[i], 0, 0,
+                                                 0);
+}
+
 // K row fed to MFMA A-row m: bits 2 and 3 of m swapped.
 __device__ __forceinline__ int perm_row(int m) {
     return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
@@ -113,13 +131,14 @@ __device__ __forceinline__ float half_sum(float x) { return x + partner(x); }
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(Params p) {
+    // the host pass only needs the launch stub; the body uses device-only
+    // types (buffer descriptors, LDS address space)
+#if defined(__HIP_DEVICE_COMPILE__)
     constexpr int RB = 2 * D;                  // bytes per LDS row
     constexpr int NCH = D / 8;                 // 16-byte chunks per row
     constexpr int KT = kKB * RB;               // bytes of one K or V tile
     constexpr int DS = D / 16;                 // MFMA steps over d
     constexpr int DT = D / 32;                 // 32-row d tiles of O^T
-    constexpr int RPP = kThreads / NCH;        // tile rows per load pass
-    constexpr int LPT = kKB / RPP;             // 16-byte loads per thread per tensor
     __shared__ __attribute__((aligned(16))) uint8_t lds[2][2][KT];
 
     // ---- (batch, head, query block) of this workgroup
@@ -167,15 +186,22 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(Params p) {
             qf[s] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rq, voff + 32 * s, 0, 0));
     }
 
-    // ---- per-thread constants of the tile loads and LDS writes
-    const int ld_row = tid / NCH;      // + RPP * i
-    const int ld_ch = tid % NCH;
-    const int k_voff = ld_row * p.k_s * 2 + 16 * ld_ch;
-    const int v_voff = ld_row * p.v_s * 2 + 16 * ld_ch;
-    const int k_wr = ld_row * RB + ((ld_ch ^ kswz<D>(ld_row)) << 4);
-    const int v_wr = ld_row * RB + ((ld_ch ^ vswz<D>(ld_row)) << 4);
-    const int k_rstep = RPP * p.k_s * 2;
-    const int v_rstep = RPP * p.v_s * 2;
+    // ---- K/V tiles go global -> LDS by buffer_load ... lds: one wave
+    // instruction fills 1 KiB of LDS (lane i at byte 16 i), i.e. RPI rows;
+    // the lane fetches the global chunk that the swizzle places there.  Each
+    // lane's whole offset (row and chunk) is in voffset, so rows past seq_k
+    // fall outside the tile's descriptor and load as zero.
+    constexpr int RPI = 1024 / RB;             // rows per DMA instruction
+    constexpr int NDMA = kKB / RPI / 4;        // instructions per wave per tensor
+    int k_dma[NDMA], v_dma[NDMA];
+#pragma unroll
+    for (int i = 0; i < NDMA; ++i) {
+        const int n = 4 * i + wave;            // instruction index within the tile
+        const int row = n * RPI + lane / NCH;
+        const int pc = lane % NCH;             // physical chunk in LDS
+        k_dma[i] = row * p.k_s * 2 + 16 * (pc ^ kswz<D>(row));
+        v_dma[i] = row * p.v_s * 2 + 16 * (pc ^ vswz<D>(row));
+    }
 
     // ---- per-lane constants of the fragment reads
     // K: A-row m = l32 reads key row perm_row(l32) (+32 for the second tile),
@@ -198,43 +224,28 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(Params p) {
         }
     }
 
-    i32x4 kreg[LPT], vreg[LPT];
-    auto issue_loads = [&](int t) {
+    auto issue_loads = [&](int t, int buf) {
         const int64_t kofs = (int64_t)t * kKB * p.k_s * 2;
         const int64_t vofs = (int64_t)t * kKB * p.v_s * 2;
-        const auto rk = make_rsrc(kbase + kofs, kbytes - kofs);
-        const auto rv = make_rsrc(vbase + vofs, vbytes - vofs);
-#pragma unroll
-        for (int i = 0; i < LPT; ++i) {
-            kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, k_voff + i * k_rstep, 0, 0);
-            vreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, v_voff + i * v_rstep, 0, 0);
-        }
-    };
-    auto write_tile = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < LPT; ++i) {
-            *(i32x4 ALDS*)(&lds[buf][0][0] + k_wr + i * RPP * RB) = kreg[i];
-            *(i32x4 ALDS*)(&lds[buf][1][0] + v_wr + i * RPP * RB) = vreg[i];
-        }
+        dma_tile<NDMA>(make_rsrc(kbase + kofs, kbytes - kofs), (uint8_t ALDS*)&lds[buf][0][0], k_dma, wave);
+        dma_tile<NDMA>(make_rsrc(vbase + vofs, vbytes - vofs), (uint8_t ALDS*)&lds[buf][1][0], v_dma, wave);
     };
 
     f32x16 oacc[DT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
         for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.0f;
-    float m_run = -INFINITY;  // running max of the raw scores q.k of this lane's row
+    float m_run = -INFINITY;  // reference max of the raw scores q.k of this lane's row
     float l_run = 0.0f;       // this lane's part of the running sum
 
-    if (nt > 0) {
-        issue_loads(0);
-        write_tile(0);
-    }
+    if (nt > 0) issue_loads(0, 0);
+    wait_vm0();
     __syncthreads();
 
     for (int t = 0; t < nt; ++t) {
         const int buf = t & 1;
         const int k0 = t * kKB;
-        if (t + 1 < nt) issue_loads(t + 1);
+        if (t + 1 < nt) issue_loads(t + 1, buf ^ 1);
 
         if (wave_rows && k0 < wend) {
             const uint8_t ALDS* kt = (const uint8_t ALDS*)&lds[buf][0][0];
@@ -271,7 +282,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(Params p) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[st][r]);
             mx = half_max(mx);
-            const float m_new = fmaxf(m_run, mx);
+            // The reference maximum moves only when the block's maximum passes
+            // it by more than kLazy in log2 units: weights then stay below
+            // 2^kLazy, O and the row sum keep one common reference, and the
+            // rescale of O is skipped for most blocks.
+            const bool move = (mx - m_run) * p.c > kLazy;   // true while m_run = -inf and mx finite
+            const float m_new = move ? mx : m_run;
             const float alpha = (m_run == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f((m_run - m_new) * p.c);
             const float mc = (m_new == -INFINITY) ? 0.0f : m_new * p.c;
             m_run = m_new;
@@ -312,7 +328,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(Params p) {
             }
         }
 
-        if (t + 1 < nt) write_tile(buf ^ 1);
+        wait_vm0();  // this wave's DMA of block t + 1 has landed in LDS
         __syncthreads();
     }
 
@@ -335,6 +351,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(Params p) {
         if (p.lse && hh == 0)
             p.lse[((int64_t)b * p.Hq + h) * p.Sq + myq] = empty ? -INFINITY : m_run * p.scale + logf(l_tot);
     }
+#endif
 }
 
 struct DeviceInfo {
