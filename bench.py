@@ -377,7 +377,8 @@ def measured_traffic(workload: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary of
     this workload, or None if there is none or the kernels changed since."""
     from dense_gemm_mxfp8_amd import profiling
-    return profiling.read_traffic(os.path.join(ROOT, "profiles", f"traffic_{workload}.md"))
+    return profiling.read_traffic(os.path.join(ROOT, "profiles", f"traffic_{workload}.md"),
+                                  profiling.family_of(workload))
 
 
 def line(res, steps, warmup, cpu=None, headline=True):

@@ -31,11 +31,25 @@ import re
 PKG = os.path.dirname(os.path.abspath(__file__))
 
 
-def source_hash() -> str:
-    """sha256 over the HIP sources and the public header, in a fixed order."""
+# The sources each kernel family is built from: a counter summary stays valid
+# while these files are unchanged.
+FAMILIES = {
+    "gemm": ["csrc/libgemm.hip", "csrc/gemm_*.h", "../include/libgemm.h"],
+    "attention": ["csrc/attention.hip", "../include/attention.h"],
+}
+
+
+def family_of(workload_or_kernel: str) -> str:
+    """Kernel family of a workload or kernel name."""
+    return "attention" if "attn" in workload_or_kernel else "gemm"
+
+
+def source_hash(family: str = "gemm") -> str:
+    """sha256 over one kernel family's sources, in a fixed order."""
     h = hashlib.sha256()
-    files = sorted(glob.glob(os.path.join(PKG, "csrc", "*")))
-    files.append(os.path.join(os.path.dirname(PKG), "include", "libgemm.h"))
+    files = []
+    for pat in FAMILIES[family]:
+        files += sorted(glob.glob(os.path.normpath(os.path.join(PKG, pat))))
     for f in files:
         with open(f, "rb") as fh:
             h.update(os.path.basename(f).encode())
@@ -67,7 +81,8 @@ def traffic(args) -> None:
     lines = [
         f"# HBM traffic per launch: {args.title or args.kernel}",
         "",
-        f"source_sha256: {source_hash()}",
+        f"source_sha256: {source_hash(family_of(args.kernel))}",
+        f"source_family: {family_of(args.kernel)}",
         f"kernel_match: {args.kernel}",
         f"dispatches: fetch {len(fetch)}, write {len(write)}",
         f"fetch_kib_raw: {sum(fetch) / len(fetch):.1f}",
@@ -101,7 +116,7 @@ def stats(args) -> None:
                 continue
             rows.append(r)
     lines = [f"# rocprofv3 kernel statistics{': ' + args.title if args.title else ''}", "",
-             f"source_sha256: {source_hash()}", "",
+             f"source_sha256: {source_hash(family_of(args.match))} ({family_of(args.match)} sources)", "",
              "| kernel | calls | avg us | min us | max us | % time |", "|---|---|---|---|---|---|"]
     for r in rows:
         name = r["Name"]
@@ -155,15 +170,15 @@ def stats(args) -> None:
     print("\n".join(lines))
 
 
-def read_traffic(path: str):
+def read_traffic(path: str, family: str = "gemm"):
     """traffic_bytes_per_launch from a traffic summary if its source hash
-    matches the current sources, else None."""
+    matches the current sources of the kernel family, else None."""
     if not os.path.exists(path):
         return None
     text = open(path).read()
     m = re.search(r"^source_sha256: (\w+)", text, re.M)
     t = re.search(r"^traffic_bytes_per_launch: (\d+)", text, re.M)
-    if not m or not t or m.group(1) != source_hash():
+    if not m or not t or m.group(1) != source_hash(family):
         return None
     return int(t.group(1))
 
@@ -184,7 +199,8 @@ def main():
     s.add_argument("--bench-json", default="", help="the JSON line bench.py printed in the same run")
     t = sub.add_parser("traffic")
     t.add_argument("--kernel", required=True)
-    t.add_argument("--copy-kernel", default="elementwise")
+    t.add_argument("--copy-kernel", default="neg_kernel",
+                   help="kernel name of the copy (the calibration run also launches a fill kernel)")
     t.add_argument("--fetch", required=True)
     t.add_argument("--write", required=True)
     t.add_argument("--copy-fetch", required=True)
