@@ -51,6 +51,7 @@
 #include <math.h>
 #include <mutex>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include "attention.h"
@@ -129,8 +130,11 @@ __device__ __forceinline__ float partner(float x) { return __shfl_xor(x, 32); }
 __device__ __forceinline__ float half_max(float x) { return fmaxf(x, partner(x)); }
 __device__ __forceinline__ float half_sum(float x) { return x + partner(x); }
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(Params p) {
+// G: query groups of 32 rows per wave.  With G = 2 every K and V fragment
+// read from LDS feeds two MFMAs (half the LDS reads per FLOP) at one wave per
+// SIMD; with G = 1 two waves share each SIMD.
+template <int D, bool CAUSAL, int G>
+__global__ __launch_bounds__(kThreads, G == 1 ? 2 : 1) void attn_fwd_kernel(Params p) {
     // the host pass only needs the launch stub; the body uses device-only
     // types (buffer descriptors, LDS address space)
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -139,6 +143,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(Params p) {
     constexpr int KT = kKB * RB;               // bytes of one K or V tile
     constexpr int DS = D / 16;                 // MFMA steps over d
     constexpr int DT = D / 32;                 // 32-row d tiles of O^T
+    constexpr int QB = kQB * G;                // query rows per workgroup
     __shared__ __attribute__((aligned(16))) uint8_t lds[2][2][KT];
 
     // ---- (batch, head, query block) of this workgroup
@@ -149,22 +154,24 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(Params p) {
     const int b = bh / p.Hq;
     const int h = bh - b * p.Hq;
     const int hk = h / p.group;
-    const int q0 = qb * kQB;
+    const int q0 = qb * QB;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31;
     const int hh = lane >> 5;
-    const int qw0 = q0 + wave * kQW;   // first query row of this wave
-    const int myq = qw0 + l32;         // this lane's query row
+    const int qw0 = q0 + wave * kQW * G;  // first query row of this wave
+    int myq[G];                           // this lane's query row in group g
+#pragma unroll
+    for (int g = 0; g < G; ++g) myq[g] = qw0 + kQW * g + l32;
 
     // keys any row of the workgroup / of this wave can see
     int kend = p.Sk, wend = p.Sk;
     if constexpr (CAUSAL) {
-        const int qlast = min(q0 + kQB, p.Sq);
+        const int qlast = min(q0 + QB, p.Sq);
         kend = min(p.Sk, qlast + p.off);
-        wend = min(p.Sk, min(qw0 + kQW, p.Sq) + p.off);
+        wend = min(p.Sk, min(qw0 + kQW * G, p.Sq) + p.off);
     }
     const int nt = kend > 0 ? (kend + kKB - 1) / kKB : 0;
     const bool wave_rows = qw0 < p.Sq;
@@ -177,13 +184,16 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(Params p) {
     const int64_t vbytes = p.Sk > 0 ? 2 * ((int64_t)(p.Sk - 1) * p.v_s + D) : 0;
 
     // ---- this wave's query rows, resident as the B operand of S^T = K Q^T
-    bf16x8 qf[DS];
+    bf16x8 qf[G][DS];
     {
         const auto rq = make_rsrc(qbase, qbytes);
-        const int voff = myq * p.q_s * 2 + 16 * hh;
 #pragma unroll
-        for (int s = 0; s < DS; ++s)
-            qf[s] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rq, voff + 32 * s, 0, 0));
+        for (int g = 0; g < G; ++g) {
+            const int voff = myq[g] * p.q_s * 2 + 16 * hh;
+#pragma unroll
+            for (int s = 0; s < DS; ++s)
+                qf[g][s] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rq, voff + 32 * s, 0, 0));
+        }
     }
 
     // ---- K/V tiles go global -> LDS by buffer_load ... lds: one wave
@@ -231,12 +241,16 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(Params p) {
         dma_tile<NDMA>(make_rsrc(vbase + vofs, vbytes - vofs), (uint8_t ALDS*)&lds[buf][1][0], v_dma, wave);
     };
 
-    f32x16 oacc[DT];
+    f32x16 oacc[G][DT];
+    float m_run[G], l_run[G];  // reference max of the raw scores q.k of the row; this lane's part of its sum
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-        for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.0f;
-    float m_run = -INFINITY;  // reference max of the raw scores q.k of this lane's row
-    float l_run = 0.0f;       // this lane's part of the running sum
+    for (int g = 0; g < G; ++g) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+            for (int r = 0; r < 16; ++r) oacc[g][dt][r] = 0.0f;
+        m_run[g] = -INFINITY;
+        l_run[g] = 0.0f;
+    }
 
     if (nt > 0) issue_loads(0, 0);
     wait_vm0();
@@ -250,71 +264,85 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(Params p) {
         if (wave_rows && k0 < wend) {
             const uint8_t ALDS* kt = (const uint8_t ALDS*)&lds[buf][0][0];
             const uint8_t ALDS* vt = (const uint8_t ALDS*)&lds[buf][1][0];
-            // ---- S^T = K Q^T over the 64 keys (two 32-key tiles)
-            f32x16 sacc[2];
+            // ---- S^T = K Q^T over the 64 keys (two 32-key tiles); each K
+            // fragment feeds the G query groups
+            f32x16 sacc[G][2];
 #pragma unroll
-            for (int st = 0; st < 2; ++st)
-                for (int r = 0; r < 16; ++r) sacc[st][r] = 0.0f;
+            for (int g = 0; g < G; ++g)
+                for (int st = 0; st < 2; ++st)
+                    for (int r = 0; r < 16; ++r) sacc[g][st][r] = 0.0f;
 #pragma unroll
             for (int s = 0; s < DS; ++s) {
 #pragma unroll
                 for (int st = 0; st < 2; ++st) {
                     const bf16x8 kf = *(const bf16x8 ALDS*)(kt + k_rd[s] + st * 32 * RB);
-                    sacc[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc[st], 0, 0, 0);
+#pragma unroll
+                    for (int g = 0; g < G; ++g)
+                        sacc[g][st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[g][s], sacc[g][st], 0, 0, 0);
                 }
             }
             // ---- mask: keys past seq_k, and (causal) keys after the row's limit
             const bool need_mask = (k0 + kKB > p.Sk) || (CAUSAL && k0 + kKB - 1 > qw0 + p.off);
             if (need_mask) {
-                const int lim = CAUSAL ? min(p.Sk - 1, myq + p.off) : p.Sk - 1;
+#pragma unroll
+                for (int g = 0; g < G; ++g) {
+                    const int lim = CAUSAL ? min(p.Sk - 1, myq[g] + p.off) : p.Sk - 1;
+#pragma unroll
+                    for (int st = 0; st < 2; ++st)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int key = k0 + 32 * st + 16 * (r >> 3) + 8 * hh + (r & 7);
+                            if (key > lim) sacc[g][st][r] = -INFINITY;
+                        }
+                }
+            }
+            // ---- online softmax (reference max, rescale), per group
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                float mx = sacc[g][0][0];
+#pragma unroll
+                for (int st = 0; st < 2; ++st)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[g][st][r]);
+                mx = half_max(mx);
+                // The reference maximum moves only when the block's maximum
+                // passes it by more than kLazy in log2 units: weights then stay
+                // below 2^kLazy, O and the row sum keep one common reference,
+                // and the rescale of O is skipped for most blocks.
+                const bool move = (mx - m_run[g]) * p.c > kLazy;  // true while m_run = -inf and mx finite
+                const float m_new = move ? mx : m_run[g];
+                const float alpha =
+                    (m_run[g] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f((m_run[g] - m_new) * p.c);
+                const float mc = (m_new == -INFINITY) ? 0.0f : m_new * p.c;
+                m_run[g] = m_new;
+                float psum = 0.0f;
 #pragma unroll
                 for (int st = 0; st < 2; ++st)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
-                        const int key = k0 + 32 * st + 16 * (r >> 3) + 8 * hh + (r & 7);
-                        if (key > lim) sacc[st][r] = -INFINITY;
+                        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[g][st][r], p.c, -mc));
+                        sacc[g][st][r] = e;
+                        psum += e;
                     }
-            }
-            // ---- online softmax (running max, rescale)
-            float mx = sacc[0][0];
+                l_run[g] = l_run[g] * alpha + psum;
+                if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
 #pragma unroll
-            for (int st = 0; st < 2; ++st)
+                    for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[st][r]);
-            mx = half_max(mx);
-            // The reference maximum moves only when the block's maximum passes
-            // it by more than kLazy in log2 units: weights then stay below
-            // 2^kLazy, O and the row sum keep one common reference, and the
-            // rescale of O is skipped for most blocks.
-            const bool move = (mx - m_run) * p.c > kLazy;   // true while m_run = -inf and mx finite
-            const float m_new = move ? mx : m_run;
-            const float alpha = (m_run == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f((m_run - m_new) * p.c);
-            const float mc = (m_new == -INFINITY) ? 0.0f : m_new * p.c;
-            m_run = m_new;
-            float psum = 0.0f;
-#pragma unroll
-            for (int st = 0; st < 2; ++st)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[st][r], p.c, -mc));
-                    sacc[st][r] = e;
-                    psum += e;
+                        for (int r = 0; r < 16; ++r) oacc[g][dt][r] *= alpha;
                 }
-            l_run = l_run * alpha + psum;
-            if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
-#pragma unroll
-                for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
             }
-            // ---- O^T += V^T P^T, 16 keys per MFMA step
+            // ---- O^T += V^T P^T, 16 keys per MFMA step; each V fragment
+            // feeds the G query groups
 #pragma unroll
             for (int st = 0; st < 2; ++st) {
 #pragma unroll
                 for (int u = 0; u < 2; ++u) {
-                    bf16x8 pf;
+                    bf16x8 pf[G];
 #pragma unroll
-                    for (int x = 0; x < 8; ++x) pf[x] = (__bf16)sacc[st][8 * u + x];
+                    for (int g = 0; g < G; ++g)
+#pragma unroll
+                        for (int x = 0; x < 8; ++x) pf[g][x] = (__bf16)sacc[g][st][8 * u + x];
                     const int krow = 32 * st + 16 * u;
 #pragma unroll
                     for (int dt = 0; dt < DT; ++dt) {
@@ -322,7 +350,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(Params p) {
                         const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((bf16x4 ALDS*)pv);
                         const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((bf16x4 ALDS*)(pv + 4 * RB));
                         const bf16x8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-                        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, oacc[dt], 0, 0, 0);
+#pragma unroll
+                        for (int g = 0; g < G; ++g)
+                            oacc[g][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[g], oacc[g][dt], 0, 0, 0);
                     }
                 }
             }
@@ -334,22 +364,26 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(Params p) {
 
     // ---- normalise and store
     if (!wave_rows) return;
-    const float l_tot = half_sum(l_run);
-    if (myq < p.Sq) {
-        float* orow = p.O + (b * p.o_b + h * p.o_h) + (int64_t)myq * p.o_s;
-        // no visible key: every weight was 0 (a visible row has one weight of exactly 1)
-        const bool empty = l_tot == 0.0f;
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
+    for (int g = 0; g < G; ++g) {
+        const float l_tot = half_sum(l_run[g]);
+        if (myq[g] < p.Sq) {
+            float* orow = p.O + (b * p.o_b + h * p.o_h) + (int64_t)myq[g] * p.o_s;
+            // no visible key: every weight was 0 (a visible row has one weight of exactly 1)
+            const bool empty = l_tot == 0.0f;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                f32x4 v;
+            for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) v[j] = empty ? 0.0f : oacc[dt][4 * i + j] / l_tot;
-                *(f32x4*)(orow + 32 * dt + 8 * i + 4 * hh) = v;
-            }
-        if (p.lse && hh == 0)
-            p.lse[((int64_t)b * p.Hq + h) * p.Sq + myq] = empty ? -INFINITY : m_run * p.scale + logf(l_tot);
+                for (int i = 0; i < 4; ++i) {
+                    f32x4 v;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) v[j] = empty ? 0.0f : oacc[g][dt][4 * i + j] / l_tot;
+                    *(f32x4*)(orow + 32 * dt + 8 * i + 4 * hh) = v;
+                }
+            if (p.lse && hh == 0)
+                p.lse[((int64_t)b * p.Hq + h) * p.Sq + myq[g]] =
+                    empty ? -INFINITY : m_run[g] * p.scale + logf(l_tot);
+        }
     }
 #endif
 }
@@ -383,6 +417,14 @@ int device_supported() {
     return d.supported ? GEMM_OK : GEMM_ERR_UNSUPPORTED;
 }
 
+// Query groups per wave: 1 (two waves per SIMD, the faster form measured on
+// MI355X) unless the environment variable ATTN_GROUPS=2 selects two groups
+// (one wave per SIMD, half the LDS reads per FLOP); read at every call.
+int attn_groups() {
+    const char* e = getenv("ATTN_GROUPS");
+    return (e && e[0] == '2') ? 2 : 1;
+}
+
 bool aligned(const void* p, uintptr_t a) { return (((uintptr_t)p) & (a - 1)) == 0; }
 
 // Strides (batch, head, seq) of a tensor, defaulting to dense [B][H][S][D].
@@ -409,9 +451,9 @@ bool span_ok(int64_t rows, int64_t stride, int64_t D, int64_t esize) {
     return (rows * stride + D) * esize <= (int64_t)0x7fffffff;
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, int G>
 int launch(const Params& p, int grid, hipStream_t stream) {
-    hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL>), dim3(grid), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, G>), dim3(grid), dim3(kThreads), 0, stream, p);
     return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
 }
 
@@ -439,7 +481,7 @@ extern "C" int attn_fwd_bf16(int64_t batch, int64_t heads_q, int64_t heads_kv,
         return GEMM_ERR_INVALID_ARG;
     if (qs[2] < head_dim || ks[2] < head_dim || vs[2] < head_dim || os[2] < head_dim)
         return GEMM_ERR_INVALID_ARG;
-    if (!span_ok(seq_q + kQB, qs[2], head_dim, 2) || !span_ok(seq_q + kQB, os[2], head_dim, 4) ||
+    if (!span_ok(seq_q + 2 * kQB, qs[2], head_dim, 2) || !span_ok(seq_q + 2 * kQB, os[2], head_dim, 4) ||
         !span_ok(seq_k + kKB, ks[2], head_dim, 2) || !span_ok(seq_k + kKB, vs[2], head_dim, 2))
         return GEMM_ERR_INVALID_ARG;
     const bool rows = batch > 0 && seq_q > 0;
@@ -473,7 +515,8 @@ extern "C" int attn_fwd_bf16(int64_t batch, int64_t heads_q, int64_t heads_kv,
     p.group = (int)(heads_q / heads_kv);
     p.Sq = (int)seq_q;
     p.Sk = (int)seq_k;
-    p.qblocks = (int)((seq_q + kQB - 1) / kQB);
+    const int G = attn_groups();
+    p.qblocks = (int)((seq_q + kQB * G - 1) / (kQB * G));
     p.off = (int)(seq_k - seq_q);
     p.scale = scale;
     p.c = (float)((double)scale * 1.4426950408889634);  // log2(e)
@@ -482,7 +525,12 @@ extern "C" int attn_fwd_bf16(int64_t batch, int64_t heads_q, int64_t heads_kv,
     p.xcd_remap = (grid % 8 == 0) ? 1 : 0;
     hipStream_t st = (hipStream_t)stream;
     const bool c = causal != 0;
+    if (G == 2) {
+        if (head_dim == 128)
+            return c ? launch<128, true, 2>(p, (int)grid, st) : launch<128, false, 2>(p, (int)grid, st);
+        return c ? launch<64, true, 2>(p, (int)grid, st) : launch<64, false, 2>(p, (int)grid, st);
+    }
     if (head_dim == 128)
-        return c ? launch<128, true>(p, (int)grid, st) : launch<128, false>(p, (int)grid, st);
-    return c ? launch<64, true>(p, (int)grid, st) : launch<64, false>(p, (int)grid, st);
+        return c ? launch<128, true, 1>(p, (int)grid, st) : launch<128, false, 1>(p, (int)grid, st);
+    return c ? launch<64, true, 1>(p, (int)grid, st) : launch<64, false, 1>(p, (int)grid, st);
 }

@@ -274,3 +274,22 @@ def test_attention_workload_sampled(name):
     O = Od.cpu().numpy()[rows[:, 0], rows[:, 1], rows[:, 2]]
     L = Ld.cpu().numpy()[rows[:, 0], rows[:, 1], rows[:, 2]]
     check(O, L, Ow, Om, Lw, p.scale, p.D, p.Sk, qk_abs_max(Qb, Kb, rows), name)
+
+
+@pytest.mark.parametrize("shape", [(2, 4, 2, 300, 257, 128, True), (1, 2, 1, 513, 200, 64, False),
+                                   (1, 2, 2, 700, 700, 128, True)], ids=lambda s: "x".join(map(str, s)))
+def test_attention_two_groups(shape, monkeypatch):
+    """The two-query-group form (ATTN_GROUPS=2: 64 rows per wave, one wave
+    per SIMD) against the oracle, and bit-identical to the default form
+    (every row goes through the same operations in the same order)."""
+    B, Hq, Hkv, Sq, Sk, D, causal = shape
+    P.note(f"attention two groups {shape}")
+    p = inputs.attn_problem(B, Hq, Hkv, Sq, Sk, D, causal, seed=90 + Sq)
+    monkeypatch.setenv("ATTN_GROUPS", "2")
+    O, L = run(*to_dev(p), p.scale, causal)
+    Qb, Kb, Vb = P.bits16(p.Q), P.bits16(p.K), P.bits16(p.V)
+    Ow, Om, Lw = oracle.attention_fwd(Qb, Kb, Vb, p.scale, causal)
+    check(O, L, Ow, Om, Lw, p.scale, D, Sk, qk_abs_max(Qb, Kb), f"two groups {shape}")
+    monkeypatch.delenv("ATTN_GROUPS")
+    O1, L1 = run(*to_dev(p), p.scale, causal)
+    assert np.array_equal(O, O1) and np.array_equal(L, L1)

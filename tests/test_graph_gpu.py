@@ -6,8 +6,8 @@ times with new operand values copied into the same buffers between replays
 replay bit for bit with an eager call of the same entry point on the same
 operands.  Covers the plain 256 x 256 kernel, the small-M kernel, split-K with
 dense planes (partial kernel + reduction), the stream-K style plan (partial
-kernel + tile reduction), the dynamic schedule (counter fill kernel + GEMM)
-and MX-fp8."""
+kernel + tile reduction), the dynamic schedule (counter fill kernel + GEMM),
+MX-fp8 and the attention forward (causal, GQA)."""
 import numpy as np
 import pytest
 import torch
@@ -74,6 +74,26 @@ def _mx_call(M, N, K):
     return fill, call
 
 
+def _attn_call(B, Hq, Hkv, S, D, causal):
+    """Attention with O viewed as a (B*Hq*S, D) matrix; lse goes to its own buffer."""
+    Q = torch.empty((B, Hq, S, D), dtype=torch.bfloat16, device=DEV)
+    K = torch.empty((B, Hkv, S, D), dtype=torch.bfloat16, device=DEV)
+    V = torch.empty_like(K)
+    L = torch.empty((B, Hq, S), dtype=torch.float32, device=DEV)
+
+    def call(C):
+        rc = dg.attn_fwd_bf16(B, Hq, Hkv, S, S, D, Q.data_ptr(), None, K.data_ptr(), None, V.data_ptr(), None,
+                              C.data_ptr(), None, L.data_ptr(), D ** -0.5, causal, P.stream())
+        assert rc == dg.GEMM_OK, dg.gemm_strerror(rc)
+
+    def fill(seed):
+        prob = inputs.attn_problem(B, Hq, Hkv, S, S, D, causal, seed=seed)
+        for dst, src in ((Q, prob.Q), (K, prob.K), (V, prob.V)):
+            dst.copy_(src.to(DEV))
+
+    return fill, call
+
+
 CASES = {
     "fast_nt_4096x4096x512": lambda: _bf16_call("plain", 4096, 4096, 512, True),
     "small_m_16x4096x2048": lambda: _bf16_call("plain", 16, 4096, 2048, False),
@@ -82,6 +102,7 @@ CASES = {
     "streamk_4352x4352x1024": lambda: _bf16_call("streamk", 4352, 4352, 1024, True),
     "dynamic_4352x4352x512": lambda: _bf16_call("dynamic", 4352, 4352, 512, True),
     "mx_4096x4096x1024": lambda: _mx_call(4096, 4096, 1024),
+    "attention_2x8x2x700x128_causal": lambda: _attn_call(2, 8, 2, 700, 128, True),
 }
 
 
@@ -91,7 +112,7 @@ def test_captured_call_replays(name):
     M_N = {"fast_nt_4096x4096x512": (4096, 4096), "small_m_16x4096x2048": (16, 4096),
            "splitk_planes_1024x1024x8192": (1024, 1024), "splitk_small_16x2048x4096": (16, 2048),
            "streamk_4352x4352x1024": (4352, 4352), "dynamic_4352x4352x512": (4352, 4352),
-           "mx_4096x4096x1024": (4096, 4096)}[name]
+           "mx_4096x4096x1024": (4096, 4096), "attention_2x8x2x700x128_causal": (2 * 8 * 700, 128)}[name]
     Cg = torch.full(M_N, -7.0, dtype=torch.float32, device=DEV)
     Ce = torch.empty(M_N, dtype=torch.float32, device=DEV)
     P.note(f"graph capture {name}")
