@@ -85,6 +85,7 @@ struct Params {
     float c;      // scale * log2(e)
     float scale;
     int xcd_remap;
+    int prio;     // raise the wave's issue priority around its MFMA phases
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
@@ -266,6 +267,7 @@ __global__ __launch_bounds__(kThreads, G == 1 ? 2 : 1) void attn_fwd_kernel(Para
             const uint8_t ALDS* vt = (const uint8_t ALDS*)&lds[buf][1][0];
             // ---- S^T = K Q^T over the 64 keys (two 32-key tiles); each K
             // fragment feeds the G query groups
+            if (p.prio) __builtin_amdgcn_s_setprio(1);
             f32x16 sacc[G][2];
 #pragma unroll
             for (int g = 0; g < G; ++g)
@@ -281,6 +283,7 @@ __global__ __launch_bounds__(kThreads, G == 1 ? 2 : 1) void attn_fwd_kernel(Para
                         sacc[g][st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[g][s], sacc[g][st], 0, 0, 0);
                 }
             }
+            if (p.prio) __builtin_amdgcn_s_setprio(0);
             // ---- mask: keys past seq_k, and (causal) keys after the row's limit
             const bool need_mask = (k0 + kKB > p.Sk) || (CAUSAL && k0 + kKB - 1 > qw0 + p.off);
             if (need_mask) {
@@ -334,6 +337,7 @@ __global__ __launch_bounds__(kThreads, G == 1 ? 2 : 1) void attn_fwd_kernel(Para
             }
             // ---- O^T += V^T P^T, 16 keys per MFMA step; each V fragment
             // feeds the G query groups
+            if (p.prio) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
             for (int st = 0; st < 2; ++st) {
 #pragma unroll
@@ -358,6 +362,7 @@ __global__ __launch_bounds__(kThreads, G == 1 ? 2 : 1) void attn_fwd_kernel(Para
             }
         }
 
+        if (p.prio) __builtin_amdgcn_s_setprio(0);
         wait_vm0();  // this wave's DMA of block t + 1 has landed in LDS
         __syncthreads();
     }
@@ -423,6 +428,12 @@ int device_supported() {
 int attn_groups() {
     const char* e = getenv("ATTN_GROUPS");
     return (e && e[0] == '2') ? 2 : 1;
+}
+
+// Wave priority around the MFMA phases: ATTN_PRIO=0 turns it off.
+int attn_prio() {
+    const char* e = getenv("ATTN_PRIO");
+    return (e && e[0] == '0') ? 0 : 1;
 }
 
 bool aligned(const void* p, uintptr_t a) { return (((uintptr_t)p) & (a - 1)) == 0; }
@@ -523,6 +534,7 @@ extern "C" int attn_fwd_bf16(int64_t batch, int64_t heads_q, int64_t heads_kv,
     const int64_t grid = batch * heads_q * p.qblocks;
     if (grid > INT32_MAX) return GEMM_ERR_INVALID_ARG;
     p.xcd_remap = (grid % 8 == 0) ? 1 : 0;
+    p.prio = attn_prio();
     hipStream_t st = (hipStream_t)stream;
     const bool c = causal != 0;
     if (G == 2) {
