@@ -51,6 +51,7 @@
 #include <math.h>
 #include <mutex>
 #include <stdint.h>
+#include <type_traits>
 #include <stdlib.h>
 #include <string.h>
 
@@ -257,8 +258,11 @@ __global__ __launch_bounds__(kThreads, G == 1 ? 2 : 1) void attn_fwd_kernel(Para
     wait_vm0();
     __syncthreads();
 
-    for (int t = 0; t < nt; ++t) {
-        const int buf = t & 1;
+    // One block; the LDS buffer is a compile-time constant (the loop is
+    // unrolled by two), so buffer and tile offsets fold into the LDS
+    // instructions' immediate offsets.
+    auto block = [&](auto BUF, int t) {
+        constexpr int buf = decltype(BUF)::value;
         const int k0 = t * kKB;
         if (t + 1 < nt) issue_loads(t + 1, buf ^ 1);
 
@@ -365,6 +369,10 @@ __global__ __launch_bounds__(kThreads, G == 1 ? 2 : 1) void attn_fwd_kernel(Para
         if (p.prio) __builtin_amdgcn_s_setprio(0);
         wait_vm0();  // this wave's DMA of block t + 1 has landed in LDS
         __syncthreads();
+    };
+    for (int t = 0; t < nt; t += 2) {
+        block(std::integral_constant<int, 0>{}, t);
+        if (t + 1 < nt) block(std::integral_constant<int, 1>{}, t + 1);
     }
 
     // ---- normalise and store
