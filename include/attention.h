@@ -29,7 +29,7 @@
  *     heads_kv; batch, seq_q, seq_k >= 0; scale finite and > 0;
  *   - Q, K, V 16-byte aligned with every stride a multiple of 8 elements;
  *     O (and lse) 16-byte (4-byte) aligned, O's strides multiples of 4;
- *   - within one head, (seq_q + 128) rows of Q and O and (seq_k + 64) rows of
+ *   - within one head, (seq_q + 256) rows of Q and O and (seq_k + 64) rows of
  *     K and V span less than 2 GiB (32-bit buffer offsets);
  *   - non-NULL Q, K, V, O whenever the extents they cover are non-empty.
  * Returns GEMM_OK, GEMM_ERR_INVALID_ARG, GEMM_ERR_UNSUPPORTED (not a gfx950
@@ -39,10 +39,10 @@
  * softmax runs in fp32, and its probabilities are rounded to bf16 (nearest
  * even) as the value product's operand, while the row sums that normalise O
  * add the unrounded fp32 values.  Elementwise,
- * |O - exact| <= 2^-7 * sum_j p(i, j) |V(j, d)| plus fp32 summation terms
- * (stated with the tests).  O is divided by the row sum with an IEEE
- * division, so a row whose probabilities are exact (equal scores, or one
- * dominant key) with integer V gives the exact quotient.
+ * |O - exact| <= 2^-8 (1 + 2^-6) * sum_j p(i, j) |V(j, d)| plus fp32
+ * summation terms (stated with the tests).  O is divided by the row sum
+ * with an IEEE division, so a row whose probabilities are exact (equal
+ * scores, or one dominant key) with integer V gives the exact quotient.
  *
  * Ownership and execution are those of every libgemm entry point: device
  * pointers owned by the caller, no allocation, copy or host synchronisation,
