@@ -253,6 +253,24 @@ def test_attention_tensor_helper():
     assert np.array_equal(O.cpu().numpy(), O2) and np.array_equal(L.cpu().numpy(), L2)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_attention_long_keys(causal):
+    """16384 keys (256 key blocks): the longest fp32 sums of the bound's
+    gamma(Sk) term, in [B][S][H][D] storage with 8 heads."""
+    B, Hq, Hkv, Sq, Sk, D = 1, 8, 2, 300, 16384, 128
+    P.note(f"attention long keys causal={causal}")
+    p = inputs.attn_problem(B, Hq, Hkv, Sq, Sk, D, causal, seed=95)
+    Qs = p.Q.transpose(1, 2).contiguous().to(DEV).transpose(1, 2)
+    Ks = p.K.transpose(1, 2).contiguous().to(DEV).transpose(1, 2)
+    Vs = p.V.transpose(1, 2).contiguous().to(DEV).transpose(1, 2)
+    O, L = run(Qs, Ks, Vs, p.scale, causal)
+    Qb, Kb, Vb = P.bits16(p.Q), P.bits16(p.K), P.bits16(p.V)
+    rows = np.array([(0, h, i) for h in (0, 5, 7) for i in (0, 1, 150, Sq - 1)], np.int64)
+    Ow, Om, Lw = oracle.attention_fwd_at(Qb, Kb, Vb, p.scale, causal, rows)
+    check(O[rows[:, 0], rows[:, 1], rows[:, 2]], L[rows[:, 0], rows[:, 1], rows[:, 2]], Ow, Om, Lw, p.scale, D,
+          Sk, qk_abs_max(Qb, Kb, rows), f"long keys causal={causal}")
+
+
 @pytest.mark.parametrize("name", sorted(inputs.ATTN_WORKLOADS))
 def test_attention_workload_sampled(name):
     """The benchmark's workloads at full size in its launch configuration:
