@@ -146,7 +146,13 @@ __global__ __launch_bounds__(kThreads, G == 1 ? 2 : 1) void attn_fwd_kernel(Para
     constexpr int DS = D / 16;                 // MFMA steps over d
     constexpr int DT = D / 32;                 // 32-row d tiles of O^T
     constexpr int QB = kQB * G;                // query rows per workgroup
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2][2][KT];
+    // K and V tiles of the two buffers, each its own __shared__ object: the
+    // compiler can then tell the in-flight DMA into one buffer apart from the
+    // fragment reads of the other and does not make the reads wait for it
+    __shared__ __attribute__((aligned(16))) uint8_t k_lds0[KT];
+    __shared__ __attribute__((aligned(16))) uint8_t k_lds1[KT];
+    __shared__ __attribute__((aligned(16))) uint8_t v_lds0[KT];
+    __shared__ __attribute__((aligned(16))) uint8_t v_lds1[KT];
 
     // ---- (batch, head, query block) of this workgroup
     int bid = blockIdx.x;
@@ -236,11 +242,17 @@ __global__ __launch_bounds__(kThreads, G == 1 ? 2 : 1) void attn_fwd_kernel(Para
         }
     }
 
-    auto issue_loads = [&](int t, int buf) {
+    auto k_tile = [&](auto BUF) {
+        return (uint8_t ALDS*)(decltype(BUF)::value ? k_lds1 : k_lds0);
+    };
+    auto v_tile = [&](auto BUF) {
+        return (uint8_t ALDS*)(decltype(BUF)::value ? v_lds1 : v_lds0);
+    };
+    auto issue_loads = [&](int t, auto BUF) {
         const int64_t kofs = (int64_t)t * kKB * p.k_s * 2;
         const int64_t vofs = (int64_t)t * kKB * p.v_s * 2;
-        dma_tile<NDMA>(make_rsrc(kbase + kofs, kbytes - kofs), (uint8_t ALDS*)&lds[buf][0][0], k_dma, wave);
-        dma_tile<NDMA>(make_rsrc(vbase + vofs, vbytes - vofs), (uint8_t ALDS*)&lds[buf][1][0], v_dma, wave);
+        dma_tile<NDMA>(make_rsrc(kbase + kofs, kbytes - kofs), k_tile(BUF), k_dma, wave);
+        dma_tile<NDMA>(make_rsrc(vbase + vofs, vbytes - vofs), v_tile(BUF), v_dma, wave);
     };
 
     f32x16 oacc[G][DT];
@@ -254,7 +266,7 @@ __global__ __launch_bounds__(kThreads, G == 1 ? 2 : 1) void attn_fwd_kernel(Para
         l_run[g] = 0.0f;
     }
 
-    if (nt > 0) issue_loads(0, 0);
+    if (nt > 0) issue_loads(0, std::integral_constant<int, 0>{});
     wait_vm0();
     __syncthreads();
 
@@ -264,11 +276,11 @@ __global__ __launch_bounds__(kThreads, G == 1 ? 2 : 1) void attn_fwd_kernel(Para
     auto block = [&](auto BUF, int t) {
         constexpr int buf = decltype(BUF)::value;
         const int k0 = t * kKB;
-        if (t + 1 < nt) issue_loads(t + 1, buf ^ 1);
+        if (t + 1 < nt) issue_loads(t + 1, std::integral_constant<int, buf ^ 1>{});
 
         if (wave_rows && k0 < wend) {
-            const uint8_t ALDS* kt = (const uint8_t ALDS*)&lds[buf][0][0];
-            const uint8_t ALDS* vt = (const uint8_t ALDS*)&lds[buf][1][0];
+            const uint8_t ALDS* kt = k_tile(BUF);
+            const uint8_t ALDS* vt = v_tile(BUF);
             // ---- S^T = K Q^T over the 64 keys (two 32-key tiles); each K
             // fragment feeds the G query groups
             if (p.prio) __builtin_amdgcn_s_setprio(1);
