@@ -289,14 +289,51 @@ __global__ __launch_bounds__(kThreads, G == 1 ? 2 : 1) void attn_fwd_kernel(Para
             for (int g = 0; g < G; ++g)
                 for (int st = 0; st < 2; ++st)
                     for (int r = 0; r < 16; ++r) sacc[g][st][r] = 0.0f;
+            if constexpr (CAUSAL) {
+                // Causal launches run below the power limit, where LDS
+                // latency shows: their K fragments run KLA steps ahead of the
+                // MFMAs (a ring of KLA + 1 steps).  Measured: +4% causal, -1%
+                // unmasked (power-limited), so the unmasked form keeps reads
+                // next to their MFMAs.
+                constexpr int KLA = 2;
+                bf16x8 kf[KLA + 1][2];
 #pragma unroll
-            for (int s = 0; s < DS; ++s) {
+                for (int s = 0; s < KLA; ++s)
 #pragma unroll
-                for (int st = 0; st < 2; ++st) {
-                    const bf16x8 kf = *(const bf16x8 ALDS*)(kt + k_rd[s] + st * 32 * RB);
+                    for (int st = 0; st < 2; ++st) kf[s][st] = *(const bf16x8 ALDS*)(kt + k_rd[s] + st * 32 * RB);
 #pragma unroll
-                    for (int g = 0; g < G; ++g)
-                        sacc[g][st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[g][s], sacc[g][st], 0, 0, 0);
+                for (int s = 0; s < DS; ++s) {
+                    if (s + KLA < DS) {
+#pragma unroll
+                        for (int st = 0; st < 2; ++st)
+                            kf[(s + KLA) % (KLA + 1)][st] = *(const bf16x8 ALDS*)(kt + k_rd[s + KLA] + st * 32 * RB);
+                    }
+#pragma unroll
+                    for (int st = 0; st < 2; ++st) {
+#pragma unroll
+                        for (int g = 0; g < G; ++g)
+                            sacc[g][st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s % (KLA + 1)][st], qf[g][s],
+                                                                                   sacc[g][st], 0, 0, 0);
+                    }
+                }
+                // keep that order: KLA steps of reads first, then per step two
+                // reads and the step's MFMAs
+                __builtin_amdgcn_sched_group_barrier(0x100, 2 * KLA, 0);
+#pragma unroll
+                for (int s = 0; s < DS; ++s) {
+                    if (s + KLA < DS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x008, 2 * G, 0);
+                }
+            } else {
+#pragma unroll
+                for (int s = 0; s < DS; ++s) {
+#pragma unroll
+                    for (int st = 0; st < 2; ++st) {
+                        const bf16x8 kf = *(const bf16x8 ALDS*)(kt + k_rd[s] + st * 32 * RB);
+#pragma unroll
+                        for (int g = 0; g < G; ++g)
+                            sacc[g][st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[g][s], sacc[g][st], 0, 0, 0);
+                    }
                 }
             }
             if (p.prio) __builtin_amdgcn_s_setprio(0);
