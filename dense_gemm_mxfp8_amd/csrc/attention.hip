@@ -433,13 +433,22 @@ __global__ __launch_bounds__(kThreads, G == 1 ? 2 : 1) void attn_fwd_kernel(Para
             float* orow = p.O + (b * p.o_b + h * p.o_h) + (int64_t)myq[g] * p.o_s;
             // no visible key: every weight was 0 (a visible row has one weight of exactly 1)
             const bool empty = l_tot == 0.0f;
+            // a / l correctly rounded, one division per row: with the
+            // correctly rounded reciprocal r, q = a r is within an ulp and one
+            // fma residual step q + r (a - q l) rounds to the IEEE quotient
+            // (Markstein's correction)
+            const float r = empty ? 0.0f : 1.0f / l_tot;
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     f32x4 v;
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) v[j] = empty ? 0.0f : oacc[g][dt][4 * i + j] / l_tot;
+                    for (int j = 0; j < 4; ++j) {
+                        const float a = oacc[g][dt][4 * i + j];
+                        const float q = a * r;
+                        v[j] = empty ? 0.0f : __builtin_fmaf(__builtin_fmaf(-q, l_tot, a), r, q);
+                    }
                     *(f32x4*)(orow + 32 * dt + 8 * i + 4 * hh) = v;
                 }
             if (p.lse && hh == 0)

@@ -40,9 +40,11 @@
  * even) as the value product's operand, while the row sums that normalise O
  * add the unrounded fp32 values.  Elementwise,
  * |O - exact| <= 2^-8 (1 + 2^-6) * sum_j p(i, j) |V(j, d)| plus fp32
- * summation terms (stated with the tests).  O is divided by the row sum
- * with an IEEE division, so a row whose probabilities are exact (equal
- * scores, or one dominant key) with integer V gives the exact quotient.
+ * summation terms (stated with the tests).  O is the value sum times the
+ * correctly rounded reciprocal of the row sum, refined by one fma residual
+ * step (Markstein's correction); rows whose probabilities are exact (equal
+ * scores, or one dominant key) with integer V give the IEEE quotient, as
+ * the tests check bit for bit.
  *
  * Ownership and execution are those of every libgemm entry point: device
  * pointers owned by the caller, no allocation, copy or host synchronisation,

@@ -14,7 +14,8 @@ Acceptance bound (floating point), elementwise for output (b, h, i, d):
                                          fp32 score sums over d, which move
                                          each weight by exp of that error
       + 2^-20                            exp2, the fma that applies the scale,
-                                         and the final division
+                                         and the final division (reciprocal
+                                         and one fma step, within 2 ulp)
       + 1e-30 absolute                   weights below fp32's normal range
                                          (2^-126) flush to 0 on the GPU, which
                                          moves O by at most Sk 2^-126 max|v|,
@@ -22,7 +23,8 @@ Acceptance bound (floating point), elementwise for output (b, h, i, d):
   |lse_gpu - lse| <= 4 scale gamma(D) max|qk| + 4 gamma(Sk) + 2^-20 (1 + |lse|)
 Cases whose probabilities are exact (equal scores; one score thousands above
 the rest) with integer V must match bit for bit: the sums are then exact and
-O is one IEEE division.
+O must equal their IEEE quotient (the kernel forms it from the reciprocal of
+the row sum and one fma residual step).
 """
 from __future__ import annotations
 
