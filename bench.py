@@ -351,7 +351,10 @@ def cpu_baseline(prob, rows: int, single_rows: int = 32):
                             "sample": f"rows 0..{n1 - 1} ({n1}x{prob.N}x{prob.K}), {dt1:.2f} s wall"}}
 
 
-def cpu_baseline_attention(p, rows: int = 65536):
+ATTN_CPU_ROWS = 131072  # about 15 s of the oracle on 16 host threads at 4096 keys
+
+
+def cpu_baseline_attention(p, rows: int = ATTN_CPU_ROWS):
     """The attention oracle, untouched, on the first `rows` query rows of head
     (0, 0) onward (all the host threads it uses), scaled by the rows' own
     algorithmic FLOPs."""
@@ -443,10 +446,11 @@ def main():
         res, prob = bench_workload(name, args.steps, args.warmup, args.settle)
         cpu = None
         if i == 0 and not args.no_cpu_baseline:
-            print(f"[bench] oracle on {args.cpu_rows} rows", file=sys.stderr, flush=True)
             if name.startswith("attn"):
-                cpu = cpu_baseline_attention(prob)
+                print(f"[bench] oracle on {ATTN_CPU_ROWS} query rows", file=sys.stderr, flush=True)
+                cpu = cpu_baseline_attention(prob, ATTN_CPU_ROWS)
             else:
+                print(f"[bench] oracle on {args.cpu_rows} rows", file=sys.stderr, flush=True)
                 cpu = cpu_baseline(prob, args.cpu_rows)
         print(json.dumps(line(res, args.steps, args.warmup, cpu, headline=(name == HEADLINE))), flush=True)
         del prob
