@@ -30,7 +30,7 @@
 //     2^8 and the rescale of O (skipped when no row of the wave moved, its
 //     factor then being exactly 1) is rare after the first block.
 //   * the two halves of the wave hold different keys of the same query; the
-//     row maximum is combined across them with a cross-lane exchange, and the
+//     row maximum is combined across them with v_permlane32_swap, and the
 //     row sums are kept per lane and combined once at the end.
 //   * K/V tiles are double-buffered in LDS: the DMA of block t+1
 //     (buffer_load ... lds, 16 bytes per lane, no VGPR round trip) is issued
@@ -125,12 +125,30 @@ __device__ __forceinline__ int perm_row(int m) {
     return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
 }
 
-// The value of the lane 32 away (the other half of the wave holds the other
-// keys of the same query).  Both halves combine (own, partner) with a
-// symmetric operation, so they end with the same result.
-__device__ __forceinline__ float partner(float x) { return __shfl_xor(x, 32); }
-__device__ __forceinline__ float half_max(float x) { return fmaxf(x, partner(x)); }
-__device__ __forceinline__ float half_sum(float x) { return x + partner(x); }
+// Own value and the value of the lane 32 away (the other half of the wave
+// holds the other keys of the same query), in one v_permlane32_swap: it
+// swaps lanes 32-63 of its first operand with lanes 0-31 of its second, so
+// with both holding x, every lane ends with its own x in one register and its
+// partner's in the other.  Written as an instruction rather than the builtin,
+// whose two results the compiler treats as one value; the s_nops cover the
+// VALU-write / permlane-read hazards that the compiler cannot see inside asm.
+// Both halves combine the pair with a symmetric operation and end with the
+// same value.
+__device__ __forceinline__ void own_and_partner(float x, float& a, float& b) {
+    a = x;
+    b = x;
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ float half_max(float x) {
+    float a, b;
+    own_and_partner(x, a, b);
+    return fmaxf(a, b);
+}
+__device__ __forceinline__ float half_sum(float x) {
+    float a, b;
+    own_and_partner(x, a, b);
+    return a + b;
+}
 
 // G: query groups of 32 rows per wave.  With G = 2 every K and V fragment
 // read from LDS feeds two MFMAs (half the LDS reads per FLOP) at one wave per
