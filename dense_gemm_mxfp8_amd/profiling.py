@@ -1,6 +1,6 @@
 """Turn rocprofv3 CSV output into the short text summaries kept in profiles/.
 
-Two kinds of summary:
+Three kinds of summary:
 
 * ``stats``: the per-kernel table of ``rocprofv3 --kernel-trace --stats``
   (calls, average / min / max duration) for the kernels of one run.
@@ -170,6 +170,33 @@ def stats(args) -> None:
     print("\n".join(lines))
 
 
+def counters(args) -> None:
+    """Mean of each counter per dispatch of the matching kernel, over one or
+    more --pmc runs' counter_collection.csv files, as a markdown table."""
+    import collections
+    acc = collections.defaultdict(list)
+    for path in args.csv:
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                if args.match in r["Kernel_Name"]:
+                    acc[r["Counter_Name"]].append(float(r["Counter_Value"]))
+    if not acc:
+        raise SystemExit("no counter rows for that kernel")
+    lines = [f"# rocprofv3 counters per dispatch: {args.title or args.match}", "",
+             f"source_sha256: {source_hash(family_of(args.match))} ({family_of(args.match)} sources)",
+             f"kernel_match: {args.match}", "",
+             "| counter | dispatches | mean per dispatch |", "|---|---|---|"]
+    for k in sorted(acc):
+        v = acc[k]
+        lines.append(f"| `{k}` | {len(v)} | {sum(v) / len(v):.6g} |")
+    if args.note:
+        lines += ["", args.note.strip()]
+    lines += ["", "Commands:", "", "```", args.cmd.strip(), "```", ""]
+    with open(args.out, "w") as fh:
+        fh.write("\n".join(lines))
+    print("\n".join(lines))
+
+
 def read_traffic(path: str, family: str = "gemm"):
     """traffic_bytes_per_launch from a traffic summary if its source hash
     matches the current sources of the kernel family, else None."""
@@ -209,9 +236,18 @@ def main():
     t.add_argument("--out", required=True)
     t.add_argument("--cmd", required=True)
     t.add_argument("--title", default="")
+    c = sub.add_parser("counters")
+    c.add_argument("--match", required=True)
+    c.add_argument("--out", required=True)
+    c.add_argument("--cmd", required=True)
+    c.add_argument("--title", default="")
+    c.add_argument("--note", default="")
+    c.add_argument("csv", nargs="+")
     a = ap.parse_args()
     if a.cmd_name == "stats":
         stats(a)
+    elif a.cmd_name == "counters":
+        counters(a)
     else:
         traffic(a)
 
