@@ -6,7 +6,7 @@ stream.  If the library is missing the calls raise; there is no fallback.
 
 Raw entry points mirror the C ABI of include/libgemm.h and
 include/attention.h one to one (``gemm_bf16``, ``gemm_bf16_nt``,
-``gemm_mxfp8``, ..., ``attn_fwd_bf16``, ``gemm_strerror``, ``gemm_version``)
+``gemm_mxfp8``, ..., ``attn_fwd_bf16``, ``attn_fwd_bf16_out``, ``gemm_strerror``, ``gemm_version``)
 and take integers for pointers and the stream.  The tensor helpers ``bf16``,
 ``mxfp8`` and ``attention`` build those arguments from torch tensors.
 """
@@ -63,6 +63,9 @@ def library() -> ctypes.CDLL:
                                           ctypes.c_size_t, _vp]
         lib.attn_fwd_bf16.restype = ctypes.c_int
         lib.attn_fwd_bf16.argtypes = [_i64] * 6 + [_vp, _vp] * 4 + [_vp, ctypes.c_float, ctypes.c_int, _vp]
+        lib.attn_fwd_bf16_out.restype = ctypes.c_int
+        lib.attn_fwd_bf16_out.argtypes = ([_i64] * 6 + [_vp, _vp] * 4 + [ctypes.c_int, _vp, ctypes.c_float,
+                                          ctypes.c_int, _vp])
         lib.gemm_strerror.restype = ctypes.c_char_p
         lib.gemm_strerror.argtypes = [ctypes.c_int]
         lib.gemm_version.restype = ctypes.c_int
@@ -117,18 +120,29 @@ def gemm_bf16_dynamic(M, N, K, A, lda, B, ldb, b_colmajor, C, ldc, workspace, wo
                                        workspace_bytes, stream)
 
 
+def _strides3(s):
+    """None, or 3 element strides as a host int64 array (the pointer keeps the array alive)."""
+    if s is None:
+        return None
+    a = (ctypes.c_int64 * 3)(*[int(x) for x in s])
+    return ctypes.cast(a, _vp)
+
+
 def attn_fwd_bf16(batch, heads_q, heads_kv, seq_q, seq_k, head_dim, Q, q_strides, K, k_strides, V,
                   v_strides, O, o_strides, lse, scale, causal, stream) -> int:
     """Strides: None (dense [B][H][S][D]) or a sequence of 3 element strides
     (batch, head, sequence), passed to the library as a host int64 array."""
-    def arr(s):
-        if s is None:
-            return None
-        a = (ctypes.c_int64 * 3)(*[int(x) for x in s])
-        return ctypes.cast(a, _vp)
-    qa, ka, va, oa = (arr(s) for s in (q_strides, k_strides, v_strides, o_strides))
+    qa, ka, va, oa = (_strides3(s) for s in (q_strides, k_strides, v_strides, o_strides))
     return library().attn_fwd_bf16(batch, heads_q, heads_kv, seq_q, seq_k, head_dim, Q, qa, K, ka, V, va, O,
                                    oa, lse, float(scale), int(bool(causal)), stream)
+
+
+def attn_fwd_bf16_out(batch, heads_q, heads_kv, seq_q, seq_k, head_dim, Q, q_strides, K, k_strides, V,
+                      v_strides, O, o_strides, out_type, lse, scale, causal, stream) -> int:
+    """attn_fwd_bf16 with the output type chosen by out_type (GEMM_OUT_F32 or GEMM_OUT_BF16)."""
+    qa, ka, va, oa = (_strides3(s) for s in (q_strides, k_strides, v_strides, o_strides))
+    return library().attn_fwd_bf16_out(batch, heads_q, heads_kv, seq_q, seq_k, head_dim, Q, qa, K, ka, V, va,
+                                       O, oa, int(out_type), lse, float(scale), int(bool(causal)), stream)
 
 
 def gemm_strerror(code: int) -> str:
@@ -281,14 +295,15 @@ def mxfp8(A, SA, B, SB, out=None, *, out_dtype=None, row_scale=None, col_scale=N
     return C
 
 
-def attention(Q, K, V, *, causal=False, scale=None, out=None, lse=False):
-    """Fused attention forward (``attn_fwd_bf16``) of bf16 CUDA tensors.
+def attention(Q, K, V, *, causal=False, scale=None, out=None, lse=False, out_dtype=None):
+    """Fused attention forward (``attn_fwd_bf16_out``) of bf16 CUDA tensors.
 
     Q: (B, Hq, Sq, D); K, V: (B, Hkv, Sk, D), Hq a multiple of Hkv, D 64 or
     128, any strides with a contiguous last dimension (so [B][S][H][D]
-    storage viewed as (B, H, S, D) works).  Returns the fp32 output
-    (B, Hq, Sq, D), and with lse=True also the fp32 log-sum-exp (B, Hq, Sq).
-    scale defaults to 1/sqrt(D)."""
+    storage viewed as (B, H, S, D) works).  Returns the output (B, Hq, Sq, D)
+    in out_dtype (float32 by default, or bfloat16; an ``out`` tensor sets it),
+    and with lse=True also the fp32 log-sum-exp (B, Hq, Sq).  scale defaults
+    to 1/sqrt(D)."""
     import math
     import torch
     for t, name in ((Q, "Q"), (K, "K"), (V, "V")):
@@ -302,13 +317,18 @@ def attention(Q, K, V, *, causal=False, scale=None, out=None, lse=False):
         raise ValueError("K and V must be (B, Hkv, Sk, D) with Q's B and D")
     if scale is None:
         scale = 1.0 / math.sqrt(D)
+    if out_dtype is None:
+        out_dtype = out.dtype if out is not None else torch.float32
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("out_dtype must be torch.float32 or torch.bfloat16")
     if out is None:
-        out = torch.empty((B, Hq, Sq, D), dtype=torch.float32, device=Q.device)
-    elif out.shape != (B, Hq, Sq, D) or out.dtype != torch.float32 or (D > 1 and out.stride(3) != 1):
-        raise ValueError("out must be a float32 (B, Hq, Sq, D) tensor with a contiguous last dimension")
+        out = torch.empty((B, Hq, Sq, D), dtype=out_dtype, device=Q.device)
+    elif out.shape != (B, Hq, Sq, D) or out.dtype != out_dtype or (D > 1 and out.stride(3) != 1):
+        raise ValueError("out must be a (B, Hq, Sq, D) tensor of out_dtype with a contiguous last dimension")
     L = torch.empty((B, Hq, Sq), dtype=torch.float32, device=Q.device) if lse else None
     st = lambda t: (t.stride(0), t.stride(1), t.stride(2))
-    _check(attn_fwd_bf16(B, Hq, Hkv, Sq, Sk, D, Q.data_ptr(), st(Q), K.data_ptr(), st(K), V.data_ptr(), st(V),
-                         out.data_ptr(), st(out), L.data_ptr() if lse else None, scale, causal,
-                         _stream(Q.device)))
+    out_type = GEMM_OUT_BF16 if out_dtype == torch.bfloat16 else GEMM_OUT_F32
+    _check(attn_fwd_bf16_out(B, Hq, Hkv, Sq, Sk, D, Q.data_ptr(), st(Q), K.data_ptr(), st(K), V.data_ptr(),
+                             st(V), out.data_ptr(), st(out), out_type, L.data_ptr() if lse else None, scale,
+                             causal, _stream(Q.device)))
     return (out, L) if lse else out

@@ -78,7 +78,7 @@ struct Params {
     const uint8_t* Q;
     const uint8_t* K;
     const uint8_t* V;
-    float* O;
+    uint8_t* O;   // fp32 or bf16 elements, as o_bf16 says
     float* lse;
     int64_t q_b, q_h, k_b, k_h, v_b, v_h, o_b, o_h;  // batch / head strides, elements
     int q_s, k_s, v_s, o_s;                          // sequence strides, elements
@@ -87,6 +87,7 @@ struct Params {
     float scale;
     int xcd_remap;
     int prio;     // raise the wave's issue priority around its MFMA phases
+    int o_bf16;   // store O as bf16 (nearest even) instead of fp32
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
@@ -448,7 +449,7 @@ __global__ __launch_bounds__(kThreads, G == 1 ? 2 : 1) void attn_fwd_kernel(Para
     for (int g = 0; g < G; ++g) {
         const float l_tot = half_sum(l_run[g]);
         if (myq[g] < p.Sq) {
-            float* orow = p.O + (b * p.o_b + h * p.o_h) + (int64_t)myq[g] * p.o_s;
+            const int64_t orow = (b * p.o_b + h * p.o_h) + (int64_t)myq[g] * p.o_s;  // elements
             // no visible key: every weight was 0 (a visible row has one weight of exactly 1)
             const bool empty = l_tot == 0.0f;
             // a / l correctly rounded, one division per row: with the
@@ -467,7 +468,15 @@ __global__ __launch_bounds__(kThreads, G == 1 ? 2 : 1) void attn_fwd_kernel(Para
                         const float q = a * r;
                         v[j] = empty ? 0.0f : __builtin_fmaf(__builtin_fmaf(-q, l_tot, a), r, q);
                     }
-                    *(f32x4*)(orow + 32 * dt + 8 * i + 4 * hh) = v;
+                    const int64_t e = orow + 32 * dt + 8 * i + 4 * hh;
+                    if (p.o_bf16) {
+                        bf16x4 w;
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) w[j] = (__bf16)v[j];  // nearest even
+                        *(bf16x4*)(p.O + 2 * e) = w;
+                    } else {
+                        *(f32x4*)(p.O + 4 * e) = v;
+                    }
                 }
             if (p.lse && hh == 0)
                 p.lse[((int64_t)b * p.Hq + h) * p.Sq + myq[g]] =
@@ -554,13 +563,15 @@ int launch(const Params& p, int grid, hipStream_t stream) {
 
 }  // namespace
 
-extern "C" int attn_fwd_bf16(int64_t batch, int64_t heads_q, int64_t heads_kv,
-                             int64_t seq_q, int64_t seq_k, int64_t head_dim,
-                             const void* Q, const int64_t* q_strides,
-                             const void* K, const int64_t* k_strides,
-                             const void* V, const int64_t* v_strides,
-                             float* O, const int64_t* o_strides,
-                             float* lse, float scale, int causal, void* stream) {
+extern "C" int attn_fwd_bf16_out(int64_t batch, int64_t heads_q, int64_t heads_kv,
+                                 int64_t seq_q, int64_t seq_k, int64_t head_dim,
+                                 const void* Q, const int64_t* q_strides,
+                                 const void* K, const int64_t* k_strides,
+                                 const void* V, const int64_t* v_strides,
+                                 void* O, const int64_t* o_strides, int out_type,
+                                 float* lse, float scale, int causal, void* stream) {
+    if (out_type != GEMM_OUT_F32 && out_type != GEMM_OUT_BF16) return GEMM_ERR_INVALID_ARG;
+    const int64_t o_size = out_type == GEMM_OUT_BF16 ? 2 : 4;
     if (batch < 0 || seq_q < 0 || seq_k < 0 || heads_q < 1 || heads_kv < 1) return GEMM_ERR_INVALID_ARG;
     if (heads_q % heads_kv != 0) return GEMM_ERR_INVALID_ARG;
     if (head_dim != 64 && head_dim != 128) return GEMM_ERR_INVALID_ARG;
@@ -576,13 +587,13 @@ extern "C" int attn_fwd_bf16(int64_t batch, int64_t heads_q, int64_t heads_kv,
         return GEMM_ERR_INVALID_ARG;
     if (qs[2] < head_dim || ks[2] < head_dim || vs[2] < head_dim || os[2] < head_dim)
         return GEMM_ERR_INVALID_ARG;
-    if (!span_ok(seq_q + 2 * kQB, qs[2], head_dim, 2) || !span_ok(seq_q + 2 * kQB, os[2], head_dim, 4) ||
+    if (!span_ok(seq_q + 2 * kQB, qs[2], head_dim, 2) || !span_ok(seq_q + 2 * kQB, os[2], head_dim, o_size) ||
         !span_ok(seq_k + kKB, ks[2], head_dim, 2) || !span_ok(seq_k + kKB, vs[2], head_dim, 2))
         return GEMM_ERR_INVALID_ARG;
     const bool rows = batch > 0 && seq_q > 0;
     if (rows && (Q == nullptr || O == nullptr)) return GEMM_ERR_INVALID_ARG;
     if (rows && seq_k > 0 && (K == nullptr || V == nullptr)) return GEMM_ERR_INVALID_ARG;
-    if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16) || !aligned(lse, 4))
+    if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 4 * o_size) || !aligned(lse, 4))
         return GEMM_ERR_INVALID_ARG;
     const int rc = device_supported();
     if (rc != GEMM_OK) return rc;
@@ -592,7 +603,8 @@ extern "C" int attn_fwd_bf16(int64_t batch, int64_t heads_q, int64_t heads_kv,
     p.Q = (const uint8_t*)Q;
     p.K = (const uint8_t*)K;
     p.V = (const uint8_t*)V;
-    p.O = O;
+    p.O = (uint8_t*)O;
+    p.o_bf16 = out_type == GEMM_OUT_BF16;
     p.lse = lse;
     p.q_b = qs[0];
     p.q_h = qs[1];
@@ -629,4 +641,15 @@ extern "C" int attn_fwd_bf16(int64_t batch, int64_t heads_q, int64_t heads_kv,
     if (head_dim == 128)
         return c ? launch<128, true, 1>(p, (int)grid, st) : launch<128, false, 1>(p, (int)grid, st);
     return c ? launch<64, true, 1>(p, (int)grid, st) : launch<64, false, 1>(p, (int)grid, st);
+}
+
+extern "C" int attn_fwd_bf16(int64_t batch, int64_t heads_q, int64_t heads_kv,
+                             int64_t seq_q, int64_t seq_k, int64_t head_dim,
+                             const void* Q, const int64_t* q_strides,
+                             const void* K, const int64_t* k_strides,
+                             const void* V, const int64_t* v_strides,
+                             float* O, const int64_t* o_strides,
+                             float* lse, float scale, int causal, void* stream) {
+    return attn_fwd_bf16_out(batch, heads_q, heads_kv, seq_q, seq_k, head_dim, Q, q_strides, K, k_strides, V,
+                             v_strides, O, o_strides, GEMM_OUT_F32, lse, scale, causal, stream);
 }

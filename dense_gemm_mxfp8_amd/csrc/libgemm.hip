@@ -1317,6 +1317,6 @@ const char* gemm_strerror(int code) {
     }
 }
 
-int gemm_version(void) { return 300; }
+int gemm_version(void) { return 301; }
 
 }  // extern "C"

@@ -71,6 +71,24 @@ int attn_fwd_bf16(int64_t batch, int64_t heads_q, int64_t heads_kv,
                   float* O, const int64_t* o_strides,
                   float* lse, float scale, int causal, void* stream);
 
+/* The same operation with the output type chosen by out_type (the constants
+ * of libgemm.h): GEMM_OUT_F32 is attn_fwd_bf16 exactly; GEMM_OUT_BF16 stores
+ * O as bf16, each element the fp32 result above rounded to nearest even
+ * (NaN stays NaN), so the output has Q's type and half the bytes.  O is then
+ * a 2-byte element array, 8-byte aligned, with strides (in its own elements)
+ * that are multiples of 4; the 2 GiB span rule counts its 2-byte rows.  The
+ * error bound adds that final rounding, 2^-8 |O| relative (bf16's unit
+ * roundoff).  lse stays fp32.
+ * Any other out_type, or any requirement above broken, returns
+ * GEMM_ERR_INVALID_ARG with nothing written. */
+int attn_fwd_bf16_out(int64_t batch, int64_t heads_q, int64_t heads_kv,
+                      int64_t seq_q, int64_t seq_k, int64_t head_dim,
+                      const void* Q, const int64_t* q_strides,
+                      const void* K, const int64_t* k_strides,
+                      const void* V, const int64_t* v_strides,
+                      void* O, const int64_t* o_strides, int out_type,
+                      float* lse, float scale, int causal, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -180,3 +180,23 @@ def test_attention_rejects_bad_arguments():
     for change in bad:
         args = dict(ok, **change)
         assert dg.attn_fwd_bf16(**args) == dg.GEMM_ERR_INVALID_ARG, change
+
+
+def test_attention_out_type_rejects_bad_arguments():
+    """attn_fwd_bf16_out checks its output type and the alignment that type
+    needs before any device call; every attn_fwd_bf16 rejection holds too."""
+    F = FAKE * 16
+    ok = dict(batch=2, heads_q=4, heads_kv=2, seq_q=100, seq_k=90, head_dim=128, Q=F, q_strides=None, K=F,
+              k_strides=None, V=F, v_strides=None, O=F, o_strides=None, out_type=dg.GEMM_OUT_BF16, lse=None,
+              scale=0.1, causal=0, stream=0)
+    bad = [
+        dict(out_type=2), dict(out_type=-1),
+        dict(O=F + 4),                                        # bf16 O: 8-byte aligned
+        dict(O=F + 8, out_type=dg.GEMM_OUT_F32),              # fp32 O: 16-byte aligned
+        dict(o_strides=(0, 0, 130)),                          # multiples of 4 elements
+        dict(o_strides=(0, 0, 64)),                           # sequence stride below head_dim
+        dict(head_dim=96), dict(Q=F + 2), dict(scale=0.0), dict(O=0),
+    ]
+    for change in bad:
+        args = dict(ok, **change)
+        assert dg.attn_fwd_bf16_out(**args) == dg.GEMM_ERR_INVALID_ARG, change

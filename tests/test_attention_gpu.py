@@ -313,3 +313,61 @@ def test_attention_two_groups(shape, monkeypatch):
     monkeypatch.delenv("ATTN_GROUPS")
     O1, L1 = run(*to_dev(p), p.scale, causal)
     assert np.array_equal(O, O1) and np.array_equal(L, L1)
+
+
+def run_bf16_out(Q, K, V, scale, causal, O=None):
+    """attn_fwd_bf16_out with a bf16 output (NaN-filled beforehand) through
+    the C ABI; returns the output's raw bits and lse."""
+    B, Hq, Sq, D = Q.shape
+    Hkv, Sk = K.shape[1], K.shape[2]
+    if O is None:
+        O = torch.full((B, Hq, Sq, D), float("nan"), dtype=torch.bfloat16, device=DEV)
+    L = torch.full((B, Hq, Sq), float("nan"), dtype=torch.float32, device=DEV)
+    rc = dg.attn_fwd_bf16_out(B, Hq, Hkv, Sq, Sk, D, Q.data_ptr(), dense_strides(Q), K.data_ptr(),
+                              dense_strides(K), V.data_ptr(), dense_strides(V), O.data_ptr(), dense_strides(O),
+                              dg.GEMM_OUT_BF16, L.data_ptr(), scale, causal, P.stream())
+    assert rc == dg.GEMM_OK, dg.gemm_strerror(rc)
+    torch.cuda.synchronize()
+    return P.bits16(O.cpu()), L.cpu().numpy()
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", [(2, 4, 2, 300, 257, 128), (1, 4, 1, 200, 70, 64), (1, 8, 2, 513, 513, 128)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_attention_bf16_output(shape, causal):
+    """bf16 output: every element is the fp32 output rounded to nearest even
+    (bit for bit, against torch's rounding of the fp32 entry point's result),
+    lse is unchanged, and against the oracle the bound above plus bf16's
+    unit roundoff 2^-8 |O| holds."""
+    B, Hq, Hkv, Sq, Sk, D = shape
+    seed = 2000 + sum(shape) + int(causal)
+    P.note(f"attention bf16 output {shape} causal={causal} seed={seed}")
+    p = inputs.attn_problem(B, Hq, Hkv, Sq, Sk, D, causal, dist="normal", seed=seed)
+    Ob, Lb = run_bf16_out(*to_dev(p), p.scale, causal)
+    O32, L32 = run(*to_dev(p), p.scale, causal)
+    want = P.bits16(torch.from_numpy(O32).to(torch.bfloat16))
+    assert np.array_equal(Ob, want), f"{(Ob != want).sum()} outputs differ from the rounded fp32 result"
+    assert np.array_equal(Lb, L32)
+    Qb, Kb, Vb = P.bits16(p.Q), P.bits16(p.K), P.bits16(p.V)
+    Ow, Om, Lw = oracle.attention_fwd(Qb, Kb, Vb, p.scale, causal)
+    rel = 2.0 ** -8 * (1 + 2.0 ** -6) + 4 * gamma(Sk) + 4 * p.scale * gamma(D) * qk_abs_max(Qb, Kb)[..., None] \
+        + 2.0 ** -20
+    lim = rel * Om * (1 + 2.0 ** -8) + 2.0 ** -8 * np.abs(Ow) + 1e-30
+    O = (Ob.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    err = np.abs(O - Ow)
+    assert (err <= lim).all(), f"worst err/bound {(err / lim).max():.3g}"
+
+
+def test_attention_bf16_output_strided_and_helper():
+    """bf16 output into a [B][S][H][D] view equals the dense one, and the
+    tensor helper's out_dtype=bfloat16 goes through the same entry point."""
+    B, Hq, Hkv, Sq, Sk, D = 2, 4, 2, 150, 190, 128
+    P.note("attention bf16 output strided + helper")
+    p = inputs.attn_problem(B, Hq, Hkv, Sq, Sk, D, True, seed=82)
+    Os = torch.full((B, Sq, Hq, D), float("nan"), dtype=torch.bfloat16, device=DEV).transpose(1, 2)
+    Ob_s, _ = run_bf16_out(*to_dev(p), p.scale, True, O=Os)
+    Ob, _ = run_bf16_out(*to_dev(p), p.scale, True)
+    assert np.array_equal(Ob_s, Ob)
+    Oh = dg.attention(*to_dev(p), causal=True, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert Oh.dtype == torch.bfloat16 and np.array_equal(P.bits16(Oh.cpu()), Ob)
