@@ -51,6 +51,18 @@ def integer_bf16(shape, gen: torch.Generator, lo: int = -4, hi: int = 4) -> torc
     return torch.randint(lo, hi + 1, shape, generator=gen, dtype=torch.int32).to(torch.bfloat16)
 
 
+def integer_bf16_large(rows: int, cols: int, gen: torch.Generator, lo: int = -4, hi: int = 4,
+                       chunk_rows: int = 8192) -> torch.Tensor:
+    """A [rows, cols] integer_bf16 matrix drawn chunk_rows rows at a time from
+    one generator, so that operands of several GiB need only one chunk of
+    int32 scratch (deterministic for a given chunk_rows)."""
+    out = torch.empty((rows, cols), dtype=torch.bfloat16)
+    for r0 in range(0, rows, chunk_rows):
+        r1 = min(rows, r0 + chunk_rows)
+        out[r0:r1] = integer_bf16((r1 - r0, cols), gen, lo, hi)
+    return out
+
+
 def mx_quantize(x: torch.Tensor):
     """Quantise a float32 [R, K] tensor (K a multiple of 32) into OCP MX form.
 

@@ -17,7 +17,11 @@
  *
  * Conventions shared by every entry point (the correctness contract of
  * "GPU 执行模型", section "正确性契约"):
- *   - Sizes and leading dimensions are in ELEMENTS, as int64_t.
+ *   - Sizes and leading dimensions are in ELEMENTS, as int64_t.  M, N and K
+ *     may each be up to 2^31 - 1 (GEMM_ERR_INVALID_ARG beyond); operands and
+ *     C may be larger than 4 GiB.  Operands whose rows or K-panels would span
+ *     more than 2 GiB in one 32-bit buffer descriptor are routed to kernels
+ *     with 64-bit addressing, which are slower but give the same contract.
  *   - A is row-major: element (i, k) at A[i*lda + k], lda >= K.
  *   - C is row-major fp32: element (i, j) at C[i*ldc + j], ldc >= N.  C is
  *     overwritten (no alpha/beta); elements outside the M x N block and the
