@@ -58,6 +58,11 @@ def library() -> ctypes.CDLL:
         lib.gemm_bf16_splitk_plan.restype = ctypes.c_int
         lib.gemm_bf16_splitk_plan.argtypes = [_i64, _i64, _i64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                               ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_size_t)]
+        lib.gemm_bf16_splitk_workspace.restype = ctypes.c_int
+        lib.gemm_bf16_splitk_workspace.argtypes = [_i64, _i64, _i64, _vp, _i64, _vp, _i64, ctypes.c_int, _vp,
+                                                   _i64, ctypes.c_int, _vp, _vp, _vp, ctypes.c_int, ctypes.c_int,
+                                                   ctypes.POINTER(ctypes.c_int),
+                                                   ctypes.POINTER(ctypes.c_size_t)]
         lib.gemm_bf16_dynamic.restype = ctypes.c_int
         lib.gemm_bf16_dynamic.argtypes = [_i64, _i64, _i64, _vp, _i64, _vp, _i64, ctypes.c_int, _vp, _i64, _vp,
                                           ctypes.c_size_t, _vp]
@@ -112,6 +117,18 @@ def gemm_bf16_splitk_plan(M, N, K, b_colmajor, splits=0, cus=0):
     ws = ctypes.c_size_t(0)
     rc = library().gemm_bf16_splitk_plan(M, N, K, int(b_colmajor), splits, cus, ctypes.byref(used),
                                          ctypes.byref(ws))
+    return rc, used.value, ws.value
+
+
+def gemm_bf16_splitk_workspace(M, N, K, A, lda, B, ldb, b_colmajor, C, ldc, out_type, row_scale, col_scale,
+                               bias, splits=0, cus=0):
+    """(return code, K ranges used, workspace bytes) of the plan gemm_bf16_splitk
+    runs for these arguments (pointers are inspected, never dereferenced)."""
+    used = ctypes.c_int(0)
+    ws = ctypes.c_size_t(0)
+    rc = library().gemm_bf16_splitk_workspace(M, N, K, A, lda, B, ldb, int(b_colmajor), C, ldc, out_type,
+                                              row_scale, col_scale, bias, splits, cus, ctypes.byref(used),
+                                              ctypes.byref(ws))
     return rc, used.value, ws.value
 
 
@@ -199,35 +216,53 @@ def _epilogue(out_dtype, row_scale, col_scale, bias, M, N):
     return fused, out_type, ptrs
 
 
-def _bf16_operands(A, B):
-    """(M, N, K, lda, ldb, b_colmajor) of bf16 operands A (M, K) and B (K, N)."""
+def _bf16_operands(A, B, b_colmajor=None):
+    """(M, N, K, lda, ldb, b_colmajor) of bf16 operands A (M, K) and B.
+
+    b_colmajor None: B is the (K, N) operand, and its strides say whether it
+    is row-major (unit column stride) or column-major (unit row stride).
+    b_colmajor True: B is the (N, K) storage of a column-major K x N operand
+    (unit stride along K), as gemm_bf16_nt reads it.  False: B is a (K, N)
+    row-major tensor (unit column stride), as gemm_bf16 reads it."""
     import torch
     if A.dtype != torch.bfloat16 or B.dtype != torch.bfloat16:
         raise TypeError("A and B must be bfloat16")
+    if b_colmajor:
+        if B.dim() != 2:
+            raise ValueError("B must be 2-D")
+        if B.shape[0] > 1 and B.shape[1] > 1 and B.stride(1) != 1:
+            raise ValueError("b_colmajor=True: B must be (N, K) with unit stride along K")
+        B = B.t()
     if A.dim() != 2 or B.dim() != 2 or A.shape[1] != B.shape[0]:
-        raise ValueError("A must be (M, K) and B (K, N)")
+        raise ValueError("A must be (M, K) and B (K, N)" + (" (given as (N, K))" if b_colmajor else ""))
     M, K = A.shape
     N = B.shape[1]
     if M > 0 and K > 1 and A.stride(1) != 1:
         raise ValueError("A needs unit column stride")
     lda = A.stride(0) if M > 1 else max(K, 1)
+    if b_colmajor:
+        return M, N, K, lda, (B.stride(1) if N > 1 else max(K, 1)), True
     if N <= 1 or B.stride(1) == 1:
         return M, N, K, lda, (B.stride(0) if K > 1 else max(N, 1)), False
-    if B.stride(0) == 1:
+    if b_colmajor is None and B.stride(0) == 1:
         return M, N, K, lda, B.stride(1), True
-    raise ValueError("B must have a unit stride along N (row-major) or K (column-major)")
+    raise ValueError("B must have a unit stride along N (row-major)" +
+                     (" or K (column-major)" if b_colmajor is None else ""))
 
 
-def bf16(A, B, out=None, *, out_dtype=None, row_scale=None, col_scale=None, bias=None):
+def bf16(A, B, out=None, *, b_colmajor=None, out_dtype=None, row_scale=None, col_scale=None, bias=None):
     """C = A @ B in fp32 from bf16 CUDA tensors.
 
-    A: (M, K), row-major rows (unit column stride).  B: a (K, N) tensor that is
-    either row-major (unit column stride: ``gemm_bf16``) or column-major
-    (unit row stride, e.g. ``Bt.t()`` of an (N, K) tensor: ``gemm_bf16_nt``).
+    A: (M, K), row-major rows (unit column stride).  B, with b_colmajor None
+    (the default): a (K, N) tensor that is either row-major (unit column
+    stride: ``gemm_bf16``) or column-major (unit row stride, e.g. ``Bt.t()``
+    of an (N, K) tensor: ``gemm_bf16_nt``), told apart by its strides.
+    b_colmajor=True: B is that (N, K) tensor itself (``gemm_bf16_nt``);
+    b_colmajor=False: B must be row-major (K, N) (``gemm_bf16``).
     With any of out_dtype (float32 or bfloat16), row_scale (M), col_scale (N)
     or bias (N) the fused epilogue applies: C = A @ B * row_scale[:, None] *
     col_scale[None, :] + bias[None, :] (``gemm_bf16_fused``)."""
-    M, N, K, lda, ldb, colmajor = _bf16_operands(A, B)
+    M, N, K, lda, ldb, colmajor = _bf16_operands(A, B, b_colmajor)
     fn = gemm_bf16_nt if colmajor else gemm_bf16
     fused, out_type, (rs, cs, bs) = _epilogue(out_dtype, row_scale, col_scale, bias, M, N)
     C = _out(out, M, N, A.device, out_dtype)
@@ -240,19 +275,21 @@ def bf16(A, B, out=None, *, out_dtype=None, row_scale=None, col_scale=None, bias
     return C
 
 
-def bf16_splitk(A, B, out=None, *, splits=0, workspace=None, out_dtype=None, row_scale=None, col_scale=None,
-                bias=None):
+def bf16_splitk(A, B, out=None, *, b_colmajor=None, splits=0, workspace=None, out_dtype=None, row_scale=None,
+                col_scale=None, bias=None):
     """``bf16`` through ``gemm_bf16_splitk``: K cut into `splits` ranges (0:
     the library's plan) whose fp32 partial products are added in range
-    order.  workspace: a CUDA tensor of at least the planned bytes (16-byte
+    order.  workspace: a CUDA tensor of at least the bytes
+    ``gemm_bf16_splitk_workspace`` reports for these arguments (16-byte
     aligned); None allocates one with torch for this call."""
     import torch
-    M, N, K, lda, ldb, colmajor = _bf16_operands(A, B)
+    M, N, K, lda, ldb, colmajor = _bf16_operands(A, B, b_colmajor)
     _, out_type, (rs, cs, bs) = _epilogue(out_dtype, row_scale, col_scale, bias, M, N)
     C = _out(out, M, N, A.device, out_dtype)
     ldc = C.stride(0) if M > 1 else max(N, 1)
     if workspace is None:
-        rc, _, nbytes = gemm_bf16_splitk_plan(M, N, K, colmajor, splits)
+        rc, _, nbytes = gemm_bf16_splitk_workspace(M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, colmajor,
+                                                   C.data_ptr(), ldc, out_type, rs, cs, bs, splits)
         _check(rc)
         workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=A.device)
     nbytes = workspace.numel() * workspace.element_size()

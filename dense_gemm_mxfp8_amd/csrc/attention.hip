@@ -523,10 +523,16 @@ int attn_groups() {
     return (e && e[0] == '2') ? 2 : 1;
 }
 
-// Wave priority around the MFMA phases: ATTN_PRIO=0 turns it off.
+// Wave priority around the MFMA phases.  Measurement builds
+// (-DLIBGEMM_MEASURE) turn it off with ATTN_PRIO=0; the default build always
+// raises it.
 int attn_prio() {
+#ifdef LIBGEMM_MEASURE
     const char* e = getenv("ATTN_PRIO");
     return (e && e[0] == '0') ? 0 : 1;
+#else
+    return 1;
+#endif
 }
 
 bool aligned(const void* p, uintptr_t a) { return (((uintptr_t)p) & (a - 1)) == 0; }

@@ -17,6 +17,12 @@
 //   k-step 1:             wait for LDS, barrier (stage t+1 complete, stage t
 //                         fully read), read step 0 of t+1, multiply step 1.
 //
+// A load is thus issued PF k-tiles before its registers are stored: with
+// one 256 x 192 tile per CU a k-tile is 24 MFMAs (768 matrix-core cycles) per
+// wave, and the loads come from L2 or the Infinity Cache, whose latency under
+// load is one to two such k-tiles, so more than one register set in flight
+// is what keeps the matrix cores fed.
+//
 // Bounds: rows past M / N and k-rows past K (row-major B) lie outside the
 // per-tile buffer descriptors and load as zero.  A descriptor starts at the
 // operand's address rounded down to 4 bytes (the difference goes into the
@@ -51,14 +57,19 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t span_rsrc(const uint8_t* p, in
     return make_rsrc(p - shift, (shift + bytes + 3) & ~(int64_t)3);
 }
 
-// PF: k-tiles held in registers ahead of the stage being filled (1 or 2
-// register sets).  BN: tile columns, 256 or 192 (wave tiles 128 x BN/2); the
-// narrower tile lets the host match the tile count to the CU count.
+// PF: k-tiles held in registers ahead of the stage being filled (1, 2 or 4
+// register sets; k-tile j lives in set j % PF).  BN: tile columns, 256 or
+// 192 (wave tiles 128 x BN/2); the narrower tile lets the host match the
+// tile count to the CU count.
 // FUSED: the fused epilogue of gemm_epi.h instead of the plain fp32 store.
 template <int KIND, bool TAIL, int PF = 2, int BN = kTile, bool FUSED = false>
 __global__ __launch_bounds__(kThreads, 1) void gemm_reg_kernel(Args a) {
     static_assert(KIND == kNT || KIND == kNN, "bf16 only");
-    static_assert(PF == 1 || PF == 2, "one or two register sets");
+    static_assert(PF == 1 || PF == 2 || PF == 4, "1, 2 or 4 register sets");
+    // the K loop is unrolled by U k-tiles so that the stage (k-tile parity)
+    // and the register set (k-tile mod PF) of every unrolled k-tile are
+    // compile-time constants
+    constexpr int U = PF > 2 ? PF : 2;
     static_assert(BN == 256 || BN == 192, "tile columns");
     constexpr int NBJ = BN / 64;      // 32-column MFMA blocks per wave tile
     constexpr int WTN = BN / 2;       // wave tile columns
@@ -118,7 +129,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_reg_kernel(Args a) {
     }
 
     const int KT = a.kt_full;
-    const int KTM = (KT + 1) / 2 * 2;
+    const int KTM = (KT + U - 1) / U * U;  // the k-tiles past KT are dead (zero)
 
     const int G = gridDim.x;
     for (int t = logical_block(a); t < a.num_tiles; t += G) {
@@ -195,11 +206,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_reg_kernel(Args a) {
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
         };
 
-        // prologue: k-tile 0 into stage 0, k-tiles 1 .. PF in flight to registers
+        // prologue: k-tile 0 into stage 0, k-tiles 1 .. PF in flight to
+        // registers (k-tile j in set j % PF)
         using Z = std::integral_constant<int, 0>;
-        using O = std::integral_constant<int, PF - 1>;
         load(Z{}, 0, 0 < KT);
-        if constexpr (PF == 2) load(O{}, 1, 1 < KT);
+        static_for<1, PF>([&](auto qc) { load(qc, decltype(qc)::value, decltype(qc)::value < KT); });
         store(Z{}, Z{});
         load(Z{}, PF, PF < KT);
         wait_lgkm0();
@@ -207,15 +218,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_reg_kernel(Args a) {
         bf16x8 F0a[kBlocks], F0b[NBJ], F1a[kBlocks], F1b[NBJ];
         read_frags(std::integral_constant<int, 0>{}, 0, F0a, F0b);
 
-        auto body = [&](auto sidx, int kt) {
-            constexpr int sn = decltype(sidx)::value ^ 1;
-            // k-step 0: stage of k-tile kt+1 <- registers, loads of kt+2,
-            // fragments of step 1
-            // k-tile kt+1 sits in set (kt+1) % PF; kt+1+PF goes there next
-            using Q = std::integral_constant<int, PF == 2 ? sn : 0>;
+        auto body = [&](auto qidx, int kt) {
+            constexpr int q = decltype(qidx)::value;  // kt % U
+            using sidx = std::integral_constant<int, q % 2>;
+            constexpr int sn = (q % 2) ^ 1;
+            // k-step 0: stage of k-tile kt+1 <- registers, loads of
+            // kt+1+PF, fragments of step 1.  k-tile kt+1 sits in set
+            // (kt+1) % PF; kt+1+PF goes there next.
+            using Q = std::integral_constant<int, (q + 1) % PF>;
             store(Q{}, std::integral_constant<int, sn>{});
             load(Q{}, kt + 1 + PF, kt + 1 + PF < KT);
-            read_frags(sidx, 1, F1a, F1b);
+            read_frags(sidx{}, 1, F1a, F1b);
             mfma(F0a, F0b);
             __builtin_amdgcn_sched_barrier(0);
             // k-step 1
@@ -225,9 +238,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_reg_kernel(Args a) {
             mfma(F1a, F1b);
             __builtin_amdgcn_sched_barrier(0);
         };
-        for (int kt0 = 0; kt0 < KTM; kt0 += 2) {
-            body(std::integral_constant<int, 0>{}, kt0);
-            body(std::integral_constant<int, 1>{}, kt0 + 1);
+        for (int kt0 = 0; kt0 < KTM; kt0 += U) {
+            static_for<0, U>([&](auto qc) { body(qc, kt0 + decltype(qc)::value); });
         }
 
         if constexpr (TAIL) {
@@ -284,7 +296,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_reg_kernel(Args a) {
             }
             // the last body ended with a barrier after every wave's reads of
             // k-tile data in stage 0 (KTM is even, so stage 0 is free; the
-            // reads that follow that barrier fetch the unused dead k-tile)
+            // reads that follow that barrier fetch the unused dead k-tile).
+            // Register set 0 is reused: loads still in flight into it (dead
+            // k-tiles) are waited for before it is overwritten.
             store(Z{}, Z{});
             wait_lgkm0();
             barrier();

@@ -33,8 +33,11 @@
 //     with element predicates and zero fill;
 //   * epilogue: predicated fp32 stores straight from the accumulators.
 //
-// Lane layouts used below (checked on gfx950 with one-hot / random-integer
-// single-instruction tests):
+// Lane layouts used below.  They are not checked one instruction at a time:
+// the GEMM parity tests pin them as a whole, since a map that pairs a(i, k)
+// with b(k', j) for k' != k, applies a block scale to the wrong 32 elements,
+// or stores a sum at the wrong (i, j) breaks the bit-exact integer-operand
+// results:
 //   v_mfma_f32_32x32x16_bf16: lane l supplies A[l%32][8*(l/32) + j] and
 //     B[8*(l/32) + j][l%32], j = 0..7; accumulator register i of lane l is
 //     D[8*(i/4) + 4*(l/32) + i%4][l%32].
@@ -637,10 +640,17 @@ struct FastVariant {
     int rb, stages, group, early, spread, waves;
 };
 
-// LIBGEMM_VARIANT=<rb>x<stages>[e<early>[d<spread>]] picks the pipeline (and
-// for two stages the early-DMA split); LIBGEMM_GROUP=<n> the number of tile
-// rows per raster band.
+// Measurement builds (-DLIBGEMM_MEASURE) read switches from the environment
+// that select other compiled pipelines for A/B timing:
+// LIBGEMM_VARIANT=<rb>x<stages>[e<early>[d<spread>[w<waves>]]] picks the
+// pipeline (and for two stages the early-DMA split); LIBGEMM_GROUP=<n> the
+// number of tile rows per raster band.  The library as built by default
+// compiles none of those instances and reads no environment variable: every
+// call runs the defaults below.
 FastVariant env_variant() {
+#ifndef LIBGEMM_MEASURE
+    return FastVariant{0, 0, 0, -1, 0, 4};
+#else
     static FastVariant v = [] {
         FastVariant r{0, 0, 0, -1, 0, 4};
         const char* e = getenv("LIBGEMM_VARIANT");
@@ -660,6 +670,7 @@ FastVariant env_variant() {
         return r;
     }();
     return v;
+#endif
 }
 
 // SPLIT: split-K units (a.kslice set, `splits` K ranges): the partial sums
@@ -753,11 +764,15 @@ fast::Args make_fast_args(int64_t M, int64_t N, int64_t K, const void* A, int64_
     // each line is written in two parts by two stores, and caching lets L2
     // merge them instead of sending partial lines to memory (measured on
     // MI355X: 4001 x 3003 x 2050 with ldc = 3003, 112 -> 92 us).
-    // LIBGEMM_C_NT=0|1 overrides the choice (measurement switch).
+    // LIBGEMM_C_NT=0|1 overrides the choice (measurement builds only).
+#ifdef LIBGEMM_MEASURE
     static int c_nt_env = [] {
         const char* e = getenv("LIBGEMM_C_NT");
         return e ? atoi(e) : -1;
     }();
+#else
+    constexpr int c_nt_env = -1;
+#endif
     // bf16 output: a 32-column segment is 64 bytes, half a line
     const bool lines = !e.out_bf16 && ((uintptr_t)C % 128 == 0) && (ldc % 32 == 0);
     a.c_nt = c_nt_env >= 0 ? c_nt_env : (lines ? 1 : 0);
@@ -775,18 +790,22 @@ int launch_fast_bf16(bool nt, const fast::Args& a, int cus, hipStream_t s) {
         return launch_fast<fast::kNN, 128, 2, 1, 6, 2, 4, true>(a, cus, s, g);
     }
     if (nt) {
+#ifdef LIBGEMM_MEASURE
         if (v.rb == 64 && v.stages == 4) return launch_fast<fast::kNT, 64, 4>(a, cus, s, g);
         // 8 waves (two per SIMD, 128 x 64 wave tiles): measured 1% slower
         // than 4 waves at 8192^3 on MI355X; kept for measurements
         if (v.waves == 8) return launch_fast<fast::kNT, 128, 2, 1, 4, 2, 8>(a, cus, s, g);
         if (v.early == 0) return launch_fast<fast::kNT, 128, 2>(a, cus, s, g);
+#endif
         // default: 6 DMA instructions of k-tile t+2 right after the barrier
         // of k-tile t, the other 10 over k-steps 0 and 1 of t+1 (MI355X,
         // 8192^3, same box: 776.5 -> 746.5 us and 797.6 -> 778.2 us)
         return launch_fast<fast::kNT, 128, 2, 1, 6, 2>(a, cus, s, g);
     }
+#ifdef LIBGEMM_MEASURE
     if (v.rb == 64 && v.stages == 4) return launch_fast<fast::kNN, 64, 4>(a, cus, s, g);
     if (v.rb == 128 && v.stages == 2 && v.early == 0) return launch_fast<fast::kNN, 128, 2>(a, cus, s, g);
+#endif
     // default: as NT (MI355X, 4096^3: 108.8 -> 105.5 us against 64 x 4;
     // 8192^3: 801.5 -> 771.2 us)
     return launch_fast<fast::kNN, 128, 2, 1, 6, 2>(a, cus, s, g);
@@ -851,29 +870,35 @@ int reg_tile_n(int64_t M, int64_t N, int cus) {
     return cost(192) < cost(256) ? 192 : 256;
 }
 
-// LIBGEMM_REGPF=1|2: register sets of prefetch (measurement switch)
+// Register sets of prefetch of the register kernel.
+constexpr int kRegPF = 1;
+
+// Measurement builds: LIBGEMM_REGPF=1|2|4 (register sets of prefetch) and
+// LIBGEMM_REG_BN=192|256 (tile columns) select other compiled instances.
 int launch_reg(bool nt, const fast::Args& a, int cus, hipStream_t stream) {
+    int bn = reg_tile_n(a.M, a.N, cus);
+#ifdef LIBGEMM_MEASURE
     static int pf = [] {
         const char* e = getenv("LIBGEMM_REGPF");
         return e ? atoi(e) : 0;
     }();
-    // one register set measured faster than two on MI355X (4001x3003x2050:
-    // 111.6 vs 116.7 us; 4096^3 with odd ld: 149 vs 160 us)
     static int bn_env = [] {
         const char* e = getenv("LIBGEMM_REG_BN");
         return e ? atoi(e) : 0;
     }();
-    const int bn = bn_env == 192 || bn_env == 256 ? bn_env : reg_tile_n(a.M, a.N, cus);
+    if (bn_env == 192 || bn_env == 256) bn = bn_env;
+    if (!a.epi.on && (pf == 1 || pf == 2 || pf == 4) && pf != kRegPF) {
+        if (pf == 1) return bn == 192 ? launch_reg_pf<1, 192>(nt, a, cus, stream) : launch_reg_pf<1, 256>(nt, a, cus, stream);
+        if (pf == 2) return bn == 192 ? launch_reg_pf<2, 192>(nt, a, cus, stream) : launch_reg_pf<2, 256>(nt, a, cus, stream);
+        return bn == 192 ? launch_reg_pf<4, 192>(nt, a, cus, stream) : launch_reg_pf<4, 256>(nt, a, cus, stream);
+    }
+#endif
     if (a.epi.on) {
-        if (bn == 192) return launch_reg_pf<1, 192, true>(nt, a, cus, stream);
-        return launch_reg_pf<1, 256, true>(nt, a, cus, stream);
+        if (bn == 192) return launch_reg_pf<kRegPF, 192, true>(nt, a, cus, stream);
+        return launch_reg_pf<kRegPF, 256, true>(nt, a, cus, stream);
     }
-    if (bn == 192) {
-        if (pf == 2) return launch_reg_pf<2, 192>(nt, a, cus, stream);
-        return launch_reg_pf<1, 192>(nt, a, cus, stream);
-    }
-    if (pf == 2) return launch_reg_pf<2, 256>(nt, a, cus, stream);
-    return launch_reg_pf<1, 256>(nt, a, cus, stream);
+    if (bn == 192) return launch_reg_pf<kRegPF, 192>(nt, a, cus, stream);
+    return launch_reg_pf<kRegPF, 256>(nt, a, cus, stream);
 }
 
 // ---------------------------------------------------------------------------
@@ -913,12 +938,14 @@ int launch_small(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, co
     const int64_t per = (kslice + WAVES - 1) / WAVES;
     a.kw = (int)((per + small::kStepK - 1) / small::kStepK * small::kStepK);
     const int grid = (int)((N + COLS - 1) / COLS);
+    a.pair_xcd = (COLS == 32 && grid % 16 == 0) ? 1 : 0;
+#ifdef LIBGEMM_MEASURE
     static const int pair_env = [] {
         const char* e = getenv("LIBGEMM_SMALL_PAIR");
         return e ? atoi(e) : -1;
     }();
-    a.pair_xcd = (COLS == 32 && grid % 16 == 0) ? 1 : 0;
-    if (pair_env == 0) a.pair_xcd = 0;  // measurement switch
+    if (pair_env == 0) a.pair_xcd = 0;  // LIBGEMM_SMALL_PAIR=0: no XCD pairing
+#endif
     hipLaunchKernelGGL((small::gemm_small_m_nn<MB, NP, COLS, WAVES>), dim3(grid, splits > 1 ? splits : 1),
                        dim3(64 * WAVES), 0, stream, a);
     return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
@@ -927,14 +954,15 @@ int launch_small(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, co
 int launch_small_bf16(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
                       void* C, int64_t ldc, const epi::Params& e, hipStream_t s, int splits = 1,
                       int64_t kslice = 0) {
-    // LIBGEMM_SMALL=<np>x<cols>x<waves> selects a compiled variant for measurements
-    static int sv = [] {
-        const char* e = getenv("LIBGEMM_SMALL");
-        int np = 0, c = 0, w = 0;
-        if (e && sscanf(e, "%dx%dx%d", &np, &c, &w) == 3) return np * 10000 + c * 100 + w;
-        return 0;
-    }();
     if (M <= 16) {
+#ifdef LIBGEMM_MEASURE
+        // LIBGEMM_SMALL=<np>x<cols>x<waves> selects another compiled variant
+        static int sv = [] {
+            const char* e = getenv("LIBGEMM_SMALL");
+            int np = 0, c = 0, w = 0;
+            if (e && sscanf(e, "%dx%dx%d", &np, &c, &w) == 3) return np * 10000 + c * 100 + w;
+            return 0;
+        }();
         if (sv == 120000 + 3208)
             return launch_small<1, 12, 32, 8>(M, N, K, A, lda, B, ldb, C, ldc, e, s, splits, kslice);
         if (sv == 80000 + 3216)
@@ -943,6 +971,7 @@ int launch_small_bf16(int64_t M, int64_t N, int64_t K, const void* A, int64_t ld
             return launch_small<1, 8, 64, 16>(M, N, K, A, lda, B, ldb, C, ldc, e, s, splits, kslice);
         if (sv == 80000 + 3208)
             return launch_small<1, 8, 32, 8>(M, N, K, A, lda, B, ldb, C, ldc, e, s, splits, kslice);
+#endif
         return launch_small<1, 4, 32, 16>(M, N, K, A, lda, B, ldb, C, ldc, e, s, splits, kslice);
     }
     if (M <= 32) return launch_small<2, 8, 32, 8>(M, N, K, A, lda, B, ldb, C, ldc, e, s, splits, kslice);
@@ -965,11 +994,13 @@ int bf16_dispatch(bool nt, int64_t M, int64_t N, int64_t K, const void* A, int64
     if (small_ok(nt, M, N, K, A, lda, B, ldb))
         return launch_small_bf16(M, N, K, A, lda, B, ldb, C, ldc, e, s);
     const bool big = use_big_tiles(M, N, dev.cus);
+#ifdef LIBGEMM_MEASURE
     // LIBGEMM_FORCE_REG=1 runs the register-load kernel where the direct-load
-    // one would (measurement switch)
+    // one would
     static const bool force_reg = getenv("LIBGEMM_FORCE_REG") != nullptr;
     if (force_reg && big && c_ok(ldc) && reg_ok(nt, K, lda, ldb))
         return launch_reg(nt, make_fast_args(M, N, K, A, lda, B, ldb, C, ldc, 2, e), dev.cus, s);
+#endif
     if (big && c_ok(ldc) && fast_ok(nt ? fast::kNT : fast::kNN, M, N, K, A, lda, B, ldb, nullptr, nullptr))
         return launch_fast_bf16(nt, make_fast_args(M, N, K, A, lda, B, ldb, C, ldc, 2, e), dev.cus, s);
     if (big && c_ok(ldc) && reg_ok(nt, K, lda, ldb))
@@ -1080,6 +1111,18 @@ SplitPlan plan_split(bool nt, int64_t M, int64_t N, int64_t K, bool aligned, int
     return p;
 }
 
+// The plan a split-K call runs: plan_split on the real operands, except that
+// the stream-K style plan stores whole tiles straight to C with the plain
+// fp32 epilogue (the split kernel has no fused store), so any other
+// epilogue, or a C too wide for 32-bit offsets, runs unsplit.
+SplitPlan resolve_split(bool nt, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+                        int64_t ldb, int64_t ldc, const epi::Params& e, int cus, int splits) {
+    SplitPlan p = plan_split(nt, M, N, K, aligned16(A) && aligned16(B), lda, ldb, cus, splits);
+    const bool plain = !e.out_bf16 && !e.rs && !e.cs && !e.bias;
+    if (p.rem > 0 && (!plain || !c_ok(ldc))) p.splits = 1;
+    return p;
+}
+
 int splitk_dispatch(bool nt, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
                     int64_t ldb, void* C, int64_t ldc, const epi::Params& e, int splits, void* ws,
                     size_t ws_bytes, void* stream) {
@@ -1090,11 +1133,7 @@ int splitk_dispatch(bool nt, int64_t M, int64_t N, int64_t K, const void* A, int
     DeviceInfo dev;
     rc = device_info(&dev);
     if (rc != GEMM_OK) return rc;
-    SplitPlan p = plan_split(nt, M, N, K, aligned16(A) && aligned16(B), lda, ldb, dev.cus, splits);
-    // the stream-K style plan stores whole tiles straight to C with the plain
-    // fp32 epilogue (the split kernel has no fused store)
-    const bool plain = !e.out_bf16 && !e.rs && !e.cs && !e.bias;
-    if (p.rem > 0 && (!plain || !c_ok(ldc))) p.splits = 1;
+    const SplitPlan p = resolve_split(nt, M, N, K, A, lda, B, ldb, ldc, e, dev.cus, splits);
     if (p.splits <= 1) return bf16_dispatch(nt, M, N, K, A, lda, B, ldb, C, ldc, e, stream);
     const int64_t need = plan_bytes(p, M, N);
     if (ws == nullptr || (int64_t)ws_bytes < need || ((uintptr_t)ws & 15)) return GEMM_ERR_INVALID_ARG;
@@ -1212,9 +1251,12 @@ int mx_dispatch(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, con
             if (word_scales) return launch_fast<fast::kMX, 128, 2, 1, 0, 0, 4, true>(f, dev.cus, s, v.group);
             return launch_fast<fast::kMX, 64, 4, 1, 0, 0, 4, true>(f, dev.cus, s, v.group);
         }
+#ifdef LIBGEMM_MEASURE
         if (v.rb == 64 && v.stages == 4) return launch_fast<fast::kMX, 64, 4>(f, dev.cus, s, v.group);
-        if (ring && !(v.rb == 128 && v.stages == 2)) {
-            if (v.early == 0) return launch_fast<fast::kMX, 128, 2, 4>(f, dev.cus, s, v.group);
+        if (ring && v.early == 0) return launch_fast<fast::kMX, 128, 2, 4>(f, dev.cus, s, v.group);
+        if (word_scales && v.rb == 128 && v.stages == 2) return launch_fast<fast::kMX, 128, 2>(f, dev.cus, s, v.group);
+#endif
+        if (ring) {
             // default: 12 of the 16 DMA instructions of k-tile t+2 right
             // after the barrier of k-tile t (MI355X, 8192^3, same box:
             // 491.5 -> 427.4 us)
@@ -1300,6 +1342,32 @@ int gemm_bf16_splitk_plan(int64_t M, int64_t N, int64_t K, int b_colmajor, int s
     // operands assumed 16-byte aligned with dense leading dimensions
     SplitPlan p{kSplitNone, 1, K, 0, 0};
     if (M > 0 && N > 0) p = plan_split(nt, M, N, K, true, K, nt ? K : N, cus, splits);
+    if (splits_used) *splits_used = p.splits;
+    if (workspace_bytes) *workspace_bytes = (size_t)plan_bytes(p, M, N);
+    return GEMM_OK;
+}
+
+int gemm_bf16_splitk_workspace(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+                                int64_t ldb, int b_colmajor, const void* C, int64_t ldc, int out_type,
+                                const float* row_scale, const float* col_scale, const float* bias, int splits,
+                                int cus, int* splits_used, size_t* workspace_bytes) {
+    epi::Params e;
+    int rc = fused_params(out_type, C, row_scale, col_scale, bias, &e);
+    if (rc != GEMM_OK) return rc;
+    if (splits < 0 || cus < 0) return GEMM_ERR_INVALID_ARG;
+    const bool nt = b_colmajor != 0;
+    rc = check_common(M, N, K, A, lda, B, ldb, nt ? K : N, C, ldc);
+    SplitPlan p{kSplitNone, 1, K, 0, 0};
+    if (rc != 1) {
+        if (rc != GEMM_OK) return rc;
+        if (cus == 0) {
+            DeviceInfo dev;
+            rc = device_info(&dev);
+            if (rc != GEMM_OK) return rc;
+            cus = dev.cus;
+        }
+        p = resolve_split(nt, M, N, K, A, lda, B, ldb, ldc, e, cus, splits);
+    }
     if (splits_used) *splits_used = p.splits;
     if (workspace_bytes) *workspace_bytes = (size_t)plan_bytes(p, M, N);
     return GEMM_OK;

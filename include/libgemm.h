@@ -201,6 +201,25 @@ int gemm_bf16_splitk(int64_t M, int64_t N, int64_t K,
 int gemm_bf16_splitk_plan(int64_t M, int64_t N, int64_t K, int b_colmajor, int splits, int cus,
                           int* splits_used, size_t* workspace_bytes);
 
+/* The split plan gemm_bf16_splitk runs for exactly these arguments (those of
+ * gemm_bf16_splitk without the workspace and the stream): the K ranges it
+ * uses (*splits_used, 1 = unsplit) and the workspace bytes they need
+ * (*workspace_bytes, 0 when unsplit).  Unlike gemm_bf16_splitk_plan it takes
+ * the real operand pointers and leading dimensions, whose alignment decides
+ * which kernel computes the partial products, and the epilogue, which
+ * decides whether a stream-K style plan applies.  The pointers are only
+ * inspected (for NULL and alignment), never dereferenced.  cus: compute
+ * units to plan for, 0 = those of the current device.  Errors: those
+ * gemm_bf16_splitk reports for these arguments before any device work
+ * (GEMM_ERR_INVALID_ARG; GEMM_ERR_UNSUPPORTED with cus == 0 and no gfx950
+ * device).  Runs on the host only. */
+int gemm_bf16_splitk_workspace(int64_t M, int64_t N, int64_t K,
+                               const void* A, int64_t lda,
+                               const void* B, int64_t ldb, int b_colmajor,
+                               const void* C, int64_t ldc, int out_type,
+                               const float* row_scale, const float* col_scale, const float* bias,
+                               int splits, int cus, int* splits_used, size_t* workspace_bytes);
+
 /* ---- dynamic tile schedule -----------------------------------------------
  *
  * "Modern GPU Programming For MLSys - 书籍总结", section 2.9 (Cluster Launch

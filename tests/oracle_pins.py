@@ -365,12 +365,51 @@ def pin_mx_nan(orc):
     assert np.isnan(C[:, 2]).all() and np.array_equal(np.delete(C, 2, 1), np.delete(clean, 2, 1))
 
 
+def pin_mx_sampled(orc):
+    """The sampled MX entry point equals the full product element for element,
+    at M != N, for positions that include the last row and column; a scale
+    shift on a sampled row doubles exactly that row's sampled outputs."""
+    M, N, K = 53, 37, 160
+    A, Bt, SA, SB = _mx_random(M, N, K, 800)
+    C, absC = orc.gemm_mxfp8(A, Bt.T, SA, SB)
+    g = rng(801)
+    # positions inside the leading min(M, N) square first: a sampler that
+    # swaps or repeats the indices reads in bounds there and must disagree
+    sq = min(M, N)
+    rows = np.concatenate([g.integers(0, sq, 60), np.arange(sq)])
+    cols = np.concatenate([g.integers(0, sq, 60), (np.arange(sq) * 7 + 3) % sq])
+    s, sabs = orc.gemm_mxfp8_at(A, Bt.T, SA, SB, rows, cols)
+    assert np.array_equal(s, C[rows, cols]) and np.array_equal(sabs, absC[rows, cols])
+    # the whole range: every last row and last column position
+    rows = np.concatenate([g.integers(0, M, 80), np.full(N, M - 1), np.arange(M)])
+    cols = np.concatenate([g.integers(0, N, 80), np.arange(N), np.full(M, N - 1)])
+    s, sabs = orc.gemm_mxfp8_at(A, Bt.T, SA, SB, rows, cols)
+    assert np.array_equal(s, C[rows, cols]) and np.array_equal(sabs, absC[rows, cols])
+    # +1 on every scale code of row 11 doubles its sampled outputs; +2 on
+    # block 3 of column 5 adds 3 times that block's part to column 5
+    SA2 = SA.copy()
+    SA2[11, :] += 1
+    s2, _ = orc.gemm_mxfp8_at(A, Bt.T, SA2, SB, rows, cols)
+    on = rows == 11
+    assert on.any() and np.array_equal(s2[on], 2 * s[on]) and np.array_equal(s2[~on], s[~on])
+    SB2 = SB.copy()
+    SB2[5, 3] += 2
+    s3, _ = orc.gemm_mxfp8_at(A, Bt.T, SA, SB2, rows, cols)
+    part, _ = orc.gemm_mxfp8(np.ascontiguousarray(A[:, 96:128]), np.ascontiguousarray(Bt[:, 96:128]).T,
+                             np.ascontiguousarray(SA[:, 3:4]), np.ascontiguousarray(SB[:, 3:4]))
+    on = cols == 5
+    want = s[on] + 3.0 * part[rows[on], 5]
+    assert on.any() and np.all(np.abs(s3[on] - want) <= 1e-12 * np.abs(absC[rows[on], 5]))
+    assert np.array_equal(s3[~on], s[~on])
+
+
 ALL_PINS = [
     pin_ledger_worked_example, pin_ledger_invariants,
     pin_bf16_decode, pin_e4m3_decode, pin_e8m0_decode,
     pin_bf16_bruteforce, pin_bf16_identity_permutation, pin_bf16_integer_exact,
     pin_bf16_freivalds, pin_bf16_strided_views, pin_bf16_special_values,
     pin_mx_bruteforce, pin_mx_unit_scales, pin_mx_scale_algebra, pin_mx_integer_exact, pin_mx_nan,
+    pin_mx_sampled,
 ]
 
 

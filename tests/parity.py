@@ -66,21 +66,52 @@ def assert_exact(got: np.ndarray, want: np.ndarray, what: str):
         raise AssertionError(f"{what}: not bit-exact at {d.tolist()}")
 
 
-def sample_positions(M: int, N: int, n: int, seed: int, tile: int = 256):
+def sample_positions(M: int, N: int, n: int, seed: int, tile_m: int = 256, tile_n: int = 256):
     """Random output positions plus the corners, the last row/column and
-    positions straddling tile boundaries."""
+    positions straddling the boundaries of the kernel's tiles (tile_m rows by
+    tile_n columns: 256 x 256 for the direct-load kernels, 256 x 192 when the
+    register kernel picks narrower tiles, 32-column blocks for small M)."""
     g = np.random.default_rng(seed)
     rows = list(g.integers(0, M, n))
     cols = list(g.integers(0, N, n))
-    edge_r = sorted({0, M - 1, max(M - 2, 0)} | {min(M - 1, t + d) for t in range(tile, M, tile)
+    edge_r = sorted({0, M - 1, max(M - 2, 0)} | {min(M - 1, t + d) for t in range(tile_m, M, tile_m)
                                                   for d in (-1, 0)})
-    edge_c = sorted({0, N - 1, max(N - 2, 0)} | {min(N - 1, t + d) for t in range(tile, N, tile)
+    edge_c = sorted({0, N - 1, max(N - 2, 0)} | {min(N - 1, t + d) for t in range(tile_n, N, tile_n)
                                                   for d in (-1, 0)})
     for r in edge_r[:64]:
         for c in g.choice(edge_c, size=min(8, len(edge_c)), replace=False):
             rows.append(r)
             cols.append(int(c))
     return np.array(rows, np.int64), np.array(cols, np.int64)
+
+
+def band_lines(extent: int, tile: int, seed: int) -> np.ndarray:
+    """Indices that cross every tile band of one dimension: one random index
+    inside each band [b tile, (b + 1) tile), both sides of four band
+    boundaries spread over the extent, and the first and last index."""
+    g = np.random.default_rng(seed)
+    idx = {0, extent - 1}
+    for b0 in range(0, extent, tile):
+        idx.add(int(g.integers(b0, min(b0 + tile, extent))))
+    bounds = list(range(tile, extent, tile))
+    for t in (bounds[:: max(1, len(bounds) // 4)] if bounds else []):
+        idx.update((t - 1, t))
+    return np.array(sorted(idx), np.int64)
+
+
+def check_lines(C: np.ndarray, oracle_rows, oracle_cols, rows, cols, what: str, exact: bool = False):
+    """Whole rows `rows` and whole columns `cols` of C against the oracle:
+    oracle_rows(rows) -> (C[rows, :], mag) and oracle_cols(cols) -> (C[:, cols], mag)."""
+    want, mag = oracle_rows(rows)
+    got = C[rows, :]
+    if exact:
+        assert_exact(got, want, what + " (rows)")
+    assert_within_bound(got, want, mag, what + " (rows)")
+    want, mag = oracle_cols(cols)
+    got = C[:, cols]
+    if exact:
+        assert_exact(got, want, what + " (columns)")
+    assert_within_bound(got, want, mag, what + " (columns)")
 
 
 # ------------------------------------------------------------------ bf16
@@ -114,6 +145,14 @@ def oracle_bf16_at(A_bits, B_bits, b_colmajor, rows, cols):
     return oracle.gemm_bf16_at(A_bits, Bv, rows, cols)
 
 
+def check_lines_bf16(C, A_bits, B_bits, b_colmajor, rows, cols, what, exact=False):
+    """Whole rows and columns of a bf16 product against the oracle's full
+    product of the matching rows of A / columns of B."""
+    Bv = B_bits.T if b_colmajor else B_bits
+    check_lines(C, lambda r: oracle.gemm_bf16(np.ascontiguousarray(A_bits[r]), Bv),
+                lambda c: oracle.gemm_bf16(A_bits, np.ascontiguousarray(Bv[:, c])), rows, cols, what, exact)
+
+
 # ------------------------------------------------------------------ MX
 
 def run_mx(A: torch.Tensor, B: torch.Tensor, SA: torch.Tensor, SB: torch.Tensor,
@@ -135,3 +174,12 @@ def oracle_mx(A, B, SA, SB):
 
 def oracle_mx_at(A, B, SA, SB, rows, cols):
     return oracle.gemm_mxfp8_at(bits8(A), bits8(B).T, bits8(SA), bits8(SB), rows, cols)
+
+
+def check_lines_mx(C, A, B, SA, SB, rows, cols, what, exact=False):
+    """Whole rows and columns of an MX product against the oracle's full
+    product of the matching rows of A (and scale rows) / columns of B."""
+    a, b, sa, sb = bits8(A), bits8(B), bits8(SA), bits8(SB)
+    check_lines(C, lambda r: oracle.gemm_mxfp8(np.ascontiguousarray(a[r]), b.T, np.ascontiguousarray(sa[r]), sb),
+                lambda c: oracle.gemm_mxfp8(a, np.ascontiguousarray(b[c]).T, sa, np.ascontiguousarray(sb[c])),
+                rows, cols, what, exact)

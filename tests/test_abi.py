@@ -200,3 +200,116 @@ def test_attention_out_type_rejects_bad_arguments():
     for change in bad:
         args = dict(ok, **change)
         assert dg.attn_fwd_bf16_out(**args) == dg.GEMM_ERR_INVALID_ARG, change
+
+
+# ---------------------------------------------------------------- no device
+
+NO_DEVICE = pytest.mark.skipif(__import__("torch").cuda.device_count() > 0,
+                               reason="checks the behaviour without a GPU")
+
+
+@NO_DEVICE
+def test_valid_calls_without_a_device_are_unsupported_and_write_nothing():
+    """Every entry point checks for a gfx950 device before any work: with no
+    device a valid call returns GEMM_ERR_UNSUPPORTED and leaves C untouched
+    (here host buffers stand in for the operands; they are never read)."""
+    import numpy as np
+    M, N, K = 64, 48, 96
+    A = np.zeros(M * K, np.uint16)
+    B = np.zeros(K * N, np.uint16)
+    S = np.full(M * K // 32 + N * K // 32, 127, np.uint8)
+    C = np.full(M * N, 12345.0, np.float32)
+    W = np.zeros(1 << 16, np.uint8)
+    a, b, c, s, w = (x.ctypes.data for x in (A, B, C, S, W))
+    UN = dg.GEMM_ERR_UNSUPPORTED
+    assert dg.gemm_bf16(M, N, K, a, K, b, N, c, N, 0) == UN
+    assert dg.gemm_bf16_nt(M, N, K, a, K, b, K, c, N, 0) == UN
+    assert dg.gemm_mxfp8(M, N, K, a, K, b, K, s, s, c, N, 0) == UN
+    assert dg.gemm_bf16_fused(M, N, K, a, K, b, N, 0, c, N, dg.GEMM_OUT_BF16, None, None, None, 0) == UN
+    assert dg.gemm_mxfp8_fused(M, N, K, a, K, b, K, s, s, c, N, dg.GEMM_OUT_F32, None, None, None, 0) == UN
+    assert dg.gemm_bf16_splitk(M, N, K, a, K, b, K, 1, c, N, dg.GEMM_OUT_F32, None, None, None, 2, w, W.size,
+                               0) == UN
+    assert dg.gemm_bf16_dynamic(M, N, K, a, K, b, N, 0, c, N, w, W.size, 0) == UN
+    # K == 0 would zero C: still refused before any work
+    assert dg.gemm_bf16(M, N, 0, 0, 1, 0, N, c, N, 0) == UN
+    assert dg.gemm_bf16_splitk_plan(M, N, K, 1, 0, 0)[0] == UN          # cus = 0: the device's
+    assert dg.gemm_bf16_splitk_workspace(M, N, K, a, K, b, K, 1, c, N, dg.GEMM_OUT_F32, None, None, None,
+                                         0, 0)[0] == UN
+    assert (C == 12345.0).all()
+
+
+# ------------------------------------------------- split-K workspace query
+
+F16 = FAKE * 16  # 16-byte aligned, never dereferenced
+
+
+@pytest.mark.parametrize("case", [
+    # (M, N, K, lda, ldb, b_colmajor): padded views whose extent is not a
+    # multiple of 8 elements but whose leading dimension is
+    (512, 512, 8193, 8200, 8200, 1),
+    (512, 520, 8193, 8200, 528, 0),
+    (16, 2049, 8192, 8192, 2056, 0),     # small M, row-major B, odd N
+    (48, 2049, 8192, 8200, 2056, 0),
+])
+def test_splitk_workspace_uses_the_real_leading_dimensions(case):
+    """gemm_bf16_splitk_plan assumes dense leading dimensions; for padded
+    views the workspace query plans with the real ones, as the call does."""
+    M, N, K, lda, ldb, colmajor = case
+    rc, used, nbytes = dg.gemm_bf16_splitk_workspace(M, N, K, F16, lda, F16, ldb, colmajor, F16, N,
+                                                     dg.GEMM_OUT_F32, None, None, None, 0, 256)
+    assert rc == dg.GEMM_OK
+    assert used > 1 and nbytes == used * M * N * 4
+    # the dense-layout query cannot see that these operands split
+    assert dg.gemm_bf16_splitk_plan(M, N, K, colmajor, 0, 256)[1] == 1
+
+
+def test_splitk_workspace_matches_the_plan_for_dense_operands():
+    for (M, N, K, colmajor, splits, cus), want in SPLIT_PLANS:
+        if M == 0:
+            continue
+        ldb = K if colmajor else N
+        lda = K
+        rc, used, nbytes = dg.gemm_bf16_splitk_workspace(M, N, K, F16, lda, F16, ldb, colmajor, F16, N,
+                                                         dg.GEMM_OUT_F32, None, None, None, splits, cus)
+        assert rc == dg.GEMM_OK and (used, nbytes) == dg.gemm_bf16_splitk_plan(M, N, K, colmajor, splits,
+                                                                                cus)[1:]
+
+
+def test_splitk_workspace_follows_the_epilogue_and_alignment():
+    # stream-K style plan (289 tiles): only with the plain fp32 store
+    args = (4352, 4352, 4096, F16, 4096, F16, 4096, 1, F16, 4352)
+    assert dg.gemm_bf16_splitk_workspace(*args, dg.GEMM_OUT_F32, None, None, None, 0, 256)[1] == 7
+    assert dg.gemm_bf16_splitk_workspace(*args, dg.GEMM_OUT_BF16, None, None, None, 0, 256)[1:] == (1, 0)
+    assert dg.gemm_bf16_splitk_workspace(*args, dg.GEMM_OUT_F32, None, None, F16, 0, 256)[1:] == (1, 0)
+    # operands off 16-byte alignment never split
+    assert dg.gemm_bf16_splitk_workspace(2048, 2048, 16384, F16 + 2, 16384, F16, 16384, 1, F16, 2048,
+                                         dg.GEMM_OUT_F32, None, None, None, 0, 256)[1:] == (1, 0)
+    # argument errors as gemm_bf16_splitk's
+    assert dg.gemm_bf16_splitk_workspace(64, 64, 64, F16, 63, F16, 64, 1, F16, 64, dg.GEMM_OUT_F32, None,
+                                         None, None, 0, 256)[0] == dg.GEMM_ERR_INVALID_ARG
+    assert dg.gemm_bf16_splitk_workspace(64, 64, 64, F16, 64, F16, 64, 1, F16, 64, 5, None, None, None, 0,
+                                         256)[0] == dg.GEMM_ERR_INVALID_ARG
+    assert dg.gemm_bf16_splitk_workspace(64, 64, 64, F16, 64, F16, 64, 1, F16, 64, dg.GEMM_OUT_F32, None,
+                                         None, None, -1, 256)[0] == dg.GEMM_ERR_INVALID_ARG
+
+
+# ------------------------------------------------------ tensor helper layout
+
+def test_bf16_helper_layout_keyword():
+    """b_colmajor=None infers the layout of B from its strides; True takes B
+    as the (N, K) storage of a column-major operand; False needs row-major B."""
+    import torch
+    A = torch.zeros((5, 7), dtype=torch.bfloat16)
+    Bnk = torch.zeros((3, 7), dtype=torch.bfloat16)       # (N, K) storage
+    Bkn = torch.zeros((7, 3), dtype=torch.bfloat16)       # row-major (K, N)
+    op = dg._bf16_operands
+    assert op(A, Bnk.t()) == (5, 3, 7, 7, 7, True)
+    assert op(A, Bkn) == (5, 3, 7, 7, 3, False)
+    assert op(A, Bnk, True) == (5, 3, 7, 7, 7, True)
+    assert op(A, Bkn, False) == (5, 3, 7, 7, 3, False)
+    with pytest.raises(ValueError):
+        op(A, Bnk.t(), False)      # column-major B where row-major is asked for
+    with pytest.raises(ValueError):
+        op(A, Bkn.t(), True)       # (N, K) view with unit stride along N
+    with pytest.raises(ValueError):
+        op(A, Bkn, True)           # (K, N) is not (N, K)

@@ -66,18 +66,41 @@ def _run(kind, prob, out_bf16, vecs, ldc_pad=3):
     return np.ascontiguousarray(C[:, :N]).astype(np.float64)
 
 
-def _reference(kind, prob, vecs, rows=None, cols=None):
+# The last problem built and its oracle product are kept, so the output
+# types of one shape share them (problems are dataclasses, not hashable: the
+# cache is keyed by the arguments that built the problem).
+_LAST = {"key": None, "prob": None, "product": None}
+
+
+def _problem(kind, M, N, K, colmajor, exact, seed):
+    key = (kind, M, N, K, colmajor, exact, seed)
+    if _LAST["key"] != key:
+        _LAST.update(key=key, product=None, prob=(
+            inputs.mx_problem(M, N, K, dist="integer" if exact else "normal", seed=seed) if kind == "mx"
+            else _bf16_prob(M, N, K, colmajor, exact, seed)))
+    return _LAST["prob"]
+
+
+def _product(kind, prob):
+    """The oracle's full product of one problem (cached for the last problem)."""
+    if prob is _LAST["prob"] and _LAST["product"] is not None:
+        return _LAST["product"]
     if kind == "mx":
-        if rows is None:
-            acc, mag = P.oracle_mx(prob.A, prob.B, prob.SA, prob.SB)
-        else:
-            acc, mag = P.oracle_mx_at(prob.A, prob.B, prob.SA, prob.SB, rows, cols)
+        res = P.oracle_mx(prob.A, prob.B, prob.SA, prob.SB)
     else:
-        Ab, Bb = P.bits16(prob.A), P.bits16(prob.B)
-        if rows is None:
-            acc, mag = P.oracle_bf16(Ab, Bb, prob.b_colmajor)
-        else:
-            acc, mag = P.oracle_bf16_at(Ab, Bb, prob.b_colmajor, rows, cols)
+        res = P.oracle_bf16(P.bits16(prob.A), P.bits16(prob.B), prob.b_colmajor)
+    if prob is _LAST["prob"]:
+        _LAST["product"] = res
+    return res
+
+
+def _reference(kind, prob, vecs, rows=None, cols=None):
+    if rows is None:
+        acc, mag = _product(kind, prob)
+    elif kind == "mx":
+        acc, mag = P.oracle_mx_at(prob.A, prob.B, prob.SA, prob.SB, rows, cols)
+    else:
+        acc, mag = P.oracle_bf16_at(P.bits16(prob.A), P.bits16(prob.B), prob.b_colmajor, rows, cols)
     rs, cs, bias = vecs
     t, m = oracle.epilogue(acc, mag, rs, cs, bias, rows=rows, cols=cols)
     b = np.zeros_like(t) if bias is None else np.abs(bias.astype(np.float64)[None, :] if rows is None
@@ -121,39 +144,42 @@ def test_fused_generic_kernel(shape, out_bf16, which, exact):
 
 # (M, N, K, b_colmajor): 256 x 256 direct-load tiles with partial tiles and a
 # partial last k-tile, the register-load kernel on 2-byte aligned rows with
-# 192-column tiles, and the small-M kernel
+# 192-column tiles, and the small-M kernel; every output against the oracle.
+# Cases of one shape and distribution run in a row so that they share one
+# oracle product.
 BIG = [(4096 + 77, 4096 + 133, 520, True), (4096 + 77, 4096 + 8, 520, False), (4001, 3003, 2050, False),
        (16, 4096, 776, False)]
+OUTS = [False, True]
+BIG_CASES = [(shape, exact, out) for shape in BIG for exact in (True, False) for out in OUTS]
 
 
-@pytest.mark.parametrize("shape", BIG, ids=lambda s: f"{s[0]}x{s[1]}x{s[2]}_{'nt' if s[3] else 'nn'}")
-@pytest.mark.parametrize("out_bf16", [False, True], ids=["f32", "bf16"])
-@pytest.mark.parametrize("exact", [True, False], ids=["integer", "normal"])
-def test_fused_fast_kernels(shape, out_bf16, exact):
-    M, N, K, colmajor = shape
-    prob = _bf16_prob(M, N, K, colmajor, exact, seed=63)
+@pytest.mark.parametrize("case", BIG_CASES, ids=lambda c: f"{c[0][0]}x{c[0][1]}x{c[0][2]}_{'nt' if c[0][3] else 'nn'}"
+                         f"_{'integer' if c[1] else 'normal'}_{'bf16' if c[2] else 'f32'}")
+def test_fused_fast_kernels(case):
+    (M, N, K, colmajor), exact, out_bf16 = case
+    prob = _problem("bf16", M, N, K, colmajor, exact, 63)
     vecs = _vectors(M, N, exact, 64, "rcb")
     P.note(f"fused big {M}x{N}x{K} {'NT' if colmajor else 'NN'} out {'bf16' if out_bf16 else 'f32'}")
     got = _run("bf16", prob, out_bf16, vecs)
-    rows, cols = P.sample_positions(M, N, 1024, seed=65)
-    t, m, b = _reference("bf16", prob, vecs, rows, cols)
-    _compare(got[rows, cols], t, m, b, out_bf16, exact, prob.name)
+    t, m, b = _reference("bf16", prob, vecs)
+    _compare(got, t, m, b, out_bf16, exact, prob.name)
 
 
-MX = [(4096 + 40, 4096 + 8, 1024), (300, 200, 96)]
+# MX: the scale ring (K a multiple of 512), the 64-code k-tile pipeline (K =
+# 64 mod 128) and the generic kernel; every output against the oracle.
+MX = [(4096 + 40, 4096 + 8, 1024), (4096 + 40, 4096 + 8, 192), (300, 200, 96)]
+MX_CASES = [(shape, out) for shape in MX for out in OUTS]
 
 
-@pytest.mark.parametrize("shape", MX, ids=lambda s: "x".join(map(str, s)))
-@pytest.mark.parametrize("out_bf16", [False, True], ids=["f32", "bf16"])
-def test_fused_mx(shape, out_bf16):
-    M, N, K = shape
-    prob = inputs.mx_problem(M, N, K, dist="integer", seed=66)
+@pytest.mark.parametrize("case", MX_CASES, ids=lambda c: "x".join(map(str, c[0])) + ("_bf16" if c[1] else "_f32"))
+def test_fused_mx(case):
+    (M, N, K), out_bf16 = case
+    prob = _problem("mx", M, N, K, False, True, 66)
     vecs = _vectors(M, N, True, 67, "rcb")
     P.note(f"fused mx {M}x{N}x{K} out {'bf16' if out_bf16 else 'f32'}")
     got = _run("mx", prob, out_bf16, vecs)
-    rows, cols = P.sample_positions(M, N, 1024, seed=68)
-    t, m, b = _reference("mx", prob, vecs, rows, cols)
-    _compare(got[rows, cols], t, m, b, out_bf16, True, prob.name)
+    t, m, b = _reference("mx", prob, vecs)
+    _compare(got, t, m, b, out_bf16, True, prob.name)
 
 
 @pytest.mark.parametrize("out_bf16", [False, True], ids=["f32", "bf16"])

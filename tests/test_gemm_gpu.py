@@ -178,24 +178,6 @@ def test_tensor_helper_layouts():
 
 # ---------------------------------------------------------------- fast (256 x 256) path
 
-def _check_sampled(C, want_fn, M, N, nsample, seed, exact=False, what=""):
-    """Sampled positions (random plus every tile-boundary row / column) against
-    the oracle, computed one by one."""
-    rows, cols = P.sample_positions(M, N, nsample, seed=seed)
-    want, mag = want_fn(rows, cols)
-    if exact:
-        P.assert_exact(C[rows, cols], want, what)
-    P.assert_within_bound(C[rows, cols], want, mag, what)
-
-
-def _freivalds(C, Af, Bmat, seed):
-    x = np.random.default_rng(seed).standard_normal(C.shape[1])
-    lhs = C.astype(np.float64) @ x
-    rhs = Af @ (Bmat @ x)
-    lim = P.BOUND * (np.abs(Af) @ (np.abs(Bmat) @ np.abs(x)))
-    assert np.all(np.abs(lhs - rhs) <= lim), "Freivalds check failed"
-
-
 # Shapes large enough for the 256 x 256 kernel (enough tiles for every CU),
 # with partial tiles in M and N and a partial last k-tile.
 FAST_BF16 = [(4096 + 77, 4096 + 133, 513, True), (4096 + 77, 4096 + 8, 520, False),
@@ -205,32 +187,46 @@ FAST_BF16 = [(4096 + 77, 4096 + 133, 513, True), (4096 + 77, 4096 + 8, 520, Fals
 @pytest.mark.parametrize("case", FAST_BF16, ids=lambda c: f"{c[0]}x{c[1]}x{c[2]}_{'nt' if c[3] else 'nn'}")
 @pytest.mark.parametrize("dist", ["normal", "integer"])
 def test_fast_path_bf16_tails(case, dist):
+    """Every output of the 256 x 256 direct-load kernel against the oracle."""
     M, N, K, colmajor = case
     prob = _bf16_case(M, N, K, colmajor, dist, seed=31)
     P.note(f"fast path bf16 {'NT' if colmajor else 'NN'} {M}x{N}x{K} {dist}")
     C = P.run_bf16(prob.A.to(DEV), prob.B.to(DEV), colmajor).cpu().numpy()
-    assert np.isfinite(C).all()
-    Ab, Bb = P.bits16(prob.A), P.bits16(prob.B)
-    _check_sampled(C, lambda r, c: P.oracle_bf16_at(Ab, Bb, colmajor, r, c), M, N, 1024, 4,
-                   exact=(dist == "integer"), what=prob.name)
-    Af = prob.A.double().numpy()
-    Bf = prob.B.double().numpy()
-    _freivalds(C, Af, Bf.T if colmajor else Bf, 5)
+    want, mag = P.oracle_bf16(P.bits16(prob.A), P.bits16(prob.B), colmajor)
+    if dist == "integer":
+        P.assert_exact(C, want, prob.name)
+    P.assert_within_bound(C, want, mag, prob.name)
 
 
-FAST_MX = [(4096 + 40, 4096 + 8, 640), (4096 + 40, 4096 + 200, 1024)]
+# 256 x 256 MX kernels, every output against the oracle: the scale ring (K a
+# multiple of 512), the word-scale pipeline (K a multiple of 128), and the
+# 64-code k-tile pipeline with 4 stages, taken when K is 64 mod 128 or when
+# the scale arrays are only 2-byte aligned (scale_offset = 2).
+FAST_MX = [(4096 + 40, 4096 + 200, 512, 0), (4096 + 40, 4096 + 8, 384, 0), (4096 + 40, 4096 + 8, 192, 0),
+           (4096 + 40, 4096 + 72, 256, 2)]
 
 
-@pytest.mark.parametrize("shape", FAST_MX, ids=lambda s: "x".join(map(str, s)))
+def _mx_scales_at(S: torch.Tensor, offset: int) -> torch.Tensor:
+    """A device copy of the scale codes starting `offset` bytes past a 256-byte
+    boundary (the view keeps the storage alive)."""
+    buf = torch.zeros(S.numel() + 256, dtype=torch.uint8, device=DEV)
+    view = buf[offset:offset + S.numel()].view(S.shape)
+    view.copy_(S.to(DEV))
+    return view
+
+
+@pytest.mark.parametrize("shape", FAST_MX, ids=lambda s: "x".join(map(str, s[:3])) + f"_soff{s[3]}")
 @pytest.mark.parametrize("dist", ["normal", "integer"])
 def test_fast_path_mx_tails(shape, dist):
-    M, N, K = shape
+    M, N, K, soff = shape
     prob = inputs.mx_problem(M, N, K, dist=dist, seed=32)
-    P.note(f"fast path mx {M}x{N}x{K} {dist}")
-    C = P.run_mx(prob.A.to(DEV), prob.B.to(DEV), prob.SA.to(DEV), prob.SB.to(DEV)).cpu().numpy()
-    assert np.isfinite(C).all()
-    _check_sampled(C, lambda r, c: P.oracle_mx_at(prob.A, prob.B, prob.SA, prob.SB, r, c), M, N, 1024,
-                   6, exact=(dist == "integer"), what=prob.name)
+    P.note(f"fast path mx {M}x{N}x{K} scale offset {soff} {dist}")
+    SA, SB = _mx_scales_at(prob.SA, soff), _mx_scales_at(prob.SB, soff)
+    C = P.run_mx(prob.A.to(DEV), prob.B.to(DEV), SA, SB).cpu().numpy()
+    want, mag = P.oracle_mx(prob.A, prob.B, prob.SA, prob.SB)
+    if dist == "integer":
+        P.assert_exact(C, want, prob.name)
+    P.assert_within_bound(C, want, mag, prob.name)
 
 
 # ---------------------------------------------------------------- 2-byte aligned rows
@@ -271,13 +267,10 @@ def test_unaligned_rows_big_tiles(case, dist):
     Cfull = Cst.cpu().numpy()
     assert (Cfull[:, N:] == -12345.0).all(), "C written outside M x N"
     C = np.ascontiguousarray(Cfull[:, :N])
-    assert np.isfinite(C).all()
-    Ab, Bb = P.bits16(prob.A), P.bits16(prob.B)
-    _check_sampled(C, lambda r, c: P.oracle_bf16_at(Ab, Bb, colmajor, r, c), M, N, 1024, 9,
-                   exact=(dist == "integer"), what=prob.name)
-    Af = prob.A.double().numpy()
-    Bf = prob.B.double().numpy()
-    _freivalds(C, Af, Bf.T if colmajor else Bf, 10)
+    want, mag = P.oracle_bf16(P.bits16(prob.A), P.bits16(prob.B), colmajor)
+    if dist == "integer":
+        P.assert_exact(C, want, prob.name)
+    P.assert_within_bound(C, want, mag, prob.name)
 
 
 # ---------------------------------------------------------------- small-M path
@@ -309,31 +302,27 @@ def test_small_m_path(case, dist):
 
 # ---------------------------------------------------------------- full-size workloads
 
-def _check_sampled_bf16(name, nsample=2048):
-    prob = inputs.workload(name, seed=0)
-    P.note(f"{name} full size (sampled)")
-    C = P.run_bf16(prob.A.to(DEV), prob.B.to(DEV), prob.b_colmajor)
-    Ch = C.cpu().numpy()
-    assert np.isfinite(Ch).all()
-    rows, cols = P.sample_positions(prob.M, prob.N, nsample, seed=1)
-    want, mag = P.oracle_bf16_at(P.bits16(prob.A), P.bits16(prob.B), prob.b_colmajor, rows, cols)
-    P.assert_within_bound(Ch[rows, cols], want, mag, name)
-    # Freivalds' identity over every output: C x = A (B x) within the same
-    # bound, aggregated (binary64 numpy matrix-vector products).
-    x = np.random.default_rng(2).standard_normal(prob.N)
-    Af = prob.A.double().numpy()
-    Bf = prob.B.double().numpy()
-    Bmat = Bf.T if prob.b_colmajor else Bf
-    lhs = Ch.astype(np.float64) @ x
-    rhs = Af @ (Bmat @ x)
-    lim = P.BOUND * (np.abs(Af) @ (np.abs(Bmat) @ np.abs(x)))
-    assert np.all(np.abs(lhs - rhs) <= lim), "Freivalds check failed"
-
-
-@pytest.mark.parametrize("name", ["square4096_nn", "square8192_nt", "ragged4001x3003x2050_nn",
-                                  "skinny16x8192x8192_nn"])
+@pytest.mark.parametrize("name", ["square4096_nn", "ragged4001x3003x2050_nn", "skinny16x8192x8192_nn"])
 def test_workload_full_size(name):
-    _check_sampled_bf16(name)
+    """The workloads at full size, in the benchmark's launch configuration,
+    every output against the oracle."""
+    prob = inputs.workload(name, seed=0)
+    P.note(f"{name} full size (every output)")
+    C = P.run_bf16(prob.A.to(DEV), prob.B.to(DEV), prob.b_colmajor).cpu().numpy()
+    want, mag = P.oracle_bf16(P.bits16(prob.A), P.bits16(prob.B), prob.b_colmajor)
+    P.assert_within_bound(C, want, mag, name)
+
+
+def test_headline_workload_lines():
+    """8192^3 NT at full size: whole rows and whole columns that cross every
+    256-row and 256-column tile band (one inside each band, both sides of
+    several band boundaries, the first and the last), against the oracle."""
+    prob = inputs.workload("square8192_nt", seed=0)
+    P.note("square8192_nt full size (rows and columns over every tile band)")
+    C = P.run_bf16(prob.A.to(DEV), prob.B.to(DEV), prob.b_colmajor).cpu().numpy()
+    rows = P.band_lines(prob.M, 256, seed=1)
+    cols = P.band_lines(prob.N, 256, seed=2)
+    P.check_lines_bf16(C, P.bits16(prob.A), P.bits16(prob.B), True, rows, cols, "square8192_nt")
 
 
 # ---------------------------------------------------------------- MX fp8
@@ -380,10 +369,14 @@ def test_mx_scale_spread_and_nan():
 
 
 def test_mx_full_size_workload():
+    """MX 8192^3 at full size: whole rows and columns over every tile band,
+    plus sampled positions at the tile edges."""
     prob = inputs.workload("mx8192", seed=0)
-    P.note("mx8192 full size (sampled)")
+    P.note("mx8192 full size (rows and columns over every tile band)")
     C = P.run_mx(prob.A.to(DEV), prob.B.to(DEV), prob.SA.to(DEV), prob.SB.to(DEV)).cpu().numpy()
-    assert np.isfinite(C).all()
-    rows, cols = P.sample_positions(prob.M, prob.N, 2048, seed=3)
-    want, mag = P.oracle_mx_at(prob.A, prob.B, prob.SA, prob.SB, rows, cols)
-    P.assert_within_bound(C[rows, cols], want, mag, "mx8192")
+    rows = P.band_lines(prob.M, 256, seed=3)
+    cols = P.band_lines(prob.N, 256, seed=4)
+    P.check_lines_mx(C, prob.A, prob.B, prob.SA, prob.SB, rows, cols, "mx8192")
+    r, c = P.sample_positions(prob.M, prob.N, 1024, seed=5)
+    want, mag = P.oracle_mx_at(prob.A, prob.B, prob.SA, prob.SB, r, c)
+    P.assert_within_bound(C[r, c], want, mag, "mx8192 (sampled)")

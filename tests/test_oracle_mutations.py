@@ -29,6 +29,15 @@ MUTATIONS = {
     "mx_block_index_lost": ("J->SA[i * J->sa_ld + b]", "J->SA[i * J->sa_ld]"),
     "mx_transposed_B": ("J->B8[k * J->b_rs + j * J->b_cs]", "J->B8[j * J->b_rs + k * J->b_cs]"),
     "mx_block_width": ("k < 32 * b + 32; ++k", "k < 32 * b + 31; ++k"),
+    # the sampled MX entry point (the checker of every at-size MX comparison)
+    "mx_sample_swapped": ("mx_element(J, J->rows[t], J->cols[t], &c, &a);",
+                          "mx_element(J, J->cols[t], J->rows[t], &c, &a);"),
+    "mx_sample_col_from_row": ("mx_element(J, J->rows[t], J->cols[t], &c, &a);",
+                               "mx_element(J, J->rows[t], J->rows[t], &c, &a);"),
+    "mx_sample_abs_is_value": ("        mx_element(J, J->rows[t], J->cols[t], &c, &a);\n        J->out[t] = c;\n"
+                               "        if (J->absout) J->absout[t] = a;",
+                               "        mx_element(J, J->rows[t], J->cols[t], &c, &a);\n        J->out[t] = c;\n"
+                               "        if (J->absout) J->absout[t] = c;"),
     "abs_product_signed": ("        m += fabs(x) * fabs(y);\n    }\n    *c = s;",
                            "        m += x * y;\n    }\n    *c = s;"),
     "rowloop_sign": ("crow[j] += x * y;", "crow[j] -= x * y;"),
