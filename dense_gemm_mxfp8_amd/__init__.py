@@ -24,6 +24,7 @@ GEMM_ERR_UNSUPPORTED = -2
 GEMM_ERR_LAUNCH = -3
 GEMM_OUT_F32 = 0
 GEMM_OUT_BF16 = 1
+GEMM_OUT_E4M3 = 2
 GEMM_DYNAMIC_WORKSPACE_BYTES = 1024
 
 _lib = None
@@ -202,8 +203,8 @@ def _epilogue(out_dtype, row_scale, col_scale, bias, M, N):
     """(fused?, out_type, pointers) of the optional epilogue arguments."""
     import torch
     fused = out_dtype is not None or row_scale is not None or col_scale is not None or bias is not None
-    if out_dtype not in (None, torch.float32, torch.bfloat16):
-        raise TypeError("out_dtype must be torch.float32 or torch.bfloat16")
+    if out_dtype not in (None, torch.float32, torch.bfloat16, torch.float8_e4m3fn):
+        raise TypeError("out_dtype must be torch.float32, torch.bfloat16 or torch.float8_e4m3fn")
     ptrs = []
     for v, n, name in ((row_scale, M, "row_scale"), (col_scale, N, "col_scale"), (bias, N, "bias")):
         if v is None:
@@ -212,7 +213,7 @@ def _epilogue(out_dtype, row_scale, col_scale, bias, M, N):
         if v.dtype != torch.float32 or v.dim() != 1 or v.shape[0] != n or (n > 1 and v.stride(0) != 1):
             raise ValueError(f"{name} must be a contiguous float32 vector of length {n}")
         ptrs.append(v.data_ptr())
-    out_type = GEMM_OUT_BF16 if out_dtype == torch.bfloat16 else GEMM_OUT_F32
+    out_type = {torch.bfloat16: GEMM_OUT_BF16, torch.float8_e4m3fn: GEMM_OUT_E4M3}.get(out_dtype, GEMM_OUT_F32)
     return fused, out_type, ptrs
 
 
@@ -259,8 +260,9 @@ def bf16(A, B, out=None, *, b_colmajor=None, out_dtype=None, row_scale=None, col
     of an (N, K) tensor: ``gemm_bf16_nt``), told apart by its strides.
     b_colmajor=True: B is that (N, K) tensor itself (``gemm_bf16_nt``);
     b_colmajor=False: B must be row-major (K, N) (``gemm_bf16``).
-    With any of out_dtype (float32 or bfloat16), row_scale (M), col_scale (N)
-    or bias (N) the fused epilogue applies: C = A @ B * row_scale[:, None] *
+    With any of out_dtype (float32, bfloat16 or float8_e4m3fn: OCP E4M3,
+    nearest even, saturating to +-448), row_scale (M), col_scale (N) or bias
+    (N) the fused epilogue applies: C = A @ B * row_scale[:, None] *
     col_scale[None, :] + bias[None, :] (``gemm_bf16_fused``)."""
     M, N, K, lda, ldb, colmajor = _bf16_operands(A, B, b_colmajor)
     fn = gemm_bf16_nt if colmajor else gemm_bf16

@@ -70,7 +70,7 @@ struct Args {
     int sld;       // MX scale bytes per row (K / 32)
     int xcd_remap;
     int c_nt;      // C stores non-temporal (1) or cached (0)
-    epi::Params epi;  // fused epilogue (C is bf16 when epi.out_bf16)
+    epi::Params epi;  // fused epilogue (C holds epi.out elements)
     // split-K instances: units 0 .. dp_units-1 are whole tiles 0 .. dp_units-1
     // (stored to C); unit dp_units + u is tile tile0 + u % tiles_per_split of
     // K range ks = u / tiles_per_split ([ks kslice, min(K, (ks + 1) kslice)),
@@ -275,13 +275,14 @@ __device__ __forceinline__ void store_c_aux(const Args& a, const f32x16 (&acc)[k
 }
 
 // Fused epilogue (gemm_epi.h): t = acc * rs[row] * cs[col] + bias[col] in
-// fp32, stored as fp32 or bf16, with the descriptor scheme of store_c_aux.
+// fp32, stored as fp32, bf16 or E4M3 (OUT), with the descriptor scheme of
+// store_c_aux.
 // The tile's scale and bias values were loaded into registers when the tile
 // started (epi_prefetch) and staged in LDS before the epilogue (epi_stage),
 // so no global load latency shows here: ev points at 3 x 256 floats (row
 // scales, column scales, biases of the tile), evr / evc are this wave's
 // first row / column within the tile.
-template <int AUX, int NBJ, bool BF16>
+template <int AUX, int NBJ, int OUT>
 __device__ __forceinline__ void store_c_fused(const Args& a, const f32x16 (&acc)[kBlocks][NBJ], int m0w, int n0w,
                                               int h, int l32, const float FAST_LDS* ev, int evr, int evc) {
     const int rlim = a.M - m0w;
@@ -289,7 +290,7 @@ __device__ __forceinline__ void store_c_fused(const Args& a, const f32x16 (&acc)
     if (rlim <= 0 || clim <= 0) return;
     const int rows = rlim < kWaveTile ? rlim : kWaveTile;
     const int cols = clim < 32 * NBJ ? clim : 32 * NBJ;
-    constexpr int ESZ = BF16 ? 2 : 4;
+    constexpr int ESZ = OUT == epi::kF32 ? 4 : OUT == epi::kBF16 ? 2 : 1;
     const int ldcb = (int)a.ldc * ESZ;
     const __amdgpu_buffer_rsrc_t rc = make_rsrc((const uint8_t*)a.C + ((int64_t)m0w * a.ldc + n0w) * ESZ,
                                                 ((int64_t)(rows - 1) * a.ldc + cols) * ESZ);
@@ -316,8 +317,10 @@ __device__ __forceinline__ void store_c_fused(const Args& a, const f32x16 (&acc)
                     if (has_r) t *= rf[r];
                     if (has_c) t *= cf[j];
                     if (has_b) t += cb[j];
-                    if constexpr (BF16)
+                    if constexpr (OUT == epi::kBF16)
                         __builtin_amdgcn_raw_buffer_store_b16(epi::to_bf16(t), rc, voff + 64 * j, row * ldcb, AUX);
+                    else if constexpr (OUT == epi::kE4M3)
+                        __builtin_amdgcn_raw_buffer_store_b8(epi::to_e4m3(t), rc, voff + 32 * j, row * ldcb, AUX);
                     else
                         __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, t), rc, voff + 128 * j,
                                                               row * ldcb, AUX);
@@ -361,9 +364,10 @@ __device__ __forceinline__ void store_c(const Args& a, const f32x16 (&acc)[kBloc
                                         int l32, const float FAST_LDS* ev = nullptr, int evr = 0, int evc = 0,
                                         float* cw = nullptr, int cld = 0, bool nt = true) {
     if constexpr (FUSED) {
-        if (a.epi.out_bf16) store_c_fused<0, NBJ, true>(a, acc, m0w, n0w, h, l32, ev, evr, evc);
-        else if (a.c_nt) store_c_fused<2, NBJ, false>(a, acc, m0w, n0w, h, l32, ev, evr, evc);
-        else store_c_fused<0, NBJ, false>(a, acc, m0w, n0w, h, l32, ev, evr, evc);
+        if (a.epi.out == epi::kBF16) store_c_fused<0, NBJ, epi::kBF16>(a, acc, m0w, n0w, h, l32, ev, evr, evc);
+        else if (a.epi.out == epi::kE4M3) store_c_fused<0, NBJ, epi::kE4M3>(a, acc, m0w, n0w, h, l32, ev, evr, evc);
+        else if (a.c_nt) store_c_fused<2, NBJ, epi::kF32>(a, acc, m0w, n0w, h, l32, ev, evr, evc);
+        else store_c_fused<0, NBJ, epi::kF32>(a, acc, m0w, n0w, h, l32, ev, evr, evc);
     } else {
         if (cw != nullptr) store_c_aux<0, NBJ, true>(a, acc, m0w, n0w, h, l32, cw, cld);
         else if (a.c_nt && nt) store_c_aux<2, NBJ>(a, acc, m0w, n0w, h, l32);

@@ -41,7 +41,7 @@ constexpr int kRsrcWord3 = 0x00020000;
 struct Args {
     const uint8_t* A;
     const uint8_t* B;
-    void* C;             // fp32, or bf16 when epi.out_bf16
+    void* C;             // elements of type epi.out
     int64_t lda_b, ldb_b, ldc;
     int M, N, K;
     int kw;   // k-rows per wave (a multiple of kStepK)

@@ -90,7 +90,7 @@ struct Args {
     int kt_total;  // kt_full, plus one if K leaves a partial tile
     int sld;       // scale codes per row: K / 32
     int xcd_remap; // 1: grid is a multiple of 8, spread tiles per XCD
-    epi::Params epi;  // fused epilogue (C is bf16 when epi.out_bf16)
+    epi::Params epi;  // fused epilogue (C holds epi.out elements)
 };
 
 // ---------------------------------------------------------------------------
@@ -773,8 +773,8 @@ fast::Args make_fast_args(int64_t M, int64_t N, int64_t K, const void* A, int64_
 #else
     constexpr int c_nt_env = -1;
 #endif
-    // bf16 output: a 32-column segment is 64 bytes, half a line
-    const bool lines = !e.out_bf16 && ((uintptr_t)C % 128 == 0) && (ldc % 32 == 0);
+    // bf16 or E4M3 output: a 32-column segment is 64 or 32 bytes, part of a line
+    const bool lines = e.out == epi::kF32 && ((uintptr_t)C % 128 == 0) && (ldc % 32 == 0);
     a.c_nt = c_nt_env >= 0 ? c_nt_env : (lines ? 1 : 0);
     a.epi = e;
     return a;
@@ -1118,7 +1118,7 @@ SplitPlan plan_split(bool nt, int64_t M, int64_t N, int64_t K, bool aligned, int
 SplitPlan resolve_split(bool nt, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
                         int64_t ldb, int64_t ldc, const epi::Params& e, int cus, int splits) {
     SplitPlan p = plan_split(nt, M, N, K, aligned16(A) && aligned16(B), lda, ldb, cus, splits);
-    const bool plain = !e.out_bf16 && !e.rs && !e.cs && !e.bias;
+    const bool plain = e.out == epi::kF32 && !e.rs && !e.cs && !e.bias;
     if (p.rem > 0 && (!plain || !c_ok(ldc))) p.splits = 1;
     return p;
 }
@@ -1208,13 +1208,15 @@ int dynamic_dispatch(bool nt, int64_t M, int64_t N, int64_t K, const void* A, in
 // no vectors is the plain store (the lean kernel instances).
 int fused_params(int out_type, const void* C, const float* rs, const float* cs, const float* bias,
                  epi::Params* e) {
-    if (out_type != GEMM_OUT_F32 && out_type != GEMM_OUT_BF16) return GEMM_ERR_INVALID_ARG;
-    if (((uintptr_t)C) & (out_type == GEMM_OUT_BF16 ? 1 : 3)) return GEMM_ERR_INVALID_ARG;
+    if (out_type != GEMM_OUT_F32 && out_type != GEMM_OUT_BF16 && out_type != GEMM_OUT_E4M3)
+        return GEMM_ERR_INVALID_ARG;
+    if (((uintptr_t)C) & (out_type == GEMM_OUT_F32 ? 3 : out_type == GEMM_OUT_BF16 ? 1 : 0))
+        return GEMM_ERR_INVALID_ARG;
     e->rs = rs;
     e->cs = cs;
     e->bias = bias;
-    e->out_bf16 = out_type == GEMM_OUT_BF16;
-    e->on = (e->out_bf16 || rs || cs || bias) ? 1 : 0;
+    e->out = out_type;
+    e->on = (out_type != GEMM_OUT_F32 || rs || cs || bias) ? 1 : 0;
     return GEMM_OK;
 }
 

@@ -70,6 +70,7 @@ extern "C" {
 /* the HIP runtime reported an error when the kernel was enqueued */
 #define GEMM_ERR_LAUNCH (-3)
 
+
 /* bf16 GEMM, B row-major: A bf16 M x K (lda >= K), B bf16 K x N with
  * element (k, j) at B[k*ldb + j] (ldb >= N), C fp32 M x N (ldc >= N). */
 int gemm_bf16(int64_t M, int64_t N, int64_t K,
@@ -113,13 +114,19 @@ int gemm_mxfp8(int64_t M, int64_t N, int64_t K,
  * multiply-add).  row_scale (M floats), col_scale (N floats) and bias
  * (N floats) are device pointers; each may be NULL, meaning 1, 1 and 0.
  * out_type GEMM_OUT_F32 stores fp32 (C is float*); GEMM_OUT_BF16 stores bf16
- * rounded to nearest even (C is a 2-byte element array; NaN stays NaN).
- * ldc counts elements of the output type.  K == 0 stores t with acc = 0.
- * Every other convention is that of the entry points above; the accuracy
- * bound applies to acc, and t adds the fp32 rounding of the epilogue and,
- * for bf16, the final rounding. */
+ * rounded to nearest even (C is a 2-byte element array; NaN stays NaN);
+ * GEMM_OUT_E4M3 stores OCP FP8 E4M3 codes (C is a byte array), t rounded to
+ * nearest even with saturation: |t| beyond the largest finite E4M3 value 448,
+ * infinities included, stores +-448 (0x7E / 0xFE); NaN stores a NaN code
+ * (0x7F or 0xFF).  The pages name fp8 outputs without an encoding; the OCP
+ * FP8 format and its saturating conversion are the reading taken here, the
+ * format the MX operands already use.  ldc counts elements of the output
+ * type.  K == 0 stores t with acc = 0.  Every other convention is that of the
+ * entry points above; the accuracy bound applies to acc, and t adds the fp32
+ * rounding of the epilogue and, for bf16 and E4M3, the final rounding. */
 #define GEMM_OUT_F32 0
 #define GEMM_OUT_BF16 1
+#define GEMM_OUT_E4M3 2
 
 /* bf16 operands, B row-major (b_colmajor == 0, as gemm_bf16) or column-major
  * (b_colmajor != 0, as gemm_bf16_nt). */

@@ -382,3 +382,29 @@ def round_bf16(x):
     r = np.where(np.abs(r) > big, np.copysign(np.inf, v), r)
     out[fin] = r
     return out
+
+
+def round_e4m3(x):
+    """Round float64 values to OCP FP8 E4M3 ("fn": 4 exponent bits with bias 7,
+    3 mantissa bits, no infinities, largest finite value 448), nearest even,
+    with saturation: results beyond +-448, infinities included, become +-448;
+    NaN stays NaN.  Returned as float64 (zeros keep their sign).  Written from
+    the format's definition: the quantum of a value in [2^e, 2^(e+1)) is
+    2^(e-3), and 2^-9 below the normal range (e < -6).  Saturation is the
+    reading taken for the fused epilogue's fp8 output (the pages name fp8
+    outputs but no encoding or overflow rule)."""
+    x = np.asarray(x, dtype=np.float64)
+    out = np.array(x, dtype=np.float64, copy=True)
+    inf = np.isinf(x)
+    out[inf] = np.copysign(448.0, x[inf])
+    fin = np.isfinite(x) & (x != 0)
+    v = x[fin]
+    e = np.floor(np.log2(np.abs(v)))
+    # log2 can be off by one next to powers of two: correct the exponent
+    e = np.where(np.abs(v) >= np.exp2(e + 1), e + 1, e)
+    e = np.where(np.abs(v) < np.exp2(e), e - 1, e)
+    q = np.exp2(np.maximum(e, -6.0) - 3.0)
+    r = np.rint(v / q) * q  # np.rint rounds half to even
+    r = np.where(np.abs(r) > 448.0, np.copysign(448.0, v), r)
+    out[fin] = r
+    return out

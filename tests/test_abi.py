@@ -190,7 +190,8 @@ def test_attention_out_type_rejects_bad_arguments():
               k_strides=None, V=F, v_strides=None, O=F, o_strides=None, out_type=dg.GEMM_OUT_BF16, lse=None,
               scale=0.1, causal=0, stream=0)
     bad = [
-        dict(out_type=2), dict(out_type=-1),
+        dict(out_type=3), dict(out_type=-1),
+        dict(out_type=dg.GEMM_OUT_E4M3),                      # no fp8 output for attention
         dict(O=F + 4),                                        # bf16 O: 8-byte aligned
         dict(O=F + 8, out_type=dg.GEMM_OUT_F32),              # fp32 O: 16-byte aligned
         dict(o_strides=(0, 0, 130)),                          # multiples of 4 elements
@@ -227,6 +228,8 @@ def test_valid_calls_without_a_device_are_unsupported_and_write_nothing():
     assert dg.gemm_mxfp8(M, N, K, a, K, b, K, s, s, c, N, 0) == UN
     assert dg.gemm_bf16_fused(M, N, K, a, K, b, N, 0, c, N, dg.GEMM_OUT_BF16, None, None, None, 0) == UN
     assert dg.gemm_mxfp8_fused(M, N, K, a, K, b, K, s, s, c, N, dg.GEMM_OUT_F32, None, None, None, 0) == UN
+    # E4M3 output: any C byte address is accepted
+    assert dg.gemm_bf16_fused(M, N, K, a, K, b, N, 0, c + 1, N, dg.GEMM_OUT_E4M3, None, None, None, 0) == UN
     assert dg.gemm_bf16_splitk(M, N, K, a, K, b, K, 1, c, N, dg.GEMM_OUT_F32, None, None, None, 2, w, W.size,
                                0) == UN
     assert dg.gemm_bf16_dynamic(M, N, K, a, K, b, N, 0, c, N, w, W.size, 0) == UN

@@ -34,7 +34,11 @@ def _plan(M, N, K, colmajor, splits):
     return used, nbytes
 
 
-def _run(prob, splits, *, ldc_pad=3, out_bf16=False, vecs=(None, None, None), ws=None, ws_fill=float("nan")):
+OUT_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16, "e4m3": torch.float8_e4m3fn}
+OUT_TYPE = {"f32": dg.GEMM_OUT_F32, "bf16": dg.GEMM_OUT_BF16, "e4m3": dg.GEMM_OUT_E4M3}
+
+
+def _run(prob, splits, *, ldc_pad=3, out="f32", vecs=(None, None, None), ws=None, ws_fill=float("nan")):
     """gemm_bf16_splitk on the problem's operands; returns (C as float64,
     splits the plan uses, workspace tensor)."""
     M, N, K = prob.M, prob.N, prob.K
@@ -44,12 +48,11 @@ def _run(prob, splits, *, ldc_pad=3, out_bf16=False, vecs=(None, None, None), ws
     if ws is None:
         # contents on entry must not matter: start from NaN
         ws = torch.full((max(nbytes, 16) // 4,), ws_fill, dtype=torch.float32, device=DEV)
-    odt = torch.bfloat16 if out_bf16 else torch.float32
     ldc = N + ldc_pad
-    Cst = torch.full((M, ldc), -7.0, dtype=odt, device=DEV)
+    Cst = torch.full((M, ldc), -7.0, dtype=OUT_DTYPE[out], device=DEV)
     rs, cs, bias = (None if v is None else torch.from_numpy(v).to(DEV) for v in vecs)
     ptr = lambda t: 0 if t is None else t.data_ptr()
-    out_type = dg.GEMM_OUT_BF16 if out_bf16 else dg.GEMM_OUT_F32
+    out_type = OUT_TYPE[out]
     rc = dg.gemm_bf16_splitk(M, N, K, A.data_ptr(), K, B.data_ptr(), ldb, prob.b_colmajor, Cst.data_ptr(), ldc,
                              out_type, ptr(rs), ptr(cs), ptr(bias), splits, ws.data_ptr(), ws.numel() * 4,
                              P.stream())
@@ -122,20 +125,21 @@ def test_splitk_long_k_sampled():
                        P.band_lines(2048, 256, 86), prob.name)
 
 
-@pytest.mark.parametrize("out_bf16", [False, True], ids=["f32", "bf16"])
-def test_splitk_fused_epilogue(out_bf16):
+@pytest.mark.parametrize("out", ["f32", "bf16", "e4m3"])
+def test_splitk_fused_epilogue(out):
     M, N, K = 700, 600, 2048
     prob = _prob(M, N, K, True, True, seed=86)
     g = np.random.default_rng(87)
     rs = np.exp2(g.integers(-2, 3, size=M)).astype(np.float32)
     cs = np.exp2(g.integers(-2, 3, size=N)).astype(np.float32)
     bias = g.integers(-8, 9, size=N).astype(np.float32)
-    P.note(f"splitk fused {prob.name} out {'bf16' if out_bf16 else 'f32'}")
-    got, used, _ = _run(prob, 4, out_bf16=out_bf16, vecs=(rs, cs, bias))
+    P.note(f"splitk fused {prob.name} out {out}")
+    got, used, _ = _run(prob, 4, out=out, vecs=(rs, cs, bias))
     assert used == 4
     acc, mag = P.oracle_bf16(P.bits16(prob.A), P.bits16(prob.B), True)
     t, _ = oracle.epilogue(acc, mag, rs, cs, bias)
-    P.assert_exact(got, oracle.round_bf16(t) if out_bf16 else t, prob.name)
+    want = oracle.round_bf16(t) if out == "bf16" else oracle.round_e4m3(t) if out == "e4m3" else t
+    P.assert_exact(got, want, prob.name)
 
 
 def test_splitk_unsplit_fallback_leaves_workspace():
