@@ -22,6 +22,8 @@ GEMM_OK = 0
 GEMM_ERR_INVALID_ARG = -1
 GEMM_ERR_UNSUPPORTED = -2
 GEMM_ERR_LAUNCH = -3
+GEMM_ERR_SCRATCH = -4
+GEMM_SCRATCH_BYTES = 64 << 20
 GEMM_OUT_F32 = 0
 GEMM_OUT_BF16 = 1
 GEMM_OUT_E4M3 = 2
@@ -59,6 +61,9 @@ def library() -> ctypes.CDLL:
         lib.gemm_bf16_splitk_plan.restype = ctypes.c_int
         lib.gemm_bf16_splitk_plan.argtypes = [_i64, _i64, _i64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                               ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_size_t)]
+        lib.gemm_bf16_splitk_noalloc.restype = ctypes.c_int
+        lib.gemm_bf16_splitk_noalloc.argtypes = [_i64, _i64, _i64, _vp, _i64, _vp, _i64, ctypes.c_int, _vp, _i64,
+                                                 ctypes.c_int, _vp, _vp, _vp, ctypes.c_int, _vp]
         lib.gemm_bf16_splitk_workspace.restype = ctypes.c_int
         lib.gemm_bf16_splitk_workspace.argtypes = [_i64, _i64, _i64, _vp, _i64, _vp, _i64, ctypes.c_int, _vp,
                                                    _i64, ctypes.c_int, _vp, _vp, _vp, ctypes.c_int, ctypes.c_int,
@@ -119,6 +124,12 @@ def gemm_bf16_splitk_plan(M, N, K, b_colmajor, splits=0, cus=0):
     rc = library().gemm_bf16_splitk_plan(M, N, K, int(b_colmajor), splits, cus, ctypes.byref(used),
                                          ctypes.byref(ws))
     return rc, used.value, ws.value
+
+
+def gemm_bf16_splitk_noalloc(M, N, K, A, lda, B, ldb, b_colmajor, C, ldc, out_type, row_scale, col_scale, bias,
+                             splits, stream) -> int:
+    return library().gemm_bf16_splitk_noalloc(M, N, K, A, lda, B, ldb, int(b_colmajor), C, ldc, out_type,
+                                              row_scale, col_scale, bias, splits, stream)
 
 
 def gemm_bf16_splitk_workspace(M, N, K, A, lda, B, ldb, b_colmajor, C, ldc, out_type, row_scale, col_scale,

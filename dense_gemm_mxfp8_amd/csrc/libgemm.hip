@@ -61,6 +61,14 @@
 #include "gemm_small.h"
 #include "gemm_reg.h"
 
+// Fixed device scratch of gemm_bf16_splitk_noalloc, for callers that cannot
+// allocate: the split-K partial products go here instead of into a caller's
+// workspace.  Every GPU the library runs on holds its own copy, at its own
+// address, from the first call on it until the process ends.  In host code
+// the name stands for a host-side shadow, never the device memory: the host
+// uses only the address hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) uint8_t scratch[GEMM_SCRATCH_BYTES];
+
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -1176,6 +1184,30 @@ int splitk_dispatch(bool nt, int64_t M, int64_t N, int64_t K, const void* A, int
     return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
 }
 
+// Device address of the current device's `scratch` array, looked up once per
+// device (with that device current) and kept.
+void* g_scratch[kMaxDevices];
+std::mutex g_scratch_mutex;
+
+int scratch_address(void** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return GEMM_ERR_UNSUPPORTED;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (g_scratch[dev] == nullptr) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+            (void)hipGetLastError();
+            return GEMM_ERR_LAUNCH;
+        }
+        g_scratch[dev] = p;
+    }
+    *out = g_scratch[dev];
+    return GEMM_OK;
+}
+
 // ---------------------------------------------------------------------------
 // Dynamic tile schedule (gemm_bf16_dynamic).
 // ---------------------------------------------------------------------------
@@ -1349,6 +1381,31 @@ int gemm_bf16_splitk_plan(int64_t M, int64_t N, int64_t K, int b_colmajor, int s
     return GEMM_OK;
 }
 
+int gemm_bf16_splitk_noalloc(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+                              int64_t ldb, int b_colmajor, void* C, int64_t ldc, int out_type,
+                              const float* row_scale, const float* col_scale, const float* bias, int splits,
+                              void* stream) {
+    epi::Params e;
+    int rc = fused_params(out_type, C, row_scale, col_scale, bias, &e);
+    if (rc != GEMM_OK) return rc;
+    if (splits < 0) return GEMM_ERR_INVALID_ARG;
+    const bool nt = b_colmajor != 0;
+    rc = check_common(M, N, K, A, lda, B, ldb, nt ? K : N, C, ldc);
+    if (rc == 1) return GEMM_OK;
+    if (rc != GEMM_OK) return rc;
+    DeviceInfo dev;
+    rc = device_info(&dev);
+    if (rc != GEMM_OK) return rc;
+    const SplitPlan p = resolve_split(nt, M, N, K, A, lda, B, ldb, ldc, e, dev.cus, splits);
+    // the same plan as gemm_bf16_splitk: unsplit products need no scratch
+    if (p.splits <= 1) return bf16_dispatch(nt, M, N, K, A, lda, B, ldb, C, ldc, e, stream);
+    if (plan_bytes(p, M, N) > (int64_t)GEMM_SCRATCH_BYTES) return GEMM_ERR_SCRATCH;
+    void* ws = nullptr;
+    rc = scratch_address(&ws);
+    if (rc != GEMM_OK) return rc;
+    return splitk_dispatch(nt, M, N, K, A, lda, B, ldb, C, ldc, e, splits, ws, GEMM_SCRATCH_BYTES, stream);
+}
+
 int gemm_bf16_splitk_workspace(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
                                 int64_t ldb, int b_colmajor, const void* C, int64_t ldc, int out_type,
                                 const float* row_scale, const float* col_scale, const float* bias, int splits,
@@ -1383,6 +1440,9 @@ const char* gemm_strerror(int code) {
                    "head dimension or scale)";
         case GEMM_ERR_UNSUPPORTED: return "unsupported device (a gfx950 GPU is required)";
         case GEMM_ERR_LAUNCH: return "kernel launch failed";
+        case GEMM_ERR_SCRATCH:
+            return "the split plan needs more than the library's fixed scratch (GEMM_SCRATCH_BYTES); use "
+                   "gemm_bf16_splitk with a workspace, or ask for fewer K ranges";
         default: return "unknown error code";
     }
 }

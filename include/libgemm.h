@@ -69,7 +69,9 @@ extern "C" {
 #define GEMM_ERR_UNSUPPORTED (-2)
 /* the HIP runtime reported an error when the kernel was enqueued */
 #define GEMM_ERR_LAUNCH (-3)
-
+/* gemm_bf16_splitk_noalloc: the split plan needs more scratch than the
+ * library's fixed array holds (GEMM_SCRATCH_BYTES) */
+#define GEMM_ERR_SCRATCH (-4)
 
 /* bf16 GEMM, B row-major: A bf16 M x K (lda >= K), B bf16 K x N with
  * element (k, j) at B[k*ldb + j] (ldb >= N), C fp32 M x N (ldc >= N). */
@@ -226,6 +228,36 @@ int gemm_bf16_splitk_workspace(int64_t M, int64_t N, int64_t K,
                                const void* C, int64_t ldc, int out_type,
                                const float* row_scale, const float* col_scale, const float* bias,
                                int splits, int cus, int* splits_used, size_t* workspace_bytes);
+
+/* ---- split-K without a workspace -----------------------------------------
+ *
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, serving loops, harnesses that forbid allocation): gemm_bf16_splitk
+ * with the partial products in a fixed device array that the library itself
+ * holds, GEMM_SCRATCH_BYTES per GPU, kept from the first call on that GPU
+ * until the process ends.  Arguments as gemm_bf16_splitk without the
+ * workspace; the split plan, the kernels and hence the results are those of
+ * gemm_bf16_splitk, bit for bit.  The call allocates nothing (no hipMalloc,
+ * no library routine that allocates).
+ *
+ * Every call on one GPU shares that GPU's array: calls that may overlap in
+ * time on one GPU (different streams, different host threads without
+ * ordering) race and give undefined results; order them on one stream.  The
+ * array's contents between calls do not matter (every partial product is
+ * written before it is read).
+ * Errors: those of gemm_bf16_splitk, and GEMM_ERR_SCRATCH (C untouched) when
+ * the plan needs more than GEMM_SCRATCH_BYTES, i.e. splits_used * M * N * 4
+ * bytes (or the compact stream-K style blocks) as gemm_bf16_splitk_workspace
+ * reports them; GEMM_ERR_LAUNCH if the runtime cannot give the array's
+ * device address. */
+#define GEMM_SCRATCH_BYTES ((size_t)64 << 20)
+
+int gemm_bf16_splitk_noalloc(int64_t M, int64_t N, int64_t K,
+                             const void* A, int64_t lda,
+                             const void* B, int64_t ldb, int b_colmajor,
+                             void* C, int64_t ldc, int out_type,
+                             const float* row_scale, const float* col_scale, const float* bias,
+                             int splits, void* stream);
 
 /* ---- dynamic tile schedule -----------------------------------------------
  *
