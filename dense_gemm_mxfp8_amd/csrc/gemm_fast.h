@@ -184,12 +184,14 @@ __device__ __forceinline__ int next_tile(const Args& a, int x, int idx, int P, i
 __device__ __forceinline__ int64_t round4(int64_t bytes) { return (bytes + 3) & ~(int64_t)3; }
 
 // Keep the first nb bytes (0 .. 16) of a 16-byte chunk, zero the rest.
+// Branch-free: dword w keeps min(max(nb - 4 w, 0), 4) bytes, through the
+// mask 2^(8 b) - 1 formed in 64 bits (b = 4 gives all ones, b = 0 none).
 __device__ __forceinline__ i32x4 keep_bytes(i32x4 v, int nb) {
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-        const int b = nb - 4 * w;
-        if (b <= 0) v[w] = 0;
-        else if (b < 4) v[w] = (int)((uint32_t)v[w] & ((1u << (8 * b)) - 1u));
+        const int b = min(max(nb - 4 * w, 0), 4);
+        const uint32_t m = (uint32_t)((1ull << (8 * b)) - 1ull);
+        v[w] = (int)((uint32_t)v[w] & m);
     }
     return v;
 }
@@ -198,35 +200,59 @@ __device__ __forceinline__ i32x4 keep_bytes(i32x4 v, int nb) {
 // a stage: buffer loads at byte soff of each row through `rs` (rows past the
 // operand lie outside it and read as zero), bytes at or past kvalid_b zeroed.
 // The rows are 16-byte aligned, so the loads read aligned dwords and a range
-// rounded up to a dword touches nothing past the operand's last dword.
+// rounded up to a dword touches nothing past the operand's last dword.  Every
+// chunk is loaded, past K too (inside a row that is the row's padding or the
+// next row, inside the descriptor either way; past the descriptor, zero),
+// and masked afterwards: with the loads under per-lane branches the compiler
+// waited for each one in turn, a full memory round trip per chunk.
 template <int RB, int THREADS = kThreads>
 __device__ __forceinline__ void tail_kc(uint8_t FAST_LDS* dst, __amdgpu_buffer_rsrc_t rs, int ld_b, int soff,
                                         int kvalid_b, int tid) {
     constexpr int CPR = RB / 16;
+    constexpr int NI = kTile * CPR / THREADS;
+    // the offsets below are invariant over the persistent tile loop; hoisted
+    // out of it they would stay live through the K loop and spill
+    asm volatile("" : "+v"(tid));
+    i32x4 v[NI];
 #pragma unroll
-    for (int i = 0; i < kTile * CPR / THREADS; ++i) {
+    for (int i = 0; i < NI; ++i) {
         const int idx = i * THREADS + tid;
         const int r = idx / CPR, c = idx % CPR;
-        i32x4 v = {0, 0, 0, 0};
-        if (c * 16 < kvalid_b)
-            v = keep_bytes(__builtin_amdgcn_raw_buffer_load_b128(rs, r * ld_b + c * 16, soff, 0), kvalid_b - c * 16);
-        *(i32x4 FAST_LDS*)(dst + kc_off<RB>(r, c)) = v;
+        v[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, r * ld_b + c * 16, soff, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        const int idx = i * THREADS + tid;
+        const int r = idx / CPR, c = idx % CPR;
+        *(i32x4 FAST_LDS*)(dst + kc_off<RB>(r, c)) = keep_bytes(v[i], kvalid_b - c * 16);
     }
 }
 
 // Partial k-tile of row-major B (k rows of 256 bf16) into a stage: k-rows at
 // or past kvalid and 8-column chunks at or past ncols are zero (N % 8 == 0,
-// so a chunk is either wholly inside N or wholly outside).
+// so a chunk is either wholly inside N or wholly outside).  Loaded
+// unconditionally and masked afterwards, as tail_kc (k-rows past the data
+// lie outside the descriptor; chunks past N inside a row are the padding or
+// the next row).
 template <int BK, int THREADS = kThreads>
 __device__ __forceinline__ void tail_nn(uint8_t FAST_LDS* dst, __amdgpu_buffer_rsrc_t rs, int ldb_b, int soff,
                                         int kvalid, int ncols, int tid) {
+    constexpr int NI = BK * 32 / THREADS;
+    asm volatile("" : "+v"(tid));  // keep the offsets inside the tile loop (as tail_kc)
+    i32x4 v[NI];
 #pragma unroll
-    for (int i = 0; i < BK * 32 / THREADS; ++i) {
+    for (int i = 0; i < NI; ++i) {
         const int idx = i * THREADS + tid;
         const int kk = idx >> 5, c = idx & 31;
-        i32x4 v = {0, 0, 0, 0};
-        if (kk < kvalid && c * 8 < ncols) v = __builtin_amdgcn_raw_buffer_load_b128(rs, kk * ldb_b + c * 16, soff, 0);
-        *(i32x4 FAST_LDS*)(dst + nn_off(kk, c * 8)) = v;
+        v[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, kk * ldb_b + c * 16, soff, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        const int idx = i * THREADS + tid;
+        const int kk = idx >> 5, c = idx & 31;
+        const bool keep = kk < kvalid && c * 8 < ncols;
+        i32x4 z = {0, 0, 0, 0};
+        *(i32x4 FAST_LDS*)(dst + nn_off(kk, c * 8)) = keep ? v[i] : z;
     }
 }
 
@@ -388,6 +414,7 @@ __device__ __forceinline__ void static_for(F&& f) {
 constexpr int kSgMfma = 0x008;
 constexpr int kSgVmem = 0x010;
 constexpr int kSgDsRead = 0x100;
+constexpr int kSgDsWrite = 0x200;
 
 // Interleave the 16 MFMAs of one k-step with NR LDS fragment reads and ND
 // DMA instructions so that memory instructions issue while the matrix core

@@ -10,12 +10,22 @@
 // the stage being filled, and writes them into the swizzled stage with
 // ds_write_b128:
 //
-//   k-step 0 of k-tile t: store the registers of k-tile t+1 into the other
-//                         stage, issue the loads of k-tile t+1+PF into the
-//                         freed registers, read the fragments of step 1,
-//                         multiply step 0;
+//   k-step 0 of k-tile t: multiply step 0, and between its MFMAs read the
+//                         fragments of step 1 (first), store the registers
+//                         of k-tile t+1 into the other stage, and issue the
+//                         loads of k-tile t+1+PF into the freed registers;
 //   k-step 1:             wait for LDS, barrier (stage t+1 complete, stage t
-//                         fully read), read step 0 of t+1, multiply step 1.
+//                         fully read), multiply step 1 with the reads of
+//                         step 0 of t+1 between its MFMAs.
+//
+// The interleave is fixed with sched_group_barrier: left to itself the
+// compiler issued each step's fragment reads after most of the previous
+// step's MFMAs, so their LDS latency showed at every step.
+//
+// The partial last k-tile (K mod 32 != 0) is loaded into a register set of
+// its own in the tile's prologue, with the predicated loads described below,
+// and stored and multiplied after the K loop; loaded after the K loop
+// instead, its latency was paid once per tile in the open.
 //
 // A load is thus issued PF k-tiles before its registers are stored: with
 // one 256 x 192 tile per CU a k-tile is 24 MFMAs (768 matrix-core cycles) per
@@ -156,7 +166,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_reg_kernel(Args a) {
         // 2^31, so the sum cannot wrap).  Selecting the offset rather than a
         // second descriptor keeps the descriptors in scalar registers.
         constexpr int kDead = 0x7fffffff;
-        auto load = [&](auto qidx, int kt, bool live) {
+        auto load_full = [&](auto qidx, int kt, bool live) {
             constexpr int q = decltype(qidx)::value;
             const int ka = live ? sa + kt * RB : kDead;
             const int kb = live ? sb + ((KIND == kNN) ? kt * BK * (int)a.ldb_b : kt * RB) : kDead;
@@ -165,6 +175,63 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_reg_kernel(Args a) {
 #pragma unroll
             for (int i = 0; i < NCB; ++i) rb_reg[q][i] = __builtin_amdgcn_raw_buffer_load_b128(rb, b_g[i], kb, 0);
         };
+        // Partial k-tile KT, holding kvalid (1 .. 32) k.  Chunks lying wholly
+        // inside the data are 16-byte loads; the chunk that straddles the end
+        // of a row (K-contiguous operands) or of the last columns (row-major
+        // B) is read as 2-byte elements, so no load reaches past the
+        // operand's last element; the rest is zero.  Rows past M / N read as
+        // zero through the descriptors.
+        const int kvalid = a.K - KT * BK;
+        // 8 elements from byte offset voff + soff, element e kept if e < n;
+        // 2-byte loads never straddle the end of the data
+        auto gather = [](__amdgpu_buffer_rsrc_t rs, int voff, int soff, int n) {
+            i32x4 v = {0, 0, 0, 0};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t x = __builtin_amdgcn_raw_buffer_load_b16(rs, voff + 2 * e, soff, 0);
+                if (e < n) v[e >> 1] |= (int)(x << (16 * (e & 1)));
+            }
+            return v;
+        };
+        i32x4 ta_reg[NC], tb_reg[NCB];  // the partial k-tile
+        auto load_tail = [&]() {
+#pragma unroll
+            for (int i = 0; i < NC; ++i) {
+                const int idx = i * kThreads + tid;
+                const int c8 = 8 * (idx & 3);
+                i32x4 va = {0, 0, 0, 0};
+                if (c8 + 8 <= kvalid)
+                    va = __builtin_amdgcn_raw_buffer_load_b128(ra, a_g[i], sa + KT * RB, 0);
+                else if (c8 < kvalid)
+                    va = gather(ra, a_g[i], sa + KT * RB, kvalid - c8);
+                ta_reg[i] = va;
+            }
+#pragma unroll
+            for (int i = 0; i < NCB; ++i) {
+                const int idx = i * kThreads + tid;
+                i32x4 vb = {0, 0, 0, 0};
+                if constexpr (KIND == kNN) {
+                    const int kk = idx / CPK, n8 = 8 * (idx % CPK);
+                    const int soff = sb + KT * BK * (int)a.ldb_b;
+                    if (kk < kvalid) {
+                        if (n8 + 8 <= rows_b)
+                            vb = __builtin_amdgcn_raw_buffer_load_b128(rb, b_g[i], soff, 0);
+                        else if (n8 < rows_b)
+                            vb = gather(rb, b_g[i], soff, rows_b - n8);
+                    }
+                } else {
+                    const int c8 = 8 * (idx & 3);
+                    if (c8 + 8 <= kvalid)
+                        vb = __builtin_amdgcn_raw_buffer_load_b128(rb, b_g[i], sb + KT * RB, 0);
+                    else if (c8 < kvalid)
+                        vb = gather(rb, b_g[i], sb + KT * RB, kvalid - c8);
+                }
+                tb_reg[i] = vb;
+            }
+        };
+        // k-tile kt into register set q: zero (no traffic) past the full
+        // k-tiles
+        auto load = [&](auto qidx, int kt) { load_full(qidx, kt, kt < KT); };
         auto store = [&](auto qidx, auto sidx) {
             constexpr int q = decltype(qidx)::value;
             uint8_t FAST_LDS* base = decltype(sidx)::value ? (uint8_t FAST_LDS*)st1 : (uint8_t FAST_LDS*)st0;
@@ -205,14 +272,52 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_reg_kernel(Args a) {
                 for (int j = 0; j < NBJ; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
         };
+        // Instruction order of a k-step (sched_group_barrier): MFMA slot m is
+        // followed by the memory instructions given it.  Step 0: the NR
+        // fragment reads of step 1 over the first half of the MFMAs, then the
+        // NW stores into the next stage, then the NW loads of a later k-tile
+        // (they reuse the stored registers).  Step 1: the NR reads of the
+        // next k-tile's step 0 over the first half of the MFMAs, so that they
+        // have landed when that step's MFMAs start.
+        constexpr int NMF = kBlocks * NBJ;
+        constexpr int NR = (KIND == kNN) ? kBlocks + 2 * NBJ : kBlocks + NBJ;
+        constexpr int NW = NC + NCB;
+        auto interleave0 = [&]() {
+            static_for<0, NMF>([&](auto mc) {
+                constexpr int m = decltype(mc)::value;
+                constexpr int H = NMF / 2;
+                // reads spread over slots 0 .. H-1, stores and loads over H .. NMF-1
+                constexpr int r0 = m < H ? m * NR / H : NR, r1 = m < H ? (m + 1) * NR / H : NR;
+                constexpr int w0 = m < H ? 0 : (m - H) * NW / (NMF - H), w1 = m < H ? 0 : (m + 1 - H) * NW / (NMF - H);
+                __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+                if constexpr (r1 > r0) __builtin_amdgcn_sched_group_barrier(kSgDsRead, r1 - r0, 0);
+                if constexpr (w1 > w0) {
+                    __builtin_amdgcn_sched_group_barrier(kSgDsWrite, w1 - w0, 0);
+                    __builtin_amdgcn_sched_group_barrier(kSgVmem, w1 - w0, 0);
+                }
+            });
+        };
+        auto interleave1 = [&]() {
+            static_for<0, NMF>([&](auto mc) {
+                constexpr int m = decltype(mc)::value;
+                constexpr int H = NMF / 2;
+                constexpr int r0 = m < H ? m * NR / H : NR, r1 = m < H ? (m + 1) * NR / H : NR;
+                __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+                if constexpr (r1 > r0) __builtin_amdgcn_sched_group_barrier(kSgDsRead, r1 - r0, 0);
+            });
+        };
 
         // prologue: k-tile 0 into stage 0, k-tiles 1 .. PF in flight to
         // registers (k-tile j in set j % PF)
         using Z = std::integral_constant<int, 0>;
-        load(Z{}, 0, 0 < KT);
-        static_for<1, PF>([&](auto qc) { load(qc, decltype(qc)::value, decltype(qc)::value < KT); });
+        load(Z{}, 0);
+        static_for<1, PF>([&](auto qc) { load(qc, decltype(qc)::value); });
+        // the partial k-tile after k-tile 0: the element loads of a
+        // straddling chunk wait for their data inside their branch, and that
+        // wait then overlaps the wait for k-tile 0 the prologue has anyway
+        if constexpr (TAIL) load_tail();
         store(Z{}, Z{});
-        load(Z{}, PF, PF < KT);
+        load(Z{}, PF);
         wait_lgkm0();
         barrier();
         bf16x8 F0a[kBlocks], F0b[NBJ], F1a[kBlocks], F1b[NBJ];
@@ -226,16 +331,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_reg_kernel(Args a) {
             // kt+1+PF, fragments of step 1.  k-tile kt+1 sits in set
             // (kt+1) % PF; kt+1+PF goes there next.
             using Q = std::integral_constant<int, (q + 1) % PF>;
-            store(Q{}, std::integral_constant<int, sn>{});
-            load(Q{}, kt + 1 + PF, kt + 1 + PF < KT);
             read_frags(sidx{}, 1, F1a, F1b);
+            store(Q{}, std::integral_constant<int, sn>{});
+            load(Q{}, kt + 1 + PF);
             mfma(F0a, F0b);
+            interleave0();
             __builtin_amdgcn_sched_barrier(0);
             // k-step 1
             wait_lgkm0();
             barrier();
             read_frags(std::integral_constant<int, sn>{}, 0, F0a, F0b);
             mfma(F1a, F1b);
+            interleave1();
             __builtin_amdgcn_sched_barrier(0);
         };
         for (int kt0 = 0; kt0 < KTM; kt0 += U) {
@@ -243,63 +350,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_reg_kernel(Args a) {
         }
 
         if constexpr (TAIL) {
-            // Last k-tile KT, holding kvalid (1 .. 32) k.  Chunks lying
-            // wholly inside the data are 16-byte loads; the chunk that
-            // straddles the end of a row (K-contiguous operands) or of the
-            // last columns (row-major B) is read as 2-byte elements, so no
-            // load reaches past the operand's last element; the rest is zero.
-            // Rows past M / N read as zero through the descriptors.
-            const int kvalid = a.K - KT * BK;
-            // 8 elements from byte offset voff + soff, element e kept if e < n;
-            // 2-byte loads never straddle the end of the data
-            auto gather = [](__amdgpu_buffer_rsrc_t rs, int voff, int soff, int n) {
-                i32x4 v = {0, 0, 0, 0};
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const uint32_t x = __builtin_amdgcn_raw_buffer_load_b16(rs, voff + 2 * e, soff, 0);
-                    if (e < n) v[e >> 1] |= (int)(x << (16 * (e & 1)));
-                }
-                return v;
-            };
-#pragma unroll
-            for (int i = 0; i < NC; ++i) {
-                const int idx = i * kThreads + tid;
-                const int c8 = 8 * (idx & 3);
-                i32x4 va = {0, 0, 0, 0};
-                if (c8 + 8 <= kvalid)
-                    va = __builtin_amdgcn_raw_buffer_load_b128(ra, a_g[i], sa + KT * RB, 0);
-                else if (c8 < kvalid)
-                    va = gather(ra, a_g[i], sa + KT * RB, kvalid - c8);
-                ra_reg[0][i] = va;
-            }
-#pragma unroll
-            for (int i = 0; i < NCB; ++i) {
-                const int idx = i * kThreads + tid;
-                const int c8 = 8 * (idx & 3);
-                i32x4 vb = {0, 0, 0, 0};
-                if constexpr (KIND == kNN) {
-                    const int kk = idx / CPK, n8 = 8 * (idx % CPK);
-                    const int soff = sb + KT * BK * (int)a.ldb_b;
-                    if (kk < kvalid) {
-                        if (n8 + 8 <= rows_b)
-                            vb = __builtin_amdgcn_raw_buffer_load_b128(rb, b_g[i], soff, 0);
-                        else if (n8 < rows_b)
-                            vb = gather(rb, b_g[i], soff, rows_b - n8);
-                    }
-                } else {
-                    if (c8 + 8 <= kvalid)
-                        vb = __builtin_amdgcn_raw_buffer_load_b128(rb, b_g[i], sb + KT * RB, 0);
-                    else if (c8 < kvalid)
-                        vb = gather(rb, b_g[i], sb + KT * RB, kvalid - c8);
-                }
-                rb_reg[0][i] = vb;
-            }
             // the last body ended with a barrier after every wave's reads of
             // k-tile data in stage 0 (KTM is even, so stage 0 is free; the
-            // reads that follow that barrier fetch the unused dead k-tile).
-            // Register set 0 is reused: loads still in flight into it (dead
-            // k-tiles) are waited for before it is overwritten.
-            store(Z{}, Z{});
+            // reads that follow that barrier fetch the unused dead k-tile)
+            uint8_t FAST_LDS* base = (uint8_t FAST_LDS*)st0;
+#pragma unroll
+            for (int i = 0; i < NC; ++i) *(i32x4 FAST_LDS*)(base + a_l[i]) = ta_reg[i];
+#pragma unroll
+            for (int i = 0; i < NCB; ++i) *(i32x4 FAST_LDS*)(base + b_l[i]) = tb_reg[i];
             wait_lgkm0();
             barrier();
 #pragma unroll
