@@ -175,13 +175,30 @@ def bench_workload(name: str, steps: int, warmup: int, settle: float = 0.0):
     if w["kind"] == "mx":
         ops = [(prob.A.to(dev), prob.B.to(dev), prob.SA.to(dev), prob.SB.to(dev))
                for _ in range(copies)]
-
-        def step(i):
-            A, B, SA, SB = ops[i % copies]
-            rc = dg.gemm_mxfp8(M, N, K, A.data_ptr(), K, B.data_ptr(), K, SA.data_ptr(),
-                               SB.data_ptr(), C.data_ptr(), N, s)
+        if w.get("splitk"):
+            # split-K: the library's plan, with its workspace allocated once
+            A0, B0, SA0, SB0 = ops[0]
+            rc, splits, nbytes = dg.gemm_mxfp8_splitk_workspace(M, N, K, A0.data_ptr(), K, B0.data_ptr(), K,
+                                                                SA0.data_ptr(), SB0.data_ptr(), C.data_ptr(), N,
+                                                                dg.GEMM_OUT_F32, None, None, None, 0)
             if rc:
                 raise RuntimeError(dg.gemm_strerror(rc))
+            ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+
+            def step(i):
+                A, B, SA, SB = ops[i % copies]
+                rc = dg.gemm_mxfp8_splitk(M, N, K, A.data_ptr(), K, B.data_ptr(), K, SA.data_ptr(), SB.data_ptr(),
+                                          C.data_ptr(), N, dg.GEMM_OUT_F32, None, None, None, 0, ws.data_ptr(),
+                                          ws.numel(), s)
+                if rc:
+                    raise RuntimeError(dg.gemm_strerror(rc))
+        else:
+            def step(i):
+                A, B, SA, SB = ops[i % copies]
+                rc = dg.gemm_mxfp8(M, N, K, A.data_ptr(), K, B.data_ptr(), K, SA.data_ptr(),
+                                   SB.data_ptr(), C.data_ptr(), N, s)
+                if rc:
+                    raise RuntimeError(dg.gemm_strerror(rc))
         dtype, peak_key = "fp8(e4m3)+e8m0", "fp8"
     else:
         ops = [(prob.A.to(dev), prob.B.to(dev)) for _ in range(copies)]
@@ -189,7 +206,10 @@ def bench_workload(name: str, steps: int, warmup: int, settle: float = 0.0):
         ldb = K if prob.b_colmajor else N
         if w.get("splitk"):
             # split-K: the library's plan, with its workspace allocated once
-            rc, splits, nbytes = dg.gemm_bf16_splitk_plan(M, N, K, prob.b_colmajor, 0)
+            A0, B0 = ops[0]
+            rc, splits, nbytes = dg.gemm_bf16_splitk_workspace(M, N, K, A0.data_ptr(), K, B0.data_ptr(), ldb,
+                                                               prob.b_colmajor, C.data_ptr(), N, dg.GEMM_OUT_F32,
+                                                               None, None, None, 0)
             if rc:
                 raise RuntimeError(dg.gemm_strerror(rc))
             ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)

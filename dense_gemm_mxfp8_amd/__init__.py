@@ -61,6 +61,13 @@ def library() -> ctypes.CDLL:
         lib.gemm_bf16_splitk_plan.restype = ctypes.c_int
         lib.gemm_bf16_splitk_plan.argtypes = [_i64, _i64, _i64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                               ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_size_t)]
+        lib.gemm_mxfp8_splitk.restype = ctypes.c_int
+        lib.gemm_mxfp8_splitk.argtypes = [_i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _i64, ctypes.c_int,
+                                          _vp, _vp, _vp, ctypes.c_int, _vp, ctypes.c_size_t, _vp]
+        lib.gemm_mxfp8_splitk_workspace.restype = ctypes.c_int
+        lib.gemm_mxfp8_splitk_workspace.argtypes = [_i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _i64,
+                                                    ctypes.c_int, _vp, _vp, _vp, ctypes.c_int, ctypes.c_int,
+                                                    ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_size_t)]
         lib.gemm_bf16_splitk_noalloc.restype = ctypes.c_int
         lib.gemm_bf16_splitk_noalloc.argtypes = [_i64, _i64, _i64, _vp, _i64, _vp, _i64, ctypes.c_int, _vp, _i64,
                                                  ctypes.c_int, _vp, _vp, _vp, ctypes.c_int, _vp]
@@ -123,6 +130,23 @@ def gemm_bf16_splitk_plan(M, N, K, b_colmajor, splits=0, cus=0):
     ws = ctypes.c_size_t(0)
     rc = library().gemm_bf16_splitk_plan(M, N, K, int(b_colmajor), splits, cus, ctypes.byref(used),
                                          ctypes.byref(ws))
+    return rc, used.value, ws.value
+
+
+def gemm_mxfp8_splitk(M, N, K, A, lda, B, ldb, scaleA, scaleB, C, ldc, out_type, row_scale, col_scale, bias,
+                      splits, workspace, workspace_bytes, stream) -> int:
+    return library().gemm_mxfp8_splitk(M, N, K, A, lda, B, ldb, scaleA, scaleB, C, ldc, out_type, row_scale,
+                                       col_scale, bias, splits, workspace, workspace_bytes, stream)
+
+
+def gemm_mxfp8_splitk_workspace(M, N, K, A, lda, B, ldb, scaleA, scaleB, C, ldc, out_type, row_scale, col_scale,
+                                bias, splits=0, cus=0):
+    """(return code, K ranges used, workspace bytes) of gemm_mxfp8_splitk's plan."""
+    used = ctypes.c_int(0)
+    ws = ctypes.c_size_t(0)
+    rc = library().gemm_mxfp8_splitk_workspace(M, N, K, A, lda, B, ldb, scaleA, scaleB, C, ldc, out_type,
+                                               row_scale, col_scale, bias, splits, cus, ctypes.byref(used),
+                                               ctypes.byref(ws))
     return rc, used.value, ws.value
 
 

@@ -452,7 +452,8 @@ template <int KIND, int RB, int S, bool TAIL, int SG = 1, int E = 0, int D = 0, 
           bool SPLIT = false, bool DYN = false>
 __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(Args a) {
     static_assert(NW == 4 || (NW == 8 && KIND != kMX), "8 waves: bf16 only");
-    static_assert(!SPLIT || (KIND != kMX && !FUSED && NW == 4), "split-K: plain bf16 only");
+    static_assert(!SPLIT || (!FUSED && NW == 4), "split-K: plain fp32 partial stores, 4 waves");
+    static_assert(!SPLIT || KIND != kMX || SG > 1, "MX split-K: the scale-ring pipeline");
     static_assert(!DYN || (!SPLIT && NW == 4), "dynamic schedule: whole tiles, 4 waves");
     constexpr int THREADS = 64 * NW;
     constexpr int NBJ = NW == 8 ? 2 : kBlocks;  // 32-column MFMA blocks per wave tile
@@ -642,8 +643,12 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(Args a) {
         const __amdgpu_buffer_rsrc_t rdead = make_rsrc(a.A, 0);
         __amdgpu_buffer_rsrc_t rsa = rdead, rsb = rdead;
         if constexpr (KIND == kMX) {
-            rsa = make_rsrc(a.SA + (int64_t)m0 * a.sld, (int64_t)rows_a * a.sld);
-            rsb = make_rsrc(a.SB + (int64_t)n0 * a.sld, (int64_t)rows_b * a.sld);
+            // the scale codes of this unit's K range: sk0 codes of each row
+            // precede it, and it holds Kl / 32 of them
+            const int sk0 = k0 / 32;
+            const int sl = SPLIT ? Kl / 32 : a.sld;
+            rsa = make_rsrc(a.SA + (int64_t)m0 * a.sld + sk0, (int64_t)(rows_a - 1) * a.sld + sl);
+            rsb = make_rsrc(a.SB + (int64_t)n0 * a.sld + sk0, (int64_t)(rows_b - 1) * a.sld + sl);
         }
 
         // DMA instruction d (0 .. L-1) of k-tile kt into stage s.

@@ -66,8 +66,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 
 // MB: 16-row blocks of A (M <= 16 MB); NP: steps of B prefetched in
 // registers; COLS: columns per workgroup (32: 64-byte row segments, 64: full
-// 128-byte lines); WAVES: waves per workgroup, each owning a K range.
-template <int MB, int NP, int COLS, int WAVES>
+// 128-byte lines, 128: 256-byte segments); WAVES: waves per workgroup, each
+// owning a K range; BAUX: cache-policy bits of the B loads (2: non-temporal,
+// B is read once).
+template <int MB, int NP, int COLS, int WAVES, int BAUX = 0>
 __global__ __launch_bounds__(64 * WAVES, 1) void gemm_small_m_nn(Args a) {
     constexpr int kCols = COLS;
     constexpr int kWaves = WAVES;
@@ -149,7 +151,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_small_m_nn(Args a) {
 #pragma unroll
         for (int h = 0; h < NL; ++h)
             rB[slot][h] = __builtin_amdgcn_raw_buffer_load_b128(live ? rb : rdead, b_voff,
-                                                                k * (int)a.ldb_b + h * b_stepr, 0);
+                                                                k * (int)a.ldb_b + h * b_stepr, BAUX);
 #pragma unroll
         for (int b = 0; b < MB; ++b)
             rA[slot][b] = __builtin_amdgcn_raw_buffer_load_b128(live ? ra : rdead,

@@ -925,7 +925,7 @@ bool small_ok(bool nt, int64_t M, int64_t N, int64_t K, const void* A, int64_t l
 
 // splits > 1: K ranges of kslice rows (a multiple of small::kStepK), fp32
 // partial sums to `splits` stacked M x N planes at C (ldc == N, plain e).
-template <int MB, int NP, int COLS, int WAVES>
+template <int MB, int NP, int COLS, int WAVES, int BAUX = 0>
 int launch_small(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
                  void* C, int64_t ldc, const epi::Params& e, hipStream_t stream, int splits = 1,
                  int64_t kslice = 0) {
@@ -954,14 +954,35 @@ int launch_small(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, co
     }();
     if (pair_env == 0) a.pair_xcd = 0;  // LIBGEMM_SMALL_PAIR=0: no XCD pairing
 #endif
-    hipLaunchKernelGGL((small::gemm_small_m_nn<MB, NP, COLS, WAVES>), dim3(grid, splits > 1 ? splits : 1),
+    hipLaunchKernelGGL((small::gemm_small_m_nn<MB, NP, COLS, WAVES, BAUX>), dim3(grid, splits > 1 ? splits : 1),
                        dim3(64 * WAVES), 0, stream, a);
     return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
 }
 
 int launch_small_bf16(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
                       void* C, int64_t ldc, const epi::Params& e, hipStream_t s, int splits = 1,
-                      int64_t kslice = 0) {
+                      int64_t kslice = 0, int cols = 32) {
+    // wide strips (split-K partials only, M <= 16): 128 columns, 8 waves
+    // (two per SIMD, so the 4 steps of B prefetch fit the registers)
+    if (cols == 128 && M <= 16) {
+#ifdef LIBGEMM_MEASURE
+        // LIBGEMM_WIDE=<np>x<aux>: prefetch steps and B cache policy of the wide strips
+        static int wv = [] {
+            const char* e = getenv("LIBGEMM_WIDE");
+            int np = 0, aux = 0;
+            if (e && sscanf(e, "%dx%d", &np, &aux) == 2) return np * 10 + aux;
+            return 0;
+        }();
+        if (wv == 42) return launch_small<1, 4, 128, 8, 2>(M, N, K, A, lda, B, ldb, C, ldc, e, s, splits, kslice);
+        if (wv == 60) return launch_small<1, 6, 128, 8>(M, N, K, A, lda, B, ldb, C, ldc, e, s, splits, kslice);
+        if (wv == 62) return launch_small<1, 6, 128, 8, 2>(M, N, K, A, lda, B, ldb, C, ldc, e, s, splits, kslice);
+        if (wv == 40) return launch_small<1, 4, 128, 8>(M, N, K, A, lda, B, ldb, C, ldc, e, s, splits, kslice);
+        if (wv == 22) return launch_small<1, 2, 128, 8, 2>(M, N, K, A, lda, B, ldb, C, ldc, e, s, splits, kslice);
+#endif
+        // 2 steps of prefetch: as fast as 4 on 16 x 8192 x 8192 (31.1 against
+        // 31.3-32.1 us per call, MI355X) with half the registers
+        return launch_small<1, 2, 128, 8>(M, N, K, A, lda, B, ldb, C, ldc, e, s, splits, kslice);
+    }
     if (M <= 16) {
 #ifdef LIBGEMM_MEASURE
         // LIBGEMM_SMALL=<np>x<cols>x<waves> selects another compiled variant
@@ -1040,6 +1061,7 @@ struct SplitPlan {
     int64_t kslice;  // K elements per range, the last range takes the rest
     int64_t dp;      // stream-K style: whole tiles computed first (0: every tile split)
     int64_t rem;     // stream-K style: tiles split after them
+    int cols;        // small-M kernel: columns per workgroup (32, or 128 for wide strips)
 };
 
 // Workspace bytes of a plan.
@@ -1069,7 +1091,12 @@ int split_kernel(bool nt, int64_t M, int64_t N, int64_t K, bool aligned, int64_t
 //     3/4 of a round, cut K so that tiles x ranges fills about one round,
 //     each range at least 8 k-tiles (512) long;
 //   - small M (small kernel): when its 32-column blocks give fewer
-//     workgroups than CUs, the same with ranges of at least 1024;
+//     workgroups than CUs, the same with ranges of at least 1024.  With
+//     M <= 16, when 128-column blocks times ranges of at least 1024 fill
+//     at least 3/4 of the CUs, those wide strips are used instead, even
+//     where the 32-column blocks alone would fill the CUs: each workgroup
+//     then reads 256-byte row segments of B instead of 64-byte ones, which
+//     streams B from HBM faster (16 x 8192 x 8192: 4 ranges of 2048);
 //   - 256 x 256 tiles filling more than one round with a last round at most
 //     half full (stream-K style): the full rounds run whole tiles, and only
 //     the last round's tiles are split, into about CUs / (those tiles)
@@ -1079,10 +1106,23 @@ int split_kernel(bool nt, int64_t M, int64_t N, int64_t K, bool aligned, int64_t
 //     multiple of 8.
 SplitPlan plan_split(bool nt, int64_t M, int64_t N, int64_t K, bool aligned, int64_t lda, int64_t ldb, int cus,
                      int requested) {
-    SplitPlan p{split_kernel(nt, M, N, K, aligned, lda, ldb), 1, K, 0, 0};
+    SplitPlan p{split_kernel(nt, M, N, K, aligned, lda, ldb), 1, K, 0, 0, 32};
     if (p.kernel == kSplitNone || K <= 0) return p;
     const int64_t gran = p.kernel == kSplitFast ? 64 : small::kStepK;  // k-tile of the partial kernel
     int64_t want = requested;
+    // wide strips of the small-M kernel: 128-column blocks times `s` ranges
+    // of at least 1024 filling at least 3/4 of the CUs
+    const int64_t wide_units = (N + 127) / 128;
+    auto wide_ok = [&](int64_t s) {
+        return p.kernel == kSplitSmall && M <= 16 && s >= 2 && s <= K / 1024 && wide_units * s * 4 >= (int64_t)cus * 3;
+    };
+    if (want <= 0 && p.kernel == kSplitSmall) {
+        int64_t s = cus / wide_units;
+        if (s > K / 1024) s = K / 1024;
+        if (s > kMaxSplits) s = kMaxSplits;
+        if (wide_ok(s)) want = s;
+    }
+    if (p.kernel == kSplitSmall && wide_ok(want)) p.cols = 128;
     if (want <= 0) {
         const int64_t units = p.kernel == kSplitFast ? ((M + 255) / 256) * ((N + 255) / 256) : (N + 31) / 32;
         const int64_t min_range = p.kernel == kSplitFast ? 512 : 1024;
@@ -1166,7 +1206,7 @@ int splitk_dispatch(bool nt, int64_t M, int64_t N, int64_t K, const void* A, int
         return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
     }
     if (p.kernel == kSplitSmall) {
-        rc = launch_small_bf16(M, N, K, A, lda, B, ldb, ws, N, kPlain, s, p.splits, p.kslice);
+        rc = launch_small_bf16(M, N, K, A, lda, B, ldb, ws, N, kPlain, s, p.splits, p.kslice, p.cols);
     } else {
         fast::Args a = make_fast_args(M, N, K, A, lda, B, ldb, ws, N, 2, kPlain);
         a.kslice = (int)p.kslice;
@@ -1307,6 +1347,79 @@ int mx_dispatch(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, con
                   : launch<128, 128, kMx, false>(a, dev.cus, s);
 }
 
+// ---------------------------------------------------------------------------
+// MX split-K: the K ranges of the scale-ring pipeline (ranges a multiple of
+// 1024, so that every range starts on a 16-byte boundary of the scale rows
+// and runs whole rounds of the unrolled K loop).
+// ---------------------------------------------------------------------------
+
+// The plan of gemm_mxfp8_splitk: splits only when the 256 x 256 tiles give the
+// CUs less than 3/4 of a round (as the bf16 plan), into about CUs / tiles
+// ranges of at least 1024, at most kMaxSplits; the operands must suit the
+// scale-ring pipeline (16-byte aligned operands and scales, rows 16-byte
+// aligned, K a multiple of 512) and C's planes 32-bit offsets.  Products
+// the plan leaves whole run as gemm_mxfp8_fused.
+SplitPlan plan_split_mx(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
+                        const void* SA, const void* SB, int cus, int requested) {
+    SplitPlan p{kSplitNone, 1, K, 0, 0, 32};
+    const uintptr_t sal = ((uintptr_t)SA) | ((uintptr_t)SB);
+    if (K <= 0 || K % 512 || (sal & 15) || !c_ok(N) || !fast_ok(fast::kMX, M, N, K, A, lda, B, ldb, SA, SB))
+        return p;
+    p.kernel = kSplitFast;
+    // ranges of whole scale-ring rounds (8 k-tiles of 128): the pipeline runs
+    // a multiple of 8 k-tiles, so a shorter remainder would be dead k-tiles
+    constexpr int64_t gran = 1024;
+    int64_t want = requested;
+    if (want <= 0) {
+        const int64_t units = ((M + 255) / 256) * ((N + 255) / 256);
+        if (units * 4 >= (int64_t)cus * 3) return p;
+        want = cus / units;
+        if (want > K / 1024) want = K / 1024;
+    }
+    if (want > kMaxSplits) want = kMaxSplits;
+    if (want <= 1) return p;
+    int64_t kslice = (K + want - 1) / want;
+    kslice = (kslice + gran - 1) / gran * gran;
+    const int64_t splits = (K + kslice - 1) / kslice;
+    if (splits <= 1) return p;
+    p.splits = (int)splits;
+    p.kslice = kslice;
+    return p;
+}
+
+int mx_splitk_dispatch(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
+                       const uint8_t* SA, const uint8_t* SB, void* C, int64_t ldc, const epi::Params& e, int splits,
+                       void* ws, size_t ws_bytes, void* stream) {
+    if (splits < 0) return GEMM_ERR_INVALID_ARG;
+    int rc = check_common(M, N, K, A, lda, B, ldb, K, C, ldc);
+    if (rc == 1) return GEMM_OK;
+    if (rc != GEMM_OK) return rc;
+    if (K % 32 != 0) return GEMM_ERR_INVALID_ARG;
+    if (K > 0 && (SA == nullptr || SB == nullptr)) return GEMM_ERR_INVALID_ARG;
+    DeviceInfo dev;
+    rc = device_info(&dev);
+    if (rc != GEMM_OK) return rc;
+    const SplitPlan p = plan_split_mx(M, N, K, A, lda, B, ldb, SA, SB, dev.cus, splits);
+    if (p.splits <= 1) return mx_dispatch(M, N, K, A, lda, B, ldb, SA, SB, C, ldc, e, stream);
+    const int64_t need = plan_bytes(p, M, N);
+    if (ws == nullptr || (int64_t)ws_bytes < need || ((uintptr_t)ws & 15)) return GEMM_ERR_INVALID_ARG;
+    hipStream_t s = (hipStream_t)stream;
+    fast::Args f = make_fast_args(M, N, K, A, lda, B, ldb, ws, N, 1, kPlain);
+    f.SA = SA;
+    f.SB = SB;
+    f.sld = (int)(K / 32);
+    f.kslice = (int)p.kslice;
+    f.c_nt = 0;  // the partial sums are read back at once: keep them cached
+    rc = launch_fast<fast::kMX, 128, 2, 4, 12, 0, 4, false, true>(f, dev.cus, s, env_variant().group, p.splits);
+    if (rc != GEMM_OK) return rc;
+    int64_t blocks = (M * N / 4 + 255) / 256;
+    if (blocks > (int64_t)dev.cus * 8) blocks = (int64_t)dev.cus * 8;
+    if (blocks < 1) blocks = 1;
+    hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, s, (const float*)ws, p.splits,
+                       (int)M, (int)N, C, ldc, e);
+    return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1374,7 +1487,7 @@ int gemm_bf16_splitk_plan(int64_t M, int64_t N, int64_t K, int b_colmajor, int s
     }
     const bool nt = b_colmajor != 0;
     // operands assumed 16-byte aligned with dense leading dimensions
-    SplitPlan p{kSplitNone, 1, K, 0, 0};
+    SplitPlan p{kSplitNone, 1, K, 0, 0, 32};
     if (M > 0 && N > 0) p = plan_split(nt, M, N, K, true, K, nt ? K : N, cus, splits);
     if (splits_used) *splits_used = p.splits;
     if (workspace_bytes) *workspace_bytes = (size_t)plan_bytes(p, M, N);
@@ -1406,6 +1519,44 @@ int gemm_bf16_splitk_noalloc(int64_t M, int64_t N, int64_t K, const void* A, int
     return splitk_dispatch(nt, M, N, K, A, lda, B, ldb, C, ldc, e, splits, ws, GEMM_SCRATCH_BYTES, stream);
 }
 
+int gemm_mxfp8_splitk(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
+                      const uint8_t* scaleA, const uint8_t* scaleB, void* C, int64_t ldc, int out_type,
+                      const float* row_scale, const float* col_scale, const float* bias, int splits,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+    epi::Params e;
+    const int rc = fused_params(out_type, C, row_scale, col_scale, bias, &e);
+    if (rc != GEMM_OK) return rc;
+    return mx_splitk_dispatch(M, N, K, A, lda, B, ldb, scaleA, scaleB, C, ldc, e, splits, workspace,
+                              workspace_bytes, stream);
+}
+
+int gemm_mxfp8_splitk_workspace(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+                                int64_t ldb, const uint8_t* scaleA, const uint8_t* scaleB, const void* C,
+                                int64_t ldc, int out_type, const float* row_scale, const float* col_scale,
+                                const float* bias, int splits, int cus, int* splits_used, size_t* workspace_bytes) {
+    epi::Params e;
+    int rc = fused_params(out_type, C, row_scale, col_scale, bias, &e);
+    if (rc != GEMM_OK) return rc;
+    if (splits < 0 || cus < 0) return GEMM_ERR_INVALID_ARG;
+    rc = check_common(M, N, K, A, lda, B, ldb, K, C, ldc);
+    SplitPlan p{kSplitNone, 1, K, 0, 0, 32};
+    if (rc != 1) {
+        if (rc != GEMM_OK) return rc;
+        if (K % 32 != 0) return GEMM_ERR_INVALID_ARG;
+        if (K > 0 && (scaleA == nullptr || scaleB == nullptr)) return GEMM_ERR_INVALID_ARG;
+        if (cus == 0) {
+            DeviceInfo dev;
+            rc = device_info(&dev);
+            if (rc != GEMM_OK) return rc;
+            cus = dev.cus;
+        }
+        p = plan_split_mx(M, N, K, A, lda, B, ldb, scaleA, scaleB, cus, splits);
+    }
+    if (splits_used) *splits_used = p.splits;
+    if (workspace_bytes) *workspace_bytes = (size_t)plan_bytes(p, M, N);
+    return GEMM_OK;
+}
+
 int gemm_bf16_splitk_workspace(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
                                 int64_t ldb, int b_colmajor, const void* C, int64_t ldc, int out_type,
                                 const float* row_scale, const float* col_scale, const float* bias, int splits,
@@ -1416,7 +1567,7 @@ int gemm_bf16_splitk_workspace(int64_t M, int64_t N, int64_t K, const void* A, i
     if (splits < 0 || cus < 0) return GEMM_ERR_INVALID_ARG;
     const bool nt = b_colmajor != 0;
     rc = check_common(M, N, K, A, lda, B, ldb, nt ? K : N, C, ldc);
-    SplitPlan p{kSplitNone, 1, K, 0, 0};
+    SplitPlan p{kSplitNone, 1, K, 0, 0, 32};
     if (rc != 1) {
         if (rc != GEMM_OK) return rc;
         if (cus == 0) {

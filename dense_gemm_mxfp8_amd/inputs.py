@@ -161,6 +161,10 @@ WORKLOADS = {
                                     splitk=True),
     "skinny16x8192x8192_nt": dict(kind="bf16", M=16, N=8192, K=8192, dist="normal", b_colmajor=True,
                                   splitk=True),
+    # the skinny product through split-K: 128-column strips over 4 K ranges
+    "skinny16x8192x8192_nn_splitk": dict(kind="bf16", M=16, N=8192, K=8192, dist="normal", splitk=True),
+    # MX with a long K through split-K: 16 tiles, 16 ranges of 2048
+    "mx1024x1024x32768_splitk": dict(kind="mx", M=1024, N=1024, K=32768, dist="normal", splitk=True),
 }
 
 

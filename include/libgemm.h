@@ -229,6 +229,38 @@ int gemm_bf16_splitk_workspace(int64_t M, int64_t N, int64_t K,
                                const float* row_scale, const float* col_scale, const float* bias,
                                int splits, int cus, int* splits_used, size_t* workspace_bytes);
 
+/* MX-fp8 split-K: gemm_mxfp8_fused's product with K cut into ranges, as
+ * gemm_bf16_splitk (fp32 partial products in the caller's workspace, dense
+ * M x N planes added in range order, then the epilogue).  Ranges are a
+ * multiple of 1024 (the last takes the rest, a multiple of 512), so that each
+ * starts on a 16-byte boundary of the scale rows; the plan (splits == 0)
+ * splits when the 256 x 256 tiles give the
+ * compute units less than 3/4 of a round, into about CUs / tiles ranges of at
+ * least 1024.  Products that do not suit the split kernel (operands or
+ * scales not 16-byte aligned, rows not 16-byte aligned, K not a multiple of
+ * 512) or that the plan leaves whole run as gemm_mxfp8_fused and the
+ * workspace is not touched.  Arguments and errors as gemm_mxfp8_fused plus
+ * those of gemm_bf16_splitk for splits and the workspace. */
+int gemm_mxfp8_splitk(int64_t M, int64_t N, int64_t K,
+                      const void* A, int64_t lda,
+                      const void* B, int64_t ldb,
+                      const uint8_t* scaleA, const uint8_t* scaleB,
+                      void* C, int64_t ldc, int out_type,
+                      const float* row_scale, const float* col_scale, const float* bias,
+                      int splits, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+/* The plan gemm_mxfp8_splitk runs for these arguments (pointers inspected,
+ * never dereferenced): K ranges used and workspace bytes, as
+ * gemm_bf16_splitk_workspace.  Host only. */
+int gemm_mxfp8_splitk_workspace(int64_t M, int64_t N, int64_t K,
+                                const void* A, int64_t lda,
+                                const void* B, int64_t ldb,
+                                const uint8_t* scaleA, const uint8_t* scaleB,
+                                const void* C, int64_t ldc, int out_type,
+                                const float* row_scale, const float* col_scale, const float* bias,
+                                int splits, int cus, int* splits_used, size_t* workspace_bytes);
+
 /* ---- split-K without a workspace -----------------------------------------
  *
  * For callers that cannot allocate device memory (code under HIP graph

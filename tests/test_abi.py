@@ -115,7 +115,8 @@ SPLIT_PLANS = [
     ((2048, 2048, 1024, 1, 0, 256), 2),     # ranges of at least 512
     ((2048, 2048, 16384, 1, 0, 128), 2),    # fewer CUs, fewer ranges
     ((16, 2048, 8192, 0, 0, 256), 4),       # small M: 64 column blocks
-    ((16, 8192, 8192, 0, 0, 256), 1),       # small M: 256 column blocks
+    ((16, 8192, 8192, 0, 0, 256), 4),       # small M: 64 wide 128-column strips x 4 ranges
+    ((48, 8192, 8192, 0, 0, 256), 1),       # M > 16: 256 column blocks of 32 fill the GPU
     ((16, 8192, 8192, 1, 0, 256), 8),       # column-major B: 32 tiles
     ((1000, 777, 4104, 1, 5, 256), 5),
     ((1000, 1000, 1000, 1, 5, 256), 4),     # 200 -> 256 per range: 4 ranges
@@ -316,3 +317,29 @@ def test_bf16_helper_layout_keyword():
         op(A, Bkn.t(), True)       # (N, K) view with unit stride along N
     with pytest.raises(ValueError):
         op(A, Bkn, True)           # (K, N) is not (N, K)
+
+
+@pytest.mark.parametrize("case,want", [
+    ((1024, 1024, 8192, 0, 0), 8),      # 16 tiles: 8 ranges of 1024
+    ((1000, 777, 4096, 0, 0), 4),
+    ((512, 520, 3584, 2, 0), 2),        # ranges of 2048 and 1536
+    ((8192, 8192, 8192, 0, 0), 1),      # the GPU is full
+    ((1024, 1024, 8192 - 128, 0, 0), 1),  # K not a multiple of 512: no split kernel
+    ((1024, 1024, 8192, 0, 4), 1),      # scales 4 bytes off 16-byte alignment
+    ((1024, 1024, 8192, 100, 0), 8),    # asked counts are cut to ranges of at least 1024
+])
+def test_mxfp8_splitk_plan(case, want):
+    M, N, K, splits, soff = case
+    rc, used, nbytes = dg.gemm_mxfp8_splitk_workspace(M, N, K, F16, K, F16, K, F16 + soff, F16 + soff, F16, N,
+                                                      dg.GEMM_OUT_F32, None, None, None, splits, 256)
+    assert rc == dg.GEMM_OK
+    assert used == want and nbytes == (used * M * N * 4 if used > 1 else 0)
+
+
+def test_mxfp8_splitk_rejects_bad_arguments():
+    args = (64, 64, 1024, F16, 1024, F16, 1024, F16, F16, F16, 64, dg.GEMM_OUT_F32, None, None, None)
+    assert dg.gemm_mxfp8_splitk(*args, -1, None, 0, None) == dg.GEMM_ERR_INVALID_ARG
+    assert dg.gemm_mxfp8_splitk_workspace(*args, -1, 256)[0] == dg.GEMM_ERR_INVALID_ARG
+    bad_k = (64, 64, 1000, F16, 1024, F16, 1024, F16, F16, F16, 64, dg.GEMM_OUT_F32, None, None, None)
+    assert dg.gemm_mxfp8_splitk(*bad_k, 0, None, 0, None) == dg.GEMM_ERR_INVALID_ARG
+    assert dg.gemm_mxfp8_splitk_workspace(*bad_k, 0, 256)[0] == dg.GEMM_ERR_INVALID_ARG

@@ -100,8 +100,12 @@ def test_splitk_fast_kernel(case, exact):
 
 
 # small-M partial kernel (row-major B, M <= 64, N >= 2048): 64 column
-# blocks (the plan splits), K ending inside a 32-row step, 48 rows
-SMALL = [(16, 2048, 8192, 0), (16, 2048, 1000, 3), (48, 4096, 2056, 4), (1, 2048, 4096, 0), (16, 8192, 8192, 2)]
+# blocks (the plan splits), K ending inside a 32-row step, 48 rows; with
+# M <= 16 and enough columns the plan takes 128-column strips (16 x 8192 x
+# 8192: 4 ranges; N = 8232 leaves a partial strip, 3 ranges; K = 4104 ends
+# inside a step; M = 1)
+SMALL = [(16, 2048, 8192, 0), (16, 2048, 1000, 3), (48, 4096, 2056, 4), (1, 2048, 4096, 0), (16, 8192, 8192, 2),
+         (16, 8192, 8192, 0), (7, 8192 + 40, 4104, 0), (1, 8192, 8192, 4)]
 
 
 @pytest.mark.parametrize("case", SMALL, ids=lambda c: f"{c[0]}x{c[1]}x{c[2]}_s{c[3]}")
@@ -196,7 +200,8 @@ def test_splitk_tensor_helper():
     P.assert_exact(C.cpu().numpy().astype(np.float64), want, "bf16_splitk")
 
 
-@pytest.mark.parametrize("name,ranges", [("longk1024x1024x32768_nt", 16), ("skinny16x8192x8192_nt", 8)])
+@pytest.mark.parametrize("name,ranges", [("longk1024x1024x32768_nt", 16), ("skinny16x8192x8192_nt", 8),
+                                        ("skinny16x8192x8192_nn_splitk", 4)])
 def test_splitk_bench_workloads(name, ranges):
     """The split-K workloads at full size, in the launch configuration the
     benchmark times (the library's plan, ldc = N), on every output.  With
@@ -267,3 +272,136 @@ def test_splitk_helper_sizes_workspace_for_padded_views(case):
     torch.cuda.synchronize()
     want, _ = P.oracle_bf16(P.bits16(prob.A), P.bits16(prob.B), colmajor)
     P.assert_exact(C.cpu().numpy().astype(np.float64), want, prob.name)
+
+
+# ---------------------------------------------------------------- MX split-K
+
+def _mx_run(prob, splits, *, out="f32", vecs=(None, None, None), scale_off=0, ws_fill=float("nan"), ws=None):
+    """gemm_mxfp8_splitk on the problem; returns (C as float64, ranges used, workspace)."""
+    M, N, K = prob.M, prob.N, prob.K
+    A, B = prob.A.to(DEV), prob.B.to(DEV)
+
+    def at(S):  # scale codes starting scale_off bytes past a 256-byte boundary
+        buf = torch.zeros(S.numel() + 256, dtype=torch.uint8, device=DEV)
+        v = buf[scale_off:scale_off + S.numel()].view(S.shape)
+        v.copy_(S.to(DEV))
+        return v
+    SA, SB = at(prob.SA), at(prob.SB)
+    ldc = N + 3
+    Cst = torch.full((M, ldc), -7.0, dtype=OUT_DTYPE[out], device=DEV)
+    rs, cs, bias = (None if v is None else torch.from_numpy(v).to(DEV) for v in vecs)
+    ptr = lambda t: 0 if t is None else t.data_ptr()
+    rc, used, nbytes = dg.gemm_mxfp8_splitk_workspace(M, N, K, A.data_ptr(), K, B.data_ptr(), K, SA.data_ptr(),
+                                                      SB.data_ptr(), Cst.data_ptr(), ldc, OUT_TYPE[out], ptr(rs),
+                                                      ptr(cs), ptr(bias), splits)
+    assert rc == dg.GEMM_OK
+    if ws is None:
+        ws = torch.full((max(nbytes, 16) // 4,), ws_fill, dtype=torch.float32, device=DEV)
+    rc = dg.gemm_mxfp8_splitk(M, N, K, A.data_ptr(), K, B.data_ptr(), K, SA.data_ptr(), SB.data_ptr(),
+                              Cst.data_ptr(), ldc, OUT_TYPE[out], ptr(rs), ptr(cs), ptr(bias), splits, ws.data_ptr(),
+                              ws.numel() * 4, P.stream())
+    assert rc == dg.GEMM_OK, dg.gemm_strerror(rc)
+    torch.cuda.synchronize()
+    C = Cst.float().cpu().numpy()
+    assert (C[:, N:] == -7.0).all(), "C written outside M x N"
+    return np.ascontiguousarray(C[:, :N]).astype(np.float64), used, ws
+
+
+# (M, N, K, splits, ranges): 16 tiles with the plan (8 ranges of 1024; 4
+# ranges of 1024), asked counts whose last range is shorter (3584 in ranges
+# of 2048 and 1536) or with 2 tiles in N, partial tiles in M and N
+MX_SPLIT = [(1024, 1024, 8192, 0, 8), (1000, 777, 4096, 0, 4), (512, 520, 3584, 2, 2), (300, 1100, 2048, 2, 2)]
+
+
+@pytest.mark.parametrize("case", MX_SPLIT, ids=lambda c: f"{c[0]}x{c[1]}x{c[2]}_s{c[3]}")
+@pytest.mark.parametrize("exact", [True, False], ids=["integer", "normal"])
+def test_mx_splitk(case, exact):
+    M, N, K, splits, ranges = case
+    prob = inputs.mx_problem(M, N, K, dist="integer" if exact else "normal", seed=102)
+    P.note(f"mx splitk {M}x{N}x{K} splits={splits}")
+    got, used, _ = _mx_run(prob, splits)
+    assert used == ranges
+    want, mag = P.oracle_mx(prob.A, prob.B, prob.SA, prob.SB)
+    if exact:
+        P.assert_exact(got, want, prob.name)
+    P.assert_within_bound(got, want, mag, prob.name)
+    # the unsplit entry point gives the same result within the bound (equal
+    # for integer operands)
+    C1 = P.run_mx(prob.A.to(DEV), prob.B.to(DEV), prob.SA.to(DEV), prob.SB.to(DEV)).cpu().numpy()
+    if exact:
+        assert np.array_equal(C1.astype(np.float64), got)
+
+
+@pytest.mark.parametrize("out", ["f32", "bf16", "e4m3"])
+def test_mx_splitk_fused_epilogue(out):
+    M, N, K = 700, 600, 4096
+    prob = inputs.mx_problem(M, N, K, dist="integer", seed=103)
+    g = np.random.default_rng(104)
+    rs = np.exp2(g.integers(-2, 3, size=M)).astype(np.float32)
+    cs = np.exp2(g.integers(-2, 3, size=N)).astype(np.float32)
+    bias = g.integers(-8, 9, size=N).astype(np.float32)
+    P.note(f"mx splitk fused out {out}")
+    got, used, _ = _mx_run(prob, 4, out=out, vecs=(rs, cs, bias))
+    assert used == 4
+    acc, mag = P.oracle_mx(prob.A, prob.B, prob.SA, prob.SB)
+    t, _ = oracle.epilogue(acc, mag, rs, cs, bias)
+    want = oracle.round_bf16(t) if out == "bf16" else oracle.round_e4m3(t) if out == "e4m3" else t
+    P.assert_exact(got, want, prob.name)
+
+
+def test_mx_splitk_unsplit_fallback_and_errors():
+    prob = inputs.mx_problem(1024, 1024, 8192, dist="integer", seed=105)
+    P.note("mx splitk fallback (scales 4 bytes off 16-byte alignment)")
+    ws = torch.full((64,), 12345.0, dtype=torch.float32, device=DEV)
+    got, used, ws = _mx_run(prob, 4, scale_off=4, ws=ws)
+    assert used == 1 and (ws == 12345.0).all().item()
+    want, _ = P.oracle_mx(prob.A, prob.B, prob.SA, prob.SB)
+    P.assert_exact(got, want, prob.name)
+    # a short or misaligned workspace is refused with C untouched
+    M, N, K = prob.M, prob.N, prob.K
+    A, B, SA, SB = (x.to(DEV) for x in (prob.A, prob.B, prob.SA, prob.SB))
+    C = torch.full((M, N), -7.0, dtype=torch.float32, device=DEV)
+    rc, used, nbytes = dg.gemm_mxfp8_splitk_workspace(M, N, K, A.data_ptr(), K, B.data_ptr(), K, SA.data_ptr(),
+                                                      SB.data_ptr(), C.data_ptr(), N, dg.GEMM_OUT_F32, None, None,
+                                                      None, 0)
+    assert used == 8 and nbytes == 8 * M * N * 4
+    w = torch.empty(nbytes // 4, dtype=torch.float32, device=DEV)
+    args = (M, N, K, A.data_ptr(), K, B.data_ptr(), K, SA.data_ptr(), SB.data_ptr(), C.data_ptr(), N,
+            dg.GEMM_OUT_F32, None, None, None, 0)
+    assert dg.gemm_mxfp8_splitk(*args, w.data_ptr(), nbytes - 4, P.stream()) == dg.GEMM_ERR_INVALID_ARG
+    assert dg.gemm_mxfp8_splitk(*args, w.data_ptr() + 4, nbytes - 4, P.stream()) == dg.GEMM_ERR_INVALID_ARG
+    assert dg.gemm_mxfp8_splitk(*args[:-1], -1, w.data_ptr(), nbytes, P.stream()) == dg.GEMM_ERR_INVALID_ARG
+    torch.cuda.synchronize()
+    assert (C == -7.0).all().item()
+
+
+def test_mx_splitk_deterministic():
+    prob = inputs.mx_problem(1000, 777, 4096, dist="normal", seed=106)
+    P.note("mx splitk determinism")
+    a, _, _ = _mx_run(prob, 0)
+    b, _, _ = _mx_run(prob, 0, ws_fill=0.0)
+    assert np.array_equal(a, b)
+
+
+def test_mx_splitk_bench_workload():
+    """The MX split-K workload at full size in the benchmark's launch
+    configuration (the plan: 16 ranges of 2048, ldc = N): whole rows and
+    columns over every tile band against the oracle.  Each range sums 2048
+    block-scaled products in fp32 and 16 partials are added, so the 1e-3
+    bound holds although K = 32768."""
+    prob = inputs.workload("mx1024x1024x32768_splitk", seed=0)
+    M, N, K = prob.M, prob.N, prob.K
+    A, B, SA, SB = (x.to(DEV) for x in (prob.A, prob.B, prob.SA, prob.SB))
+    C = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    rc, used, nbytes = dg.gemm_mxfp8_splitk_workspace(M, N, K, A.data_ptr(), K, B.data_ptr(), K, SA.data_ptr(),
+                                                      SB.data_ptr(), C.data_ptr(), N, dg.GEMM_OUT_F32, None, None,
+                                                      None, 0)
+    assert rc == dg.GEMM_OK and used == 16
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+    P.note("mx splitk workload mx1024x1024x32768_splitk")
+    rc = dg.gemm_mxfp8_splitk(M, N, K, A.data_ptr(), K, B.data_ptr(), K, SA.data_ptr(), SB.data_ptr(), C.data_ptr(),
+                              N, dg.GEMM_OUT_F32, None, None, None, 0, ws.data_ptr(), nbytes, P.stream())
+    assert rc == dg.GEMM_OK
+    torch.cuda.synchronize()
+    P.check_lines_mx(C.cpu().numpy(), prob.A, prob.B, prob.SA, prob.SB, P.band_lines(M, 256, 107),
+                     P.band_lines(N, 256, 108), prob.name)
