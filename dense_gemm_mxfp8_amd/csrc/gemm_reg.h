@@ -53,12 +53,8 @@ namespace regpath {
 
 using namespace fast;
 
-constexpr int RB = 64;            // bytes of K per LDS row (32 bf16)
-constexpr int BK = 32;            // k per k-tile
-constexpr int KS = 2;             // 16-deep MFMA steps per k-tile
-constexpr int OPB = kTile * RB;   // 16 KiB per operand per stage
-constexpr int STAGE = 2 * OPB;
-constexpr int NC = OPB / 16 / kThreads;  // 16-byte chunks of A per thread (4)
+// k per k-tile of the register kernel with RB bytes of K per LDS row
+__host__ __device__ constexpr int bk_of(int rb) { return rb / 2; }
 
 // Descriptor over [p, p + bytes) with its base rounded down to a dword;
 // `shift` receives the byte offset of p from that base.
@@ -70,11 +66,20 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t span_rsrc(const uint8_t* p, in
 // PF: k-tiles held in registers ahead of the stage being filled (1, 2 or 4
 // register sets; k-tile j lives in set j % PF).  BN: tile columns, 256 or
 // 192 (wave tiles 128 x BN/2); the narrower tile lets the host match the
-// tile count to the CU count.
+// tile count to the CU count.  RB: bytes of K per LDS row, 64 (k-tiles of
+// 32, 2 MFMA steps) or 128 (k-tiles of 64, 4 steps: half the barriers and
+// stage hand-offs per MFMA).
 // FUSED: the fused epilogue of gemm_epi.h instead of the plain fp32 store.
-template <int KIND, bool TAIL, int PF = 2, int BN = kTile, bool FUSED = false>
+template <int KIND, bool TAIL, int PF = 2, int BN = kTile, bool FUSED = false, int RB = 64>
 __global__ __launch_bounds__(kThreads, 1) void gemm_reg_kernel(Args a) {
     static_assert(KIND == kNT || KIND == kNN, "bf16 only");
+    static_assert(RB == 64 || RB == 128, "k-tile rows of 64 or 128 bytes");
+    constexpr int BK = bk_of(RB);              // k per k-tile
+    constexpr int KS = BK / 16;                // 16-deep MFMA steps per k-tile
+    constexpr int OPB = kTile * RB;            // bytes per operand per stage
+    constexpr int STAGE = 2 * OPB;
+    constexpr int CPR = RB / 16;               // 16-byte chunks per K-contiguous row
+    constexpr int NC = OPB / 16 / kThreads;    // 16-byte chunks of A per thread
     static_assert(PF == 1 || PF == 2 || PF == 4, "1, 2 or 4 register sets");
     // the K loop is unrolled by U k-tiles so that the stage (k-tile parity)
     // and the register set (k-tile mod PF) of every unrolled k-tile are
@@ -84,7 +89,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_reg_kernel(Args a) {
     constexpr int NBJ = BN / 64;      // 32-column MFMA blocks per wave tile
     constexpr int WTN = BN / 2;       // wave tile columns
     constexpr int CPK = BN / 8;       // row-major B: 16-byte chunks per k-row
-    constexpr int NCB = 4 * BN / kThreads;  // 16-byte chunks of B per thread
+    constexpr int NCB = BN * RB / 16 / kThreads;  // 16-byte chunks of B per thread
     __shared__ __attribute__((aligned(1024))) uint8_t st0[STAGE];
     __shared__ __attribute__((aligned(1024))) uint8_t st1[STAGE];
     __shared__ float evl[FUSED ? 3 * 256 : 1];  // fused epilogue: the tile's scales and biases
@@ -96,14 +101,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_reg_kernel(Args a) {
     const int h = lane >> 5;
     const int l32 = lane & 31;
 
-    // Chunk i of this thread.  K-contiguous operand: row idx / 4, 16-byte
-    // chunk idx % 4 of the row's 64 bytes.  Row-major B: k-row idx / CPK,
+    // Chunk i of this thread.  K-contiguous operand: row idx / CPR, 16-byte
+    // chunk idx % CPR of the row's RB bytes.  Row-major B: k-row idx / CPK,
     // columns 8 (idx % CPK) .. +7 (LDS rows keep the 512-byte pitch).
     int a_g[NC], b_g[NCB], a_l[NC], b_l[NCB];
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
         const int idx = i * kThreads + tid;
-        const int r = idx >> 2, c = idx & 3;
+        const int r = idx / CPR, c = idx % CPR;
         a_g[i] = r * (int)a.lda_b + c * 16;
         a_l[i] = kc_off<RB>(r, c);
     }
@@ -115,7 +120,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_reg_kernel(Args a) {
             b_g[i] = kk * (int)a.ldb_b + cn * 16;
             b_l[i] = OPB + nn_off(kk, cn * 8);
         } else {
-            const int r = idx >> 2, c = idx & 3;
+            const int r = idx / CPR, c = idx % CPR;
             b_g[i] = r * (int)a.ldb_b + c * 16;
             b_l[i] = OPB + kc_off<RB>(r, c);
         }
@@ -166,16 +171,21 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_reg_kernel(Args a) {
         // 2^31, so the sum cannot wrap).  Selecting the offset rather than a
         // second descriptor keeps the descriptors in scalar registers.
         constexpr int kDead = 0x7fffffff;
-        auto load_full = [&](auto qidx, int kt, bool live) {
+        // chunks W0 .. W1-1 of k-tile kt into register set q (chunk w < NC:
+        // A's chunk w, else B's chunk w - NC)
+        auto load_range = [&](auto qidx, auto w0c, auto w1c, int kt, bool live) {
             constexpr int q = decltype(qidx)::value;
             const int ka = live ? sa + kt * RB : kDead;
             const int kb = live ? sb + ((KIND == kNN) ? kt * BK * (int)a.ldb_b : kt * RB) : kDead;
-#pragma unroll
-            for (int i = 0; i < NC; ++i) ra_reg[q][i] = __builtin_amdgcn_raw_buffer_load_b128(ra, a_g[i], ka, 0);
-#pragma unroll
-            for (int i = 0; i < NCB; ++i) rb_reg[q][i] = __builtin_amdgcn_raw_buffer_load_b128(rb, b_g[i], kb, 0);
+            static_for<decltype(w0c)::value, decltype(w1c)::value>([&](auto wc) {
+                constexpr int w = decltype(wc)::value;
+                if constexpr (w < NC) ra_reg[q][w] = __builtin_amdgcn_raw_buffer_load_b128(ra, a_g[w], ka, 0);
+                else rb_reg[q][w - NC] = __builtin_amdgcn_raw_buffer_load_b128(rb, b_g[w - NC], kb, 0);
+            });
         };
-        // Partial k-tile KT, holding kvalid (1 .. 32) k.  Chunks lying wholly
+        using W0 = std::integral_constant<int, 0>;
+        using WN = std::integral_constant<int, NC + NCB>;
+        // Partial k-tile KT, holding kvalid (1 .. BK) k.  Chunks lying wholly
         // inside the data are 16-byte loads; the chunk that straddles the end
         // of a row (K-contiguous operands) or of the last columns (row-major
         // B) is read as 2-byte elements, so no load reaches past the
@@ -198,7 +208,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_reg_kernel(Args a) {
 #pragma unroll
             for (int i = 0; i < NC; ++i) {
                 const int idx = i * kThreads + tid;
-                const int c8 = 8 * (idx & 3);
+                const int c8 = 8 * (idx % CPR);
                 i32x4 va = {0, 0, 0, 0};
                 if (c8 + 8 <= kvalid)
                     va = __builtin_amdgcn_raw_buffer_load_b128(ra, a_g[i], sa + KT * RB, 0);
@@ -220,7 +230,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_reg_kernel(Args a) {
                             vb = gather(rb, b_g[i], soff, rows_b - n8);
                     }
                 } else {
-                    const int c8 = 8 * (idx & 3);
+                    const int c8 = 8 * (idx % CPR);
                     if (c8 + 8 <= kvalid)
                         vb = __builtin_amdgcn_raw_buffer_load_b128(rb, b_g[i], sb + KT * RB, 0);
                     else if (c8 < kvalid)
@@ -231,15 +241,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_reg_kernel(Args a) {
         };
         // k-tile kt into register set q: zero (no traffic) past the full
         // k-tiles
-        auto load = [&](auto qidx, int kt) { load_full(qidx, kt, kt < KT); };
-        auto store = [&](auto qidx, auto sidx) {
+        auto load = [&](auto qidx, int kt) { load_range(qidx, W0{}, WN{}, kt, kt < KT); };
+        // chunks W0 .. W1-1 of register set q into stage s
+        auto store_range = [&](auto qidx, auto sidx, auto w0c, auto w1c) {
             constexpr int q = decltype(qidx)::value;
             uint8_t FAST_LDS* base = decltype(sidx)::value ? (uint8_t FAST_LDS*)st1 : (uint8_t FAST_LDS*)st0;
-#pragma unroll
-            for (int i = 0; i < NC; ++i) *(i32x4 FAST_LDS*)(base + a_l[i]) = ra_reg[q][i];
-#pragma unroll
-            for (int i = 0; i < NCB; ++i) *(i32x4 FAST_LDS*)(base + b_l[i]) = rb_reg[q][i];
+            static_for<decltype(w0c)::value, decltype(w1c)::value>([&](auto wc) {
+                constexpr int w = decltype(wc)::value;
+                if constexpr (w < NC) *(i32x4 FAST_LDS*)(base + a_l[w]) = ra_reg[q][w];
+                else *(i32x4 FAST_LDS*)(base + b_l[w - NC]) = rb_reg[q][w - NC];
+            });
         };
+        auto store = [&](auto qidx, auto sidx) { store_range(qidx, sidx, W0{}, WN{}); };
         auto read_frags = [&](auto sidx, int ks, bf16x8* fa, bf16x8* fb) {
             const uint8_t FAST_LDS* base =
                 decltype(sidx)::value ? (const uint8_t FAST_LDS*)st1 : (const uint8_t FAST_LDS*)st0;
@@ -273,22 +286,25 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_reg_kernel(Args a) {
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
         };
         // Instruction order of a k-step (sched_group_barrier): MFMA slot m is
-        // followed by the memory instructions given it.  Step 0: the NR
-        // fragment reads of step 1 over the first half of the MFMAs, then the
-        // NW stores into the next stage, then the NW loads of a later k-tile
-        // (they reuse the stored registers).  Step 1: the NR reads of the
-        // next k-tile's step 0 over the first half of the MFMAs, so that they
-        // have landed when that step's MFMAs start.
+        // followed by the memory instructions given it.  Steps 0 .. KS-2:
+        // the NR fragment reads of the next step over the first half of the
+        // MFMAs, then the step's share NWS of the stores into the next stage,
+        // then as many loads of a later k-tile (they reuse the stored
+        // registers).  Step KS-1: the NR reads of the next k-tile's step 0
+        // over the first half of the MFMAs, so that they have landed when
+        // that step's MFMAs start.
         constexpr int NMF = kBlocks * NBJ;
         constexpr int NR = (KIND == kNN) ? kBlocks + 2 * NBJ : kBlocks + NBJ;
         constexpr int NW = NC + NCB;
-        auto interleave0 = [&]() {
+        auto interleave0 = [&](auto nwc) {
+            constexpr int NWS = decltype(nwc)::value;
             static_for<0, NMF>([&](auto mc) {
                 constexpr int m = decltype(mc)::value;
                 constexpr int H = NMF / 2;
                 // reads spread over slots 0 .. H-1, stores and loads over H .. NMF-1
                 constexpr int r0 = m < H ? m * NR / H : NR, r1 = m < H ? (m + 1) * NR / H : NR;
-                constexpr int w0 = m < H ? 0 : (m - H) * NW / (NMF - H), w1 = m < H ? 0 : (m + 1 - H) * NW / (NMF - H);
+                constexpr int w0 = m < H ? 0 : (m - H) * NWS / (NMF - H);
+                constexpr int w1 = m < H ? 0 : (m + 1 - H) * NWS / (NMF - H);
                 __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
                 if constexpr (r1 > r0) __builtin_amdgcn_sched_group_barrier(kSgDsRead, r1 - r0, 0);
                 if constexpr (w1 > w0) {
@@ -327,23 +343,35 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_reg_kernel(Args a) {
             constexpr int q = decltype(qidx)::value;  // kt % U
             using sidx = std::integral_constant<int, q % 2>;
             constexpr int sn = (q % 2) ^ 1;
-            // k-step 0: stage of k-tile kt+1 <- registers, loads of
-            // kt+1+PF, fragments of step 1.  k-tile kt+1 sits in set
-            // (kt+1) % PF; kt+1+PF goes there next.
+            // k-steps 0 .. KS-2: stage of k-tile kt+1 <- registers and loads
+            // of kt+1+PF, a share per step, fragments of the next step.
+            // k-tile kt+1 sits in set (kt+1) % PF; kt+1+PF goes there next.
             using Q = std::integral_constant<int, (q + 1) % PF>;
-            read_frags(sidx{}, 1, F1a, F1b);
-            store(Q{}, std::integral_constant<int, sn>{});
-            load(Q{}, kt + 1 + PF);
-            mfma(F0a, F0b);
-            interleave0();
-            __builtin_amdgcn_sched_barrier(0);
-            // k-step 1
-            wait_lgkm0();
-            barrier();
-            read_frags(std::integral_constant<int, sn>{}, 0, F0a, F0b);
-            mfma(F1a, F1b);
-            interleave1();
-            __builtin_amdgcn_sched_barrier(0);
+            static_for<0, KS>([&](auto ksc) {
+                constexpr int ks = decltype(ksc)::value;
+                bf16x8* ca = (ks % 2) ? F1a : F0a;
+                bf16x8* cb = (ks % 2) ? F1b : F0b;
+                bf16x8* na = (ks % 2) ? F0a : F1a;
+                bf16x8* nb = (ks % 2) ? F0b : F1b;
+                if constexpr (ks + 1 < KS) {
+                    using w0 = std::integral_constant<int, ks * NW / (KS - 1)>;
+                    using w1 = std::integral_constant<int, (ks + 1) * NW / (KS - 1)>;
+                    read_frags(sidx{}, ks + 1, na, nb);
+                    store_range(Q{}, std::integral_constant<int, sn>{}, w0{}, w1{});
+                    load_range(Q{}, w0{}, w1{}, kt + 1 + PF, kt + 1 + PF < KT);
+                    mfma(ca, cb);
+                    interleave0(std::integral_constant<int, w1::value - w0::value>{});
+                    __builtin_amdgcn_sched_barrier(0);
+                } else {
+                    // last k-step: stage sn complete, stage s fully read
+                    wait_lgkm0();
+                    barrier();
+                    read_frags(std::integral_constant<int, sn>{}, 0, na, nb);
+                    mfma(ca, cb);
+                    interleave1();
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            });
         };
         for (int kt0 = 0; kt0 < KTM; kt0 += U) {
             static_for<0, U>([&](auto qc) { body(qc, kt0 + decltype(qc)::value); });

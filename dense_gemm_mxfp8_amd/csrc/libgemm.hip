@@ -833,16 +833,17 @@ bool reg_ok(bool nt, int64_t K, int64_t lda, int64_t ldb) {
     return K * ldb * 2 + 4 < lim;
 }
 
-template <int PF, int BN, bool FUSED = false>
+template <int PF, int BN, bool FUSED = false, int RB = 64>
 int launch_reg_pf(bool nt, fast::Args a, int cus, hipStream_t stream) {
+    constexpr int BK = regpath::bk_of(RB);
     a.tiles_m = (a.M + fast::kTile - 1) / fast::kTile;
     a.tiles_n = (a.N + BN - 1) / BN;
     a.num_tiles = a.tiles_m * a.tiles_n;
     const int g = env_variant().group;
     const int group_m = g > 0 ? g : 8;
     a.group_m = a.tiles_m < group_m ? a.tiles_m : group_m;
-    a.kt_full = a.K / regpath::BK;
-    a.kt_total = (a.K + regpath::BK - 1) / regpath::BK;
+    a.kt_full = a.K / BK;
+    a.kt_total = (a.K + BK - 1) / BK;
     // row-major B with N % 8 != 0: the last k-row ends inside a 16-byte
     // chunk, which only the tail path reads safely
     if (!nt && a.N % 8 != 0 && a.kt_full == a.kt_total) a.kt_full -= 1;
@@ -853,14 +854,14 @@ int launch_reg_pf(bool nt, fast::Args a, int cus, hipStream_t stream) {
     const dim3 blk(fast::kThreads);
     if (nt) {
         if (tail)
-            hipLaunchKernelGGL((regpath::gemm_reg_kernel<fast::kNT, true, PF, BN, FUSED>), dim3(grid), blk, 0, stream, a);
+            hipLaunchKernelGGL((regpath::gemm_reg_kernel<fast::kNT, true, PF, BN, FUSED, RB>), dim3(grid), blk, 0, stream, a);
         else
-            hipLaunchKernelGGL((regpath::gemm_reg_kernel<fast::kNT, false, PF, BN, FUSED>), dim3(grid), blk, 0, stream, a);
+            hipLaunchKernelGGL((regpath::gemm_reg_kernel<fast::kNT, false, PF, BN, FUSED, RB>), dim3(grid), blk, 0, stream, a);
     } else {
         if (tail)
-            hipLaunchKernelGGL((regpath::gemm_reg_kernel<fast::kNN, true, PF, BN, FUSED>), dim3(grid), blk, 0, stream, a);
+            hipLaunchKernelGGL((regpath::gemm_reg_kernel<fast::kNN, true, PF, BN, FUSED, RB>), dim3(grid), blk, 0, stream, a);
         else
-            hipLaunchKernelGGL((regpath::gemm_reg_kernel<fast::kNN, false, PF, BN, FUSED>), dim3(grid), blk, 0, stream, a);
+            hipLaunchKernelGGL((regpath::gemm_reg_kernel<fast::kNN, false, PF, BN, FUSED, RB>), dim3(grid), blk, 0, stream, a);
     }
     return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
 }
@@ -878,11 +879,17 @@ int reg_tile_n(int64_t M, int64_t N, int cus) {
     return cost(192) < cost(256) ? 192 : 256;
 }
 
-// Register sets of prefetch of the register kernel.
+// Register sets of prefetch of the register kernel, and its k-tile row
+// bytes for the plain product: 128 (k-tiles of 64, half the barriers of 64)
+// measured 117 against 130 us at 4096^3 with odd leading dimensions and
+// 64.0-65.0 against 64.8-67.9 us on 4001 x 3003 x 2050 (MI355X, same box).
+// The fused instances keep 64-byte rows, whose epilogue fits the registers.
 constexpr int kRegPF = 1;
+constexpr int kRegRB = 128;
 
-// Measurement builds: LIBGEMM_REGPF=1|2|4 (register sets of prefetch) and
-// LIBGEMM_REG_BN=192|256 (tile columns) select other compiled instances.
+// Measurement builds: LIBGEMM_REGPF=1|2|4 (register sets of prefetch),
+// LIBGEMM_REG_BN=192|256 (tile columns) and LIBGEMM_REG_RB=64 (k-tile rows)
+// select other compiled instances.
 int launch_reg(bool nt, const fast::Args& a, int cus, hipStream_t stream) {
     int bn = reg_tile_n(a.M, a.N, cus);
 #ifdef LIBGEMM_MEASURE
@@ -895,18 +902,26 @@ int launch_reg(bool nt, const fast::Args& a, int cus, hipStream_t stream) {
         return e ? atoi(e) : 0;
     }();
     if (bn_env == 192 || bn_env == 256) bn = bn_env;
-    if (!a.epi.on && (pf == 1 || pf == 2 || pf == 4) && pf != kRegPF) {
-        if (pf == 1) return bn == 192 ? launch_reg_pf<1, 192>(nt, a, cus, stream) : launch_reg_pf<1, 256>(nt, a, cus, stream);
+    // LIBGEMM_REG_RB=64: k-tiles of 32 (plain product), with LIBGEMM_REGPF
+    static int rb_env = [] {
+        const char* e = getenv("LIBGEMM_REG_RB");
+        return e ? atoi(e) : 0;
+    }();
+    if (!a.epi.on && rb_env == 64) {
         if (pf == 2) return bn == 192 ? launch_reg_pf<2, 192>(nt, a, cus, stream) : launch_reg_pf<2, 256>(nt, a, cus, stream);
-        return bn == 192 ? launch_reg_pf<4, 192>(nt, a, cus, stream) : launch_reg_pf<4, 256>(nt, a, cus, stream);
+        if (pf == 4) return bn == 192 ? launch_reg_pf<4, 192>(nt, a, cus, stream) : launch_reg_pf<4, 256>(nt, a, cus, stream);
+        return bn == 192 ? launch_reg_pf<1, 192>(nt, a, cus, stream) : launch_reg_pf<1, 256>(nt, a, cus, stream);
     }
+    if (!a.epi.on && pf == 2)
+        return bn == 192 ? launch_reg_pf<2, 192, false, kRegRB>(nt, a, cus, stream)
+                         : launch_reg_pf<2, 256, false, kRegRB>(nt, a, cus, stream);
 #endif
     if (a.epi.on) {
         if (bn == 192) return launch_reg_pf<kRegPF, 192, true>(nt, a, cus, stream);
         return launch_reg_pf<kRegPF, 256, true>(nt, a, cus, stream);
     }
-    if (bn == 192) return launch_reg_pf<kRegPF, 192>(nt, a, cus, stream);
-    return launch_reg_pf<kRegPF, 256>(nt, a, cus, stream);
+    if (bn == 192) return launch_reg_pf<kRegPF, 192, false, kRegRB>(nt, a, cus, stream);
+    return launch_reg_pf<kRegPF, 256, false, kRegRB>(nt, a, cus, stream);
 }
 
 // ---------------------------------------------------------------------------
