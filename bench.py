@@ -54,6 +54,9 @@ def parse():
                          "leave their idle state (reported as settle_s)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain device copy of COPY_BYTES (for scaling HBM counters)")
+    ap.add_argument("--measure-build", action="store_true",
+                    help="load libgemm_measure.so (built by `python -m dense_gemm_mxfp8_amd.build "
+                         "--measure`), whose LIBGEMM_* variant switches are live")
     return ap.parse_args()
 
 
@@ -455,6 +458,10 @@ def main():
     if args.copy_calibration:
         copy_calibration(args.steps)
         return
+    if args.measure_build:
+        import dense_gemm_mxfp8_amd as dg
+        from dense_gemm_mxfp8_amd.build import MEASURE_LIBRARY
+        dg.LIBRARY = MEASURE_LIBRARY
     names = [args.workload]
     if args.all:
         from dense_gemm_mxfp8_amd.inputs import WORKLOADS
@@ -472,7 +479,11 @@ def main():
             else:
                 print(f"[bench] oracle on {args.cpu_rows} rows", file=sys.stderr, flush=True)
                 cpu = cpu_baseline(prob, args.cpu_rows)
-        print(json.dumps(line(res, args.steps, args.warmup, cpu, headline=(name == HEADLINE))), flush=True)
+        out = line(res, args.steps, args.warmup, cpu, headline=(name == HEADLINE))
+        if args.measure_build:
+            out["config"]["library"] = "measure build: " + " ".join(
+                f"{k}={v}" for k, v in sorted(os.environ.items()) if k.startswith("LIBGEMM_"))
+        print(json.dumps(out), flush=True)
         del prob
         torch.cuda.empty_cache()
 

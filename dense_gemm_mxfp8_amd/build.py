@@ -5,6 +5,12 @@ the attention kernel are separate translation units), then the objects are
 linked into one shared library.  ``build()`` always compiles every source;
 ``build(only=[...])`` recompiles just the named sources and relinks with the
 existing objects of the others.
+
+``build(measure=True)`` (``python -m dense_gemm_mxfp8_amd.build --measure``)
+makes a second library, ``libgemm_measure.so``, compiled with
+``-DLIBGEMM_MEASURE``: in it the ``LIBGEMM_*`` environment switches that force
+a kernel variant are live (the product library has none).  ``bench.py
+--measure-build`` loads it; nothing else does.
 """
 from __future__ import annotations
 
@@ -16,6 +22,7 @@ ROOT = os.path.dirname(PKG)
 SOURCES = [os.path.join(PKG, "csrc", "libgemm.hip"), os.path.join(PKG, "csrc", "attention.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(PKG, "libgemm.so")
+MEASURE_LIBRARY = os.path.join(PKG, "libgemm_measure.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
 HIPCC_FLAGS = [
@@ -33,25 +40,29 @@ def _run(cmd, verbose):
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{res.stderr}")
 
 
-def _object(src: str) -> str:
-    return os.path.join(BUILD_DIR, os.path.splitext(os.path.basename(src))[0] + ".o")
+def _object(src: str, measure: bool = False) -> str:
+    d = os.path.join(BUILD_DIR, "measure") if measure else BUILD_DIR
+    return os.path.join(d, os.path.splitext(os.path.basename(src))[0] + ".o")
 
 
-def build(verbose: bool = False, only=None) -> str:
+def build(verbose: bool = False, only=None, measure: bool = False) -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    os.makedirs(BUILD_DIR, exist_ok=True)
+    os.makedirs(os.path.dirname(_object(SOURCES[0], measure)), exist_ok=True)
+    defines = ["-DLIBGEMM_MEASURE"] if measure else []
     todo = SOURCES if only is None else [s for s in SOURCES if os.path.basename(s) in only]
     for src in todo:
-        obj = _object(src)
-        _run([hipcc, *HIPCC_FLAGS, f"-I{INCLUDE}", "-c", src, "-o", obj + ".tmp"], verbose)
+        obj = _object(src, measure)
+        _run([hipcc, *HIPCC_FLAGS, *defines, f"-I{INCLUDE}", "-c", src, "-o", obj + ".tmp"], verbose)
         os.replace(obj + ".tmp", obj)
-    tmp = LIBRARY + ".tmp"
-    _run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", *[_object(s) for s in SOURCES], "-o", tmp],
+    out = MEASURE_LIBRARY if measure else LIBRARY
+    tmp = out + ".tmp"
+    _run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", *[_object(s, measure) for s in SOURCES], "-o", tmp],
          verbose)
-    os.replace(tmp, LIBRARY)
-    return LIBRARY
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
     import sys
-    print(build(verbose=True, only=sys.argv[1:] or None))
+    args = [a for a in sys.argv[1:] if a != "--measure"]
+    print(build(verbose=True, only=args or None, measure="--measure" in sys.argv[1:]))
