@@ -79,9 +79,12 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_small_m_nn(Args a) {
     constexpr int RPI = 64 / LPR;              // B rows per load instruction
     constexpr int NL = kStepK / RPI;           // B loads per lane per step
     // per wave: one 32-row B buffer; after the loop the same LDS holds the
-    // partial sums: waves x MB blocks x 16 rows x COLS fp32
+    // partial sums: waves x MB blocks x 16 rows x (COLS + 4) fp32 (the 4
+    // padding floats put the four 16-lane groups of a store on different
+    // banks)
     constexpr int kBufBytes = kStepK * kCols * 2;
-    constexpr int kRed = kWaves * MB * 16 * kCols * 4;
+    constexpr int kRedLd = kCols + 4;
+    constexpr int kRed = kWaves * MB * 16 * kRedLd * 4;
     constexpr int kLds = (kWaves * kBufBytes > kRed) ? kWaves * kBufBytes : kRed;
     __shared__ __attribute__((aligned(1024))) uint8_t lds[kLds];
 
@@ -130,10 +133,23 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_small_m_nn(Args a) {
     const int a_voff = am * (int)a.lda_b + 16 * ag;
 
     uint8_t SMALL_LDS* buf = (uint8_t SMALL_LDS*)lds + wave * kBufBytes;
+    // Bank spread of the buffer: the 32-byte segment s of k-row r is stored
+    // at segment s ^ seg_xor(r).  A transposed read serves 16 lanes from k-rows
+    // 8 g + 0..3 (g = lane / 16) and 32 lanes from two such quartets; with
+    // 256-byte rows (128 columns) all rows start on bank 0, so without the
+    // XOR the eight rows of 32 lanes would hit the same eight banks.
+    auto seg_xor = [](int r) {
+        if constexpr (kCols == 128) return (r & 3) | ((r >> 1) & 4);
+        else if constexpr (kCols == 64) return ((r >> 1) & 1) | ((r >> 2) & 2);
+        else return (r >> 3) & 1;
+    };
     // transposed reads: lane p of each 16-lane group addresses k-row
-    // (p / 4) of its quarter and 4 columns starting at 4 (p % 4)
+    // (p / 4) of its quarter (+ 4 for the second read) and 4 columns starting
+    // at 4 (p % 4) of 16-column block c, i.e. byte 8 (p % 4) of segment c
     const int tp = lane & 15, tg = lane >> 4;
-    const int tr_off = (8 * tg + (tp >> 2)) * (kCols * 2) + 4 * (tp & 3) * 2;
+    const int tr_row = 8 * tg + (tp >> 2);
+    const int tr_lo = tr_row * (kCols * 2) + 32 * seg_xor(tr_row) + 8 * (tp & 3);
+    const int tr_hi = (tr_row + 4) * (kCols * 2) + 32 * seg_xor(tr_row + 4) + 8 * (tp & 3);
 
     f32x4 acc[MB][CB];
 #pragma unroll
@@ -169,10 +185,13 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_small_m_nn(Args a) {
         for (int p = 0; p < NP; ++p) {
             const int st = s0 + p;
             issue((p + NP - 1) % NP, st + NP - 1);
-            // this step's B rows into the wave's buffer
+            // this step's B rows into the wave's buffer (16-byte chunk q of
+            // row r at chunk q ^ 2 seg_xor(r))
 #pragma unroll
-            for (int h = 0; h < NL; ++h)
-                *(i32x4 SMALL_LDS*)(buf + (h * RPI + lane / LPR) * (kCols * 2) + (lane % LPR) * 16) = rB[p][h];
+            for (int h = 0; h < NL; ++h) {
+                const int r = h * RPI + lane / LPR;
+                *(i32x4 SMALL_LDS*)(buf + r * (kCols * 2) + ((lane % LPR) ^ (2 * seg_xor(r))) * 16) = rB[p][h];
+            }
             // A past K inside a valid row must not reach the sum
             const int kfirst = kstep(st) + 8 * ag;
             if (kfirst + 8 > K) {
@@ -193,9 +212,10 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_small_m_nn(Args a) {
             bf16x8 fb[CB];
 #pragma unroll
             for (int c = 0; c < CB; ++c) {
-                const uint8_t SMALL_LDS* q = buf + tr_off + c * 32;
-                bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((bf16x4 SMALL_LDS*)q);
-                bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((bf16x4 SMALL_LDS*)(q + 4 * kCols * 2));
+                // segment c of the row sits at c ^ seg_xor: XOR 32 c into the
+                // lane's offset (its bits 5.. hold seg_xor, bits 0..4 < 32)
+                bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((bf16x4 SMALL_LDS*)(buf + (tr_lo ^ (32 * c))));
+                bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((bf16x4 SMALL_LDS*)(buf + (tr_hi ^ (32 * c))));
                 fb[c] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
             }
 #pragma unroll
@@ -220,7 +240,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_small_m_nn(Args a) {
             for (int r = 0; r < 4; ++r) {
                 const int row = 16 * b + 4 * (lane >> 4) + r;
                 const int col = 16 * c + (lane & 15);
-                red[(wave * MB * 16 + row) * kCols + col] = acc[b][c][r];
+                red[(wave * MB * 16 + row) * kRedLd + col] = acc[b][c][r];
             }
     __syncthreads();
     // Sum over waves in wave order and store.
@@ -228,7 +248,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_small_m_nn(Args a) {
         const int row = idx / kCols, col = idx % kCols;
         float s = 0.f;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) s += red[(w * MB * 16 + row) * kCols + col];
+        for (int w = 0; w < kWaves; ++w) s += red[(w * MB * 16 + row) * kRedLd + col];
         if (row < a.M && n0 + col < a.N) epi::store(C, a.ldc, a.epi, row, n0 + col, s);
     }
 }
