@@ -448,8 +448,11 @@ __device__ __forceinline__ void interleave_step() {
 // DYN: tiles after the first are taken from per-XCD atomic counters
 // (Args::tile_ctr, next_tile) instead of the static strided walk; the grid
 // must be a multiple of 8.
+// LA: k-steps between a fragment read and the MFMAs that use it (1 or 2;
+// 2 keeps four fragment sets in registers and moves the closing wait and
+// barrier of each k-tile one k-step earlier: bf16, two stages).
 template <int KIND, int RB, int S, bool TAIL, int SG = 1, int E = 0, int D = 0, int NW = 4, bool FUSED = false,
-          bool SPLIT = false, bool DYN = false>
+          bool SPLIT = false, bool DYN = false, int LA = 1>
 __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(Args a) {
     static_assert(NW == 4 || (NW == 8 && KIND != kMX), "8 waves: bf16 only");
     static_assert(!SPLIT || (!FUSED && NW == 4), "split-K: plain fp32 partial stores, 4 waves");
@@ -477,6 +480,11 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(Args a) {
     // odd step count per k-tile the buffer parity follows the k-tile parity,
     // which the S-fold unrolled loop keeps static only for even S.
     static_assert(KS % 2 == 0 || S % 2 == 0, "odd k-steps per k-tile need an even stage count");
+    static_assert(LA == 1 || (LA == 2 && KIND != kMX && S == 2 && KS >= 3), "fragment lookahead 2: bf16, 2 stages");
+    // fragment sets in registers, and the k-step of each k-tile that opens
+    // with the closing wait and barrier (its reads are the next stage's)
+    constexpr int R = 2 * LA;
+    constexpr int BS = KS - LA;
     static_assert(KIND != kMX || SPR == 2 || SPR == 4, "MX k-tile of 64 or 128 codes");
     static_assert(S >= 2 && S * STAGE <= 160 * 1024, "LDS budget");
     // DMA instructions per wave per k-tile: both operands, plus (MX) one
@@ -485,6 +493,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(Args a) {
     // the main loop is unrolled by U k-tiles so that the stage and the scale
     // ring slot of every unrolled k-tile are compile-time constants
     constexpr int U = SG > 1 ? 2 * SG : S;
+    static_assert((U * KS) % R == 0, "fragment sets: static over the unrolled loop");
     // The DMA of k-tile kt + S - 1 is issued while k-tile kt is multiplied,
     // DPS instructions per k-step.  With S >= 3 it is spread over every
     // k-step (the part issued after the closing wait is simply younger than
@@ -802,14 +811,20 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(Args a) {
              ...);
         }(std::make_integer_sequence<int, S - 1>{});
         ring_dma(std::integral_constant<int, 0>{}, 0, 0 < KT);
-        // early part of k-tile 1 (two stages)
+        // early part of k-tile 1 (two stages), and with LA = 2 also the
+        // part a loop iteration issues after its barrier (k-step BS + 1)
+        constexpr int EP = LA == 2 ? (E + DPS < L ? E + DPS : L) : E;
 #pragma unroll
-        for (int d = 0; d < E; ++d) dma(std::integral_constant<int, 1>{}, d, 1, 1 < KT);
-        wait_vm<((SG > 1) ? 0 : (S - 2) * L) + E>();
+        for (int d = 0; d < EP; ++d) dma(std::integral_constant<int, 1>{}, d, 1, 1 < KT);
+        wait_vm<((SG > 1) ? 0 : (S - 2) * L) + EP>();
         barrier();
 
-        Frag F0a[kBlocks], F0b[NBJ], F1a[kBlocks], F1b[NBJ];
-        read_frags(std::integral_constant<int, 0>{}, 0, F0a, F0b);
+        // fragment set f holds the fragments of global k-step f mod R
+        Frag Fa[R][kBlocks], Fb[R][NBJ];
+        static_for<0, LA>([&](auto tc) {
+            constexpr int t = decltype(tc)::value;
+            read_frags(std::integral_constant<int, 0>{}, t, Fa[t], Fb[t]);
+        });
         read_scales(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
 
         // One k-tile held in stage s; meanwhile the DMA of k-tile kt + S - 1
@@ -825,15 +840,21 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(Args a) {
             int scn[2 * kBlocks];
             static_for<0, KS>([&](auto ksc) {
                 constexpr int ks = decltype(ksc)::value;
-                constexpr int gp = (s * KS + ks) & 1;  // parity of the global k-step
-                Frag* ca = gp ? F1a : F0a;
-                Frag* cb = gp ? F1b : F0b;
-                Frag* na = gp ? F0a : F1a;
-                Frag* nb = gp ? F0b : F1b;
-                constexpr int d0 = E + ks * DPS < L ? E + ks * DPS : L;
-                constexpr int d1 = E + (ks + 1) * DPS < L ? E + (ks + 1) * DPS : L;
-                if constexpr (ks + 1 < KS) {
-                    read_frags(sidx, ks + 1, na, nb);
+                constexpr int gk = q * KS + ks;  // global k-step, modulo the unrolled loop
+                Frag* ca = Fa[gk % R];
+                Frag* cb = Fb[gk % R];
+                Frag* na = Fa[(gk + LA) % R];
+                Frag* nb = Fb[(gk + LA) % R];
+                // The DMA of a k-tile after its E early instructions is spread
+                // over the KS - 1 k-steps that follow the barrier issuing
+                // them, DPS instructions per step: slot j is the j-th of them.
+                // Steps before the barrier carry k-tile kd's, steps after it
+                // (LA = 2) k-tile kt + 2's into the stage just freed.
+                constexpr int j = ks < BS ? KS - 1 - BS + ks : (ks == BS ? KS - 1 : ks - BS - 1);
+                constexpr int d0 = E + j * DPS < L ? E + j * DPS : L;
+                constexpr int d1 = E + (j + 1) * DPS < L ? E + (j + 1) * DPS : L;
+                if constexpr (ks < BS) {
+                    read_frags(sidx, ks + LA, na, nb);
                     if constexpr (KIND == kMX && SG > 1 && ks == 0) {
                         // scales of k-tile kt + 1: its ring slot landed before
                         // the barrier closing the k-tile that requested it
@@ -852,13 +873,14 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(Args a) {
                     interleave_step<NR, d1 - d0 + ((SG > 1 && ks == 0 && q % SG == 0) ? 2 : 0), NMF>();
                     // keep every MFMA of this step ahead of the closing wait
                     __builtin_amdgcn_sched_barrier(0);
-                } else {
-                    // This k-step's fragments are in registers, so stage s
-                    // is fully read; k-tile kt+1 must have landed.
+                } else if constexpr (ks == BS) {
+                    // Every fragment of stage s is in registers or being read,
+                    // so stage s is free once the reads land; k-tile kt+1
+                    // must have landed.
                     wait_lgkm0();
                     wait_vm<VM_WAIT>();
                     barrier();
-                    read_frags(std::integral_constant<int, snext>{}, 0, na, nb);
+                    read_frags(std::integral_constant<int, snext>{}, ks + LA - KS, na, nb);
                     static_for<d0, d1>([&](auto dc) {
                         dma(std::integral_constant<int, sdma>{}, decltype(dc)::value, kd, live);
                     });
@@ -878,6 +900,16 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(Args a) {
                         mfma(ks, ca, cb, sc);
                     }
                     interleave_step<NR, d1 - d0 + E, NMF>();
+                    __builtin_amdgcn_sched_barrier(0);
+                } else {
+                    // after the barrier (LA = 2): the next stage's fragments,
+                    // and the next part of k-tile kt + 2's DMA into stage s
+                    read_frags(std::integral_constant<int, snext>{}, ks + LA - KS, na, nb);
+                    static_for<d0, d1>([&](auto dc) {
+                        dma(sidx, decltype(dc)::value, kt + 2, kt + 2 < KT);
+                    });
+                    mfma(ks, ca, cb, sc);
+                    interleave_step<NR, d1 - d0, NMF>();
                     __builtin_amdgcn_sched_barrier(0);
                 }
             });
@@ -907,8 +939,8 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(Args a) {
             barrier();
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                read_frags(std::integral_constant<int, 0>{}, ks, F0a, F0b);
-                mfma(ks, F0a, F0b, sc);
+                read_frags(std::integral_constant<int, 0>{}, ks, Fa[0], Fb[0]);
+                mfma(ks, Fa[0], Fb[0], sc);
             }
         }
 

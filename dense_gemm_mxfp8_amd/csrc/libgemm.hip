@@ -645,33 +645,35 @@ constexpr int kMaxSplits = 32;
 // and 8192^3, are 128-byte rows x 2 stages for bf16 NT and NN (early 6,
 // spread 2) and for MX (scale ring, early 12).
 struct FastVariant {
-    int rb, stages, group, early, spread, waves;
+    int rb, stages, group, early, spread, waves, lookahead;
 };
 
 // Measurement builds (-DLIBGEMM_MEASURE) read switches from the environment
 // that select other compiled pipelines for A/B timing:
-// LIBGEMM_VARIANT=<rb>x<stages>[e<early>[d<spread>[w<waves>]]] picks the
-// pipeline (and for two stages the early-DMA split); LIBGEMM_GROUP=<n> the
+// LIBGEMM_VARIANT=<rb>x<stages>[e<early>[d<spread>[w<waves>[l<lookahead>]]]]
+// picks the pipeline (for two stages the early-DMA split, and the k-steps
+// between a fragment read and its MFMAs); LIBGEMM_GROUP=<n> the
 // number of tile rows per raster band.  The library as built by default
 // compiles none of those instances and reads no environment variable: every
 // call runs the defaults below.
 FastVariant env_variant() {
 #ifndef LIBGEMM_MEASURE
-    return FastVariant{0, 0, 0, -1, 0, 4};
+    return FastVariant{0, 0, 0, -1, 0, 4, 1};
 #else
     static FastVariant v = [] {
-        FastVariant r{0, 0, 0, -1, 0, 4};
+        FastVariant r{0, 0, 0, -1, 0, 4, 1};
         const char* e = getenv("LIBGEMM_VARIANT");
         if (e) {
-            int rb = 0, st = 0, ea = -1, sp = 0, nw = 4;
-            const int n = sscanf(e, "%dx%de%dd%dw%d", &rb, &st, &ea, &sp, &nw);
+            int rb = 0, st = 0, ea = -1, sp = 0, nw = 4, la = 1;
+            const int n = sscanf(e, "%dx%de%dd%dw%dl%d", &rb, &st, &ea, &sp, &nw, &la);
             if (n >= 2) {
                 r.rb = rb;
                 r.stages = st;
             }
             if (n >= 3) r.early = ea;
             if (n >= 4) r.spread = sp;
-            if (n == 5) r.waves = nw;
+            if (n >= 5) r.waves = nw;
+            if (n == 6) r.lookahead = la;
         }
         const char* g = getenv("LIBGEMM_GROUP");
         if (g) r.group = atoi(g);
@@ -687,7 +689,7 @@ FastVariant env_variant() {
 // on the stream first (falls back to the static walk when the grid is not a
 // multiple of 8).
 template <int KIND, int RB, int S, int SG = 1, int E = 0, int D = 0, int NW = 4, bool FUSED = false,
-          bool SPLIT = false, bool DYN = false>
+          bool SPLIT = false, bool DYN = false, int LA = 1>
 int launch_fast(fast::Args a, int cus, hipStream_t stream, int group_m = 0, int splits = 1) {
     constexpr int BK = RB / (KIND == fast::kMX ? 1 : 2);
     a.tiles_m = (a.M + fast::kTile - 1) / fast::kTile;
@@ -712,19 +714,19 @@ int launch_fast(fast::Args a, int cus, hipStream_t stream, int group_m = 0, int 
         if (a.xcd_remap) {
             hipLaunchKernelGGL(zero_words_kernel, dim3(1), dim3(256), 0, stream, a.tile_ctr, 256);
             if (a.kt_total > a.kt_full)
-                hipLaunchKernelGGL((fast::gemm_fast_kernel<KIND, RB, S, true, SG, E, D, NW, FUSED, false, true>),
+                hipLaunchKernelGGL((fast::gemm_fast_kernel<KIND, RB, S, true, SG, E, D, NW, FUSED, false, true, LA>),
                                    dim3(grid), dim3(64 * NW), 0, stream, a);
             else
-                hipLaunchKernelGGL((fast::gemm_fast_kernel<KIND, RB, S, false, SG, E, D, NW, FUSED, false, true>),
+                hipLaunchKernelGGL((fast::gemm_fast_kernel<KIND, RB, S, false, SG, E, D, NW, FUSED, false, true, LA>),
                                    dim3(grid), dim3(64 * NW), 0, stream, a);
             return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
         }
     }
     if (a.kt_total > a.kt_full) {
-        hipLaunchKernelGGL((fast::gemm_fast_kernel<KIND, RB, S, true, SG, E, D, NW, FUSED, SPLIT>), dim3(grid),
+        hipLaunchKernelGGL((fast::gemm_fast_kernel<KIND, RB, S, true, SG, E, D, NW, FUSED, SPLIT, false, LA>), dim3(grid),
                            dim3(64 * NW), 0, stream, a);
     } else {
-        hipLaunchKernelGGL((fast::gemm_fast_kernel<KIND, RB, S, false, SG, E, D, NW, FUSED, SPLIT>), dim3(grid),
+        hipLaunchKernelGGL((fast::gemm_fast_kernel<KIND, RB, S, false, SG, E, D, NW, FUSED, SPLIT, false, LA>), dim3(grid),
                            dim3(64 * NW), 0, stream, a);
     }
     return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
@@ -804,6 +806,8 @@ int launch_fast_bf16(bool nt, const fast::Args& a, int cus, hipStream_t s) {
         // than 4 waves at 8192^3 on MI355X; kept for measurements
         if (v.waves == 8) return launch_fast<fast::kNT, 128, 2, 1, 4, 2, 8>(a, cus, s, g);
         if (v.early == 0) return launch_fast<fast::kNT, 128, 2>(a, cus, s, g);
+        if (v.lookahead == 2)
+            return launch_fast<fast::kNT, 128, 2, 1, 6, 2, 4, false, false, false, 2>(a, cus, s, g);
 #endif
         // default: 6 DMA instructions of k-tile t+2 right after the barrier
         // of k-tile t, the other 10 over k-steps 0 and 1 of t+1 (MI355X,
@@ -813,6 +817,7 @@ int launch_fast_bf16(bool nt, const fast::Args& a, int cus, hipStream_t s) {
 #ifdef LIBGEMM_MEASURE
     if (v.rb == 64 && v.stages == 4) return launch_fast<fast::kNN, 64, 4>(a, cus, s, g);
     if (v.rb == 128 && v.stages == 2 && v.early == 0) return launch_fast<fast::kNN, 128, 2>(a, cus, s, g);
+    if (v.lookahead == 2) return launch_fast<fast::kNN, 128, 2, 1, 6, 2, 4, false, false, false, 2>(a, cus, s, g);
 #endif
     // default: as NT (MI355X, 4096^3: 108.8 -> 105.5 us against 64 x 4;
     // 8192^3: 801.5 -> 771.2 us)
