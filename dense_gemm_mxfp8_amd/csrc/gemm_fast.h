@@ -55,6 +55,11 @@ constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
 
 enum Kind { kNT = 0, kNN = 1, kMX = 2 };
 
+// Cache policies of the C stores (Args::c_pol) and their buffer-instruction
+// cache-policy bits on gfx950: non-temporal, and device scope (sc1).
+constexpr int kCStoreCached = 0, kCStoreStream = 1, kCStoreDevice = 2;
+constexpr int kAuxStream = 2, kAuxDevice = 16;
+
 struct Args {
     const uint8_t* A;
     const uint8_t* B;
@@ -69,7 +74,7 @@ struct Args {
     int kt_full;   // number of k-tiles lying entirely inside K
     int sld;       // MX scale bytes per row (K / 32)
     int xcd_remap;
-    int c_nt;      // C stores non-temporal (1) or cached (0)
+    int c_pol;     // cache policy of the C stores: kCStoreCached, kCStoreStream or kCStoreDevice
     epi::Params epi;  // fused epilogue (C holds epi.out elements)
     // split-K instances: units 0 .. dp_units-1 are whole tiles 0 .. dp_units-1
     // (stored to C); unit dp_units + u is tile tile0 + u % tiles_per_split of
@@ -384,19 +389,33 @@ __device__ __forceinline__ void epi_stage(float FAST_LDS* ev, const EpiRegs& v, 
 // FUSED: the kernel instance carries the fused epilogue (a.epi.on); plain
 // instances keep the lean store path.  cw / cld (plain only): where output
 // (m0w, n0w) goes and the row pitch there, for a split-K partial (null: C);
-// nt: non-temporal stores allowed (a partial is read back at once).
+// pol: stores to C may take a.c_pol (false: cached, a partial is read back at
+// once).  The policies' cache-policy bits: non-temporal (kAuxStream) for C
+// whose 32-column segments are whole 128-byte lines, device scope
+// (kAuxDevice) where segments share lines, cached otherwise.
 template <int NBJ = kBlocks, bool FUSED = false>
 __device__ __forceinline__ void store_c(const Args& a, const f32x16 (&acc)[kBlocks][NBJ], int m0w, int n0w, int h,
                                         int l32, const float FAST_LDS* ev = nullptr, int evr = 0, int evc = 0,
-                                        float* cw = nullptr, int cld = 0, bool nt = true) {
+                                        float* cw = nullptr, int cld = 0, bool pol = true) {
     if constexpr (FUSED) {
-        if (a.epi.out == epi::kBF16) store_c_fused<0, NBJ, epi::kBF16>(a, acc, m0w, n0w, h, l32, ev, evr, evc);
-        else if (a.epi.out == epi::kE4M3) store_c_fused<0, NBJ, epi::kE4M3>(a, acc, m0w, n0w, h, l32, ev, evr, evc);
-        else if (a.c_nt) store_c_fused<2, NBJ, epi::kF32>(a, acc, m0w, n0w, h, l32, ev, evr, evc);
-        else store_c_fused<0, NBJ, epi::kF32>(a, acc, m0w, n0w, h, l32, ev, evr, evc);
+        const bool dev = a.c_pol == kCStoreDevice;
+        if (a.epi.out == epi::kBF16) {
+            if (dev) store_c_fused<kAuxDevice, NBJ, epi::kBF16>(a, acc, m0w, n0w, h, l32, ev, evr, evc);
+            else store_c_fused<0, NBJ, epi::kBF16>(a, acc, m0w, n0w, h, l32, ev, evr, evc);
+        } else if (a.epi.out == epi::kE4M3) {
+            if (dev) store_c_fused<kAuxDevice, NBJ, epi::kE4M3>(a, acc, m0w, n0w, h, l32, ev, evr, evc);
+            else store_c_fused<0, NBJ, epi::kE4M3>(a, acc, m0w, n0w, h, l32, ev, evr, evc);
+        } else if (a.c_pol == kCStoreStream) {
+            store_c_fused<kAuxStream, NBJ, epi::kF32>(a, acc, m0w, n0w, h, l32, ev, evr, evc);
+        } else if (dev) {
+            store_c_fused<kAuxDevice, NBJ, epi::kF32>(a, acc, m0w, n0w, h, l32, ev, evr, evc);
+        } else {
+            store_c_fused<0, NBJ, epi::kF32>(a, acc, m0w, n0w, h, l32, ev, evr, evc);
+        }
     } else {
         if (cw != nullptr) store_c_aux<0, NBJ, true>(a, acc, m0w, n0w, h, l32, cw, cld);
-        else if (a.c_nt && nt) store_c_aux<2, NBJ>(a, acc, m0w, n0w, h, l32);
+        else if (pol && a.c_pol == kCStoreStream) store_c_aux<kAuxStream, NBJ>(a, acc, m0w, n0w, h, l32);
+        else if (pol && a.c_pol == kCStoreDevice) store_c_aux<kAuxDevice, NBJ>(a, acc, m0w, n0w, h, l32);
         else store_c_aux<0, NBJ>(a, acc, m0w, n0w, h, l32);
     }
 }

@@ -770,22 +770,25 @@ fast::Args make_fast_args(int64_t M, int64_t N, int64_t K, const void* A, int64_
     a.N = (int)N;
     a.K = (int)K;
     // C stores bypass the caches' retention (non-temporal) only when every
-    // 32-column segment a wave stores is a whole 128-byte line; otherwise
-    // each line is written in two parts by two stores, and caching lets L2
-    // merge them instead of sending partial lines to memory (measured on
-    // MI355X: 4001 x 3003 x 2050 with ldc = 3003, 112 -> 92 us).
-    // LIBGEMM_C_NT=0|1 overrides the choice (measurement builds only).
+    // 32-column segment a wave stores is a whole 128-byte line: then C does
+    // not evict the operand panels that L2 and the Infinity Cache serve to
+    // the other tiles (8192^3 on MI355X: 0.759 against 0.814 ms cached).
+    // Otherwise each line is written in two parts by two stores; those go
+    // with device scope, which measured best of the policies there
+    // (4001 x 3003 x 2050 with ldc = 3003, same box: 61.5-62.4 us against
+    // 63.7-65.2 us cached and 85 us non-temporal).
+    // LIBGEMM_C_NT=0|1|2 overrides the choice (measurement builds only).
 #ifdef LIBGEMM_MEASURE
-    static int c_nt_env = [] {
+    static int c_pol_env = [] {
         const char* e = getenv("LIBGEMM_C_NT");
         return e ? atoi(e) : -1;
     }();
 #else
-    constexpr int c_nt_env = -1;
+    constexpr int c_pol_env = -1;
 #endif
     // bf16 or E4M3 output: a 32-column segment is 64 or 32 bytes, part of a line
     const bool lines = e.out == epi::kF32 && ((uintptr_t)C % 128 == 0) && (ldc % 32 == 0);
-    a.c_nt = c_nt_env >= 0 ? c_nt_env : (lines ? 1 : 0);
+    a.c_pol = c_pol_env >= 0 ? c_pol_env : (lines ? fast::kCStoreStream : fast::kCStoreDevice);
     a.epi = e;
     return a;
 }
@@ -1230,7 +1233,7 @@ int splitk_dispatch(bool nt, int64_t M, int64_t N, int64_t K, const void* A, int
     } else {
         fast::Args a = make_fast_args(M, N, K, A, lda, B, ldb, ws, N, 2, kPlain);
         a.kslice = (int)p.kslice;
-        a.c_nt = 0;  // the partial sums are read back at once: keep them cached
+        a.c_pol = fast::kCStoreCached;  // the partial sums are read back at once
         const int g = env_variant().group;
         rc = nt ? launch_fast<fast::kNT, 128, 2, 1, 6, 2, 4, false, true>(a, dev.cus, s, g, p.splits)
                 : launch_fast<fast::kNN, 128, 2, 1, 6, 2, 4, false, true>(a, dev.cus, s, g, p.splits);
@@ -1429,7 +1432,7 @@ int mx_splitk_dispatch(int64_t M, int64_t N, int64_t K, const void* A, int64_t l
     f.SB = SB;
     f.sld = (int)(K / 32);
     f.kslice = (int)p.kslice;
-    f.c_nt = 0;  // the partial sums are read back at once: keep them cached
+    f.c_pol = fast::kCStoreCached;  // the partial sums are read back at once
     rc = launch_fast<fast::kMX, 128, 2, 4, 12, 0, 4, false, true>(f, dev.cus, s, env_variant().group, p.splits);
     if (rc != GEMM_OK) return rc;
     int64_t blocks = (M * N / 4 + 255) / 256;
