@@ -19,7 +19,13 @@ import subprocess
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SOURCES = [os.path.join(PKG, "csrc", "libgemm.hip"), os.path.join(PKG, "csrc", "attention.hip")]
+SOURCES = [os.path.join(PKG, "csrc", "libgemm.hip"), os.path.join(PKG, "csrc", "gemm_mf16.hip"),
+           os.path.join(PKG, "csrc", "attention.hip")]
+# Per-source flags: the 16 x 16 MFMA kernel is compiled without the machine
+# scheduler that runs before register allocation (its reordering of the 64
+# accumulator quads of a wave tile made the allocator move accumulators around
+# the MFMAs); the kernel fixes its instruction interleave itself.
+SOURCE_FLAGS = {"gemm_mf16.hip": ["-mllvm", "-enable-misched=0"]}
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(PKG, "libgemm.so")
 MEASURE_LIBRARY = os.path.join(PKG, "libgemm_measure.so")
@@ -52,7 +58,8 @@ def build(verbose: bool = False, only=None, measure: bool = False) -> str:
     todo = SOURCES if only is None else [s for s in SOURCES if os.path.basename(s) in only]
     for src in todo:
         obj = _object(src, measure)
-        _run([hipcc, *HIPCC_FLAGS, *defines, f"-I{INCLUDE}", "-c", src, "-o", obj + ".tmp"], verbose)
+        extra = SOURCE_FLAGS.get(os.path.basename(src), [])
+        _run([hipcc, *HIPCC_FLAGS, *extra, *defines, f"-I{INCLUDE}", "-c", src, "-o", obj + ".tmp"], verbose)
         os.replace(obj + ".tmp", obj)
     out = MEASURE_LIBRARY if measure else LIBRARY
     tmp = out + ".tmp"

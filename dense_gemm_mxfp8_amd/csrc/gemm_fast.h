@@ -92,6 +92,7 @@ struct Args {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
@@ -420,6 +421,54 @@ __device__ __forceinline__ void store_c(const Args& a, const f32x16 (&acc)[kBloc
     }
 }
 
+// The plain fp32 store of a 128 x 128 wave tile held as 8 x 8 blocks of the
+// 16 x 16 MFMA: lane l holds rows 4 (l / 16) + r, r = 0..3, of column l % 16
+// of each block.  One v_permlane16_swap per register of two neighbouring
+// column blocks leaves, in one register, rows 4 g + r (lanes 0..31, g even)
+// of the 32 columns and, in the other, those of the odd g: every store
+// instruction then writes two whole 128-byte row segments, as the 32 x 32
+// form does, so non-temporal stores still write whole lines.
+template <int AUX>
+__device__ __forceinline__ void store_c16_aux(const Args& a, const f32x4 (&acc)[8][8], int m0w, int n0w, int lane) {
+    const int rlim = a.M - m0w;
+    const int clim = a.N - n0w;
+    if (rlim <= 0 || clim <= 0) return;
+    const int rows = rlim < kWaveTile ? rlim : kWaveTile;
+    const int cols = clim < kWaveTile ? clim : kWaveTile;
+    const int ldc4 = (int)a.ldc * 4;
+    const __amdgpu_buffer_rsrc_t rc =
+        make_rsrc(a.C + (int64_t)m0w * a.ldc + n0w, ((int64_t)(rows - 1) * a.ldc + cols) * 4);
+    // lanes 32..63 hold the rows 8 below lanes 0..31
+    const int voff = ((lane >> 5) * 8) * ldc4 + 4 * (lane & 31);
+    // The swap reads other lanes, so it runs with every lane active: a lane
+    // whose column lies past the tile's last instead stores at an offset
+    // past the descriptor's range (2^31 - 16 plus a row offset below 2^30:
+    // no 32-bit wrap), which drops the store.
+    constexpr int kOut = 0x7ffffff0;
+#pragma unroll
+    for (int jp = 0; jp < 4; ++jp) {
+        const int vo = (32 * jp + (lane & 31) < cols) ? voff + 128 * jp : kOut;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                // copy the elements out first (a bit cast of a vector
+                // element is otherwise compiled as one of element 0)
+                const float x = acc[i][2 * jp][r], y = acc[i][2 * jp + 1][r];
+                const auto sw = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, x),
+                                                                 __builtin_bit_cast(uint32_t, y), false, false);
+                __builtin_amdgcn_raw_buffer_store_b32(sw[0], rc, vo, (16 * i + r) * ldc4, AUX);
+                __builtin_amdgcn_raw_buffer_store_b32(sw[1], rc, vo, (16 * i + 4 + r) * ldc4, AUX);
+            }
+    }
+}
+
+__device__ __forceinline__ void store_c16(const Args& a, const f32x4 (&acc)[8][8], int m0w, int n0w, int lane) {
+    if (a.c_pol == kCStoreStream) store_c16_aux<kAuxStream>(a, acc, m0w, n0w, lane);
+    else if (a.c_pol == kCStoreDevice) store_c16_aux<kAuxDevice>(a, acc, m0w, n0w, lane);
+    else store_c16_aux<0>(a, acc, m0w, n0w, lane);
+}
+
 // Compile-time loop: f(integral_constant<int, B>), ..., f(integral_constant<int, E-1>).
 template <int B, int E, typename F>
 __device__ __forceinline__ void static_for(F&& f) {
@@ -448,6 +497,23 @@ __device__ __forceinline__ void interleave_step() {
     }
 }
 
+// The 64 MFMAs of one 16 x 16 x 32 k-step (column-block major: MFMAs 8 j ..
+// 8 j + 7 read B fragment j) with the next step's fragment reads, issued in
+// the order A 0, B 0, A 1, B 1, ...: A fragment j at MFMA 8 j, B fragment j
+// (BRD reads) after MFMA 8 j + 7, the last reader of the current B fragment
+// j, so the next one can take its registers (only the A fragments are held
+// twice); the ND DMA instructions go after every other MFMA from the first.
+template <int BRD, int ND>
+__device__ __forceinline__ void interleave_step16() {
+#pragma unroll
+    for (int m = 0; m < 64; ++m) {
+        __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+        if (m % 8 == 0) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
+        if (m % 8 == 7) __builtin_amdgcn_sched_group_barrier(kSgDsRead, BRD, 0);
+        if (m % 2 == 1 && m / 2 < ND) __builtin_amdgcn_sched_group_barrier(kSgVmem, 1, 0);
+    }
+}
+
 // SG (MX only): k-tiles per scale group.  SG == 1 stages each k-tile's scale
 // codes with the tile (one 2- or 4-byte load per row); SG > 1 keeps a
 // double-buffered ring of scale groups in LDS and fetches 4 * SG bytes per
@@ -470,10 +536,17 @@ __device__ __forceinline__ void interleave_step() {
 // LA: k-steps between a fragment read and the MFMAs that use it (1 or 2;
 // 2 keeps four fragment sets in registers and moves the closing wait and
 // barrier of each k-tile one k-step earlier: bf16, two stages).
+// MF: the bf16 MFMA shape, 32 (v_mfma_f32_32x32x16_bf16, 4 x 4 blocks per
+// 128 x 128 wave tile, k-steps of 16) or 16 (v_mfma_f32_16x16x32_bf16, 8 x 8
+// blocks, k-steps of 32).  The same FLOPs and LDS bytes either way; at the
+// board's power limit the 16 x 16 form draws less power per FLOP, so the
+// clock it holds is higher.
 template <int KIND, int RB, int S, bool TAIL, int SG = 1, int E = 0, int D = 0, int NW = 4, bool FUSED = false,
-          bool SPLIT = false, bool DYN = false, int LA = 1>
+          bool SPLIT = false, bool DYN = false, int LA = 1, int MF = 32>
 __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(Args a) {
     static_assert(NW == 4 || (NW == 8 && KIND != kMX), "8 waves: bf16 only");
+    static_assert(MF == 32 || (MF == 16 && KIND != kMX && NW == 4 && !FUSED && !SPLIT && !DYN && LA == 1),
+                  "16 x 16 MFMAs: plain bf16 products, 4 waves");
     static_assert(!SPLIT || (!FUSED && NW == 4), "split-K: plain fp32 partial stores, 4 waves");
     static_assert(!SPLIT || KIND != kMX || SG > 1, "MX split-K: the scale-ring pipeline");
     static_assert(!DYN || (!SPLIT && NW == 4), "dynamic schedule: whole tiles, 4 waves");
@@ -494,7 +567,12 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(Args a) {
     constexpr int NI = RB * kTile / 1024 / NW;  // DMA instructions per wave per operand
     constexpr int RPK = 1024 / RB;              // K-contiguous rows per KiB
     // MFMA k-steps per k-tile: 16 bf16 or 64 fp8 elements per step
-    constexpr int KS = (KIND == kMX) ? BK / 64 : BK / 16;
+    constexpr int KS = (KIND == kMX) ? BK / 64 : BK / (MF == 16 ? 32 : 16);
+    // MFMA blocks per wave tile: BA row blocks of A, BB column blocks of B
+    // (32 x 32 blocks, or 16 x 16 with MF == 16), and the accumulator type
+    constexpr int BA = MF == 16 ? 8 : kBlocks;
+    constexpr int BB = MF == 16 ? 8 : NBJ;
+    typedef typename std::conditional<MF == 16, f32x4, f32x16>::type AccT;
     // Fragments are double-buffered over the global k-step sequence; with an
     // odd step count per k-tile the buffer parity follows the k-tile parity,
     // which the S-fold unrolled loop keeps static only for even S.
@@ -587,16 +665,32 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(Args a) {
     // byte offsets in a stage of this lane's A / B chunks at step ks (block
     // 0); fp8 steps read two chunks (k 16h..16h+15 and 32+16h..32+16h+15)
     int a_rd[KS][2], b_rd[KS][2];
-    int b_tr[NBJ];  // NN: offset of block j's transposed read at step 0
+    int b_tr[BB];  // NN: offset of block j's transposed read at step 0
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-        const int c0 = (KIND == kMX) ? (4 * ks + h) : (2 * ks + h);
-        a_rd[ks][0] = kc_off<RB>(wm * kWaveTile + l32, c0);
-        b_rd[ks][0] = OPB + kc_off<RB>(wn * WTN + l32, c0);
-        a_rd[ks][1] = kc_off<RB>(wm * kWaveTile + l32, c0 + 2);
-        b_rd[ks][1] = OPB + kc_off<RB>(wn * WTN + l32, c0 + 2);
+        if constexpr (MF == 16) {
+            // 16 x 16 x 32: lane l reads row l % 16 of its block, k 8 (l / 16)
+            // .. +7 of the step's 32, i.e. chunk 4 ks + l / 16 (the swizzle
+            // depends on row bits 1..3 only, so block i adds 16 i rows)
+            a_rd[ks][0] = kc_off<RB>(wm * kWaveTile + (lane & 15), 4 * ks + (lane >> 4));
+            b_rd[ks][0] = OPB + kc_off<RB>(wn * WTN + (lane & 15), 4 * ks + (lane >> 4));
+            a_rd[ks][1] = b_rd[ks][1] = 0;
+        } else {
+            const int c0 = (KIND == kMX) ? (4 * ks + h) : (2 * ks + h);
+            a_rd[ks][0] = kc_off<RB>(wm * kWaveTile + l32, c0);
+            b_rd[ks][0] = OPB + kc_off<RB>(wn * WTN + l32, c0);
+            a_rd[ks][1] = kc_off<RB>(wm * kWaveTile + l32, c0 + 2);
+            b_rd[ks][1] = OPB + kc_off<RB>(wn * WTN + l32, c0 + 2);
+        }
     }
-    if constexpr (KIND == kNN) {
+    if constexpr (KIND == kNN && MF == 16) {
+        // transposed reads for 16 x 16 x 32: lane p of each 16-lane group g
+        // addresses k-row 8 g + p / 4 (and + 4 for the second half) and the
+        // 4 columns from 4 (p % 4) of block j
+        const int g = lane >> 4, p = lane & 15;
+#pragma unroll
+        for (int j = 0; j < BB; ++j) b_tr[j] = OPB + nn_off(8 * g + (p >> 2), wn * WTN + 16 * j + 4 * (p & 3));
+    } else if constexpr (KIND == kNN) {
         const int g = lane >> 4, li = lane & 15;
 #pragma unroll
         for (int j = 0; j < NBJ; ++j) {
@@ -719,6 +813,24 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(Args a) {
 
         auto read_frags = [&](auto sidx, int ks, Frag* fa, Frag* fb) {
             const uint8_t FAST_LDS* base = stage_ptr(sidx);
+            if constexpr (MF == 16) {
+                // A fragment i, then B fragment i: the order interleave_step16
+                // places them in (B fragment j after the last MFMA that reads
+                // the current step's B fragment j, so it can take its registers)
+#pragma unroll
+                for (int j = 0; j < BB; ++j) {
+                    fa[j] = *(const bf16x8 FAST_LDS*)(base + a_rd[ks][0] + j * 16 * RB);
+                    if constexpr (KIND == kNN) {
+                        const uint8_t FAST_LDS* p = base + b_tr[j] + ks * 32 * 512;
+                        bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((bf16x4 FAST_LDS*)p);
+                        bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((bf16x4 FAST_LDS*)(p + 4 * 512));
+                        fb[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                    } else {
+                        fb[j] = *(const bf16x8 FAST_LDS*)(base + b_rd[ks][0] + j * 16 * RB);
+                    }
+                }
+                return;
+            }
 #pragma unroll
             for (int i = 0; i < kBlocks; ++i) {
                 if constexpr (KIND == kMX) {
@@ -746,8 +858,8 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(Args a) {
             }
         };
         // fragment reads per k-step (LDS instructions)
-        constexpr int NR = (KIND == kMX) ? 16 : (KIND == kNN) ? 4 + 2 * NBJ : 4 + NBJ;
-        constexpr int NMF = kBlocks * NBJ;  // MFMAs per k-step
+        constexpr int NR = (KIND == kMX) ? 16 : (KIND == kNN) ? BA + 2 * BB : BA + BB;
+        constexpr int NMF = BA * BB;  // MFMAs per k-step
 
         // MX: the scale dwords of the k-tile in stage s, pre-shifted so that
         // lane half h finds its 32-block (2 ks + h) in byte 2 ks.
@@ -792,20 +904,24 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(Args a) {
             }
         };
 
-        f32x16 acc[kBlocks][NBJ];
+        AccT acc[BA][BB];
 #pragma unroll
-        for (int i = 0; i < kBlocks; ++i)
+        for (int i = 0; i < BA; ++i)
 #pragma unroll
-            for (int j = 0; j < NBJ; ++j)
+            for (int j = 0; j < BB; ++j)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+                for (int r = 0; r < (MF == 16 ? 4 : 16); ++r) acc[i][j][r] = 0.0f;
 
         auto mfma = [&](int ks, const Frag* fa, const Frag* fb, const int* scl) {
 #pragma unroll
-            for (int i = 0; i < kBlocks; ++i)
+            for (int i = 0; i < BA; ++i)
 #pragma unroll
-                for (int j = 0; j < NBJ; ++j) {
-                    if constexpr (KIND == kMX) {
+                for (int j = 0; j < BB; ++j) {
+                    if constexpr (MF == 16) {
+                        // column-block major: B fragment i (as j) is done after
+                        // MFMAs 8 i .. 8 i + 7
+                        acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[j], fb[i], acc[j][i], 0, 0, 0);
+                    } else if constexpr (KIND == kMX) {
                         // k-step ks covers 32-blocks 2 ks and 2 ks + 1 of the
                         // k-tile: byte 2 ks of the (pre-shifted) scale word.
                         if (ks == 0)
@@ -839,7 +955,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(Args a) {
         barrier();
 
         // fragment set f holds the fragments of global k-step f mod R
-        Frag Fa[R][kBlocks], Fb[R][NBJ];
+        Frag Fa[R][BA], Fb[R][BB];
         static_for<0, LA>([&](auto tc) {
             constexpr int t = decltype(tc)::value;
             read_frags(std::integral_constant<int, 0>{}, t, Fa[t], Fb[t]);
@@ -889,7 +1005,10 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(Args a) {
                         ring_dma(std::integral_constant<int, (q / SG + 1) % 2>{}, g, g * SG < KT);
                     }
                     mfma(ks, ca, cb, sc);
-                    interleave_step<NR, d1 - d0 + ((SG > 1 && ks == 0 && q % SG == 0) ? 2 : 0), NMF>();
+                    if constexpr (MF == 16)
+                        interleave_step16<KIND == kNN ? 2 : 1, d1 - d0>();
+                    else
+                        interleave_step<NR, d1 - d0 + ((SG > 1 && ks == 0 && q % SG == 0) ? 2 : 0), NMF>();
                     // keep every MFMA of this step ahead of the closing wait
                     __builtin_amdgcn_sched_barrier(0);
                 } else if constexpr (ks == BS) {
@@ -918,7 +1037,10 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(Args a) {
                     } else {
                         mfma(ks, ca, cb, sc);
                     }
-                    interleave_step<NR, d1 - d0 + E, NMF>();
+                    if constexpr (MF == 16)
+                        interleave_step16<KIND == kNN ? 2 : 1, d1 - d0 + E>();
+                    else
+                        interleave_step<NR, d1 - d0 + E, NMF>();
                     __builtin_amdgcn_sched_barrier(0);
                 } else {
                     // after the barrier (LA = 2): the next stage's fragments,
@@ -928,7 +1050,10 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(Args a) {
                         dma(sidx, decltype(dc)::value, kt + 2, kt + 2 < KT);
                     });
                     mfma(ks, ca, cb, sc);
-                    interleave_step<NR, d1 - d0, NMF>();
+                    if constexpr (MF == 16)
+                        interleave_step16<KIND == kNN ? 2 : 1, d1 - d0>();
+                    else
+                        interleave_step<NR, d1 - d0, NMF>();
                     __builtin_amdgcn_sched_barrier(0);
                 }
             });
@@ -984,8 +1109,11 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(Args a) {
             store_c<NBJ, false>(a, acc, m0 + wm * kWaveTile, n0 + wn * WTN, h, l32, nullptr, 0, 0, cw, cld,
                                 pld == 0);
         } else {
-            store_c<NBJ, FUSED>(a, acc, m0 + wm * kWaveTile, n0 + wn * WTN, h, l32, (const float FAST_LDS*)evl,
-                                wm * kWaveTile, wn * WTN);
+            if constexpr (MF == 16)
+                store_c16(a, acc, m0 + wm * kWaveTile, n0 + wn * WTN, lane);
+            else
+                store_c<NBJ, FUSED>(a, acc, m0 + wm * kWaveTile, n0 + wn * WTN, h, l32, (const float FAST_LDS*)evl,
+                                    wm * kWaveTile, wn * WTN);
         }
         if constexpr (DYN) {
             if (tid == 0) tile_slot[slot] = next_tile(a, xcd, claim, P, G);
@@ -1002,5 +1130,32 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(Args a) {
         }
     }
 }
+
+// Launch geometry shared by the host launchers: the tile grid, the raster
+// band height (group_m rows of tiles, 8 when group_m <= 0) and the k-tile
+// counts for k-tiles of bk elements.  num_tiles may be raised afterwards
+// (split-K units) before fast_grid picks the persistent grid: the CUs, or the
+// work units when fewer, rounded down to a multiple of 8 (from 8 up), with
+// the XCD-aware renumbering when the grid is such a multiple.
+inline void fast_tiles(Args& a, int group_m, int bk) {
+    a.tiles_m = (a.M + kTile - 1) / kTile;
+    a.tiles_n = (a.N + kTile - 1) / kTile;
+    a.num_tiles = a.tiles_m * a.tiles_n;
+    if (group_m <= 0) group_m = 8;
+    a.group_m = a.tiles_m < group_m ? a.tiles_m : group_m;
+    a.kt_full = a.K / bk;
+    a.kt_total = (a.K + bk - 1) / bk;
+}
+
+inline int fast_grid(Args& a, int cus) {
+    int grid = cus < a.num_tiles ? cus : a.num_tiles;
+    if (grid >= 8) grid -= grid % 8;
+    a.xcd_remap = (grid % 8 == 0) ? 1 : 0;
+    return grid;
+}
+
+// The plain bf16 product (fp32 output, NT or NN) on the 256 x 256
+// direct-load kernel with 16 x 16 x 32 MFMAs; defined in gemm_mf16.hip.
+int launch_fast_mf16(bool nt, Args a, int cus, hipStream_t stream, int group_m);
 
 }  // namespace fast

@@ -1,0 +1,49 @@
+// gemm_mf16.hip -- the plain bf16 product (fp32 output, NT and NN) on the
+// 256 x 256 direct-load kernel of gemm_fast.h with 16 x 16 x 32 MFMAs.
+//
+// It is a translation unit of its own because it is compiled without the
+// machine scheduler that runs before register allocation (-mllvm
+// -enable-misched=0, see build.py): with it, the 64 accumulator quads of a
+// 128 x 128 wave tile were reordered into live ranges that the allocator
+// could not keep in place, and it moved accumulators between registers
+// around most MFMAs (hundreds of v_accvgpr moves per k-tile).  Without it the
+// K loop keeps every accumulator in place; the MFMA / LDS-read / DMA
+// interleave is still fixed by the kernel's sched_group_barrier groups.
+//
+// The 16 x 16 x 32 form does the same FLOPs with the same LDS bytes as the
+// 32 x 32 x 16 one, but draws less power per FLOP, so under the board's power
+// limit the clock holds higher (register-only MFMA issue on MI355X: 2045-2076
+// TFLOP/s at 2.10 GHz against 1831-1836 TFLOP/s at 1.84-1.86 GHz).  Early
+// DMA: 8 of the 16 instructions of k-tile t+2 right after the barrier of
+// k-tile t (8192^3 NT on one box: 4 -> 746.6-749.5 us, 6 -> 726-728,
+// 8 -> 718-720, 10 -> 722-725, 16 -> 750 us; the 32 x 32 form 759-762 us).
+#include <hip/hip_runtime.h>
+
+#include "libgemm.h"
+#include "gemm_fast.h"
+
+namespace fast {
+
+int launch_fast_mf16(bool nt, Args a, int cus, hipStream_t stream, int group_m) {
+    fast_tiles(a, group_m, 64);
+    const int grid = fast_grid(a, cus);
+    const bool tail = a.kt_total > a.kt_full;
+    if (nt) {
+        if (tail)
+            hipLaunchKernelGGL((gemm_fast_kernel<kNT, 128, 2, true, 1, 8, 1, 4, false, false, false, 1, 16>),
+                               dim3(grid), dim3(256), 0, stream, a);
+        else
+            hipLaunchKernelGGL((gemm_fast_kernel<kNT, 128, 2, false, 1, 8, 1, 4, false, false, false, 1, 16>),
+                               dim3(grid), dim3(256), 0, stream, a);
+    } else {
+        if (tail)
+            hipLaunchKernelGGL((gemm_fast_kernel<kNN, 128, 2, true, 1, 8, 1, 4, false, false, false, 1, 16>),
+                               dim3(grid), dim3(256), 0, stream, a);
+        else
+            hipLaunchKernelGGL((gemm_fast_kernel<kNN, 128, 2, false, 1, 8, 1, 4, false, false, false, 1, 16>),
+                               dim3(grid), dim3(256), 0, stream, a);
+    }
+    return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
+}
+
+}  // namespace fast

@@ -22,8 +22,9 @@
 //     cores work on k-tile t; one `s_waitcnt vmcnt(0)` + barrier per k-tile
 //     hands a stage from the loaders to the readers (the role the pages give
 //     to mbarrier phases);
-//   * matrix cores: v_mfma_f32_32x32x16_bf16 and
-//     v_mfma_scale_f32_32x32x64_f8f6f4 accumulating in registers;
+//   * matrix cores: v_mfma_f32_16x16x32_bf16 (plain bf16 products, in
+//     gemm_mf16.hip) or v_mfma_f32_32x32x16_bf16, and
+//     v_mfma_scale_f32_32x32x64_f8f6f4, accumulating in registers;
 //   * row-major B (NN): `ds_read_b64_tr_b16` transposes 4x16 blocks on the way
 //     out of LDS so the B fragment arrives K-contiguous per lane;
 //   * a persistent grid with a static strided tile walk, grouped raster order
@@ -41,6 +42,14 @@
 //   v_mfma_f32_32x32x16_bf16: lane l supplies A[l%32][8*(l/32) + j] and
 //     B[8*(l/32) + j][l%32], j = 0..7; accumulator register i of lane l is
 //     D[8*(i/4) + 4*(l/32) + i%4][l%32].
+//   v_mfma_f32_16x16x32_bf16: lane l supplies A[l%16][8*(l/16) + j] and
+//     B[8*(l/16) + j][l%16]; accumulator register i of lane l is
+//     D[4*(l/16) + i][l%16].
+//   v_permlane16_swap (as __builtin_amdgcn_permlane16_swap(x, y)): result 0
+//     holds x's 16-lane groups 0 and 2 in groups 0 and 2 and y's groups 0 and
+//     2 in groups 1 and 3; result 1 holds x's groups 1 and 3 in groups 0 and 2
+//     and y's groups 1 and 3 in groups 1 and 3 (checked on gfx950 with lane
+//     indices as data).
 //   v_mfma_scale_f32_32x32x64_f8f6f4 (fp8): lane l supplies row l%32; bytes
 //     0..15 hold k = 16*(l/32) + j, bytes 16..31 hold k = 32 + 16*(l/32) + j;
 //     the scale operand of lane q applies to row q%32, 32-block q/32.
@@ -645,27 +654,28 @@ constexpr int kMaxSplits = 32;
 // and 8192^3, are 128-byte rows x 2 stages for bf16 NT and NN (early 6,
 // spread 2) and for MX (scale ring, early 12).
 struct FastVariant {
-    int rb, stages, group, early, spread, waves, lookahead;
+    int rb, stages, group, early, spread, waves, lookahead, mfma;
 };
 
 // Measurement builds (-DLIBGEMM_MEASURE) read switches from the environment
 // that select other compiled pipelines for A/B timing:
-// LIBGEMM_VARIANT=<rb>x<stages>[e<early>[d<spread>[w<waves>[l<lookahead>]]]]
-// picks the pipeline (for two stages the early-DMA split, and the k-steps
-// between a fragment read and its MFMAs); LIBGEMM_GROUP=<n> the
+// LIBGEMM_VARIANT=<rb>x<stages>[e<early>[d<spread>[w<waves>[l<lookahead>[m<mfma>]]]]]
+// picks the pipeline (for two stages the early-DMA split, the k-steps
+// between a fragment read and its MFMAs, and the MFMA shape, 32 or 16);
+// LIBGEMM_GROUP=<n> the
 // number of tile rows per raster band.  The library as built by default
 // compiles none of those instances and reads no environment variable: every
 // call runs the defaults below.
 FastVariant env_variant() {
 #ifndef LIBGEMM_MEASURE
-    return FastVariant{0, 0, 0, -1, 0, 4, 1};
+    return FastVariant{0, 0, 0, -1, 0, 4, 1, 16};
 #else
     static FastVariant v = [] {
-        FastVariant r{0, 0, 0, -1, 0, 4, 1};
+        FastVariant r{0, 0, 0, -1, 0, 4, 1, 16};
         const char* e = getenv("LIBGEMM_VARIANT");
         if (e) {
-            int rb = 0, st = 0, ea = -1, sp = 0, nw = 4, la = 1;
-            const int n = sscanf(e, "%dx%de%dd%dw%dl%d", &rb, &st, &ea, &sp, &nw, &la);
+            int rb = 0, st = 0, ea = -1, sp = 0, nw = 4, la = 1, mf = 16;
+            const int n = sscanf(e, "%dx%de%dd%dw%dl%dm%d", &rb, &st, &ea, &sp, &nw, &la, &mf);
             if (n >= 2) {
                 r.rb = rb;
                 r.stages = st;
@@ -673,7 +683,8 @@ FastVariant env_variant() {
             if (n >= 3) r.early = ea;
             if (n >= 4) r.spread = sp;
             if (n >= 5) r.waves = nw;
-            if (n == 6) r.lookahead = la;
+            if (n >= 6) r.lookahead = la;
+            if (n == 7) r.mfma = mf;
         }
         const char* g = getenv("LIBGEMM_GROUP");
         if (g) r.group = atoi(g);
@@ -689,12 +700,10 @@ FastVariant env_variant() {
 // on the stream first (falls back to the static walk when the grid is not a
 // multiple of 8).
 template <int KIND, int RB, int S, int SG = 1, int E = 0, int D = 0, int NW = 4, bool FUSED = false,
-          bool SPLIT = false, bool DYN = false, int LA = 1>
+          bool SPLIT = false, bool DYN = false, int LA = 1, int MF = 32>
 int launch_fast(fast::Args a, int cus, hipStream_t stream, int group_m = 0, int splits = 1) {
     constexpr int BK = RB / (KIND == fast::kMX ? 1 : 2);
-    a.tiles_m = (a.M + fast::kTile - 1) / fast::kTile;
-    a.tiles_n = (a.N + fast::kTile - 1) / fast::kTile;
-    a.num_tiles = a.tiles_m * a.tiles_n;
+    fast::fast_tiles(a, group_m, BK);
     if (SPLIT) {
         if (a.part == nullptr) {  // every tile split, stacked dense planes
             a.dp_units = 0;
@@ -703,30 +712,24 @@ int launch_fast(fast::Args a, int cus, hipStream_t stream, int group_m = 0, int 
         }
         a.num_tiles = a.dp_units + a.tiles_per_split * splits;
     }
-    if (group_m <= 0) group_m = 8;
-    a.group_m = a.tiles_m < group_m ? a.tiles_m : group_m;
-    a.kt_full = a.K / BK;
-    a.kt_total = (a.K + BK - 1) / BK;
-    int grid = cus < a.num_tiles ? cus : a.num_tiles;
-    if (grid >= 8) grid -= grid % 8;
-    a.xcd_remap = (grid % 8 == 0) ? 1 : 0;
+    const int grid = fast::fast_grid(a, cus);
     if constexpr (DYN) {
         if (a.xcd_remap) {
             hipLaunchKernelGGL(zero_words_kernel, dim3(1), dim3(256), 0, stream, a.tile_ctr, 256);
             if (a.kt_total > a.kt_full)
-                hipLaunchKernelGGL((fast::gemm_fast_kernel<KIND, RB, S, true, SG, E, D, NW, FUSED, false, true, LA>),
+                hipLaunchKernelGGL((fast::gemm_fast_kernel<KIND, RB, S, true, SG, E, D, NW, FUSED, false, true, LA, MF>),
                                    dim3(grid), dim3(64 * NW), 0, stream, a);
             else
-                hipLaunchKernelGGL((fast::gemm_fast_kernel<KIND, RB, S, false, SG, E, D, NW, FUSED, false, true, LA>),
+                hipLaunchKernelGGL((fast::gemm_fast_kernel<KIND, RB, S, false, SG, E, D, NW, FUSED, false, true, LA, MF>),
                                    dim3(grid), dim3(64 * NW), 0, stream, a);
             return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
         }
     }
     if (a.kt_total > a.kt_full) {
-        hipLaunchKernelGGL((fast::gemm_fast_kernel<KIND, RB, S, true, SG, E, D, NW, FUSED, SPLIT, false, LA>), dim3(grid),
+        hipLaunchKernelGGL((fast::gemm_fast_kernel<KIND, RB, S, true, SG, E, D, NW, FUSED, SPLIT, false, LA, MF>), dim3(grid),
                            dim3(64 * NW), 0, stream, a);
     } else {
-        hipLaunchKernelGGL((fast::gemm_fast_kernel<KIND, RB, S, false, SG, E, D, NW, FUSED, SPLIT, false, LA>), dim3(grid),
+        hipLaunchKernelGGL((fast::gemm_fast_kernel<KIND, RB, S, false, SG, E, D, NW, FUSED, SPLIT, false, LA, MF>), dim3(grid),
                            dim3(64 * NW), 0, stream, a);
     }
     return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
@@ -811,20 +814,27 @@ int launch_fast_bf16(bool nt, const fast::Args& a, int cus, hipStream_t s) {
         if (v.early == 0) return launch_fast<fast::kNT, 128, 2>(a, cus, s, g);
         if (v.lookahead == 2)
             return launch_fast<fast::kNT, 128, 2, 1, 6, 2, 4, false, false, false, 2>(a, cus, s, g);
+        // the 32 x 32 x 16 form: 6 DMA instructions of k-tile t+2 right
+        // after the barrier of k-tile t, the other 10 over k-steps 0 and 1
+        // of t+1 (MI355X, 8192^3, same box: 776.5 -> 746.5 us and 797.6 ->
+        // 778.2 us); the default before the 16 x 16 form
+        if (v.mfma == 32) return launch_fast<fast::kNT, 128, 2, 1, 6, 2>(a, cus, s, g);
 #endif
-        // default: 6 DMA instructions of k-tile t+2 right after the barrier
-        // of k-tile t, the other 10 over k-steps 0 and 1 of t+1 (MI355X,
-        // 8192^3, same box: 776.5 -> 746.5 us and 797.6 -> 778.2 us)
-        return launch_fast<fast::kNT, 128, 2, 1, 6, 2>(a, cus, s, g);
+        // default: 16 x 16 x 32 MFMAs (gemm_mf16.hip; 8192^3 on one box:
+        // 718-720 us against 759-762 us for the 32 x 32 form)
+        return fast::launch_fast_mf16(true, a, cus, s, g);
     }
 #ifdef LIBGEMM_MEASURE
     if (v.rb == 64 && v.stages == 4) return launch_fast<fast::kNN, 64, 4>(a, cus, s, g);
     if (v.rb == 128 && v.stages == 2 && v.early == 0) return launch_fast<fast::kNN, 128, 2>(a, cus, s, g);
     if (v.lookahead == 2) return launch_fast<fast::kNN, 128, 2, 1, 6, 2, 4, false, false, false, 2>(a, cus, s, g);
+    // the 32 x 32 x 16 form, as NT (MI355X, 4096^3: 108.8 -> 105.5 us
+    // against 64 x 4; 8192^3: 801.5 -> 771.2 us)
+    if (v.mfma == 32) return launch_fast<fast::kNN, 128, 2, 1, 6, 2>(a, cus, s, g);
 #endif
-    // default: as NT (MI355X, 4096^3: 108.8 -> 105.5 us against 64 x 4;
-    // 8192^3: 801.5 -> 771.2 us)
-    return launch_fast<fast::kNN, 128, 2, 1, 6, 2>(a, cus, s, g);
+    // default: 16 x 16 x 32 MFMAs, as NT (4096^3 on one box: 101.5-103.3 us
+    // against 103.8-104.3 us)
+    return fast::launch_fast_mf16(false, a, cus, s, g);
 }
 
 // ---------------------------------------------------------------------------

@@ -34,7 +34,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 # The sources each kernel family is built from: a counter summary stays valid
 # while these files are unchanged.
 FAMILIES = {
-    "gemm": ["csrc/libgemm.hip", "csrc/gemm_*.h", "../include/libgemm.h"],
+    "gemm": ["csrc/libgemm.hip", "csrc/gemm_mf16.hip", "csrc/gemm_*.h", "../include/libgemm.h"],
     "attention": ["csrc/attention.hip", "../include/attention.h"],
 }
 
