@@ -125,10 +125,17 @@ __device__ __forceinline__ int kc_off(int row, int chunk) {
     return row * RB + ((chunk ^ swz<RB>(row)) << 4);
 }
 
+// Swizzle of the 16-byte chunks of k-row k of row-major B: bits 0..1 of k
+// select chunk groups 4 apart (the four k-rows a 16-lane transposed read
+// spans), bit 3 moves odd 8-row bands by 2 chunks (the 16 x 16 x 32 MFMA's
+// B fragment puts k-rows 8 g .. 8 g + 3 in lane group g, so two groups of a
+// 32-lane read phase read rows 8 apart at the same columns).
+__device__ __forceinline__ int nn_swz(int k) { return ((k & 3) << 2) | (((k >> 3) & 1) << 1); }
+
 // Byte offset of element column n of k-row k in the N-contiguous stage of
 // row-major B (512-byte rows of 256 bf16).
 __device__ __forceinline__ int nn_off(int k, int n) {
-    return k * 512 + ((((n >> 3) ^ ((k & 3) << 2))) << 4) + ((n & 7) << 1);
+    return k * 512 + ((((n >> 3) ^ nn_swz(k))) << 4) + ((n & 7) << 1);
 }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
@@ -646,12 +653,13 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(Args a) {
     const int kc_chunk = (lane % (RB / 16)) ^ swz<RB>(kc_row0);
     const int a_voff = (int)(kc_row0 * a.lda_b) + kc_chunk * 16;
     const int a_step = (int)(NW * RPK * a.lda_b);
-    int b_voff, b_step;
+    int b_voff, b_step, b_voff8 = 0;
     if constexpr (KIND == kNN) {
-        // k rows of 512 bytes, 2 per KiB: row 2(NW i + wave) + lane / 32.
+        // k rows of 512 bytes, 2 per KiB: row 2(NW i + wave) + lane / 32;
+        // b_voff8 for the rows with bit 3 set (nn_swz)
         const int kk0 = 2 * wave + h;
-        const int c = l32 ^ ((kk0 & 3) << 2);
-        b_voff = (int)(kk0 * a.ldb_b) + c * 16;
+        b_voff = (int)(kk0 * a.ldb_b) + (l32 ^ nn_swz(kk0 & 7)) * 16;
+        b_voff8 = (int)(kk0 * a.ldb_b) + (l32 ^ nn_swz((kk0 & 7) | 8)) * 16;
         b_step = (int)(2 * NW * a.ldb_b);
     } else {
         b_voff = (int)(kc_row0 * a.ldb_b) + kc_chunk * 16;
@@ -783,9 +791,12 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(Args a) {
             } else if (d < 2 * NI) {
                 const int i = d - NI;
                 const int koff = (KIND == kNN) ? kt * BK * (int)a.ldb_b : kt * RB;
+                // row-major B: instruction i fills k-rows 2 (NW i + wave) and
+                // + 1, whose bit 3 picks the swizzle (uniform over the wave)
+                const int bv = (KIND == kNN && (((2 * (NW * i + wave)) >> 3) & 1)) ? b_voff8 : b_voff;
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(live ? rb : rdead,
                                                          (void FAST_LDS*)(As + OPB + (NW * i + wave) * 1024), 16,
-                                                         b_voff, koff + i * b_step, 0, 0);
+                                                         bv, koff + i * b_step, 0, 0);
             } else if constexpr (KIND == kMX) {
                 const bool sb = d > 2 * NI;
                 const __amdgpu_buffer_rsrc_t rs = live ? (sb ? rsb : rsa) : rdead;
