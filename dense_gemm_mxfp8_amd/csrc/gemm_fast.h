@@ -504,21 +504,40 @@ __device__ __forceinline__ void interleave_step() {
     }
 }
 
-// The 64 MFMAs of one 16 x 16 x 32 k-step (column-block major: MFMAs 8 j ..
-// 8 j + 7 read B fragment j) with the next step's fragment reads, issued in
-// the order A 0, B 0, A 1, B 1, ...: A fragment j at MFMA 8 j, B fragment j
-// (BRD reads) after MFMA 8 j + 7, the last reader of the current B fragment
-// j, so the next one can take its registers (only the A fragments are held
-// twice); the ND DMA instructions go after every other MFMA from the first.
-template <int BRD, int ND>
-__device__ __forceinline__ void interleave_step16() {
-#pragma unroll
+// The 64 MFMAs of a 16 x 16 x 32 k-step visit the 8 x 8 blocks of the wave
+// tile in Z order (MFMA m: A block z_row(m), B block z_col(m)), so the
+// fragments a k-step needs grow as 2 sqrt(m): by MFMA 16 only 4 A and 4 B
+// fragments.  The next step's fragments are read in the order of first use
+// (z_frag) into the other register set, spread evenly over this step's MFMAs
+// (NRD LDS reads), which leaves every read at least 40 MFMAs before the one
+// that needs it; a row-first order needed all 8 A fragments within the
+// first 8 MFMAs.  The ND DMA instructions go after every other MFMA from
+// the first.
+constexpr int z_row(int m) { return ((m >> 1) & 1) | ((m >> 2) & 2) | ((m >> 3) & 4); }
+constexpr int z_col(int m) { return (m & 1) | ((m >> 1) & 2) | ((m >> 2) & 4); }
+// The o-th fragment in order of first use: A fragments 0..7, B fragments 8..15.
+constexpr int z_frag(int o) {
+    int seen = 0, n = 0;
     for (int m = 0; m < 64; ++m) {
-        __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
-        if (m % 8 == 0) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
-        if (m % 8 == 7) __builtin_amdgcn_sched_group_barrier(kSgDsRead, BRD, 0);
-        if (m % 2 == 1 && m / 2 < ND) __builtin_amdgcn_sched_group_barrier(kSgVmem, 1, 0);
+        const int f[2] = {z_row(m), 8 + z_col(m)};
+        for (int x : f) {
+            if ((seen >> x) & 1) continue;
+            if (n++ == o) return x;
+            seen |= 1 << x;
+        }
     }
+    return -1;
+}
+
+template <int NRD, int ND>
+__device__ __forceinline__ void interleave_step16() {
+    static_for<0, 64>([&](auto mc) {
+        constexpr int m = decltype(mc)::value;
+        constexpr int nr = ((m + 1) * NRD) / 64 - (m * NRD) / 64;
+        __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+        if constexpr (nr > 0) __builtin_amdgcn_sched_group_barrier(kSgDsRead, nr, 0);
+        if constexpr (m % 2 == 1 && m / 2 < ND) __builtin_amdgcn_sched_group_barrier(kSgVmem, 1, 0);
+    });
 }
 
 // SG (MX only): k-tiles per scale group.  SG == 1 stages each k-tile's scale
@@ -825,13 +844,13 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(Args a) {
         auto read_frags = [&](auto sidx, int ks, Frag* fa, Frag* fb) {
             const uint8_t FAST_LDS* base = stage_ptr(sidx);
             if constexpr (MF == 16) {
-                // A fragment i, then B fragment i: the order interleave_step16
-                // places them in (B fragment j after the last MFMA that reads
-                // the current step's B fragment j, so it can take its registers)
-#pragma unroll
-                for (int j = 0; j < BB; ++j) {
-                    fa[j] = *(const bf16x8 FAST_LDS*)(base + a_rd[ks][0] + j * 16 * RB);
-                    if constexpr (KIND == kNN) {
+                // in the order the MFMAs first use them (z_frag)
+                static_for<0, 16>([&](auto oc) {
+                    constexpr int f = z_frag(decltype(oc)::value);
+                    constexpr int j = f & 7;
+                    if constexpr (f < 8) {
+                        fa[j] = *(const bf16x8 FAST_LDS*)(base + a_rd[ks][0] + j * 16 * RB);
+                    } else if constexpr (KIND == kNN) {
                         const uint8_t FAST_LDS* p = base + b_tr[j] + ks * 32 * 512;
                         bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((bf16x4 FAST_LDS*)p);
                         bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((bf16x4 FAST_LDS*)(p + 4 * 512));
@@ -839,7 +858,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(Args a) {
                     } else {
                         fb[j] = *(const bf16x8 FAST_LDS*)(base + b_rd[ks][0] + j * 16 * RB);
                     }
-                }
+                });
                 return;
             }
 #pragma unroll
@@ -924,27 +943,31 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(Args a) {
                 for (int r = 0; r < (MF == 16 ? 4 : 16); ++r) acc[i][j][r] = 0.0f;
 
         auto mfma = [&](int ks, const Frag* fa, const Frag* fb, const int* scl) {
+            if constexpr (MF == 16) {
+                // Z order over the 8 x 8 blocks (interleave_step16)
+                static_for<0, 64>([&](auto mc) {
+                    constexpr int r = z_row(decltype(mc)::value), c = z_col(decltype(mc)::value);
+                    acc[r][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[r], fb[c], acc[r][c], 0, 0, 0);
+                });
+            } else {
 #pragma unroll
-            for (int i = 0; i < BA; ++i)
+                for (int i = 0; i < BA; ++i)
 #pragma unroll
-                for (int j = 0; j < BB; ++j) {
-                    if constexpr (MF == 16) {
-                        // column-block major: B fragment i (as j) is done after
-                        // MFMAs 8 i .. 8 i + 7
-                        acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[j], fb[i], acc[j][i], 0, 0, 0);
-                    } else if constexpr (KIND == kMX) {
-                        // k-step ks covers 32-blocks 2 ks and 2 ks + 1 of the
-                        // k-tile: byte 2 ks of the (pre-shifted) scale word.
-                        if (ks == 0)
-                            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                                fa[i], fb[j], acc[i][j], 0, 0, 0, scl[i], 0, scl[kBlocks + j]);
-                        else
-                            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                                fa[i], fb[j], acc[i][j], 0, 0, 2, scl[i], 2, scl[kBlocks + j]);
-                    } else {
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+                    for (int j = 0; j < BB; ++j) {
+                        if constexpr (KIND == kMX) {
+                            // k-step ks covers 32-blocks 2 ks and 2 ks + 1 of the
+                            // k-tile: byte 2 ks of the (pre-shifted) scale word.
+                            if (ks == 0)
+                                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                                    fa[i], fb[j], acc[i][j], 0, 0, 0, scl[i], 0, scl[kBlocks + j]);
+                            else
+                                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                                    fa[i], fb[j], acc[i][j], 0, 0, 2, scl[i], 2, scl[kBlocks + j]);
+                        } else {
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+                        }
                     }
-                }
+            }
         };
 
         // ---- prologue: k-tiles 0 .. S-2 into stages 0 .. S-2 --------------
@@ -972,6 +995,12 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(Args a) {
             read_frags(std::integral_constant<int, 0>{}, t, Fa[t], Fb[t]);
         });
         read_scales(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
+        // Let the first fragments land here, once per tile: the compiler's
+        // wait analysis merges the state at the loop entry with the state at
+        // the end of an iteration, and prologue reads left in flight (issued
+        // in no particular order) would make it wait for all reads at the top
+        // of every iteration.
+        wait_lgkm0();
 
         // One k-tile held in stage s; meanwhile the DMA of k-tile kt + S - 1
         // fills stage s - 1 (freed by the barrier that closed k-tile kt - 1).
@@ -1017,7 +1046,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(Args a) {
                     }
                     mfma(ks, ca, cb, sc);
                     if constexpr (MF == 16)
-                        interleave_step16<KIND == kNN ? 2 : 1, d1 - d0>();
+                        interleave_step16<KIND == kNN ? 24 : 16, d1 - d0>();
                     else
                         interleave_step<NR, d1 - d0 + ((SG > 1 && ks == 0 && q % SG == 0) ? 2 : 0), NMF>();
                     // keep every MFMA of this step ahead of the closing wait
@@ -1049,7 +1078,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(Args a) {
                         mfma(ks, ca, cb, sc);
                     }
                     if constexpr (MF == 16)
-                        interleave_step16<KIND == kNN ? 2 : 1, d1 - d0 + E>();
+                        interleave_step16<KIND == kNN ? 24 : 16, d1 - d0 + E>();
                     else
                         interleave_step<NR, d1 - d0 + E, NMF>();
                     __builtin_amdgcn_sched_barrier(0);
@@ -1062,7 +1091,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(Args a) {
                     });
                     mfma(ks, ca, cb, sc);
                     if constexpr (MF == 16)
-                        interleave_step16<KIND == kNN ? 2 : 1, d1 - d0>();
+                        interleave_step16<KIND == kNN ? 24 : 16, d1 - d0>();
                     else
                         interleave_step<NR, d1 - d0, NMF>();
                     __builtin_amdgcn_sched_barrier(0);
