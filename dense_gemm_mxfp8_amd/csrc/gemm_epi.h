@@ -56,4 +56,45 @@ __device__ __forceinline__ void store(void* C, int64_t ldc, const Params& e, int
     else ((float*)C)[off] = t;
 }
 
+// Four consecutive elements of one row of C, columns col .. col + 3.  With
+// `vec` (C's base and row pitch such that element (row, col) with col % 4 ==
+// 0 is aligned to 4 elements) they go out as one 16-, 8- or 4-byte store.
+__device__ __forceinline__ void store4(void* C, int64_t ldc, const Params& e, int row, int col, float a0, float a1,
+                                       float a2, float a3, bool vec) {
+    float t[4] = {a0, a1, a2, a3};
+    if (e.on) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) t[c] = apply(e, t[c], row, col + c);
+    }
+    const int64_t off = (int64_t)row * ldc + col;
+    if (!vec) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            if (e.out == kBF16) ((uint16_t*)C)[off + c] = to_bf16(t[c]);
+            else if (e.out == kE4M3) ((uint8_t*)C)[off + c] = to_e4m3(t[c]);
+            else ((float*)C)[off + c] = t[c];
+        }
+        return;
+    }
+    if (e.out == kBF16) {
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+        const u32x2 v = {(uint32_t)to_bf16(t[0]) | ((uint32_t)to_bf16(t[1]) << 16),
+                         (uint32_t)to_bf16(t[2]) | ((uint32_t)to_bf16(t[3]) << 16)};
+        *(u32x2*)((uint16_t*)C + off) = v;
+    } else if (e.out == kE4M3) {
+        *(uint32_t*)((uint8_t*)C + off) = (uint32_t)to_e4m3(t[0]) | ((uint32_t)to_e4m3(t[1]) << 8) |
+                                          ((uint32_t)to_e4m3(t[2]) << 16) | ((uint32_t)to_e4m3(t[3]) << 24);
+    } else {
+        typedef float f32x4 __attribute__((ext_vector_type(4)));
+        *(f32x4*)((float*)C + off) = f32x4{t[0], t[1], t[2], t[3]};
+    }
+}
+
+// Whether store4 may use one vector store: C's base aligned to 4 elements and
+// a row pitch that is a multiple of 4 elements.
+__device__ __forceinline__ bool vec4_ok(const void* C, int64_t ldc, const Params& e) {
+    const int esz = e.out == kBF16 ? 2 : e.out == kE4M3 ? 1 : 4;
+    return ((uintptr_t)C % (4 * esz)) == 0 && (ldc % 4) == 0;
+}
+
 }  // namespace epi

@@ -479,16 +479,13 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
     const int64_t step = (int64_t)gridDim.x * blockDim.x;
     if ((N & 3) == 0) {
         typedef float f32x4 __attribute__((ext_vector_type(4)));
+        const bool vec = epi::vec4_ok(C, ldc, e);
         for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < plane / 4; q += step) {
             f32x4 acc = *(const f32x4*)(W + 4 * q);
             for (int r = 1; r < splits; ++r) acc += *(const f32x4*)(W + r * plane + 4 * q);
             const int row = (int)(4 * q / N);
             const int col = (int)(4 * q - (int64_t)row * N);
-            const float v0 = acc[0], v1 = acc[1], v2 = acc[2], v3 = acc[3];
-            epi::store(C, ldc, e, row, col, v0);
-            epi::store(C, ldc, e, row, col + 1, v1);
-            epi::store(C, ldc, e, row, col + 2, v2);
-            epi::store(C, ldc, e, row, col + 3, v3);
+            epi::store4(C, ldc, e, row, col, acc[0], acc[1], acc[2], acc[3], vec);
         }
         return;
     }
@@ -522,6 +519,7 @@ __global__ __launch_bounds__(256) void tile_reduce_kernel(fast::Args a, int spli
     const int m0 = tm * kT, n0 = tn * kT;
     const int64_t plane = (int64_t)a.tiles_per_split * kT * kT;
     const float* blk = a.part + (int64_t)i * kT * kT;
+    const bool vec = epi::vec4_ok(C, ldc, e);
     for (int v = threadIdx.x; v < 16 * kT / 4; v += blockDim.x) {
         const int row = 16 * q + v / (kT / 4), col = 4 * (v % (kT / 4));
         if (m0 + row >= a.M || n0 + col >= a.N) continue;
@@ -529,10 +527,13 @@ __global__ __launch_bounds__(256) void tile_reduce_kernel(fast::Args a, int spli
         f32x4 acc = *(const f32x4*)(blk + off);
         for (int r = 1; r < splits; ++r) acc += *(const f32x4*)(blk + r * plane + off);
         const float v0 = acc[0], v1 = acc[1], v2 = acc[2], v3 = acc[3];
+        if (n0 + col + 3 < a.N) {
+            epi::store4(C, ldc, e, m0 + row, n0 + col, v0, v1, v2, v3, vec);
+            continue;
+        }
         epi::store(C, ldc, e, m0 + row, n0 + col, v0);
         if (n0 + col + 1 < a.N) epi::store(C, ldc, e, m0 + row, n0 + col + 1, v1);
         if (n0 + col + 2 < a.N) epi::store(C, ldc, e, m0 + row, n0 + col + 2, v2);
-        if (n0 + col + 3 < a.N) epi::store(C, ldc, e, m0 + row, n0 + col + 3, v3);
     }
 }
 
