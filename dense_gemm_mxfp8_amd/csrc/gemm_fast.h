@@ -435,16 +435,18 @@ __device__ __forceinline__ void store_c(const Args& a, const f32x16 (&acc)[kBloc
 // of the 32 columns and, in the other, those of the odd g: every store
 // instruction then writes two whole 128-byte row segments, as the 32 x 32
 // form does, so non-temporal stores still write whole lines.
-template <int AUX>
-__device__ __forceinline__ void store_c16_aux(const Args& a, const f32x4 (&acc)[8][8], int m0w, int n0w, int lane) {
+template <int AUX, bool AT = false>
+__device__ __forceinline__ void store_c16_aux(const Args& a, const f32x4 (&acc)[8][8], int m0w, int n0w, int lane,
+                                              float* cw = nullptr, int cld = 0) {
     const int rlim = a.M - m0w;
     const int clim = a.N - n0w;
     if (rlim <= 0 || clim <= 0) return;
     const int rows = rlim < kWaveTile ? rlim : kWaveTile;
     const int cols = clim < kWaveTile ? clim : kWaveTile;
-    const int ldc4 = (int)a.ldc * 4;
+    const int ldc4 = (int)(AT ? cld : a.ldc) * 4;
     const __amdgpu_buffer_rsrc_t rc =
-        make_rsrc(a.C + (int64_t)m0w * a.ldc + n0w, ((int64_t)(rows - 1) * a.ldc + cols) * 4);
+        AT ? make_rsrc(cw, ((int64_t)(rows - 1) * cld + cols) * 4)
+           : make_rsrc(a.C + (int64_t)m0w * a.ldc + n0w, ((int64_t)(rows - 1) * a.ldc + cols) * 4);
     // lanes 32..63 hold the rows 8 below lanes 0..31
     const int voff = ((lane >> 5) * 8) * ldc4 + 4 * (lane & 31);
     // The swap reads other lanes, so it runs with every lane active: a lane
@@ -470,10 +472,100 @@ __device__ __forceinline__ void store_c16_aux(const Args& a, const f32x4 (&acc)[
     }
 }
 
-__device__ __forceinline__ void store_c16(const Args& a, const f32x4 (&acc)[8][8], int m0w, int n0w, int lane) {
-    if (a.c_pol == kCStoreStream) store_c16_aux<kAuxStream>(a, acc, m0w, n0w, lane);
-    else if (a.c_pol == kCStoreDevice) store_c16_aux<kAuxDevice>(a, acc, m0w, n0w, lane);
-    else store_c16_aux<0>(a, acc, m0w, n0w, lane);
+// The fused epilogue (gemm_epi.h) on the 16 x 16 layout: each lane applies
+// t = acc * rs[row] * cs[col] + bias[col] to its own elements (rows
+// 16 i + 4 (l / 16) + r of column 16 j + l % 16, with the tile's scales and
+// biases from their LDS copy ev, as in store_c_fused) and converts them to
+// OUT; the permlane16 swap then regroups them as in store_c16_aux, so every
+// store instruction writes 32 consecutive columns of two rows.
+template <int AUX, int OUT>
+__device__ __forceinline__ void store_c16_fused(const Args& a, const f32x4 (&acc)[8][8], int m0w, int n0w, int lane,
+                                                const float FAST_LDS* ev, int evr, int evc) {
+    const int rlim = a.M - m0w;
+    const int clim = a.N - n0w;
+    if (rlim <= 0 || clim <= 0) return;
+    const int rows = rlim < kWaveTile ? rlim : kWaveTile;
+    const int cols = clim < kWaveTile ? clim : kWaveTile;
+    constexpr int ESZ = OUT == epi::kF32 ? 4 : OUT == epi::kBF16 ? 2 : 1;
+    const int ldcb = (int)a.ldc * ESZ;
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc((const uint8_t*)a.C + ((int64_t)m0w * a.ldc + n0w) * ESZ,
+                                                ((int64_t)(rows - 1) * a.ldc + cols) * ESZ);
+    const int voff = ((lane >> 5) * 8) * ldcb + ESZ * (lane & 31);
+    constexpr int kOut = 0x7ffffff0;  // a dropped store, as in store_c16_aux
+    const bool has_r = a.epi.rs != nullptr, has_c = a.epi.cs != nullptr, has_b = a.epi.bias != nullptr;
+    const int g = lane >> 4, p = lane & 15;
+    float cf[8], cb[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        cf[j] = ev[256 + evc + 16 * j + p];
+        cb[j] = ev[512 + evc + 16 * j + p];
+    }
+    auto conv = [&](float t, int j, float rf) -> uint32_t {
+        if (has_r) t *= rf;
+        if (has_c) t *= cf[j];
+        if (has_b) t += cb[j];
+        if constexpr (OUT == epi::kBF16) return epi::to_bf16(t);
+        else if constexpr (OUT == epi::kE4M3) return epi::to_e4m3(t);
+        else return __builtin_bit_cast(uint32_t, t);
+    };
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        float rf[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) rf[r] = ev[evr + 16 * i + 4 * g + r];
+#pragma unroll
+        for (int jp = 0; jp < 4; ++jp) {
+            const int vo = (32 * jp + (lane & 31) < cols) ? voff + 32 * ESZ * jp : kOut;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float x = acc[i][2 * jp][r], y = acc[i][2 * jp + 1][r];
+                const auto sw = __builtin_amdgcn_permlane16_swap(conv(x, 2 * jp, rf[r]), conv(y, 2 * jp + 1, rf[r]),
+                                                                 false, false);
+                const int r0 = (16 * i + r) * ldcb, r1 = (16 * i + 4 + r) * ldcb;
+                if constexpr (OUT == epi::kBF16) {
+                    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)sw[0], rc, vo, r0, AUX);
+                    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)sw[1], rc, vo, r1, AUX);
+                } else if constexpr (OUT == epi::kE4M3) {
+                    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sw[0], rc, vo, r0, AUX);
+                    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sw[1], rc, vo, r1, AUX);
+                } else {
+                    __builtin_amdgcn_raw_buffer_store_b32(sw[0], rc, vo, r0, AUX);
+                    __builtin_amdgcn_raw_buffer_store_b32(sw[1], rc, vo, r1, AUX);
+                }
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// The 16 x 16 layout's epilogue.  FUSED: the fused epilogue; cw / cld (plain
+// only): a split-K partial's destination and row pitch, stored cached (null:
+// C under a.c_pol), as in store_c.
+template <bool FUSED = false>
+__device__ __forceinline__ void store_c16(const Args& a, const f32x4 (&acc)[8][8], int m0w, int n0w, int lane,
+                                          const float FAST_LDS* ev = nullptr, int evr = 0, int evc = 0,
+                                          float* cw = nullptr, int cld = 0) {
+    if constexpr (FUSED) {
+        const bool dev = a.c_pol == kCStoreDevice;
+        if (a.epi.out == epi::kBF16) {
+            if (dev) store_c16_fused<kAuxDevice, epi::kBF16>(a, acc, m0w, n0w, lane, ev, evr, evc);
+            else store_c16_fused<0, epi::kBF16>(a, acc, m0w, n0w, lane, ev, evr, evc);
+        } else if (a.epi.out == epi::kE4M3) {
+            if (dev) store_c16_fused<kAuxDevice, epi::kE4M3>(a, acc, m0w, n0w, lane, ev, evr, evc);
+            else store_c16_fused<0, epi::kE4M3>(a, acc, m0w, n0w, lane, ev, evr, evc);
+        } else if (a.c_pol == kCStoreStream) {
+            store_c16_fused<kAuxStream, epi::kF32>(a, acc, m0w, n0w, lane, ev, evr, evc);
+        } else if (dev) {
+            store_c16_fused<kAuxDevice, epi::kF32>(a, acc, m0w, n0w, lane, ev, evr, evc);
+        } else {
+            store_c16_fused<0, epi::kF32>(a, acc, m0w, n0w, lane, ev, evr, evc);
+        }
+    } else {
+        if (cw != nullptr) store_c16_aux<0, true>(a, acc, m0w, n0w, lane, cw, cld);
+        else if (a.c_pol == kCStoreStream) store_c16_aux<kAuxStream>(a, acc, m0w, n0w, lane);
+        else if (a.c_pol == kCStoreDevice) store_c16_aux<kAuxDevice>(a, acc, m0w, n0w, lane);
+        else store_c16_aux<0>(a, acc, m0w, n0w, lane);
+    }
 }
 
 // Compile-time loop: f(integral_constant<int, B>), ..., f(integral_constant<int, E-1>).
@@ -571,7 +663,7 @@ template <int KIND, int RB, int S, bool TAIL, int SG = 1, int E = 0, int D = 0, 
           bool SPLIT = false, bool DYN = false, int LA = 1, int MF = 32>
 __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(Args a) {
     static_assert(NW == 4 || (NW == 8 && KIND != kMX), "8 waves: bf16 only");
-    static_assert(MF == 32 || (MF == 16 && KIND != kMX && NW == 4 && !FUSED && !SPLIT && !DYN && LA == 1),
+    static_assert(MF == 32 || (MF == 16 && KIND != kMX && NW == 4 && LA == 1),
                   "16 x 16 MFMAs: plain bf16 products, 4 waves");
     static_assert(!SPLIT || (!FUSED && NW == 4), "split-K: plain fp32 partial stores, 4 waves");
     static_assert(!SPLIT || KIND != kMX || SG > 1, "MX split-K: the scale-ring pipeline");
@@ -1146,11 +1238,15 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(Args a) {
                 cw = a.C + (int64_t)(m0 + wm * kWaveTile + (-1 - pld) * a.M) * a.ldc + n0 + wn * WTN;
                 cld = (int)a.ldc;
             }
-            store_c<NBJ, false>(a, acc, m0 + wm * kWaveTile, n0 + wn * WTN, h, l32, nullptr, 0, 0, cw, cld,
-                                pld == 0);
+            if constexpr (MF == 16)
+                store_c16(a, acc, m0 + wm * kWaveTile, n0 + wn * WTN, lane, nullptr, 0, 0, cw, cld);
+            else
+                store_c<NBJ, false>(a, acc, m0 + wm * kWaveTile, n0 + wn * WTN, h, l32, nullptr, 0, 0, cw, cld,
+                                    pld == 0);
         } else {
             if constexpr (MF == 16)
-                store_c16(a, acc, m0 + wm * kWaveTile, n0 + wn * WTN, lane);
+                store_c16<FUSED>(a, acc, m0 + wm * kWaveTile, n0 + wn * WTN, lane, (const float FAST_LDS*)evl,
+                                 wm * kWaveTile, wn * WTN);
             else
                 store_c<NBJ, FUSED>(a, acc, m0 + wm * kWaveTile, n0 + wn * WTN, h, l32, (const float FAST_LDS*)evl,
                                     wm * kWaveTile, wn * WTN);
@@ -1194,8 +1290,11 @@ inline int fast_grid(Args& a, int cus) {
     return grid;
 }
 
-// The plain bf16 product (fp32 output, NT or NN) on the 256 x 256
-// direct-load kernel with 16 x 16 x 32 MFMAs; defined in gemm_mf16.hip.
-int launch_fast_mf16(bool nt, Args a, int cus, hipStream_t stream, int group_m);
+// Launch of a bf16 instance of the 256 x 256 direct-load kernel with
+// 16 x 16 x 32 MFMAs (two stages of 128-byte k-rows, 8 DMA instructions of
+// k-tile t+2 after the barrier of k-tile t, the rest over one k-step) on
+// `grid` workgroups; the instances are compiled in gemm_mf16.hip.
+template <int KIND, bool TAIL, bool FUSED, bool SPLIT, bool DYN>
+void launch_mf16(int grid, hipStream_t stream, const Args& a);
 
 }  // namespace fast

@@ -24,26 +24,29 @@
 
 namespace fast {
 
-int launch_fast_mf16(bool nt, Args a, int cus, hipStream_t stream, int group_m) {
-    fast_tiles(a, group_m, 64);
-    const int grid = fast_grid(a, cus);
-    const bool tail = a.kt_total > a.kt_full;
-    if (nt) {
-        if (tail)
-            hipLaunchKernelGGL((gemm_fast_kernel<kNT, 128, 2, true, 1, 8, 1, 4, false, false, false, 1, 16>),
-                               dim3(grid), dim3(256), 0, stream, a);
-        else
-            hipLaunchKernelGGL((gemm_fast_kernel<kNT, 128, 2, false, 1, 8, 1, 4, false, false, false, 1, 16>),
-                               dim3(grid), dim3(256), 0, stream, a);
-    } else {
-        if (tail)
-            hipLaunchKernelGGL((gemm_fast_kernel<kNN, 128, 2, true, 1, 8, 1, 4, false, false, false, 1, 16>),
-                               dim3(grid), dim3(256), 0, stream, a);
-        else
-            hipLaunchKernelGGL((gemm_fast_kernel<kNN, 128, 2, false, 1, 8, 1, 4, false, false, false, 1, 16>),
-                               dim3(grid), dim3(256), 0, stream, a);
-    }
-    return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
+template <int KIND, bool TAIL, bool FUSED, bool SPLIT, bool DYN>
+void launch_mf16(int grid, hipStream_t stream, const Args& a) {
+    hipLaunchKernelGGL((gemm_fast_kernel<KIND, 128, 2, TAIL, 1, 8, 1, 4, FUSED, SPLIT, DYN, 1, 16>), dim3(grid),
+                       dim3(256), 0, stream, a);
 }
+
+// plain fp32 product, fused epilogue, split-K units, dynamic schedule; each
+// with and without a partial last k-tile
+template void launch_mf16<kNT, false, false, false, false>(int, hipStream_t, const Args&);
+template void launch_mf16<kNT, true, false, false, false>(int, hipStream_t, const Args&);
+template void launch_mf16<kNN, false, false, false, false>(int, hipStream_t, const Args&);
+template void launch_mf16<kNN, true, false, false, false>(int, hipStream_t, const Args&);
+template void launch_mf16<kNT, false, true, false, false>(int, hipStream_t, const Args&);
+template void launch_mf16<kNT, true, true, false, false>(int, hipStream_t, const Args&);
+template void launch_mf16<kNN, false, true, false, false>(int, hipStream_t, const Args&);
+template void launch_mf16<kNN, true, true, false, false>(int, hipStream_t, const Args&);
+template void launch_mf16<kNT, false, false, true, false>(int, hipStream_t, const Args&);
+template void launch_mf16<kNT, true, false, true, false>(int, hipStream_t, const Args&);
+template void launch_mf16<kNN, false, false, true, false>(int, hipStream_t, const Args&);
+template void launch_mf16<kNN, true, false, true, false>(int, hipStream_t, const Args&);
+template void launch_mf16<kNT, false, false, false, true>(int, hipStream_t, const Args&);
+template void launch_mf16<kNT, true, false, false, true>(int, hipStream_t, const Args&);
+template void launch_mf16<kNN, false, false, false, true>(int, hipStream_t, const Args&);
+template void launch_mf16<kNN, true, false, false, true>(int, hipStream_t, const Args&);
 
 }  // namespace fast

@@ -11,9 +11,12 @@
 // (TMA, TMEM, mbarriers, clusters); none of that exists on CDNA4, so the
 // kernels here are built from gfx950 primitives instead:
 //
-//   * global->LDS tile loads: `global_load_lds_dwordx4` (16 bytes per lane,
-//     written straight into LDS, no VGPR round trip) when rows are 16-byte
-//     aligned, else predicated element loads through VGPRs;
+//   * global->LDS tile loads: 16 bytes per lane written straight into LDS
+//     (no VGPR round trip) when rows are 16-byte aligned -- `buffer_load_
+//     dwordx4 ... lds` against a per-tile buffer descriptor in the 256 x 256
+//     kernels (gemm_fast.h), `global_load_lds_dwordx4` in the generic kernel
+//     of this file -- else 16-byte loads into VGPRs and `ds_write_b128`
+//     (gemm_reg.h) or predicated element loads (the generic kernel);
 //   * LDS layout: every operand row holds 128 bytes of K (64 bf16 or 128
 //     fp8); its eight 16-byte chunks are XOR-swizzled with the row index so
 //     that the fragment reads of 8 consecutive rows hit 8 different bank
@@ -29,9 +32,10 @@
 //     out of LDS so the B fragment arrives K-contiguous per lane;
 //   * a persistent grid with a static strided tile walk, grouped raster order
 //     and an XCD-aware remap of workgroup ids;
-//   * tails: rows past M / columns past N re-read the last valid row or
-//     column (finite data, never stored); the partial last k-tile is loaded
-//     with element predicates and zero fill;
+//   * tails: rows past M / columns past N lie outside the per-tile
+//     descriptors and load as zero (the generic kernel re-reads the last
+//     valid row or column: finite data, never stored); the partial last
+//     k-tile is loaded with element predicates and zero fill;
 //   * epilogue: predicated fp32 stores straight from the accumulators.
 //
 // Lane layouts used below.  They are not checked one instruction at a time:
@@ -714,6 +718,22 @@ int launch_fast(fast::Args a, int cus, hipStream_t stream, int group_m = 0, int 
         a.num_tiles = a.dp_units + a.tiles_per_split * splits;
     }
     const int grid = fast::fast_grid(a, cus);
+    if constexpr (MF == 16) {
+        static_assert(KIND != fast::kMX && RB == 128 && S == 2 && SG == 1 && E == 8 && D == 1 && NW == 4 && LA == 1,
+                      "the 16 x 16 x 32 instances of gemm_mf16.hip");
+        const bool tail = a.kt_total > a.kt_full;
+        if constexpr (DYN) {
+            if (a.xcd_remap) {
+                hipLaunchKernelGGL(zero_words_kernel, dim3(1), dim3(256), 0, stream, a.tile_ctr, 256);
+                if (tail) fast::launch_mf16<KIND, true, FUSED, false, true>(grid, stream, a);
+                else fast::launch_mf16<KIND, false, FUSED, false, true>(grid, stream, a);
+                return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
+            }
+        }
+        if (tail) fast::launch_mf16<KIND, true, FUSED, SPLIT, false>(grid, stream, a);
+        else fast::launch_mf16<KIND, false, FUSED, SPLIT, false>(grid, stream, a);
+        return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
+    }
     if constexpr (DYN) {
         if (a.xcd_remap) {
             hipLaunchKernelGGL(zero_words_kernel, dim3(1), dim3(256), 0, stream, a.tile_ctr, 256);
@@ -734,6 +754,36 @@ int launch_fast(fast::Args a, int cus, hipStream_t stream, int group_m = 0, int 
                            dim3(64 * NW), 0, stream, a);
     }
     return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
+}
+
+// The bf16 instances the library runs: 16 x 16 x 32 MFMAs (gemm_mf16.hip).
+// Measurement builds run the 32 x 32 x 16 form instead under
+// LIBGEMM_VARIANT=...m32 (the fused, split-K and dynamic entry points: 6 DMA
+// instructions early, the rest over two k-steps).
+template <int KIND, bool FUSED = false, bool SPLIT = false, bool DYN = false>
+int launch_bf16_16(fast::Args a, int cus, hipStream_t s, int group_m, int splits = 1) {
+#ifdef LIBGEMM_MEASURE
+    if (env_variant().mfma == 32)
+        return launch_fast<KIND, 128, 2, 1, 6, 2, 4, FUSED, SPLIT, DYN>(a, cus, s, group_m, splits);
+#endif
+    return launch_fast<KIND, 128, 2, 1, 8, 1, 4, FUSED, SPLIT, DYN, 1, 16>(a, cus, s, group_m, splits);
+}
+
+// The split-K units of the fast kernel.  With M or N at most 32 every tile is
+// at most an eighth full in one dimension and the units mostly stream the
+// other operand; there the 32 x 32 x 16 form measured faster (NT, K = 8192,
+// 8 ranges, two boxes: 16 x 8192 29.8-31.8 us against 33.3-34.0 us with the
+// 16 x 16 form, 8192 x 16 31.0 against 39.2 us), while from 64 rows on the
+// two forms traded places between boxes and the 16 x 16 form led at
+// 1024 x 1024 x 32768 (68-70 against 70-73 us).
+int launch_split_bf16(bool nt, int64_t M, int64_t N, const fast::Args& a, int cus, hipStream_t s, int g,
+                      int splits) {
+    if (M <= 32 || N <= 32) {
+        return nt ? launch_fast<fast::kNT, 128, 2, 1, 6, 2, 4, false, true>(a, cus, s, g, splits)
+                  : launch_fast<fast::kNN, 128, 2, 1, 6, 2, 4, false, true>(a, cus, s, g, splits);
+    }
+    return nt ? launch_bf16_16<fast::kNT, false, true>(a, cus, s, g, splits)
+              : launch_bf16_16<fast::kNN, false, true>(a, cus, s, g, splits);
 }
 
 // Whether the fast kernel's preconditions hold (see gemm_fast.h).
@@ -803,8 +853,8 @@ int launch_fast_bf16(bool nt, const fast::Args& a, int cus, hipStream_t s) {
     // fused epilogue: the default pipelines only (the variants below are
     // measurement switches of the plain product)
     if (a.epi.on) {
-        if (nt) return launch_fast<fast::kNT, 128, 2, 1, 6, 2, 4, true>(a, cus, s, g);
-        return launch_fast<fast::kNN, 128, 2, 1, 6, 2, 4, true>(a, cus, s, g);
+        if (nt) return launch_bf16_16<fast::kNT, true>(a, cus, s, g);
+        return launch_bf16_16<fast::kNN, true>(a, cus, s, g);
     }
     if (nt) {
 #ifdef LIBGEMM_MEASURE
@@ -823,7 +873,7 @@ int launch_fast_bf16(bool nt, const fast::Args& a, int cus, hipStream_t s) {
 #endif
         // default: 16 x 16 x 32 MFMAs (gemm_mf16.hip; 8192^3 on one box:
         // 718-720 us against 759-762 us for the 32 x 32 form)
-        return fast::launch_fast_mf16(true, a, cus, s, g);
+        return launch_bf16_16<fast::kNT>(a, cus, s, g);
     }
 #ifdef LIBGEMM_MEASURE
     if (v.rb == 64 && v.stages == 4) return launch_fast<fast::kNN, 64, 4>(a, cus, s, g);
@@ -835,7 +885,7 @@ int launch_fast_bf16(bool nt, const fast::Args& a, int cus, hipStream_t s) {
 #endif
     // default: 16 x 16 x 32 MFMAs, as NT (4096^3 on one box: 101.5-103.3 us
     // against 103.8-104.3 us)
-    return fast::launch_fast_mf16(false, a, cus, s, g);
+    return launch_bf16_16<fast::kNN>(a, cus, s, g);
 }
 
 // ---------------------------------------------------------------------------
@@ -1228,8 +1278,7 @@ int splitk_dispatch(bool nt, int64_t M, int64_t N, int64_t K, const void* A, int
         a.tile0 = (int)p.dp;
         a.tiles_per_split = (int)p.rem;
         const int g = env_variant().group;
-        rc = nt ? launch_fast<fast::kNT, 128, 2, 1, 6, 2, 4, false, true>(a, dev.cus, s, g, p.splits)
-                : launch_fast<fast::kNN, 128, 2, 1, 6, 2, 4, false, true>(a, dev.cus, s, g, p.splits);
+        rc = launch_split_bf16(nt, M, N, a, dev.cus, s, g, p.splits);
         if (rc != GEMM_OK) return rc;
         // the same tile geometry as launch_fast's
         a.tiles_m = (a.M + fast::kTile - 1) / fast::kTile;
@@ -1246,8 +1295,7 @@ int splitk_dispatch(bool nt, int64_t M, int64_t N, int64_t K, const void* A, int
         a.kslice = (int)p.kslice;
         a.c_pol = fast::kCStoreCached;  // the partial sums are read back at once
         const int g = env_variant().group;
-        rc = nt ? launch_fast<fast::kNT, 128, 2, 1, 6, 2, 4, false, true>(a, dev.cus, s, g, p.splits)
-                : launch_fast<fast::kNN, 128, 2, 1, 6, 2, 4, false, true>(a, dev.cus, s, g, p.splits);
+        rc = launch_split_bf16(nt, M, N, a, dev.cus, s, g, p.splits);
     }
     if (rc != GEMM_OK) return rc;
     int64_t blocks = (M * N / 4 + 255) / 256;
@@ -1303,8 +1351,8 @@ int dynamic_dispatch(bool nt, int64_t M, int64_t N, int64_t K, const void* A, in
         a.tile_ctr = (int*)ws;
         hipStream_t s = (hipStream_t)stream;
         const int g = env_variant().group;
-        return nt ? launch_fast<fast::kNT, 128, 2, 1, 6, 2, 4, false, false, true>(a, dev.cus, s, g)
-                  : launch_fast<fast::kNN, 128, 2, 1, 6, 2, 4, false, false, true>(a, dev.cus, s, g);
+        return nt ? launch_bf16_16<fast::kNT, false, false, true>(a, dev.cus, s, g)
+                  : launch_bf16_16<fast::kNN, false, false, true>(a, dev.cus, s, g);
     }
     return bf16_dispatch(nt, M, N, K, A, lda, B, ldb, C, ldc, kPlain, stream);
 }

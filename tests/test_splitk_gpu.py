@@ -84,8 +84,10 @@ def _prob(M, N, K, colmajor, exact, seed):
 
 # (M, N, K, b_colmajor, splits): 256 x 256 partial kernel.  K = 4104 and 3000 end
 # inside a k-tile (the last range carries the partial k-tile); 0 = the plan.
+# M or N at most 32 takes the 32 x 32 MFMA instance, the others the 16 x 16 one.
 FAST = [(1000, 777, 4104, True, 0), (1000, 777, 4104, True, 3), (513, 1032, 3000, False, 0),
-        (513, 1032, 3000, False, 5), (300, 520, 1024, True, 2), (256, 256, 640, False, 7)]
+        (513, 1032, 3000, False, 5), (300, 520, 1024, True, 2), (256, 256, 640, False, 7),
+        (24, 1000, 4104, True, 3), (700, 24, 3000, False, 4)]
 
 
 @pytest.mark.parametrize("case", FAST, ids=lambda c: f"{c[0]}x{c[1]}x{c[2]}_{'nt' if c[3] else 'nn'}_s{c[4]}")
