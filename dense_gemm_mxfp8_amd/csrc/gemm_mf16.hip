@@ -1,5 +1,6 @@
-// gemm_mf16.hip -- the plain bf16 product (fp32 output, NT and NN) on the
-// 256 x 256 direct-load kernel of gemm_fast.h with 16 x 16 x 32 MFMAs.
+// gemm_mf16.hip -- the bf16 instances (NT and NN: plain fp32 product, fused
+// epilogue, split-K units, dynamic schedule) of the 256 x 256 direct-load
+// kernel of gemm_fast.h with 16 x 16 x 32 MFMAs.
 //
 // It is a translation unit of its own because it is compiled without the
 // machine scheduler that runs before register allocation (-mllvm
