@@ -25,17 +25,21 @@
 //     object and the K loop is unrolled by S, so the compiler can tell the
 //     in-flight DMA writes of later stages apart from the reads of the
 //     current one and does not serialise them.
-//   * MFMA fragments are double-buffered across k-steps: the LDS reads of
-//     step s + 1 are in flight while step s's MFMAs run.
+//   * matrix cores: bf16 instances run v_mfma_f32_16x16x32_bf16 over the
+//     wave tile as 8 x 8 blocks in Z order (MF = 16) or
+//     v_mfma_f32_32x32x16_bf16 as 4 x 4 blocks (MF = 32); MX runs
+//     v_mfma_scale_f32_32x32x64_f8f6f4.  The fragments are double-buffered
+//     across k-steps: the LDS reads of step s + 1 are in flight while step
+//     s's MFMAs run.
 //   * the last, partial k-tile (K mod BK != 0) is loaded through registers
 //     with buffer loads, its bytes past K zeroed.
-//   * epilogue: fp32 buffer stores straight from the
-//     accumulators (store_c).
+//   * epilogue: buffer stores straight from the accumulators (store_c,
+//     store_c16), fp32 or through the fused epilogue of gemm_epi.h.
 //
 // Fast-path preconditions (checked on the host): 16-byte aligned A and B,
 // leading dimensions that keep every row 16-byte aligned, 256 rows of either
 // operand spanning less than 2 GiB, and for row-major B, N % 8 == 0.  The MX
-// variant also needs K % 128 == 0.
+// variant also needs K % 64 == 0 and 2-byte aligned scales.
 
 #pragma once
 
