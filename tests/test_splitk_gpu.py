@@ -87,7 +87,7 @@ def _prob(M, N, K, colmajor, exact, seed):
 # M or N at most 32 takes the 32 x 32 MFMA instance, the others the 16 x 16 one.
 FAST = [(1000, 777, 4104, True, 0), (1000, 777, 4104, True, 3), (513, 1032, 3000, False, 0),
         (513, 1032, 3000, False, 5), (300, 520, 1024, True, 2), (256, 256, 640, False, 7),
-        (24, 1000, 4104, True, 3), (700, 24, 3000, False, 4)]
+        (24, 1000, 4104, True, 3), (700, 24, 3000, False, 4), (33, 1000, 4104, True, 3)]
 
 
 @pytest.mark.parametrize("case", FAST, ids=lambda c: f"{c[0]}x{c[1]}x{c[2]}_{'nt' if c[3] else 'nn'}_s{c[4]}")
