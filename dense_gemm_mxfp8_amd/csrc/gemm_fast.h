@@ -439,14 +439,14 @@ __device__ __forceinline__ void store_c(const Args& a, const f32x16 (&acc)[kBloc
 // of the 32 columns and, in the other, those of the odd g: every store
 // instruction then writes two whole 128-byte row segments, as the 32 x 32
 // form does, so non-temporal stores still write whole lines.
-template <int AUX, bool AT = false>
-__device__ __forceinline__ void store_c16_aux(const Args& a, const f32x4 (&acc)[8][8], int m0w, int n0w, int lane,
+template <int AUX, bool AT = false, int BB = 8>
+__device__ __forceinline__ void store_c16_aux(const Args& a, const f32x4 (&acc)[8][BB], int m0w, int n0w, int lane,
                                               float* cw = nullptr, int cld = 0) {
     const int rlim = a.M - m0w;
     const int clim = a.N - n0w;
     if (rlim <= 0 || clim <= 0) return;
     const int rows = rlim < kWaveTile ? rlim : kWaveTile;
-    const int cols = clim < kWaveTile ? clim : kWaveTile;
+    const int cols = clim < 16 * BB ? clim : 16 * BB;
     const int ldc4 = (int)(AT ? cld : a.ldc) * 4;
     const __amdgpu_buffer_rsrc_t rc =
         AT ? make_rsrc(cw, ((int64_t)(rows - 1) * cld + cols) * 4)
@@ -459,7 +459,7 @@ __device__ __forceinline__ void store_c16_aux(const Args& a, const f32x4 (&acc)[
     // no 32-bit wrap), which drops the store.
     constexpr int kOut = 0x7ffffff0;
 #pragma unroll
-    for (int jp = 0; jp < 4; ++jp) {
+    for (int jp = 0; jp < BB / 2; ++jp) {
         const int vo = (32 * jp + (lane & 31) < cols) ? voff + 128 * jp : kOut;
 #pragma unroll
         for (int i = 0; i < 8; ++i)
@@ -545,11 +545,12 @@ __device__ __forceinline__ void store_c16_fused(const Args& a, const f32x4 (&acc
 // The 16 x 16 layout's epilogue.  FUSED: the fused epilogue; cw / cld (plain
 // only): a split-K partial's destination and row pitch, stored cached (null:
 // C under a.c_pol), as in store_c.
-template <bool FUSED = false>
-__device__ __forceinline__ void store_c16(const Args& a, const f32x4 (&acc)[8][8], int m0w, int n0w, int lane,
+template <bool FUSED = false, int BB = 8>
+__device__ __forceinline__ void store_c16(const Args& a, const f32x4 (&acc)[8][BB], int m0w, int n0w, int lane,
                                           const float FAST_LDS* ev = nullptr, int evr = 0, int evc = 0,
                                           float* cw = nullptr, int cld = 0) {
     if constexpr (FUSED) {
+        static_assert(BB == 8, "fused epilogue: 128 x 128 wave tiles");
         const bool dev = a.c_pol == kCStoreDevice;
         if (a.epi.out == epi::kBF16) {
             if (dev) store_c16_fused<kAuxDevice, epi::kBF16>(a, acc, m0w, n0w, lane, ev, evr, evc);
@@ -565,10 +566,10 @@ __device__ __forceinline__ void store_c16(const Args& a, const f32x4 (&acc)[8][8
             store_c16_fused<0, epi::kF32>(a, acc, m0w, n0w, lane, ev, evr, evc);
         }
     } else {
-        if (cw != nullptr) store_c16_aux<0, true>(a, acc, m0w, n0w, lane, cw, cld);
-        else if (a.c_pol == kCStoreStream) store_c16_aux<kAuxStream>(a, acc, m0w, n0w, lane);
-        else if (a.c_pol == kCStoreDevice) store_c16_aux<kAuxDevice>(a, acc, m0w, n0w, lane);
-        else store_c16_aux<0>(a, acc, m0w, n0w, lane);
+        if (cw != nullptr) store_c16_aux<0, true, BB>(a, acc, m0w, n0w, lane, cw, cld);
+        else if (a.c_pol == kCStoreStream) store_c16_aux<kAuxStream, false, BB>(a, acc, m0w, n0w, lane);
+        else if (a.c_pol == kCStoreDevice) store_c16_aux<kAuxDevice, false, BB>(a, acc, m0w, n0w, lane);
+        else store_c16_aux<0, false, BB>(a, acc, m0w, n0w, lane);
     }
 }
 
@@ -600,22 +601,29 @@ __device__ __forceinline__ void interleave_step() {
     }
 }
 
-// The 64 MFMAs of a 16 x 16 x 32 k-step visit the 8 x 8 blocks of the wave
-// tile in Z order (MFMA m: A block z_row(m), B block z_col(m)), so the
-// fragments a k-step needs grow as 2 sqrt(m): by MFMA 16 only 4 A and 4 B
-// fragments.  The next step's fragments are read in the order of first use
-// (z_frag) into the other register set, spread evenly over this step's MFMAs
-// (NRD LDS reads), which leaves every read at least 40 MFMAs before the one
-// that needs it; a row-first order needed all 8 A fragments within the
-// first 8 MFMAs.  The ND DMA instructions go after every other MFMA from
-// the first.
-constexpr int z_row(int m) { return ((m >> 1) & 1) | ((m >> 2) & 2) | ((m >> 3) & 4); }
-constexpr int z_col(int m) { return (m & 1) | ((m >> 1) & 2) | ((m >> 2) & 4); }
-// The o-th fragment in order of first use: A fragments 0..7, B fragments 8..15.
+// The 8 BB MFMAs of a 16 x 16 x 32 k-step visit the 8 x BB blocks of the
+// wave tile (BB = 8, or 4 for 128 x 64 wave tiles) in Z order (MFMA m: A
+// block z_row(m), B block z_col(m)), so the fragments a k-step needs grow as
+// 2 sqrt(m): by MFMA 16 only 4 A and 4 B fragments.  The next step's
+// fragments are read in the order of first use (z_frag) into the other
+// register set, spread evenly over this step's MFMAs (NRD LDS reads), which
+// leaves every read at least 40 MFMAs (of 64) before the one that needs it;
+// a row-first order needed all 8 A fragments within the first 8 MFMAs.  The
+// ND DMA instructions go after every other MFMA from the first.
+template <int BB>
+constexpr int z_row(int m) {
+    return BB == 8 ? ((m >> 1) & 1) | ((m >> 2) & 2) | ((m >> 3) & 4) : ((m >> 1) & 1) | ((m >> 2) & 6);
+}
+template <int BB>
+constexpr int z_col(int m) {
+    return BB == 8 ? (m & 1) | ((m >> 1) & 2) | ((m >> 2) & 4) : (m & 1) | ((m >> 1) & 2);
+}
+// The o-th fragment in order of first use: A fragments 0..7, B fragments 8..8+BB-1.
+template <int BB>
 constexpr int z_frag(int o) {
     int seen = 0, n = 0;
-    for (int m = 0; m < 64; ++m) {
-        const int f[2] = {z_row(m), 8 + z_col(m)};
+    for (int m = 0; m < 8 * BB; ++m) {
+        const int f[2] = {z_row<BB>(m), 8 + z_col<BB>(m)};
         for (int x : f) {
             if ((seen >> x) & 1) continue;
             if (n++ == o) return x;
@@ -625,11 +633,11 @@ constexpr int z_frag(int o) {
     return -1;
 }
 
-template <int NRD, int ND>
+template <int NRD, int ND, int NMF = 64>
 __device__ __forceinline__ void interleave_step16() {
-    static_for<0, 64>([&](auto mc) {
+    static_for<0, NMF>([&](auto mc) {
         constexpr int m = decltype(mc)::value;
-        constexpr int nr = ((m + 1) * NRD) / 64 - (m * NRD) / 64;
+        constexpr int nr = ((m + 1) * NRD) / NMF - (m * NRD) / NMF;
         __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
         if constexpr (nr > 0) __builtin_amdgcn_sched_group_barrier(kSgDsRead, nr, 0);
         if constexpr (m % 2 == 1 && m / 2 < ND) __builtin_amdgcn_sched_group_barrier(kSgVmem, 1, 0);
@@ -667,7 +675,7 @@ template <int KIND, int RB, int S, bool TAIL, int SG = 1, int E = 0, int D = 0, 
           bool SPLIT = false, bool DYN = false, int LA = 1, int MF = 32>
 __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(Args a) {
     static_assert(NW == 4 || (NW == 8 && KIND != kMX), "8 waves: bf16 only");
-    static_assert(MF == 32 || (MF == 16 && KIND != kMX && NW == 4 && LA == 1),
+    static_assert(MF == 32 || (MF == 16 && KIND != kMX && LA == 1),
                   "16 x 16 MFMAs: plain bf16 products, 4 waves");
     static_assert(!SPLIT || (!FUSED && NW == 4), "split-K: plain fp32 partial stores, 4 waves");
     static_assert(!SPLIT || KIND != kMX || SG > 1, "MX split-K: the scale-ring pipeline");
@@ -693,7 +701,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(Args a) {
     // MFMA blocks per wave tile: BA row blocks of A, BB column blocks of B
     // (32 x 32 blocks, or 16 x 16 with MF == 16), and the accumulator type
     constexpr int BA = MF == 16 ? 8 : kBlocks;
-    constexpr int BB = MF == 16 ? 8 : NBJ;
+    constexpr int BB = MF == 16 ? 2 * NBJ : NBJ;
     typedef typename std::conditional<MF == 16, f32x4, f32x16>::type AccT;
     // Fragments are double-buffered over the global k-step sequence; with an
     // odd step count per k-tile the buffer parity follows the k-tile parity,
@@ -941,8 +949,8 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(Args a) {
             const uint8_t FAST_LDS* base = stage_ptr(sidx);
             if constexpr (MF == 16) {
                 // in the order the MFMAs first use them (z_frag)
-                static_for<0, 16>([&](auto oc) {
-                    constexpr int f = z_frag(decltype(oc)::value);
+                static_for<0, 8 + BB>([&](auto oc) {
+                    constexpr int f = z_frag<BB>(decltype(oc)::value);
                     constexpr int j = f & 7;
                     if constexpr (f < 8) {
                         fa[j] = *(const bf16x8 FAST_LDS*)(base + a_rd[ks][0] + j * 16 * RB);
@@ -1041,8 +1049,8 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(Args a) {
         auto mfma = [&](int ks, const Frag* fa, const Frag* fb, const int* scl) {
             if constexpr (MF == 16) {
                 // Z order over the 8 x 8 blocks (interleave_step16)
-                static_for<0, 64>([&](auto mc) {
-                    constexpr int r = z_row(decltype(mc)::value), c = z_col(decltype(mc)::value);
+                static_for<0, BA * BB>([&](auto mc) {
+                    constexpr int r = z_row<BB>(decltype(mc)::value), c = z_col<BB>(decltype(mc)::value);
                     acc[r][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[r], fb[c], acc[r][c], 0, 0, 0);
                 });
             } else {
@@ -1142,7 +1150,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(Args a) {
                     }
                     mfma(ks, ca, cb, sc);
                     if constexpr (MF == 16)
-                        interleave_step16<KIND == kNN ? 24 : 16, d1 - d0>();
+                        interleave_step16<NR, d1 - d0, NMF>();
                     else
                         interleave_step<NR, d1 - d0 + ((SG > 1 && ks == 0 && q % SG == 0) ? 2 : 0), NMF>();
                     // keep every MFMA of this step ahead of the closing wait
@@ -1174,7 +1182,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(Args a) {
                         mfma(ks, ca, cb, sc);
                     }
                     if constexpr (MF == 16)
-                        interleave_step16<KIND == kNN ? 24 : 16, d1 - d0 + E>();
+                        interleave_step16<NR, d1 - d0 + E, NMF>();
                     else
                         interleave_step<NR, d1 - d0 + E, NMF>();
                     __builtin_amdgcn_sched_barrier(0);
@@ -1187,7 +1195,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(Args a) {
                     });
                     mfma(ks, ca, cb, sc);
                     if constexpr (MF == 16)
-                        interleave_step16<KIND == kNN ? 24 : 16, d1 - d0>();
+                        interleave_step16<NR, d1 - d0, NMF>();
                     else
                         interleave_step<NR, d1 - d0, NMF>();
                     __builtin_amdgcn_sched_barrier(0);
@@ -1300,5 +1308,9 @@ inline int fast_grid(Args& a, int cus) {
 // `grid` workgroups; the instances are compiled in gemm_mf16.hip.
 template <int KIND, bool TAIL, bool FUSED, bool SPLIT, bool DYN>
 void launch_mf16(int grid, hipStream_t stream, const Args& a);
+#ifdef LIBGEMM_MEASURE
+template <int KIND, bool TAIL>
+void launch_mf16_w8(int grid, hipStream_t stream, const Args& a);
+#endif
 
 }  // namespace fast

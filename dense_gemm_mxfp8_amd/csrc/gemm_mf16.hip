@@ -50,4 +50,19 @@ template void launch_mf16<kNT, true, false, false, true>(int, hipStream_t, const
 template void launch_mf16<kNN, false, false, false, true>(int, hipStream_t, const Args&);
 template void launch_mf16<kNN, true, false, false, true>(int, hipStream_t, const Args&);
 
+#ifdef LIBGEMM_MEASURE
+// Measurement builds: the plain product with 8 waves (two per SIMD, 128 x 64
+// wave tiles as 8 x 4 blocks); 4 of each wave's 8 DMA instructions of k-tile
+// t+2 after the barrier of k-tile t.
+template <int KIND, bool TAIL>
+void launch_mf16_w8(int grid, hipStream_t stream, const Args& a) {
+    hipLaunchKernelGGL((gemm_fast_kernel<KIND, 128, 2, TAIL, 1, 4, 1, 8, false, false, false, 1, 16>), dim3(grid),
+                       dim3(512), 0, stream, a);
+}
+template void launch_mf16_w8<kNT, false>(int, hipStream_t, const Args&);
+template void launch_mf16_w8<kNT, true>(int, hipStream_t, const Args&);
+template void launch_mf16_w8<kNN, false>(int, hipStream_t, const Args&);
+template void launch_mf16_w8<kNN, true>(int, hipStream_t, const Args&);
+#endif
+
 }  // namespace fast

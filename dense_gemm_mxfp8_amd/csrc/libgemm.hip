@@ -786,6 +786,18 @@ int launch_split_bf16(bool nt, int64_t M, int64_t N, const fast::Args& a, int cu
               : launch_bf16_16<fast::kNN, false, true>(a, cus, s, g, splits);
 }
 
+#ifdef LIBGEMM_MEASURE
+// The 8-wave 16 x 16 x 32 plain product (measurement builds).
+template <int KIND>
+int launch_w8_16(fast::Args a, int cus, hipStream_t s, int group_m) {
+    fast::fast_tiles(a, group_m, 64);
+    const int grid = fast::fast_grid(a, cus);
+    if (a.kt_total > a.kt_full) fast::launch_mf16_w8<KIND, true>(grid, s, a);
+    else fast::launch_mf16_w8<KIND, false>(grid, s, a);
+    return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
+}
+#endif
+
 // Whether the fast kernel's preconditions hold (see gemm_fast.h).
 bool fast_ok(int kind, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
              int64_t ldb, const void* SA, const void* SB) {
@@ -861,7 +873,8 @@ int launch_fast_bf16(bool nt, const fast::Args& a, int cus, hipStream_t s) {
         if (v.rb == 64 && v.stages == 4) return launch_fast<fast::kNT, 64, 4>(a, cus, s, g);
         // 8 waves (two per SIMD, 128 x 64 wave tiles): measured 1% slower
         // than 4 waves at 8192^3 on MI355X; kept for measurements
-        if (v.waves == 8) return launch_fast<fast::kNT, 128, 2, 1, 4, 2, 8>(a, cus, s, g);
+        if (v.waves == 8 && v.mfma == 32) return launch_fast<fast::kNT, 128, 2, 1, 4, 2, 8>(a, cus, s, g);
+        if (v.waves == 8) return launch_w8_16<fast::kNT>(a, cus, s, g);
         if (v.early == 0) return launch_fast<fast::kNT, 128, 2>(a, cus, s, g);
         if (v.lookahead == 2)
             return launch_fast<fast::kNT, 128, 2, 1, 6, 2, 4, false, false, false, 2>(a, cus, s, g);
@@ -876,6 +889,7 @@ int launch_fast_bf16(bool nt, const fast::Args& a, int cus, hipStream_t s) {
         return launch_bf16_16<fast::kNT>(a, cus, s, g);
     }
 #ifdef LIBGEMM_MEASURE
+    if (v.waves == 8) return launch_w8_16<fast::kNN>(a, cus, s, g);
     if (v.rb == 64 && v.stages == 4) return launch_fast<fast::kNN, 64, 4>(a, cus, s, g);
     if (v.rb == 128 && v.stages == 2 && v.early == 0) return launch_fast<fast::kNN, 128, 2>(a, cus, s, g);
     if (v.lookahead == 2) return launch_fast<fast::kNN, 128, 2, 1, 6, 2, 4, false, false, false, 2>(a, cus, s, g);
