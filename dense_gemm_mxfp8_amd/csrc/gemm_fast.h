@@ -601,7 +601,7 @@ __device__ __forceinline__ void interleave_step() {
     }
 }
 
-// The 8 BB MFMAs of a 16 x 16 x 32 k-step visit the 8 x BB blocks of the
+// The 8 x BB MFMAs of a 16 x 16 x 32 k-step visit the 8 x BB blocks of the
 // wave tile (BB = 8, or 4 for 128 x 64 wave tiles) in Z order (MFMA m: A
 // block z_row(m), B block z_col(m)), so the fragments a k-step needs grow as
 // 2 sqrt(m): by MFMA 16 only 4 A and 4 B fragments.  The next step's
@@ -632,6 +632,24 @@ constexpr int z_frag(int o) {
     }
     return -1;
 }
+
+// Every block once, and every fragment once in the read order.
+template <int BB>
+constexpr bool z_order_ok() {
+    int blocks[8] = {}, frags = 0;
+    for (int m = 0; m < 8 * BB; ++m) {
+        const int r = z_row<BB>(m), c = z_col<BB>(m);
+        if (r < 0 || r > 7 || c < 0 || c >= BB || ((blocks[r] >> c) & 1)) return false;
+        blocks[r] |= 1 << c;
+    }
+    for (int o = 0; o < 8 + BB; ++o) {
+        const int f = z_frag<BB>(o);
+        if (f < 0 || f >= 8 + BB || ((frags >> f) & 1)) return false;
+        frags |= 1 << f;
+    }
+    return true;
+}
+static_assert(z_order_ok<8>() && z_order_ok<4>(), "Z order of the 16 x 16 blocks");
 
 template <int NRD, int ND, int NMF = 64>
 __device__ __forceinline__ void interleave_step16() {
