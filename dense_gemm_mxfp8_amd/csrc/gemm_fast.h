@@ -686,15 +686,15 @@ __device__ __forceinline__ void interleave_step16() {
 // barrier of each k-tile one k-step earlier: bf16, two stages).
 // MF: the bf16 MFMA shape, 32 (v_mfma_f32_32x32x16_bf16, 4 x 4 blocks per
 // 128 x 128 wave tile, k-steps of 16) or 16 (v_mfma_f32_16x16x32_bf16, 8 x 8
-// blocks, k-steps of 32).  The same FLOPs and LDS bytes either way; at the
-// board's power limit the 16 x 16 form draws less power per FLOP, so the
-// clock it holds is higher.
+// blocks, or 8 x 4 for 8 waves, k-steps of 32).  The same FLOPs and LDS bytes
+// either way; at the board's power limit the 16 x 16 form draws less power
+// per FLOP, so the clock it holds is higher.
 template <int KIND, int RB, int S, bool TAIL, int SG = 1, int E = 0, int D = 0, int NW = 4, bool FUSED = false,
           bool SPLIT = false, bool DYN = false, int LA = 1, int MF = 32>
 __global__ __launch_bounds__(64 * NW, 1) void gemm_fast_kernel(Args a) {
     static_assert(NW == 4 || (NW == 8 && KIND != kMX), "8 waves: bf16 only");
     static_assert(MF == 32 || (MF == 16 && KIND != kMX && LA == 1),
-                  "16 x 16 MFMAs: plain bf16 products, 4 waves");
+                  "16 x 16 MFMAs: bf16, one fragment step of lookahead");
     static_assert(!SPLIT || (!FUSED && NW == 4), "split-K: plain fp32 partial stores, 4 waves");
     static_assert(!SPLIT || KIND != kMX || SG > 1, "MX split-K: the scale-ring pipeline");
     static_assert(!DYN || (!SPLIT && NW == 4), "dynamic schedule: whole tiles, 4 waves");

@@ -862,8 +862,8 @@ fast::Args make_fast_args(int64_t M, int64_t N, int64_t K, const void* A, int64_
 int launch_fast_bf16(bool nt, const fast::Args& a, int cus, hipStream_t s) {
     const FastVariant v = env_variant();
     const int g = v.group;
-    // fused epilogue: the default pipelines only (the variants below are
-    // measurement switches of the plain product)
+    // fused epilogue: the default pipeline (in measurement builds the MF
+    // switch applies; the other variants below are of the plain product)
     if (a.epi.on) {
         if (nt) return launch_bf16_16<fast::kNT, true>(a, cus, s, g);
         return launch_bf16_16<fast::kNN, true>(a, cus, s, g);
@@ -871,8 +871,10 @@ int launch_fast_bf16(bool nt, const fast::Args& a, int cus, hipStream_t s) {
     if (nt) {
 #ifdef LIBGEMM_MEASURE
         if (v.rb == 64 && v.stages == 4) return launch_fast<fast::kNT, 64, 4>(a, cus, s, g);
-        // 8 waves (two per SIMD, 128 x 64 wave tiles): measured 1% slower
-        // than 4 waves at 8192^3 on MI355X; kept for measurements
+        // 8 waves (two per SIMD, 128 x 64 wave tiles), kept for
+        // measurements: at 8192^3 on MI355X the 32 x 32 form measured 1%
+        // slower than its 4-wave form, the 16 x 16 form 2.7% slower (1.5x
+        // the LDS fragment reads)
         if (v.waves == 8 && v.mfma == 32) return launch_fast<fast::kNT, 128, 2, 1, 4, 2, 8>(a, cus, s, g);
         if (v.waves == 8) return launch_w8_16<fast::kNT>(a, cus, s, g);
         if (v.early == 0) return launch_fast<fast::kNT, 128, 2>(a, cus, s, g);
