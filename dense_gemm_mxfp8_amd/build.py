@@ -14,6 +14,7 @@ a kernel variant are live (the product library has none).  ``bench.py
 """
 from __future__ import annotations
 
+import concurrent.futures
 import os
 import subprocess
 
@@ -56,11 +57,17 @@ def build(verbose: bool = False, only=None, measure: bool = False) -> str:
     os.makedirs(os.path.dirname(_object(SOURCES[0], measure)), exist_ok=True)
     defines = ["-DLIBGEMM_MEASURE"] if measure else []
     todo = SOURCES if only is None else [s for s in SOURCES if os.path.basename(s) in only]
-    for src in todo:
+
+    def compile_one(src):
         obj = _object(src, measure)
         extra = SOURCE_FLAGS.get(os.path.basename(src), [])
         _run([hipcc, *HIPCC_FLAGS, *extra, *defines, f"-I{INCLUDE}", "-c", src, "-o", obj + ".tmp"], verbose)
         os.replace(obj + ".tmp", obj)
+
+    # the translation units compile independently (each hipcc is one process)
+    with concurrent.futures.ThreadPoolExecutor(max_workers=max(1, min(len(todo), os.cpu_count() or 1))) as pool:
+        for f in [pool.submit(compile_one, src) for src in todo]:
+            f.result()
     out = MEASURE_LIBRARY if measure else LIBRARY
     tmp = out + ".tmp"
     _run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", *[_object(s, measure) for s in SOURCES], "-o", tmp],
