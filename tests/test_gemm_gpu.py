@@ -179,9 +179,11 @@ def test_tensor_helper_layouts():
 # ---------------------------------------------------------------- fast (256 x 256) path
 
 # Shapes large enough for the 256 x 256 kernel (enough tiles for every CU),
-# with partial tiles in M and N and a partial last k-tile.
+# with partial tiles in M and N and a partial last k-tile; K = 40 and 24 are
+# shorter than one k-tile (no pipelined k-tile, only the tail).
 FAST_BF16 = [(4096 + 77, 4096 + 133, 513, True), (4096 + 77, 4096 + 8, 520, False),
-             (4096 + 200, 4096 + 64, 1000, True), (4096, 4096, 256, False)]
+             (4096 + 200, 4096 + 64, 1000, True), (4096, 4096, 256, False),
+             (4096 + 77, 4096 + 136, 40, True), (4096 + 77, 4096 + 8, 24, False)]
 
 
 @pytest.mark.parametrize("case", FAST_BF16, ids=lambda c: f"{c[0]}x{c[1]}x{c[2]}_{'nt' if c[3] else 'nn'}")
