@@ -156,12 +156,13 @@ def test_fused_generic_kernel(shape, out, which, exact):
 
 
 # (M, N, K, b_colmajor): 256 x 256 direct-load tiles with partial tiles and a
-# partial last k-tile, the register-load kernel on 2-byte aligned rows with
-# 192-column tiles, and the small-M kernel; every output against the oracle.
+# partial last k-tile (and with K = 40, only that), the register-load kernel on
+# 2-byte aligned rows with 192-column tiles, and the small-M kernel; every
+# output against the oracle.
 # Cases of one shape and distribution run in a row so that they share one
 # oracle product.
 BIG = [(4096 + 77, 4096 + 133, 520, True), (4096 + 77, 4096 + 8, 520, False), (4001, 3003, 2050, False),
-       (16, 4096, 776, False)]
+       (16, 4096, 776, False), (4096 + 77, 4096 + 136, 40, True)]
 OUTS = ["f32", "bf16", "e4m3"]
 BIG_CASES = [(shape, exact, out) for shape in BIG for exact in (True, False) for out in OUTS]
 
