@@ -132,8 +132,10 @@ def test_splitk_long_k_sampled():
 
 
 @pytest.mark.parametrize("out", ["f32", "bf16", "e4m3"])
-def test_splitk_fused_epilogue(out):
-    M, N, K = 700, 600, 2048
+@pytest.mark.parametrize("shape", [(700, 600, 2048), (24, 600, 2048)], ids=lambda s: f"{s[0]}x{s[1]}x{s[2]}")
+def test_splitk_fused_epilogue(out, shape):
+    """The epilogue applied once, after the reduction, on the 16 x 16 and (M <= 32) the 32 x 32 partial instance."""
+    M, N, K = shape
     prob = _prob(M, N, K, True, True, seed=86)
     g = np.random.default_rng(87)
     rs = np.exp2(g.integers(-2, 3, size=M)).astype(np.float32)
